@@ -1,0 +1,329 @@
+"""Plain CPU oracle of the forward DISCO convolution on the 2-sphere.
+
+TEST INFRASTRUCTURE.  Only the tests, the package's smoke check and the
+benchmark's CPU-baseline leg may import this module.  The product path (the
+C-ABI library and its Python binding) never calls it, and it imports nothing
+from the product.  It is slow on purpose: every step is the definition written
+out in float64, in the order the pages state it, so that a reader can check it
+by eye.
+
+What it computes (torch_harmonics.DiscreteContinuousConvS2 page, forward
+equation and the paragraph after it):
+
+    g[b, co, j, q] = sum_{ci, k} w[co, ci, k]
+                     * sum_{(i, p)} Psi[k, j, (i, p)] * f[b, ci, i, (q*s + p) mod nlon_in]
+
+with s = nlon_in / nlon_out.  Psi holds the filter-basis values at the input
+grid points seen from the output point (theta'_j, 0) after rotating that point
+to the north pole, times the quadrature weights; it does not depend on the
+output longitude (the p-shift symmetry stated on the same page).
+
+Points the pages leave open, and the reading taken here:
+
+* grid: equiangular colatitudes theta_i = pi*i/(nlat-1), both poles included;
+  longitudes lambda_p = 2*pi*p/nlon;
+* quadrature: Clenshaw-Curtis weights in cos(theta) times 2*pi/nlon_in;
+* rotation: about the y axis by -theta'_j, so (theta'_j, 0) goes to the pole;
+  r is the polar angle after the rotation, alpha its azimuth, alpha = 0 points
+  to local south (+theta) and alpha = pi/2 to local east (+lambda);
+* support: r < theta_cutoff * (1 - 1e-10); points at r = theta_cutoff are out;
+* basis (piecewise linear): radial hats phi_n(r) = max(0, 1 - |r - n*D|/D),
+  D = theta_cutoff/(nr-1); nr = 1 is the cap indicator.  Isotropic
+  kernel_shape (nr,) has K = nr.  Anisotropic (nr, nphi) has
+  K = 1 + (nr-1)*nphi: phi_0, then phi_n * psi_m, radial index major, with
+  periodic azimuthal hats psi_m(alpha) of width 2*pi/nphi centred at
+  2*pi*m/nphi; nphi = 1 means psi = 1;
+* no basis normalisation, no bias;
+* default theta_cutoff (when None): (nr+1)*pi/(nlat_out-1);
+* weight layout [Co, Ci/groups, K].
+
+Parity pins for every function live in tests/test_oracle_*.py.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+
+import numpy as np
+
+TIE_REL = 1e-10
+
+
+# --------------------------------------------------------------------------
+# Problem description
+# --------------------------------------------------------------------------
+@dataclass(frozen=True)
+class Desc:
+    """Shapes and basis of one DISCO layer (same fields as the layer's
+    constructor on the DiscreteContinuousConvS2 page: in_shape, out_shape,
+    kernel_shape, theta_cutoff; grids are equiangular)."""
+    nlat_in: int
+    nlon_in: int
+    nlat_out: int
+    nlon_out: int
+    kernel_shape: tuple
+    theta_cutoff: float | None = None
+
+    @property
+    def nr(self) -> int:
+        return int(self.kernel_shape[0])
+
+    @property
+    def nphi(self) -> int:
+        return int(self.kernel_shape[1]) if len(self.kernel_shape) > 1 else 0
+
+    @property
+    def K(self) -> int:
+        return num_basis(self.kernel_shape)
+
+    @property
+    def stride(self) -> int:
+        return self.nlon_in // self.nlon_out
+
+    @property
+    def cutoff(self) -> float:
+        if self.theta_cutoff is None:
+            return (self.nr + 1) * math.pi / (self.nlat_out - 1)
+        return float(self.theta_cutoff)
+
+
+def num_basis(kernel_shape) -> int:
+    """Number of basis functions K for a piecewise-linear kernel_shape."""
+    nr = int(kernel_shape[0])
+    if len(kernel_shape) == 1:
+        return nr
+    nphi = int(kernel_shape[1])
+    return 1 + (nr - 1) * nphi
+
+
+# --------------------------------------------------------------------------
+# Grid and quadrature
+# --------------------------------------------------------------------------
+def colatitudes(nlat: int) -> np.ndarray:
+    """Equiangular colatitudes including both poles."""
+    return np.array([math.pi * i / (nlat - 1) for i in range(nlat)], dtype=np.float64)
+
+
+def longitudes(nlon: int) -> np.ndarray:
+    """Equispaced longitudes 2*pi*p/nlon."""
+    return np.array([2.0 * math.pi * p / nlon for p in range(nlon)], dtype=np.float64)
+
+
+def clenshaw_curtis_weights(nlat: int) -> np.ndarray:
+    """Clenshaw-Curtis weights for nodes cos(theta_i), integrating over [-1, 1].
+
+    Closed form of Clenshaw and Curtis (1960): with n = nlat - 1,
+    w_i = (c_i/n) * (1 - sum_{k=1}^{n//2} b_k/(4k^2-1) * cos(2k theta_i)),
+    c_0 = c_n = 1, c_i = 2 otherwise, b_k = 1 if 2k = n else 2.
+    """
+    n = nlat - 1
+    theta = colatitudes(nlat)
+    w = np.zeros(nlat, dtype=np.float64)
+    for i in range(nlat):
+        acc = 0.0
+        for k in range(1, n // 2 + 1):
+            b = 1.0 if 2 * k == n else 2.0
+            acc += b / (4.0 * k * k - 1.0) * math.cos(2.0 * k * theta[i])
+        c = 1.0 if i in (0, n) else 2.0
+        w[i] = c / n * (1.0 - acc)
+    return w
+
+
+def quadrature_weights(nlat: int, nlon: int) -> np.ndarray:
+    """Per-point spherical quadrature weight of latitude row i (sums to 4*pi
+    over the whole grid): Clenshaw-Curtis in cos(theta) times 2*pi/nlon."""
+    return clenshaw_curtis_weights(nlat) * (2.0 * math.pi / nlon)
+
+
+# --------------------------------------------------------------------------
+# Geometry: input points seen from an output point rotated to the pole
+# --------------------------------------------------------------------------
+def rotated_coordinates(theta_out: float, theta_in: np.ndarray, lam: np.ndarray):
+    """Polar angle r and azimuth alpha of input points (theta_in, lam) after
+    the rotation that takes the output point (theta_out, 0) to the north pole.
+
+    The rotation is about the y axis by -theta_out.  alpha = 0 is local south
+    (+theta), alpha = pi/2 local east (+lambda).  Returns arrays shaped like
+    the broadcast of theta_in and lam.
+    """
+    theta_in, lam = np.broadcast_arrays(np.asarray(theta_in, np.float64),
+                                        np.asarray(lam, np.float64))
+    x = np.sin(theta_in) * np.cos(lam)
+    y = np.sin(theta_in) * np.sin(lam)
+    z = np.cos(theta_in)
+    ct, st = math.cos(theta_out), math.sin(theta_out)
+    xr = x * ct - z * st
+    yr = y
+    zr = x * st + z * ct
+    r = np.arctan2(np.sqrt(xr * xr + yr * yr), zr)
+    alpha = np.mod(np.arctan2(yr, xr), 2.0 * math.pi)
+    return r, alpha
+
+
+# --------------------------------------------------------------------------
+# Piecewise-linear filter basis
+# --------------------------------------------------------------------------
+def radial_hat(n: int, nr: int, cutoff: float, r: np.ndarray) -> np.ndarray:
+    """phi_n(r): hat of half-width D = cutoff/(nr-1) centred at n*D.
+    For nr = 1 the single radial function is the cap indicator (value 1)."""
+    if nr == 1:
+        return np.ones_like(r)
+    d = cutoff / (nr - 1)
+    return np.maximum(0.0, 1.0 - np.abs(r - n * d) / d)
+
+
+def azimuthal_hat(m: int, nphi: int, alpha: np.ndarray) -> np.ndarray:
+    """psi_m(alpha): periodic hat of half-width 2*pi/nphi centred at
+    2*pi*m/nphi (circular distance); identically 1 when nphi = 1."""
+    if nphi == 1:
+        return np.ones_like(alpha)
+    width = 2.0 * math.pi / nphi
+    diff = np.mod(alpha - m * width, 2.0 * math.pi)
+    dist = np.minimum(diff, 2.0 * math.pi - diff)
+    return np.maximum(0.0, 1.0 - dist / width)
+
+
+def basis_values(kernel_shape, cutoff: float, r: np.ndarray, alpha: np.ndarray) -> np.ndarray:
+    """All K basis functions at the points (r, alpha); shape [K, npoints]."""
+    nr = int(kernel_shape[0])
+    r = np.asarray(r, np.float64)
+    alpha = np.asarray(alpha, np.float64)
+    if len(kernel_shape) == 1:
+        return np.stack([radial_hat(n, nr, cutoff, r) for n in range(nr)])
+    nphi = int(kernel_shape[1])
+    rows = [radial_hat(0, nr, cutoff, r)]
+    for n in range(1, nr):
+        for m in range(nphi):
+            rows.append(radial_hat(n, nr, cutoff, r) * azimuthal_hat(m, nphi, alpha))
+    return np.stack(rows)
+
+
+# --------------------------------------------------------------------------
+# Psi: the sparse convolution tensor, canonical per-output-row CSR
+# --------------------------------------------------------------------------
+@dataclass
+class PsiCSR:
+    """Psi[k, j, (i, p)] as CSR over output rows j.
+
+    row_ptr [nlat_out+1] int64; in_lat, lon_off [nnz] int32 (input row i and
+    longitude offset p of each support point, sorted by (i, p)); vals [nnz, K]
+    float64 (all K values per support point, zeros kept).
+    """
+    row_ptr: np.ndarray
+    in_lat: np.ndarray
+    lon_off: np.ndarray
+    vals: np.ndarray
+
+    @property
+    def nnz(self) -> int:
+        return int(self.row_ptr[-1])
+
+
+def psi_row(desc: Desc, j: int, omega: np.ndarray | None = None):
+    """Support points and values of output row j: (in_lat, lon_off, vals).
+    `omega` may pass in quadrature_weights(nlat_in, nlon_in) to save time."""
+    cutoff = desc.cutoff
+    theta_in = colatitudes(desc.nlat_in)
+    theta_out = colatitudes(desc.nlat_out)[j]
+    lam = longitudes(desc.nlon_in)
+    if omega is None:
+        omega = quadrature_weights(desc.nlat_in, desc.nlon_in)
+    lat_list, lon_list, val_list = [], [], []
+    for i in range(desc.nlat_in):
+        # r >= |theta_i - theta'_j|, so rows farther away cannot be in the cap
+        if abs(theta_in[i] - theta_out) > cutoff:
+            continue
+        r, alpha = rotated_coordinates(theta_out, np.full(desc.nlon_in, theta_in[i]), lam)
+        inside = r < cutoff * (1.0 - TIE_REL)
+        p = np.nonzero(inside)[0]
+        if p.size == 0:
+            continue
+        vals = basis_values(desc.kernel_shape, cutoff, r[p], alpha[p]).T * omega[i]
+        lat_list.append(np.full(p.size, i, dtype=np.int32))
+        lon_list.append(p.astype(np.int32))
+        val_list.append(vals)
+    if not lat_list:
+        return (np.zeros(0, np.int32), np.zeros(0, np.int32), np.zeros((0, desc.K)))
+    return (np.concatenate(lat_list), np.concatenate(lon_list), np.concatenate(val_list))
+
+
+def psi(desc: Desc) -> PsiCSR:
+    """The whole Psi tensor as canonical CSR (sorted by j, then i, then p)."""
+    row_ptr = np.zeros(desc.nlat_out + 1, dtype=np.int64)
+    omega = quadrature_weights(desc.nlat_in, desc.nlon_in)
+    lats, lons, vals = [], [], []
+    for j in range(desc.nlat_out):
+        a, b, v = psi_row(desc, j, omega)
+        lats.append(a)
+        lons.append(b)
+        vals.append(v)
+        row_ptr[j + 1] = row_ptr[j] + a.size
+    return PsiCSR(row_ptr, np.concatenate(lats).astype(np.int32),
+                  np.concatenate(lons).astype(np.int32),
+                  np.concatenate(vals).reshape(-1, desc.K))
+
+
+# --------------------------------------------------------------------------
+# The two sums of the forward equation
+# --------------------------------------------------------------------------
+def contract_row(desc: Desc, x: np.ndarray, row) -> np.ndarray:
+    """Inner sum of the forward equation for one output row j:
+    X_K[b, ci, k, q] = sum_{(i,p) in row j} Psi[k, j, (i,p)] * x[b, ci, i, (q*s+p) mod nlon_in].
+
+    `row` is (in_lat, lon_off, vals) from psi_row; x is [B, Ci, nlat_in, nlon_in].
+    Accumulates support points one at a time in canonical order, so every
+    output longitude sees the same summation order.
+    """
+    in_lat, lon_off, vals = row
+    x = np.asarray(x, dtype=np.float64)
+    B, C = x.shape[:2]
+    q = np.arange(desc.nlon_out)
+    out = np.zeros((B, C, desc.K, desc.nlon_out), dtype=np.float64)
+    for e in range(in_lat.size):
+        cols = (q * desc.stride + int(lon_off[e])) % desc.nlon_in
+        xs = x[:, :, int(in_lat[e]), :][:, :, cols]                # [B, C, nlon_out]
+        out += vals[e][None, None, :, None] * xs[:, :, None, :]
+    return out
+
+
+def contract(desc: Desc, x: np.ndarray, csr: PsiCSR | None = None, rows=None) -> np.ndarray:
+    """X_K[b, ci, k, j, q] for the output rows `rows` (default: all rows).
+    Shape [B, Ci, K, len(rows), nlon_out]."""
+    if rows is None:
+        rows = range(desc.nlat_out)
+    rows = list(rows)
+    x = np.asarray(x, dtype=np.float64)
+    out = np.zeros((x.shape[0], x.shape[1], desc.K, len(rows), desc.nlon_out))
+    omega = None if csr is not None else quadrature_weights(desc.nlat_in, desc.nlon_in)
+    for jj, j in enumerate(rows):
+        if csr is not None:
+            a, b = int(csr.row_ptr[j]), int(csr.row_ptr[j + 1])
+            row = (csr.in_lat[a:b], csr.lon_off[a:b], csr.vals[a:b])
+        else:
+            row = psi_row(desc, j, omega)
+        out[:, :, :, jj, :] = contract_row(desc, x, row)
+    return out
+
+
+def einsum(xk: np.ndarray, w: np.ndarray, groups: int) -> np.ndarray:
+    """Outer sums of the forward equation:
+    g[b, co, j, q] = sum_{ci' < Ci/G} sum_k w[co, ci', k] * X_K[b, G(co)*Ci/G + ci', k, j, q],
+    G(co) = co // (Co/G).  xk is [B, Ci, K, H, W], w is [Co, Ci/G, K]."""
+    xk = np.asarray(xk, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    B, Ci, K, H, W = xk.shape
+    Co = w.shape[0]
+    cig, cog = Ci // groups, Co // groups
+    g = np.zeros((B, Co, H, W), dtype=np.float64)
+    for grp in range(groups):
+        xs = xk[:, grp * cig:(grp + 1) * cig]                     # [B, cig, K, H, W]
+        ws = w[grp * cog:(grp + 1) * cog]                           # [cog, cig, K]
+        g[:, grp * cog:(grp + 1) * cog] = np.einsum("oik,bikhw->bohw", ws, xs)
+    return g
+
+
+def forward(desc: Desc, x: np.ndarray, w: np.ndarray, groups: int = 1,
+            csr: PsiCSR | None = None, rows=None) -> np.ndarray:
+    """The forward DISCO convolution g [B, Co, len(rows), nlon_out] in float64,
+    for the output rows `rows` (default all)."""
+    return einsum(contract(desc, x, csr=csr, rows=rows), w, groups)

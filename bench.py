@@ -1,0 +1,220 @@
+"""Benchmark of the forward DISCO convolution on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c4] [--no-cpu-baseline]
+
+A step is one forward pass (the fused kernel: contraction and channel/basis
+contraction in one launch) over one batch of seeded synthetic input that is
+resident in device memory before timing starts.  Psi is built once before
+the timed region (it is a precomputed tensor of the layer).  The unfused pair
+(contraction writing the K-expanded tensor, then the channel/basis GEMM) is
+timed alongside and reported as extra fields.
+
+Prints one JSON line.  `value` is output points x output channels per second.
+`roofline` prices the fused kernel's algorithmic work (channel/basis FLOPs
+plus 2 FLOPs per non-zero Psi entry, channel and output longitude) against
+the MI355X dense bf16 matrix peak (2.5 PFLOP/s) or, for float32 workloads,
+the float32 peak (157.3 TFLOP/s).  `cpu_baseline` is the float64 CPU oracle
+timed on a bounded sample of output rows of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
+HBM_PEAK_GBS = 8000.0
+
+# rocprofv3 HBM counters of the fused kernel at the headline workload, per
+# launch (FETCH_SIZE + WRITE_SIZE, scaled by the copy-kernel calibration);
+# None until measured for the current kernel.
+MEASURED_TRAFFIC_BYTES = {}
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=None, help="c1..c5 (default: the headline case c4)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-unfused", action="store_true")
+    ap.add_argument("--fused-only", action="store_true", help="time only the fused kernel (profiling)")
+    return ap.parse_args()
+
+
+def algorithmic_flops(wl, nnz_nonzero):
+    """Channel/basis FLOPs + 2 per non-zero Psi entry per channel and output longitude."""
+    f_einsum = 2.0 * wl.B * wl.Co * (wl.Ci // wl.groups) * wl.K * wl.nlat_out * wl.nlon_out
+    f_contr = 2.0 * wl.B * wl.Ci * wl.nlon_out * nnz_nonzero
+    return f_einsum, f_contr
+
+
+def algorithmic_bytes(wl, nnz_support, dsize):
+    x = wl.B * wl.Ci * wl.nlat_in * wl.nlon_in * dsize
+    w = wl.Co * (wl.Ci // wl.groups) * wl.K * dsize
+    psi = nnz_support * (8 + 4 * wl.K)
+    y = wl.B * wl.Co * wl.nlat_out * wl.nlon_out * 4
+    return x + w + psi + y
+
+
+def time_region(fn, steps, torch):
+    """Wall time and HIP-event time of `steps` calls of fn on the current stream."""
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(steps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall, e0.elapsed_time(e1) / 1000.0
+
+
+def cpu_baseline(wl, x, w):
+    import numpy as np
+    import oracle
+    d = oracle.Desc(wl.nlat_in, wl.nlon_in, wl.nlat_out, wl.nlon_out, wl.kernel_shape,
+                    wl.theta_cutoff)
+    csr = oracle.psi(d)
+    # systematic sample of output rows, all longitudes, batches and channels
+    step = max(1, wl.nlat_out // 12)
+    rows = list(range(step // 2, wl.nlat_out, step))
+    sup = sum(int(csr.row_ptr[j + 1] - csr.row_ptr[j]) for j in rows)
+    t0 = time.perf_counter()
+    oracle.forward(d, x, w, wl.groups, csr=csr, rows=rows)
+    dt = time.perf_counter() - t0
+    pts = wl.B * len(rows) * wl.nlon_out * wl.Co
+    return {
+        "value": pts / dt,
+        "unit": "output-points*Cout/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": (f"{len(rows)} of {wl.nlat_out} output rows (every {step}th from {step // 2}), "
+                   f"all longitudes, batches and channels; {sup / len(rows):.0f} support points "
+                   f"per sampled row vs {csr.nnz / wl.nlat_out:.0f} over all rows; "
+                   f"float64 numpy, single thread; {dt:.1f} s"),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 "
+                          "(multi-GPU sharding is described, not implemented)"}), flush=True)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import spherical_disco_convolution_amd as sdc
+    from disco_workloads import HEADLINE, WORKLOADS, draw_inputs, round_bf16
+
+    key = args.workload or HEADLINE
+    wl = WORKLOADS[key]
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}), flush=True)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+
+    x, w = draw_inputs(wl)
+    if wl.dtype == "bf16":
+        x, w = round_bf16(x), round_bf16(w)
+    tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    xd = torch.from_numpy(x).cuda().to(tdt).contiguous()
+    wd = torch.from_numpy(w).cuda().to(tdt).contiguous()
+
+    t0 = time.perf_counter()
+    psi = sdc.psi_build(wl.nlat_in, wl.nlon_in, wl.nlat_out, wl.nlon_out, wl.kernel_shape,
+                        wl.theta_cutoff)
+    psi_build_s = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    psi.to_device()
+    torch.cuda.synchronize()
+    psi_upload_s = time.perf_counter() - t0
+
+    y = torch.empty((wl.B, wl.Co, wl.nlat_out, wl.nlon_out), dtype=torch.float32, device="cuda")
+    fused = lambda: sdc.fused_fwd(psi, xd, wd, groups=wl.groups, y=y)
+
+    for _ in range(args.warmup):
+        fused()
+    torch.cuda.synchronize()
+    wall, ev = time_region(fused, args.steps, torch)
+    ms_per_step = wall / args.steps * 1000.0
+    kernel_s = ev / args.steps
+    work = wl.out_points_cout
+    value = work / (ms_per_step / 1000.0)
+
+    f_einsum, f_contr = algorithmic_flops(wl, psi.nnz_nonzero)
+    f_alg = f_einsum + f_contr
+    cig = wl.Ci // wl.groups
+    if cig == 1:
+        # one input channel per group: weights fold into the taps per channel
+        f_folded = 2.0 * wl.B * wl.Co * wl.nlon_out * psi.nnz + 2.0 * wl.Co * psi.nnz_nonzero
+        f_alg = min(f_alg, f_folded)
+    dsize = 2 if wl.dtype == "bf16" else 4
+    peak = PEAK_TFLOPS[wl.dtype]
+    achieved = f_alg / kernel_s / 1e12
+    traffic = MEASURED_TRAFFIC_BYTES.get(key)
+    roofline = {"bound": "mfma" if wl.dtype == "bf16" else "alu", "achieved": round(achieved, 3),
+                "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                "traffic": traffic}
+    extra = {
+        "fused_kernel_ms": round(kernel_s * 1000, 4),
+        "algorithmic_flop": f_alg,
+        "algorithmic_bytes": algorithmic_bytes(wl, psi.nnz, dsize),
+        "hbm_GBps_algorithmic": round(algorithmic_bytes(wl, psi.nnz, dsize) / kernel_s / 1e9, 1),
+        "psi_build_s": round(psi_build_s, 3),
+        "psi_upload_s": round(psi_upload_s, 3),
+    }
+    if not args.no_unfused and not args.fused_only:
+        xk = torch.empty((wl.B, wl.Ci, wl.K, wl.nlat_out, wl.nlon_out), dtype=tdt, device="cuda")
+        contract = lambda: sdc.contract(psi, xd, xk=xk)
+        einsum = lambda: sdc.einsum(xk, wd, groups=wl.groups, y=y)
+        for _ in range(2):
+            contract()
+            einsum()
+        n = max(3, args.steps // 2)
+        _, t_c = time_region(contract, n, torch)
+        _, t_e = time_region(einsum, n, torch)
+        extra["contract_ms"] = round(t_c / n * 1000, 4)
+        extra["einsum_ms"] = round(t_e / n * 1000, 4)
+        extra["unfused_ms"] = round((t_c + t_e) / n * 1000, 4)
+        del xk
+    line = {
+        "metric": "DISCO fwd output-points*Cout/s at 721x1440 C=128 K=7",
+        "value": value,
+        "unit": "output-points*Cout/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded N(0,1) input, N(0,1/(Ci*K)) weights)",
+        "config": {"workload": f"{key}: B={wl.B} Ci={wl.Ci} Co={wl.Co} groups={wl.groups} "
+                               f"{wl.nlat_in}x{wl.nlon_in}->{wl.nlat_out}x{wl.nlon_out} "
+                               f"kernel_shape={wl.kernel_shape} K={wl.K} "
+                               f"theta_cutoff={wl.theta_cutoff:.6f} {wl.dtype}, fused forward",
+                   "global_batch": wl.B, "parallelism": "single GPU"},
+        "roofline": roofline,
+    }
+    line.update(extra)
+    if not args.no_cpu_baseline and not args.fused_only:
+        line["cpu_baseline"] = cpu_baseline(wl, x, w)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -266,34 +266,38 @@ def psi(desc: Desc) -> PsiCSR:
 # --------------------------------------------------------------------------
 # The two sums of the forward equation
 # --------------------------------------------------------------------------
-def contract_row(desc: Desc, x: np.ndarray, row) -> np.ndarray:
+def contract_row(desc: Desc, x: np.ndarray, row, cols_out=None) -> np.ndarray:
     """Inner sum of the forward equation for one output row j:
     X_K[b, ci, k, q] = sum_{(i,p) in row j} Psi[k, j, (i,p)] * x[b, ci, i, (q*s+p) mod nlon_in].
 
     `row` is (in_lat, lon_off, vals) from psi_row; x is [B, Ci, nlat_in, nlon_in].
-    Accumulates support points one at a time in canonical order, so every
-    output longitude sees the same summation order.
+    `cols_out` optionally restricts q to a list of output longitudes (default:
+    all).  Accumulates support points one at a time in canonical order, so
+    every output longitude sees the same summation order.
     """
     in_lat, lon_off, vals = row
     x = np.asarray(x, dtype=np.float64)
     B, C = x.shape[:2]
-    q = np.arange(desc.nlon_out)
-    out = np.zeros((B, C, desc.K, desc.nlon_out), dtype=np.float64)
+    q = np.arange(desc.nlon_out) if cols_out is None else np.asarray(cols_out, dtype=np.int64)
+    out = np.zeros((B, C, desc.K, q.size), dtype=np.float64)
     for e in range(in_lat.size):
         cols = (q * desc.stride + int(lon_off[e])) % desc.nlon_in
-        xs = x[:, :, int(in_lat[e]), :][:, :, cols]                # [B, C, nlon_out]
+        xs = x[:, :, int(in_lat[e]), :][:, :, cols]                # [B, C, len(q)]
         out += vals[e][None, None, :, None] * xs[:, :, None, :]
     return out
 
 
-def contract(desc: Desc, x: np.ndarray, csr: PsiCSR | None = None, rows=None) -> np.ndarray:
-    """X_K[b, ci, k, j, q] for the output rows `rows` (default: all rows).
-    Shape [B, Ci, K, len(rows), nlon_out]."""
+def contract(desc: Desc, x: np.ndarray, csr: PsiCSR | None = None, rows=None,
+             cols_out=None) -> np.ndarray:
+    """X_K[b, ci, k, j, q] for the output rows `rows` (default: all rows) and
+    output longitudes `cols_out` (default: all).
+    Shape [B, Ci, K, len(rows), len(cols_out)]."""
     if rows is None:
         rows = range(desc.nlat_out)
     rows = list(rows)
+    nq = desc.nlon_out if cols_out is None else len(cols_out)
     x = np.asarray(x, dtype=np.float64)
-    out = np.zeros((x.shape[0], x.shape[1], desc.K, len(rows), desc.nlon_out))
+    out = np.zeros((x.shape[0], x.shape[1], desc.K, len(rows), nq))
     omega = None if csr is not None else quadrature_weights(desc.nlat_in, desc.nlon_in)
     for jj, j in enumerate(rows):
         if csr is not None:
@@ -301,7 +305,7 @@ def contract(desc: Desc, x: np.ndarray, csr: PsiCSR | None = None, rows=None) ->
             row = (csr.in_lat[a:b], csr.lon_off[a:b], csr.vals[a:b])
         else:
             row = psi_row(desc, j, omega)
-        out[:, :, :, jj, :] = contract_row(desc, x, row)
+        out[:, :, :, jj, :] = contract_row(desc, x, row, cols_out)
     return out
 
 
@@ -323,7 +327,12 @@ def einsum(xk: np.ndarray, w: np.ndarray, groups: int) -> np.ndarray:
 
 
 def forward(desc: Desc, x: np.ndarray, w: np.ndarray, groups: int = 1,
-            csr: PsiCSR | None = None, rows=None) -> np.ndarray:
-    """The forward DISCO convolution g [B, Co, len(rows), nlon_out] in float64,
-    for the output rows `rows` (default all)."""
-    return einsum(contract(desc, x, csr=csr, rows=rows), w, groups)
+            csr: PsiCSR | None = None, rows=None, cols_out=None,
+            bias: np.ndarray | None = None) -> np.ndarray:
+    """The forward DISCO convolution g [B, Co, len(rows), len(cols_out)] in
+    float64, for the output rows `rows` and longitudes `cols_out` (default
+    all), plus bias[co] when given (the layer's `bias` parameter)."""
+    g = einsum(contract(desc, x, csr=csr, rows=rows, cols_out=cols_out), w, groups)
+    if bias is not None:
+        g = g + np.asarray(bias, dtype=np.float64)[None, :, None, None]
+    return g

@@ -1,0 +1,299 @@
+"""Python binding of libdisco.so, the gfx950 forward DISCO convolution on S^2.
+
+Thin ctypes layer: it marshals torch tensors (device memory and the current
+HIP stream) into the C-ABI calls declared in include/disco.h and turns status
+codes into exceptions.  All arithmetic runs in the library's HIP kernels;
+there is no Python or CPU fallback, and importing fails loudly when the
+library is missing.
+
+Entry points (same names as the C ABI, without the ``disco_`` prefix):
+    psi_build(...)      -> Psi          host float64 build of the sparse tensor
+    contract(psi, x)    -> xk           [B, C, K, nlat_out, nlon_out]
+    einsum(xk, w, ...)  -> y            [B, Co, nlat_out, nlon_out]
+    fused_fwd(psi, x, w, ...) -> y      same result without storing xk
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdisco.so")
+
+DISCO_OK = 0
+DISCO_EINVAL = -1
+DISCO_EUNSUPPORTED = -2
+DISCO_ENOMEM = -3
+DISCO_EHIP = -4
+
+F32 = 0
+BF16 = 1
+
+GRIDS = {"equiangular": 0}
+BASES = {"piecewise linear": 0}
+NORMS = {"none": 0}
+
+
+class _Desc(ctypes.Structure):
+    _fields_ = [
+        ("nlat_in", ctypes.c_int32), ("nlon_in", ctypes.c_int32),
+        ("nlat_out", ctypes.c_int32), ("nlon_out", ctypes.c_int32),
+        ("grid_in", ctypes.c_int32), ("grid_out", ctypes.c_int32),
+        ("basis_type", ctypes.c_int32), ("basis_norm", ctypes.c_int32),
+        ("kernel_shape", ctypes.c_int32 * 2),
+        ("theta_cutoff", ctypes.c_double),
+    ]
+
+
+def _load():
+    # PyTorch ships its own HIP runtime (SONAME libamdhip64.so.7).  Loading
+    # torch first makes libdisco.so bind to that same runtime, so the device
+    # pointers and stream handles torch hands over are valid in the library.
+    # Loading libdisco.so first would pull in a second HIP runtime.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with "
+            "`python -m spherical_disco_convolution_amd.build_lib` (hipcc, gfx950)")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, D = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_double
+    sig = {
+        "disco_psi_build": (ctypes.c_int, [ctypes.POINTER(_Desc), ctypes.POINTER(P)]),
+        "disco_psi_query": (ctypes.c_int, [P, ctypes.POINTER(I32), ctypes.POINTER(I64),
+                                           ctypes.POINTER(I64), ctypes.POINTER(D)]),
+        "disco_psi_export": (ctypes.c_int, [P, P, P, P, P]),
+        "disco_psi_to_device": (ctypes.c_int, [P]),
+        "disco_psi_free": (None, [P]),
+        "disco_contract": (ctypes.c_int, [P, P, ctypes.c_int, P, ctypes.c_int, I32, I32, P]),
+        "disco_einsum": (ctypes.c_int, [P, ctypes.c_int, P, ctypes.c_int, P, P, ctypes.c_int,
+                                        I32, I32, I32, I32, I32, I32, I32, P]),
+        "disco_fused_fwd": (ctypes.c_int, [P, P, ctypes.c_int, P, ctypes.c_int, P, P,
+                                           ctypes.c_int, I32, I32, I32, I32, P]),
+        "disco_last_error": (ctypes.c_char_p, []),
+        "disco_version": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+_lib = _load()
+EXPORTED = ("disco_psi_build", "disco_psi_query", "disco_psi_export", "disco_psi_to_device",
+            "disco_psi_free", "disco_contract", "disco_einsum", "disco_fused_fwd",
+            "disco_last_error", "disco_version")
+
+
+def version() -> str:
+    return _lib.disco_version().decode()
+
+
+def _check(rc: int, what: str):
+    if rc == DISCO_OK:
+        return
+    msg = f"{what}: {_lib.disco_last_error().decode()}"
+    if rc == DISCO_EINVAL:
+        raise ValueError(msg)
+    if rc == DISCO_EUNSUPPORTED:
+        raise NotImplementedError(msg)
+    if rc == DISCO_ENOMEM:
+        raise MemoryError(msg)
+    raise RuntimeError(msg)
+
+
+def _kernel_shape(ks):
+    if isinstance(ks, int):
+        return (ks, 0)
+    ks = tuple(int(v) for v in ks)
+    if len(ks) == 1:
+        return (ks[0], 0)
+    if len(ks) == 2:
+        return ks
+    raise ValueError(f"kernel_shape must be an int or a tuple of one or two ints, got {ks}")
+
+
+class Psi:
+    """Handle of a built Psi tensor (library-owned)."""
+
+    def __init__(self, handle, desc: _Desc):
+        self._h = ctypes.c_void_p(handle)
+        self.desc = desc
+        K = ctypes.c_int32()
+        nnz = ctypes.c_int64()
+        nzz = ctypes.c_int64()
+        cut = ctypes.c_double()
+        _check(_lib.disco_psi_query(self._h, ctypes.byref(K), ctypes.byref(nnz),
+                                    ctypes.byref(nzz), ctypes.byref(cut)), "psi_query")
+        self.K = K.value
+        self.nnz = nnz.value
+        self.nnz_nonzero = nzz.value
+        self.theta_cutoff = cut.value
+        self.nlat_in, self.nlon_in = desc.nlat_in, desc.nlon_in
+        self.nlat_out, self.nlon_out = desc.nlat_out, desc.nlon_out
+        self.on_device = False
+
+    @property
+    def handle(self):
+        return self._h
+
+    def export(self):
+        """Canonical CSR as numpy arrays (row_ptr, in_lat, lon_off, vals[nnz, K])."""
+        row_ptr = np.zeros(self.nlat_out + 1, dtype=np.int64)
+        in_lat = np.zeros(self.nnz, dtype=np.int32)
+        lon_off = np.zeros(self.nnz, dtype=np.int32)
+        vals = np.zeros((self.nnz, self.K), dtype=np.float64)
+        _check(_lib.disco_psi_export(self._h, row_ptr.ctypes.data, in_lat.ctypes.data,
+                                     lon_off.ctypes.data, vals.ctypes.data), "psi_export")
+        return row_ptr, in_lat, lon_off, vals
+
+    def to_device(self):
+        """Copy the device form to the current HIP device (once)."""
+        _check(_lib.disco_psi_to_device(self._h), "psi_to_device")
+        self.on_device = True
+        return self
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value:
+            _lib.disco_psi_free(h)
+            self._h = ctypes.c_void_p(0)
+
+
+def psi_build(nlat_in: int, nlon_in: int, nlat_out: int, nlon_out: int, kernel_shape,
+              theta_cutoff: float | None = None, grid_in: str = "equiangular",
+              grid_out: str = "equiangular", basis_type: str = "piecewise linear",
+              basis_norm_mode: str = "none") -> Psi:
+    """Build Psi on the host (float64).  Arguments follow the layer's
+    constructor: in_shape/out_shape as (nlat, nlon), kernel_shape, theta_cutoff
+    (None selects (nr+1)*pi/(nlat_out-1)), grids, basis type and norm."""
+    d = _Desc()
+    d.nlat_in, d.nlon_in, d.nlat_out, d.nlon_out = nlat_in, nlon_in, nlat_out, nlon_out
+    for key, table, val in (("grid_in", GRIDS, grid_in), ("grid_out", GRIDS, grid_out),
+                            ("basis_type", BASES, basis_type), ("basis_norm", NORMS, basis_norm_mode)):
+        if val not in table:
+            raise NotImplementedError(f"{key}={val!r} is not implemented (supported: {list(table)})")
+        setattr(d, key, table[val])
+    nr, nphi = _kernel_shape(kernel_shape)
+    d.kernel_shape[0], d.kernel_shape[1] = nr, nphi
+    if theta_cutoff is None:
+        d.theta_cutoff = 0.0
+    else:
+        if not (theta_cutoff > 0.0):
+            raise ValueError(f"theta_cutoff must be positive, got {theta_cutoff}")
+        d.theta_cutoff = float(theta_cutoff)
+    h = ctypes.c_void_p()
+    _check(_lib.disco_psi_build(ctypes.byref(d), ctypes.byref(h)), "psi_build")
+    return Psi(h.value, d)
+
+
+# ----------------------------------------------------------------------------
+# compute entry points (torch tensors on the current HIP device)
+# ----------------------------------------------------------------------------
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise ValueError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _torch_dtype(code: int):
+    torch = _torch()
+    return torch.float32 if code == F32 else torch.bfloat16
+
+
+def _stream(stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _need(t, name, shape):
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def contract(psi: Psi, x, xk=None, xk_dtype=None, stream=None):
+    """xk[b,c,k,j,q] = sum_(i,p) Psi[k,j,(i,p)] x[b,c,i,(q*s+p) mod nlon_in]."""
+    torch = _torch()
+    if x.dim() != 4:
+        raise ValueError("x must be [B, C, nlat_in, nlon_in]")
+    B, C = x.shape[:2]
+    _need(x, "x", (B, C, psi.nlat_in, psi.nlon_in))
+    if xk is None:
+        dt = x.dtype if xk_dtype is None else xk_dtype
+        xk = torch.empty((B, C, psi.K, psi.nlat_out, psi.nlon_out), dtype=dt, device=x.device)
+    _need(xk, "xk", (B, C, psi.K, psi.nlat_out, psi.nlon_out))
+    _check(_lib.disco_contract(psi.handle, x.data_ptr(), _dtype_code(x), xk.data_ptr(),
+                               _dtype_code(xk), B, C, _stream(stream)), "contract")
+    return xk
+
+
+def einsum(xk, w, groups: int = 1, bias=None, y=None, out_dtype=None, stream=None):
+    """y[b,co,j,q] = bias[co] + sum_(ci',k) w[co,ci',k] xk[b, G(co)*Ci/G+ci', k, j, q]."""
+    torch = _torch()
+    if xk.dim() != 5 or w.dim() != 3:
+        raise ValueError("xk must be [B, Ci, K, nlat_out, nlon_out] and w [Co, Ci/groups, K]")
+    B, Ci, K, H, W = xk.shape
+    Co = w.shape[0]
+    _need(xk, "xk", (B, Ci, K, H, W))
+    if groups < 1 or Ci % groups or Co % groups:
+        raise ValueError(f"groups ({groups}) must divide in_channels ({Ci}) and out_channels ({Co})")
+    _need(w, "w", (Co, Ci // groups, K))
+    if y is None:
+        dt = torch.float32 if out_dtype is None else out_dtype
+        y = torch.empty((B, Co, H, W), dtype=dt, device=xk.device)
+    _need(y, "y", (B, Co, H, W))
+    bptr = None
+    if bias is not None:
+        _need(bias, "bias", (Co,))
+        if bias.dtype != torch.float32:
+            raise ValueError("bias must be float32")
+        bptr = bias.data_ptr()
+    _check(_lib.disco_einsum(xk.data_ptr(), _dtype_code(xk), w.data_ptr(), _dtype_code(w), bptr,
+                             y.data_ptr(), _dtype_code(y), B, Ci, Co, groups, K, H, W,
+                             _stream(stream)), "einsum")
+    return y
+
+
+def fused_fwd(psi: Psi, x, w, groups: int = 1, bias=None, y=None, out_dtype=None, stream=None):
+    """The forward DISCO convolution without storing the K-expanded tensor."""
+    torch = _torch()
+    if x.dim() != 4 or w.dim() != 3:
+        raise ValueError("x must be [B, Ci, nlat_in, nlon_in] and w [Co, Ci/groups, K]")
+    B, Ci = x.shape[:2]
+    Co = w.shape[0]
+    _need(x, "x", (B, Ci, psi.nlat_in, psi.nlon_in))
+    if groups < 1 or Ci % groups or Co % groups:
+        raise ValueError(f"groups ({groups}) must divide in_channels ({Ci}) and out_channels ({Co})")
+    _need(w, "w", (Co, Ci // groups, psi.K))
+    if y is None:
+        dt = torch.float32 if out_dtype is None else out_dtype
+        y = torch.empty((B, Co, psi.nlat_out, psi.nlon_out), dtype=dt, device=x.device)
+    _need(y, "y", (B, Co, psi.nlat_out, psi.nlon_out))
+    bptr = None
+    if bias is not None:
+        _need(bias, "bias", (Co,))
+        if bias.dtype != torch.float32:
+            raise ValueError("bias must be float32")
+        bptr = bias.data_ptr()
+    _check(_lib.disco_fused_fwd(psi.handle, x.data_ptr(), _dtype_code(x), w.data_ptr(),
+                                _dtype_code(w), bptr, y.data_ptr(), _dtype_code(y), B, Ci, Co,
+                                groups, _stream(stream)), "fused_fwd")
+    return y
+

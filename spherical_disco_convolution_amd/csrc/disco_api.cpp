@@ -1,0 +1,344 @@
+// C-ABI layer: argument checks, error reporting, handle lifetime and the
+// device copy of Psi.  Compute entry points validate everything on the host
+// before any launch and never fall back to another path.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+
+#include "disco_internal.h"
+
+namespace disco {
+
+namespace {
+thread_local std::string g_last_error;
+}
+
+int set_error(int code, const char* fmt, ...) {
+    char buf[1024];
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return code;
+}
+
+void clear_error() { g_last_error.clear(); }
+
+namespace {
+
+int dtype_size(int dt) { return dt == DISCO_F32 ? 4 : (dt == DISCO_BF16 ? 2 : 0); }
+
+bool valid_dtype(int dt) { return dt == DISCO_F32 || dt == DISCO_BF16; }
+
+// A device pointer check: the pointer must be device (or managed) memory
+// owned by the current device.
+int check_device_ptr(const void* ptr, const char* name, int device) {
+    if (ptr == nullptr) return set_error(DISCO_EINVAL, "%s is NULL", name);
+    hipPointerAttribute_t attr;
+    std::memset(&attr, 0, sizeof(attr));
+    hipError_t e = hipPointerGetAttributes(&attr, ptr);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return set_error(DISCO_EINVAL, "%s is not a device pointer known to HIP (%s)", name,
+                         hipGetErrorString(e));
+    }
+    if (attr.type != hipMemoryTypeDevice && attr.type != hipMemoryTypeManaged)
+        return set_error(DISCO_EINVAL, "%s is not device memory", name);
+    if (attr.device != device)
+        return set_error(DISCO_EINVAL, "%s lives on device %d, the current device is %d", name,
+                         attr.device, device);
+    return DISCO_OK;
+}
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+    const char* pa = static_cast<const char*>(a);
+    const char* pb = static_cast<const char*>(b);
+    return pa < pb + nb && pb < pa + na;
+}
+
+int current_device(int* dev) {
+    hipError_t e = hipGetDevice(dev);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return set_error(DISCO_EHIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+    }
+    return DISCO_OK;
+}
+
+int check_psi_on_device(const disco_psi* psi, int dev) {
+    if (psi == nullptr) return set_error(DISCO_EINVAL, "psi handle is NULL");
+    if (psi->dev.device < 0)
+        return set_error(DISCO_EINVAL, "psi has no device copy: call disco_psi_to_device first");
+    if (psi->dev.device != dev)
+        return set_error(DISCO_EINVAL, "psi lives on device %d, the current device is %d",
+                         psi->dev.device, dev);
+    return DISCO_OK;
+}
+
+void free_device(disco::DevPsi& d) {
+    for (void* p : d.allocations) (void)hipFree(p);
+    d = disco::DevPsi();
+}
+
+int dev_alloc(disco::DevPsi& d, void** ptr, size_t bytes) {
+    if (bytes == 0) bytes = 16;
+    hipError_t e = hipMalloc(ptr, bytes);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return set_error(e == hipErrorOutOfMemory ? DISCO_ENOMEM : DISCO_EHIP,
+                         "hipMalloc(%zu) failed: %s", bytes, hipGetErrorString(e));
+    }
+    d.allocations.push_back(*ptr);
+    return DISCO_OK;
+}
+
+int dev_copy(void* dst, const void* src, size_t bytes) {
+    if (bytes == 0) return DISCO_OK;
+    hipError_t e = hipMemcpy(dst, src, bytes, hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return set_error(DISCO_EHIP, "hipMemcpy failed: %s", hipGetErrorString(e));
+    }
+    return DISCO_OK;
+}
+
+}  // namespace
+
+int build_mfma_tables(disco_psi* psi, std::vector<char>& taps, std::vector<int32_t>& info);
+
+}  // namespace disco
+
+using namespace disco;
+
+extern "C" {
+
+const char* disco_version(void) { return "disco-gfx950 0.1.0"; }
+
+const char* disco_last_error(void) { return g_last_error.c_str(); }
+
+int disco_psi_build(const disco_psi_desc* desc, disco_psi** out) {
+    clear_error();
+    if (desc == nullptr || out == nullptr)
+        return set_error(DISCO_EINVAL, "desc and out must not be NULL");
+    *out = nullptr;
+    disco_psi* psi = new (std::nothrow) disco_psi();
+    if (psi == nullptr) return set_error(DISCO_ENOMEM, "host allocation failed");
+    int rc = build_host_psi(*desc, psi->host);
+    if (rc != DISCO_OK) {
+        delete psi;
+        return rc;
+    }
+    *out = psi;
+    return DISCO_OK;
+}
+
+int disco_psi_query(const disco_psi* psi, int32_t* K, int64_t* nnz, int64_t* nnz_nonzero,
+                    double* theta_cutoff) {
+    clear_error();
+    if (psi == nullptr) return set_error(DISCO_EINVAL, "psi handle is NULL");
+    if (K) *K = psi->host.K;
+    if (nnz) *nnz = (int64_t)psi->host.in_lat.size();
+    if (nnz_nonzero) *nnz_nonzero = psi->host.nnz_nonzero;
+    if (theta_cutoff) *theta_cutoff = psi->host.cutoff;
+    return DISCO_OK;
+}
+
+int disco_psi_export(const disco_psi* psi, int64_t* row_ptr, int32_t* in_lat, int32_t* lon_off,
+                     double* vals) {
+    clear_error();
+    if (psi == nullptr) return set_error(DISCO_EINVAL, "psi handle is NULL");
+    const HostPsi& h = psi->host;
+    if (row_ptr) std::memcpy(row_ptr, h.row_ptr.data(), h.row_ptr.size() * sizeof(int64_t));
+    if (in_lat) std::memcpy(in_lat, h.in_lat.data(), h.in_lat.size() * sizeof(int32_t));
+    if (lon_off) std::memcpy(lon_off, h.lon_off.data(), h.lon_off.size() * sizeof(int32_t));
+    if (vals) std::memcpy(vals, h.vals.data(), h.vals.size() * sizeof(double));
+    return DISCO_OK;
+}
+
+int disco_psi_to_device(disco_psi* psi) {
+    clear_error();
+    if (psi == nullptr) return set_error(DISCO_EINVAL, "psi handle is NULL");
+    int dev = -1;
+    int rc = current_device(&dev);
+    if (rc != DISCO_OK) return rc;
+    if (psi->dev.device == dev) return DISCO_OK;
+    if (psi->dev.device >= 0)
+        return set_error(DISCO_EINVAL, "psi already lives on device %d (current device %d)",
+                         psi->dev.device, dev);
+    const HostPsi& h = psi->host;
+    DevPsi d;
+    const int K = h.K;
+    int KP = 1;
+    while (KP < K) KP *= 2;
+    if (KP > 8) KP = (K + 3) / 4 * 4;
+    d.KP = KP;
+    const int nlat_out = h.desc.nlat_out;
+    std::vector<int32_t> wptr(nlat_out + 1);
+    std::vector<DevWindow> wins(h.windows.size());
+    const int64_t npts = (int64_t)(h.win_vals.size() / K);
+    std::vector<float> vals;
+    try {
+        vals.assign((size_t)npts * KP, 0.0f);
+    } catch (const std::bad_alloc&) {
+        return set_error(DISCO_ENOMEM, "host allocation failed");
+    }
+    for (int64_t p = 0; p < npts; ++p)
+        for (int k = 0; k < K; ++k) vals[p * KP + k] = (float)h.win_vals[p * K + k];
+    for (int j = 0; j <= nlat_out; ++j) wptr[j] = (int32_t)h.win_ptr[j];
+    for (size_t n = 0; n < h.windows.size(); ++n) {
+        wins[n].lat = h.windows[n].lat;
+        wins[n].p_lo = h.windows[n].p_lo;
+        wins[n].width = h.windows[n].width;
+        wins[n].val_off = (int32_t)h.windows[n].val_off;
+        d.max_width = std::max(d.max_width, h.windows[n].width);
+    }
+    for (int j = 0; j < nlat_out; ++j) {
+        d.max_windows = std::max(d.max_windows, wptr[j + 1] - wptr[j]);
+        d.max_row_points = std::max(
+            d.max_row_points, (int32_t)(h.row_ptr[j + 1] - h.row_ptr[j]));
+    }
+    std::vector<char> taps;
+    std::vector<int32_t> info;
+    rc = build_mfma_tables(psi, taps, info);
+    if (rc != DISCO_OK) return rc;
+
+    void* p = nullptr;
+    if ((rc = dev_alloc(d, &p, wptr.size() * sizeof(int32_t))) != DISCO_OK) goto fail;
+    d.win_ptr = static_cast<int32_t*>(p);
+    if ((rc = dev_copy(p, wptr.data(), wptr.size() * sizeof(int32_t))) != DISCO_OK) goto fail;
+    if ((rc = dev_alloc(d, &p, wins.size() * sizeof(DevWindow))) != DISCO_OK) goto fail;
+    d.windows = static_cast<DevWindow*>(p);
+    if ((rc = dev_copy(p, wins.data(), wins.size() * sizeof(DevWindow))) != DISCO_OK) goto fail;
+    if ((rc = dev_alloc(d, &p, vals.size() * sizeof(float))) != DISCO_OK) goto fail;
+    d.vals = static_cast<float*>(p);
+    if ((rc = dev_copy(p, vals.data(), vals.size() * sizeof(float))) != DISCO_OK) goto fail;
+    if (!taps.empty()) {
+        if ((rc = dev_alloc(d, &p, taps.size())) != DISCO_OK) goto fail;
+        d.mfma_taps = p;
+        d.mfma_taps_bytes = (int64_t)taps.size();
+        if ((rc = dev_copy(p, taps.data(), taps.size())) != DISCO_OK) goto fail;
+        if ((rc = dev_alloc(d, &p, info.size() * sizeof(int32_t))) != DISCO_OK) goto fail;
+        d.mfma_row_info = static_cast<int32_t*>(p);
+        if ((rc = dev_copy(p, info.data(), info.size() * sizeof(int32_t))) != DISCO_OK) goto fail;
+        d.mfma_ok = 1;
+    }
+    d.device = dev;
+    psi->dev = d;
+    return DISCO_OK;
+fail:
+    free_device(d);
+    return rc;
+}
+
+void disco_psi_free(disco_psi* psi) {
+    if (psi == nullptr) return;
+    if (psi->dev.device >= 0) {
+        int cur = -1;
+        if (hipGetDevice(&cur) == hipSuccess && cur != psi->dev.device) {
+            (void)hipSetDevice(psi->dev.device);
+            free_device(psi->dev);
+            (void)hipSetDevice(cur);
+        } else {
+            free_device(psi->dev);
+        }
+    }
+    delete psi;
+}
+
+int disco_contract(const disco_psi* psi, const void* x, int x_dtype, void* xk, int xk_dtype,
+                   int32_t B, int32_t C, void* stream) {
+    clear_error();
+    if (psi == nullptr) return set_error(DISCO_EINVAL, "psi handle is NULL");
+    if (!valid_dtype(x_dtype) || !valid_dtype(xk_dtype))
+        return set_error(DISCO_EINVAL, "unknown dtype code (x %d, xk %d)", x_dtype, xk_dtype);
+    if (B < 0 || C < 0) return set_error(DISCO_EINVAL, "B and C must be >= 0 (got %d, %d)", B, C);
+    if (B == 0 || C == 0) return DISCO_OK;
+    int dev = -1;
+    int rc = current_device(&dev);
+    if (rc != DISCO_OK) return rc;
+    if ((rc = check_psi_on_device(psi, dev)) != DISCO_OK) return rc;
+    if ((rc = check_device_ptr(x, "x", dev)) != DISCO_OK) return rc;
+    if ((rc = check_device_ptr(xk, "xk", dev)) != DISCO_OK) return rc;
+    const disco_psi_desc& d = psi->host.desc;
+    const size_t nx = (size_t)B * C * d.nlat_in * d.nlon_in * dtype_size(x_dtype);
+    const size_t nxk = (size_t)B * C * psi->host.K * d.nlat_out * d.nlon_out * dtype_size(xk_dtype);
+    if (overlap(x, nx, xk, nxk)) return set_error(DISCO_EINVAL, "x and xk overlap");
+    return launch_contract(psi, x, x_dtype, xk, xk_dtype, B, C, stream);
+}
+
+int disco_einsum(const void* xk, int xk_dtype, const void* w, int w_dtype, const float* bias,
+                 void* y, int y_dtype, int32_t B, int32_t Ci, int32_t Co, int32_t groups,
+                 int32_t K, int32_t nlat_out, int32_t nlon_out, void* stream) {
+    clear_error();
+    if (!valid_dtype(xk_dtype) || !valid_dtype(w_dtype) || !valid_dtype(y_dtype))
+        return set_error(DISCO_EINVAL, "unknown dtype code (xk %d, w %d, y %d)", xk_dtype,
+                         w_dtype, y_dtype);
+    if (xk_dtype != w_dtype)
+        return set_error(DISCO_EUNSUPPORTED, "xk and w must have the same dtype");
+    if (B < 0 || Ci < 1 || Co < 1 || K < 1 || nlat_out < 1 || nlon_out < 1)
+        return set_error(DISCO_EINVAL, "sizes must be positive (B %d Ci %d Co %d K %d nlat_out %d "
+                         "nlon_out %d)", B, Ci, Co, K, nlat_out, nlon_out);
+    if (groups < 1 || Ci % groups != 0 || Co % groups != 0)
+        return set_error(DISCO_EINVAL,
+                         "groups (%d) must divide in_channels (%d) and out_channels (%d)", groups,
+                         Ci, Co);
+    if (B == 0) return DISCO_OK;
+    int dev = -1;
+    int rc = current_device(&dev);
+    if (rc != DISCO_OK) return rc;
+    if ((rc = check_device_ptr(xk, "xk", dev)) != DISCO_OK) return rc;
+    if ((rc = check_device_ptr(w, "w", dev)) != DISCO_OK) return rc;
+    if ((rc = check_device_ptr(y, "y", dev)) != DISCO_OK) return rc;
+    if (bias && (rc = check_device_ptr(bias, "bias", dev)) != DISCO_OK) return rc;
+    const size_t hw = (size_t)nlat_out * nlon_out;
+    const size_t nxk = (size_t)B * Ci * K * hw * dtype_size(xk_dtype);
+    const size_t nw = (size_t)Co * (Ci / groups) * K * dtype_size(w_dtype);
+    const size_t ny = (size_t)B * Co * hw * dtype_size(y_dtype);
+    if (overlap(y, ny, xk, nxk) || overlap(y, ny, w, nw) || (bias && overlap(y, ny, bias, Co * 4)))
+        return set_error(DISCO_EINVAL, "y overlaps an input");
+    return launch_einsum(xk, xk_dtype, w, w_dtype, bias, y, y_dtype, B, Ci, Co, groups, K,
+                         nlat_out, nlon_out, stream);
+}
+
+int disco_fused_fwd(const disco_psi* psi, const void* x, int x_dtype, const void* w, int w_dtype,
+                    const float* bias, void* y, int y_dtype, int32_t B, int32_t Ci, int32_t Co,
+                    int32_t groups, void* stream) {
+    clear_error();
+    if (psi == nullptr) return set_error(DISCO_EINVAL, "psi handle is NULL");
+    if (!valid_dtype(x_dtype) || !valid_dtype(w_dtype) || !valid_dtype(y_dtype))
+        return set_error(DISCO_EINVAL, "unknown dtype code (x %d, w %d, y %d)", x_dtype, w_dtype,
+                         y_dtype);
+    if (x_dtype != w_dtype)
+        return set_error(DISCO_EUNSUPPORTED, "x and w must have the same dtype");
+    if (B < 0 || Ci < 1 || Co < 1)
+        return set_error(DISCO_EINVAL, "sizes must be positive (B %d Ci %d Co %d)", B, Ci, Co);
+    if (groups < 1 || Ci % groups != 0 || Co % groups != 0)
+        return set_error(DISCO_EINVAL,
+                         "groups (%d) must divide in_channels (%d) and out_channels (%d)", groups,
+                         Ci, Co);
+    if (B == 0) return DISCO_OK;
+    int dev = -1;
+    int rc = current_device(&dev);
+    if (rc != DISCO_OK) return rc;
+    if ((rc = check_psi_on_device(psi, dev)) != DISCO_OK) return rc;
+    if ((rc = check_device_ptr(x, "x", dev)) != DISCO_OK) return rc;
+    if ((rc = check_device_ptr(w, "w", dev)) != DISCO_OK) return rc;
+    if ((rc = check_device_ptr(y, "y", dev)) != DISCO_OK) return rc;
+    if (bias && (rc = check_device_ptr(bias, "bias", dev)) != DISCO_OK) return rc;
+    const disco_psi_desc& d = psi->host.desc;
+    const size_t nx = (size_t)B * Ci * d.nlat_in * d.nlon_in * dtype_size(x_dtype);
+    const size_t nw = (size_t)Co * (Ci / groups) * psi->host.K * dtype_size(w_dtype);
+    const size_t ny = (size_t)B * Co * d.nlat_out * d.nlon_out * dtype_size(y_dtype);
+    if (overlap(y, ny, x, nx) || overlap(y, ny, w, nw) || (bias && overlap(y, ny, bias, Co * 4)))
+        return set_error(DISCO_EINVAL, "y overlaps an input");
+    return launch_fused(psi, x, x_dtype, w, bias, y, y_dtype, B, Ci, Co, groups, stream);
+}
+
+}  // extern "C"

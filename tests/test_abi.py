@@ -1,0 +1,151 @@
+"""C-ABI checks that need no GPU: every symbol declared in include/*.h is
+exported by libdisco.so, and invalid requests are rejected with the right
+status and a message before any device work.
+"""
+import ctypes
+import glob
+import math
+import os
+import re
+import subprocess
+import sys
+
+import pytest
+
+import spherical_disco_convolution_amd as sdc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"^[A-Za-z_][\w\s\*]*?\b(disco_\w+)\s*\(", text, flags=re.M):
+            names.add(m.group(1))
+    return sorted(names)
+
+
+def test_header_declares_the_entry_points():
+    names = _declared_functions()
+    for required in ("disco_psi_build", "disco_contract", "disco_einsum", "disco_fused_fwd"):
+        assert required in names
+
+
+def test_every_declared_symbol_is_exported():
+    lib = ctypes.CDLL(sdc.LIB_PATH)
+    out = subprocess.run(["nm", "-D", "--defined-only", sdc.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for name in _declared_functions():
+        assert name in exported, name
+        getattr(lib, name)
+
+
+def _rc_build(**kw):
+    d = sdc._Desc()
+    vals = dict(nlat_in=33, nlon_in=64, nlat_out=33, nlon_out=64, grid_in=0, grid_out=0,
+                basis_type=0, basis_norm=0, theta_cutoff=0.3)
+    ks = kw.pop("kernel_shape", (3, 0))
+    vals.update(kw)
+    for k, v in vals.items():
+        setattr(d, k, v)
+    d.kernel_shape[0], d.kernel_shape[1] = ks
+    h = ctypes.c_void_p()
+    rc = sdc._lib.disco_psi_build(ctypes.byref(d), ctypes.byref(h))
+    msg = sdc._lib.disco_last_error().decode()
+    if rc == 0:
+        sdc._lib.disco_psi_free(h)
+    return rc, msg
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(nlat_in=1), sdc.DISCO_EINVAL),
+    (dict(nlat_out=1), sdc.DISCO_EINVAL),
+    (dict(nlon_in=0), sdc.DISCO_EINVAL),
+    (dict(nlon_out=48), sdc.DISCO_EINVAL),            # 64 % 48 != 0
+    (dict(nlon_out=128), sdc.DISCO_EINVAL),           # upsampling in longitude
+    (dict(theta_cutoff=math.pi), sdc.DISCO_EINVAL),
+    (dict(theta_cutoff=4.0), sdc.DISCO_EINVAL),
+    (dict(theta_cutoff=float("nan")), sdc.DISCO_EINVAL),
+    (dict(kernel_shape=(0, 0)), sdc.DISCO_EINVAL),
+    (dict(kernel_shape=(3, -1)), sdc.DISCO_EINVAL),
+    (dict(kernel_shape=(10, 8)), sdc.DISCO_EUNSUPPORTED),   # K = 73 > 64
+    (dict(grid_in=1), sdc.DISCO_EUNSUPPORTED),
+    (dict(grid_out=2), sdc.DISCO_EUNSUPPORTED),
+    (dict(basis_type=1), sdc.DISCO_EUNSUPPORTED),
+    (dict(basis_norm=1), sdc.DISCO_EUNSUPPORTED),
+])
+def test_build_rejects(kw, code):
+    rc, msg = _rc_build(**kw)
+    assert rc == code
+    assert msg
+
+
+def test_build_null_arguments():
+    assert sdc._lib.disco_psi_build(None, None) == sdc.DISCO_EINVAL
+    assert sdc._lib.disco_psi_query(None, None, None, None, None) == sdc.DISCO_EINVAL
+    assert sdc._lib.disco_psi_export(None, None, None, None, None) == sdc.DISCO_EINVAL
+    assert sdc._lib.disco_psi_to_device(None) == sdc.DISCO_EINVAL
+    sdc._lib.disco_psi_free(None)   # no-op
+
+
+def test_python_errors():
+    with pytest.raises(ValueError):
+        sdc.psi_build(33, 64, 33, 48, (3,), 0.3)
+    with pytest.raises(NotImplementedError):
+        sdc.psi_build(33, 64, 33, 64, (3,), 0.3, grid_in="legendre-gauss")
+    with pytest.raises(NotImplementedError):
+        sdc.psi_build(33, 64, 33, 64, (3,), 0.3, basis_norm_mode="nodal")
+    with pytest.raises(ValueError):
+        sdc.psi_build(33, 64, 33, 64, (3, 3, 3), 0.3)
+    with pytest.raises(ValueError):
+        sdc.psi_build(33, 64, 33, 64, (3,), -1.0)
+
+
+def test_forced_host_allocation_failure():
+    code = (
+        "import ctypes, spherical_disco_convolution_amd as s\n"
+        "d = s._Desc(); d.nlat_in=d.nlat_out=33; d.nlon_in=d.nlon_out=64\n"
+        "d.kernel_shape[0]=3; d.theta_cutoff=0.3\n"
+        "h = ctypes.c_void_p()\n"
+        "print(s._lib.disco_psi_build(ctypes.byref(d), ctypes.byref(h)))\n")
+    env = dict(os.environ, DISCO_TEST_FAIL_HOST_ALLOC="1")
+    out = subprocess.run([sys.executable, "-c", code], env=env, cwd=ROOT, capture_output=True,
+                         text=True, check=True).stdout.strip()
+    assert int(out) == sdc.DISCO_ENOMEM
+
+
+def test_compute_calls_reject_bad_arguments_before_device_work():
+    L = sdc._lib
+    p = sdc.psi_build(33, 64, 33, 64, (3,), 0.3)
+    fake = ctypes.c_void_p(0x1000)
+    # unknown dtype codes
+    assert L.disco_contract(p.handle, fake, 7, fake, 0, 1, 1, None) == sdc.DISCO_EINVAL
+    assert L.disco_einsum(fake, 0, fake, 0, None, fake, 9, 1, 4, 4, 1, 3, 33, 64, None) == sdc.DISCO_EINVAL
+    # groups must divide channels (the spectral layer's source raises ValueError for this)
+    assert L.disco_einsum(fake, 0, fake, 0, None, fake, 0, 1, 6, 4, 4, 3, 33, 64, None) == sdc.DISCO_EINVAL
+    assert "groups" in L.disco_last_error().decode()
+    assert L.disco_fused_fwd(p.handle, fake, 0, fake, 0, None, fake, 0, 1, 4, 6, 4, None) == sdc.DISCO_EINVAL
+    # negative sizes
+    assert L.disco_contract(p.handle, fake, 0, fake, 0, -1, 1, None) == sdc.DISCO_EINVAL
+    assert L.disco_einsum(fake, 0, fake, 0, None, fake, 0, 1, 0, 4, 1, 3, 33, 64, None) == sdc.DISCO_EINVAL
+    # mixed input dtypes
+    assert L.disco_fused_fwd(p.handle, fake, 0, fake, 1, None, fake, 0, 1, 4, 4, 1, None) == sdc.DISCO_EUNSUPPORTED
+    # null handle
+    assert L.disco_contract(None, fake, 0, fake, 0, 1, 1, None) == sdc.DISCO_EINVAL
+    assert L.disco_fused_fwd(None, fake, 0, fake, 0, None, fake, 0, 1, 4, 4, 1, None) == sdc.DISCO_EINVAL
+    # empty batch is a no-op
+    assert L.disco_contract(p.handle, fake, 0, fake, 0, 0, 4, None) == sdc.DISCO_OK
+
+
+def test_handle_without_device_copy_is_rejected_or_no_gpu():
+    # Without disco_psi_to_device the compute calls must refuse the handle
+    # (or, on a machine without a GPU, report the HIP failure); never crash.
+    L = sdc._lib
+    p = sdc.psi_build(33, 64, 33, 64, (3,), 0.3)
+    fake = ctypes.c_void_p(0x1000)
+    rc = L.disco_contract(p.handle, fake, 0, fake, 0, 1, 1, None)
+    assert rc in (sdc.DISCO_EINVAL, sdc.DISCO_EHIP)
+    assert L.disco_last_error().decode()

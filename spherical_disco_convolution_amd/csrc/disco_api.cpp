@@ -227,6 +227,7 @@ int disco_psi_to_device(disco_psi* psi) {
         if ((rc = dev_alloc(d, &p, info.size() * sizeof(int32_t))) != DISCO_OK) goto fail;
         d.mfma_row_info = static_cast<int32_t*>(p);
         if ((rc = dev_copy(p, info.data(), info.size() * sizeof(int32_t))) != DISCO_OK) goto fail;
+        d.mfma_info_host = info;
         d.mfma_ok = 1;
     }
     d.device = dev;

@@ -69,7 +69,8 @@ struct DevPsi {
     // bf16 tap tables for the matrix-core fused kernel (see kernels_fused_mfma.hip)
     void* mfma_taps = nullptr;
     int64_t mfma_taps_bytes = 0;
-    int32_t* mfma_row_info = nullptr;
+    int32_t* mfma_row_info = nullptr;     // device copy of the info block
+    std::vector<int32_t> mfma_info_host;  // host copy (offsets, tile options)
     int32_t mfma_ok = 0;
     std::vector<void*> allocations;
 };

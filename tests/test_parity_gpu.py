@@ -198,7 +198,14 @@ def test_roll_equivariance_gpu(sdc, which):
                        groups=wl.groups).cpu().numpy()
     diff = np.max(np.abs(yr - np.roll(y, -1, axis=-1)))
     _say(f"roll equivariance {which}: max |diff| = {diff:.3e}")
-    assert rel_l2(yr, np.roll(y, -1, axis=-1)) <= 1e-6
+    if wl.dtype == "f32":
+        # vector-ALU paths sum every output in the same order: exact
+        assert diff == 0.0
+    else:
+        # the matrix-core path sums within MFMA tiles in an order that depends
+        # on the output's position in its 4-output block, and then rounds the
+        # K-expanded tile to bf16: equal up to rounding
+        assert rel_l2(yr, np.roll(y, -1, axis=-1)) <= 1e-4
 
 
 def test_determinism(sdc):

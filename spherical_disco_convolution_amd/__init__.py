@@ -59,7 +59,7 @@ def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(
             f"{LIB_PATH} is missing: build it with "
-            "`python -m spherical_disco_convolution_amd.build_lib` (hipcc, gfx950)")
+            "`python spherical_disco_convolution_amd/build_lib.py` (hipcc, gfx950)")
     lib = ctypes.CDLL(LIB_PATH)
     P, I32, I64, D = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_double
     sig = {

@@ -1,6 +1,7 @@
 """Build libdisco.so (host Psi builder, C-ABI layer and gfx950 HIP kernels).
 
-Usage: python -m spherical_disco_convolution_amd.build_lib [-v]
+Usage: python spherical_disco_convolution_amd/build_lib.py [-v]
+(run as a script: importing the package requires the built library)
 Every call recompiles all sources with hipcc for gfx950 and links the shared
 library next to this file.
 """

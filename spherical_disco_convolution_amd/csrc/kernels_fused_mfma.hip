@@ -25,9 +25,13 @@
 // Channel/basis GEMM: y[co, q] += W[co, kappa] * xk[q][kappa], kappa = ci*8 + k,
 // with W pre-tiled into operand fragments by a small preparation kernel.
 //
-// One workgroup (4 waves) owns one output row and Q output longitudes for all
-// output channels.  Work items are distributed over the 8 XCDs in contiguous
-// latitude bands of equal cost (the polar rows carry ~100x more taps than the
+// One workgroup (4 waves) owns one output row and Q = 128 output longitudes
+// for all output channels; each wave contracts 32 of the longitudes.  The
+// input is walked in "pieces" (one window, up to 6 chunks of 16 longitudes,
+// 32 channels); a piece's input and its first tap fragments are loaded into
+// registers one piece ahead, so their latency overlaps the previous piece's
+// matrix work.  Work items are spread over the 8 XCDs in contiguous latitude
+// bands of equal cost (the polar rows carry ~100x more taps than the
 // equatorial ones), so that workgroups sharing input rows share an L2.
 #include <hip/hip_runtime.h>
 
@@ -44,15 +48,45 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));   // 8 bf16 as a native vector
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float float4v __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));   // converts with v_cvt_pk_bf16_f32 (RNE)
 
 constexpr int kNumXcd = 8;
-constexpr int kXsStride = 136;      // staged row length (elements): 128 + 8 pad
-constexpr int kXsLen = 128;         // longitudes staged per piece
-constexpr int kXkPad = 8;           // xk tile row padding (elements)
+constexpr int kQ = 128;             // output longitudes per work item
+constexpr int kNbw = kQ / 16;       // 4-output blocks per wave
+constexpr int kRing = 4;            // LDS ring slots: three pieces in flight while one is consumed
+constexpr int kXkStride = 264;      // xk tile row: 256 (ci, k) pairs + 8 pad
+constexpr int kGemmSteps = 4;       // GEMM k-steps (16 kappa each) per streamed weight piece
+// Chunks of 16 input longitudes per contraction piece.
+constexpr int cp_max(int S) { return S == 1 ? 4 : 2; }
+// 16-byte groups per channel row that a piece of `cp` chunks reads: the last
+// wave's last block reaches longitude S*96 + 8*floor((7 + 4*S*7)/8) + 16*(cp-1) + 15.
+constexpr int piece_groups(int S, int cp) { return S == 1 ? 16 + 2 * cp : 31 + 2 * cp; }
+// Staged row stride in 16-byte groups (odd: the 32 channel rows fall in distinct banks).
+constexpr int row_stride(int S) { return piece_groups(S, cp_max(S)) | 1; }
+constexpr int x_instr(int S) { return (32 * row_stride(S) + 63) / 64; }   // DMA loads of one strip
+constexpr int tap_instr(int S) { return S == 1 ? 2 * cp_max(1) : cp_max(2); }
+constexpr int slot_size(int S) { return (x_instr(S) + tap_instr(S)) * 64; }   // 16-byte units
 
 struct MfmaWin {
     int32_t lat, p_lo, width, nch0, nch1, tap0, tap1, pad;
 };
+
+// One contraction piece: a window's input strip (up to cp_max chunks of 16
+// longitudes) and its tap fragments.  32 bytes, read with scalar loads.
+struct PieceDesc {
+    int32_t xoff;    // input row offset within a channel plane (lat * nlon_in)
+    int32_t uoff;    // first staged longitude before the work item's shift, in [0, nlon_in)
+    int32_t tap0;    // tap fragment of chunk 0 of this piece, alignment class 0
+    int32_t tap1;    // same for class 1 (odd strides)
+    int32_t nck;     // chunks in this piece
+    int32_t d0;      // window start modulo 8
+    int32_t nv0;     // chunks with class-0 taps (the rest are zero)
+    int32_t nv1;     // chunks with class-1 taps
+};
+static_assert(sizeof(PieceDesc) == 32, "descriptor layout");
 
 // Tap fragment values: lane l, element e of chunk c for alignment delta.
 inline float tap_value(const HostPsi& h, const Window& wd, int delta, int chunk, int lane, int e) {
@@ -74,11 +108,12 @@ uint16_t host_bf16(float f) {
 
 }  // namespace
 
-// Layout of `info` (int32): [0] magic, [1] nwin, [2] offset of the MfmaWin array,
-// [3] offset of win_ptr, [4] Q, [5] nqt, [6] offset of the work lists, [7] list stride.
-enum { kInfoMagic = 0, kInfoNwin, kInfoWins, kInfoWinPtr, kInfoQ, kInfoNqt, kInfoWork,
-       kInfoStride, kInfoSize };
-constexpr int kQ = 128;   // output longitudes per workgroup
+// Layout of `info` (int32): header, piece_ptr[nlat_out+1], the PieceDesc array
+// (8 ints each, 8-aligned), and the work items (j, q0, first piece, piece
+// count) of all XCDs, each XCD's list contiguous and in (row, longitude tile)
+// order.
+enum { kInfoMagic = 0, kInfoPiecePtr, kInfoPieces, kInfoItems, kInfoNpieces, kInfoXcdOff,
+       kInfoXcdLen = kInfoXcdOff + kNumXcd, kInfoSize = kInfoXcdLen + kNumXcd };
 
 int build_mfma_tables(disco_psi* psi, std::vector<char>& taps, std::vector<int32_t>& info) {
     taps.clear();
@@ -87,11 +122,14 @@ int build_mfma_tables(disco_psi* psi, std::vector<char>& taps, std::vector<int32
     const disco_psi_desc& D = h.desc;
     // The matrix-core path covers K <= 8, longitudes a multiple of 8 and
     // strides 1 and 2 (the latter: one alignment class).
-    if (h.K > 8 || D.nlon_in % 8 != 0 || h.stride > 2) return DISCO_OK;
+    if (h.K > 8 || D.nlon_in % 8 != 0 || h.stride > 2 || D.nlon_in > 65536) return DISCO_OK;
     const int S = h.stride;
+    const int cp = cp_max(S);
     const int nwin = (int)h.windows.size();
+    const int nlat_out = D.nlat_out;
     std::vector<MfmaWin> wins(nwin);
-    size_t nfrag = 0;
+    // fragment 0 is all zero: chunks beyond a class's band load it
+    size_t nfrag = 1;
     for (int n = 0; n < nwin; ++n) {
         const Window& wd = h.windows[n];
         MfmaWin& m = wins[n];
@@ -114,6 +152,39 @@ int build_mfma_tables(disco_psi* psi, std::vector<char>& taps, std::vector<int32
         m.pad = 0;
     }
     if (nfrag > (size_t)0x7fffffff / 1024) return DISCO_OK;
+    // pieces: a window's chunks in groups of at most cp; an output row without
+    // support gets one piece with zero taps so that its tile is still written
+    std::vector<int32_t> piece_ptr(nlat_out + 1, 0);
+    std::vector<PieceDesc> pieces;
+    std::vector<double> cost(nlat_out, 0.0);
+    for (int j = 0; j < nlat_out; ++j) {
+        double c = 4 * (2048.0 + 400.0) + 3000.0;   // weight pieces + epilogue (cycles)
+        for (int64_t n = h.win_ptr[j]; n < h.win_ptr[j + 1]; ++n) {
+            const MfmaWin& m = wins[n];
+            const int nch = std::max(m.nch0, m.nch1);
+            for (int c0 = 0; c0 < nch; c0 += cp) {
+                PieceDesc pd;
+                pd.xoff = m.lat * D.nlon_in;
+                pd.uoff = (int32_t)(((int64_t)(m.p_lo & ~7) + 16 * c0) % D.nlon_in);
+                pd.nck = std::min(cp, nch - c0);
+                pd.d0 = m.p_lo & 7;
+                pd.nv0 = std::max(0, std::min(pd.nck, m.nch0 - c0));
+                pd.nv1 = (S & 1) ? std::max(0, std::min(pd.nck, m.nch1 - c0)) : 0;
+                pd.tap0 = pd.nv0 > 0 ? m.tap0 + c0 : 0;
+                pd.tap1 = pd.nv1 > 0 ? m.tap1 + c0 : 0;
+                pieces.push_back(pd);
+                c += 8.0 * 32.0 * pd.nck + 400.0;
+            }
+        }
+        if ((int)pieces.size() == piece_ptr[j]) {
+            PieceDesc pd{0, 0, 0, 0, 1, 0, 0, 0};
+            pieces.push_back(pd);
+            c += 8.0 * 32.0 + 400.0;
+        }
+        piece_ptr[j + 1] = (int32_t)pieces.size();
+        cost[j] = c;
+        if (pieces.size() > (size_t)1 << 26) return DISCO_OK;
+    }
     try {
         taps.assign(nfrag * 1024, 0);
     } catch (const std::bad_alloc&) {
@@ -134,18 +205,10 @@ int build_mfma_tables(disco_psi* psi, std::vector<char>& taps, std::vector<int32
                             host_bf16(tap_value(h, wd, delta, c, lane, e));
         }
     }
-    // cost of one work item of row j (relative MFMA count)
-    const int nlat_out = D.nlat_out;
-    std::vector<double> cost(nlat_out, 0.0);
-    for (int j = 0; j < nlat_out; ++j) {
-        double c = 96.0;
-        for (int64_t n = h.win_ptr[j]; n < h.win_ptr[j + 1]; ++n)
-            c += 6.0 * (wins[n].nch0 + wins[n].nch1) + 8.0;
-        cost[j] = c;
-    }
     double total = 0.0;
     for (double c : cost) total += c;
-    // contiguous bands of equal cost, one per XCD; heaviest rows first in a band
+    // contiguous latitude bands of equal cost, one per XCD: rows that share
+    // input rows run close in time on the same L2
     std::vector<std::vector<int>> band(kNumXcd);
     {
         double acc = 0.0;
@@ -155,32 +218,32 @@ int build_mfma_tables(disco_psi* psi, std::vector<char>& taps, std::vector<int32
             band[k].push_back(j);
             acc += cost[j];
         }
-        for (auto& b : band)
-            std::stable_sort(b.begin(), b.end(), [&](int a, int c) { return cost[a] > cost[c]; });
     }
-    // info block
+    const int nqt = (D.nlon_out + kQ - 1) / kQ;
     info.assign(kInfoSize, 0);
     info[kInfoMagic] = 0x44495343;
-    info[kInfoNwin] = nwin;
-    info[kInfoWins] = (int32_t)info.size();
-    const int* wp = reinterpret_cast<const int*>(wins.data());
-    info.insert(info.end(), wp, wp + (size_t)nwin * (sizeof(MfmaWin) / 4));
-    info[kInfoWinPtr] = (int32_t)info.size();
-    for (int j = 0; j <= nlat_out; ++j) info.push_back((int32_t)h.win_ptr[j]);
-    const int nqt = (D.nlon_out + kQ - 1) / kQ;
-    size_t stride = 0;
-    for (auto& bd : band) stride = std::max(stride, bd.size() * (size_t)nqt);
-    const int base = (int)info.size();
-    info[kInfoQ] = kQ;
-    info[kInfoNqt] = nqt;
-    info[kInfoWork] = base;
-    info[kInfoStride] = (int32_t)stride;
-    info.resize(info.size() + stride * kNumXcd, -1);
+    info[kInfoPiecePtr] = (int32_t)info.size();
+    info.insert(info.end(), piece_ptr.begin(), piece_ptr.end());
+    while (info.size() % 8) info.push_back(0);
+    info[kInfoPieces] = (int32_t)info.size();
+    info[kInfoNpieces] = (int32_t)pieces.size();
+    const int* pp = reinterpret_cast<const int*>(pieces.data());
+    info.insert(info.end(), pp, pp + pieces.size() * 8);
+    info[kInfoItems] = (int32_t)info.size();
+    int32_t off = 0;
     for (int k = 0; k < kNumXcd; ++k) {
-        size_t n = 0;
+        info[kInfoXcdOff + k] = off;
         for (int j : band[k])
-            for (int qt = 0; qt < nqt; ++qt) info[base + k * stride + n++] = j * nqt + qt;
+            for (int qt = 0; qt < nqt; ++qt) {
+                info.push_back(j);
+                info.push_back(qt * kQ);
+                info.push_back(piece_ptr[j]);
+                info.push_back(piece_ptr[j + 1] - piece_ptr[j]);
+            }
+        info[kInfoXcdLen + k] = (int32_t)band[k].size() * nqt;
+        off += info[kInfoXcdLen + k];
     }
+    if (info.size() > (size_t)0x7fffffff) return DISCO_OK;
     return DISCO_OK;
 }
 
@@ -190,12 +253,14 @@ __device__ __forceinline__ floatx16 mfma(const bf16x8_t& a, const bf16x8_t& b, c
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+
 __device__ __forceinline__ void lds_fence() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 // Weights into operand fragments: frag f = ((chunk*16 + ks)*(Co/32) + mt)*64 + lane holds
 // w[co = mt*32 + lane%32][ci = chunk*32 + 2*ks + lane/32][k = 0..7] (zero for k >= K).
 __global__ __launch_bounds__(256) void prep_weight_frags(const bf16_t* __restrict__ w,
-                                                          uint4* __restrict__ wf, int Ci, int Co,
+                                                          u32x4* __restrict__ wf, int Ci, int Co,
                                                           int K) {
     const int f = blockIdx.x * 256 + threadIdx.x;
     const int nf = (Ci / 32) * 16 * (Co / 32) * 64;
@@ -211,7 +276,7 @@ __global__ __launch_bounds__(256) void prep_weight_frags(const bf16_t* __restric
     uint16_t v[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[e] = e < K ? w[((size_t)co * Ci + ci) * K + e] : (uint16_t)0;
-    uint4 o;
+    u32x4 o;
     o.x = v[0] | ((uint32_t)v[1] << 16);
     o.y = v[2] | ((uint32_t)v[3] << 16);
     o.z = v[4] | ((uint32_t)v[5] << 16);
@@ -219,171 +284,374 @@ __global__ __launch_bounds__(256) void prep_weight_frags(const bf16_t* __restric
     wf[f] = o;
 }
 
-template <int S, int CO, int Q, int WM, int WN, typename TY>
-__global__ __launch_bounds__(256, 1) void fused_mfma(
-    const bf16_t* __restrict__ x, const uint4* __restrict__ wfrag, const float* __restrict__ bias,
-    TY* __restrict__ y, const MfmaWin* __restrict__ wins, const int32_t* __restrict__ win_ptr,
-    const uint4* __restrict__ taps, const int32_t* __restrict__ work, int work_stride, int nqt,
+#define DISCO_VM_CASE(n) \
+    case n: asm volatile("s_waitcnt vmcnt(" #n ")" ::: "memory"); break;
+
+// Wait until at most n vector-memory operations of this wave are outstanding
+// (n is wave-uniform; counts above 47 wait for everything).
+__device__ __forceinline__ void wait_vm(int n) {
+    switch (n) {
+        DISCO_VM_CASE(1) DISCO_VM_CASE(2) DISCO_VM_CASE(3) DISCO_VM_CASE(4) DISCO_VM_CASE(5)
+        DISCO_VM_CASE(6) DISCO_VM_CASE(7) DISCO_VM_CASE(8) DISCO_VM_CASE(9) DISCO_VM_CASE(10)
+        DISCO_VM_CASE(11) DISCO_VM_CASE(12) DISCO_VM_CASE(13) DISCO_VM_CASE(14) DISCO_VM_CASE(15)
+        DISCO_VM_CASE(16) DISCO_VM_CASE(17) DISCO_VM_CASE(18) DISCO_VM_CASE(19) DISCO_VM_CASE(20)
+        DISCO_VM_CASE(21) DISCO_VM_CASE(22) DISCO_VM_CASE(23) DISCO_VM_CASE(24) DISCO_VM_CASE(25)
+        DISCO_VM_CASE(26) DISCO_VM_CASE(27) DISCO_VM_CASE(28) DISCO_VM_CASE(29) DISCO_VM_CASE(30)
+        DISCO_VM_CASE(31) DISCO_VM_CASE(32) DISCO_VM_CASE(33) DISCO_VM_CASE(34) DISCO_VM_CASE(35)
+        DISCO_VM_CASE(36) DISCO_VM_CASE(37) DISCO_VM_CASE(38) DISCO_VM_CASE(39) DISCO_VM_CASE(40)
+        DISCO_VM_CASE(41) DISCO_VM_CASE(42) DISCO_VM_CASE(43) DISCO_VM_CASE(44) DISCO_VM_CASE(45)
+        DISCO_VM_CASE(46) DISCO_VM_CASE(47)
+        default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+    }
+}
+#undef DISCO_VM_CASE
+
+__device__ __forceinline__ void barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// 16-byte-per-lane DMA from global memory into LDS: lane l's 16 bytes land at
+// lds + 16*l.  Written as inline asm on purpose: for the compiler's own
+// global_load_lds it cannot tell which ring slot a pending transfer targets and
+// waits for all of them (vmcnt(0)) before every later LDS read, which would
+// serialise the ring.  These transfers are ordered explicitly instead: wait_vm
+// on this wave's outstanding count, then a barrier.  The statement has no
+// register outputs; M0 holds the LDS address.
+__device__ __forceinline__ void dma16(const void* src, const void* lds_dst) {
+    const uint32_t la = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(const lds_void*)lds_dst);
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(src), "s"(la)
+                 : "memory", "m0");
+}
+
+// Position in the stream of pieces a workgroup walks: for each batch entry,
+// each of its work items, each 32-channel chunk: the contraction pieces of the
+// item's output row, then kNw weight pieces (the chunk's channel/basis GEMM).
+struct Cursor {
+    int t;        // work item counter (batch-major); t == total: past the end
+    int cc;       // channel chunk
+    int pi;       // piece within the chunk: < np contraction, else weight piece pi - np
+    int j, q0, pbase, np, b;
+    int nj, nq0, npbase, nnp;   // the next work item (prefetched)
+};
+
+constexpr int kWaves = 8;   // two waves per SIMD
+constexpr int kThreads = 64 * kWaves;
+
+__device__ __forceinline__ u32x4 bit_select(uint32_t m, const u32x4& a, const u32x4& b) {
+    return (a & m) | (b & ~m);   // v_bfi_b32 per dword
+}
+
+template <int S, int CO, typename TY>
+__global__ __launch_bounds__(512, 1) void fused_mfma(
+    const bf16_t* __restrict__ x, const u32x4* __restrict__ wfrag, const float* __restrict__ bias,
+    TY* __restrict__ y, const int32_t* __restrict__ info, const u32x4* __restrict__ taps, int B,
     int Ci, int nlat_in, int nlon_in, int nlat_out, int nlon_out) {
-    constexpr int QW = Q / 4;            // outputs per wave in the contraction
-    constexpr int NBW = QW / 4;          // 4-output blocks per wave
-    constexpr int MT = CO / WM / 32;     // einsum M tiles per wave
-    constexpr int NT = Q / WN / 32;      // einsum N tiles per wave
-    constexpr int XKS = 256 + kXkPad;    // xk tile row stride (elements)
-    static_assert(QW % 8 == 0, "wave output range must keep 8-alignment");
+    constexpr int Q = kQ;
+    constexpr int QW = Q / kWaves;                 // outputs per wave in the contraction
+    constexpr int NBW = QW / 4;                    // 4-output blocks per wave
+    constexpr int RS = row_stride(S);
+    constexpr int NXI = x_instr(S);
+    constexpr int NCI = NXI + tap_instr(S);        // DMA loads of a contraction piece
+    constexpr int PWC = (NCI + kWaves - 1) / kWaves;
+    constexpr int SLOT = slot_size(S);
+    constexpr int XSL = NXI * 64;
+    constexpr int WM = CO / 32;                    // GEMM wave grid WM x WN, wave tile 32 x (Q/WN)
+    constexpr int WN = kWaves / WM;
+    constexpr int NT = Q / WN / 32;
+    constexpr int NWI = kGemmSteps * (CO / 32);    // DMA loads of a weight piece
+    constexpr int PWG = NWI / kWaves;
+    constexpr int kNw = 16 / kGemmSteps;           // weight pieces per channel chunk
+    constexpr int OS = sizeof(TY) == 4 ? 132 : 136;   // output tile row stride (elements)
+    constexpr int EPC = 16 / (int)sizeof(TY);         // output elements per 16-byte store
+    constexpr int CPR = Q / EPC;                      // 16-byte stores per output row
+    constexpr int NST = CO * CPR / kThreads;          // stores per thread per item
+    static_assert(NWI % kWaves == 0 && NWI * 64 <= SLOT, "weight piece layout");
+    static_assert(WM * WN == kWaves && NT >= 1, "GEMM wave grid");
+    static_assert(CO * OS * (int)sizeof(TY) <= Q * kXkStride * 2, "output tile fits the xk tile");
+    static_assert(QW % 8 == 0 && NBW % 2 == 0, "wave output range keeps 8-alignment");
+    static_assert(NST * kThreads == CO * CPR, "store split");
 
-    __shared__ __attribute__((aligned(16))) bf16_t xk_lds[Q * XKS];
-    __shared__ __attribute__((aligned(16))) bf16_t xs_lds[4 * 32 * kXsStride];
-
-    const int xcd = blockIdx.x % kNumXcd;
-    const int item = work[xcd * work_stride + blockIdx.x / kNumXcd];
-    if (item < 0) return;
-    const int b = blockIdx.y;
-    const int j = item / nqt;
-    const int q0 = (item % nqt) * Q;
+    __shared__ __attribute__((aligned(16))) bf16_t xk_lds[Q * kXkStride];
+    __shared__ __attribute__((aligned(16))) u32x4 ring[kRing][SLOT];
+    __shared__ float bias_lds[CO];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int lg = lane >> 5;           // lane group (k half of an operand)
+    const int lg = lane >> 5;
     const int l32 = lane & 31;
-    const int qwave = q0 + wave * QW;
     const int wm = wave / WN, wn = wave % WN;
 
-    bf16_t* xs = xs_lds + wave * 32 * kXsStride;
+    const int xcd = blockIdx.x % kNumXcd;
+    const int r = blockIdx.x / kNumXcd;
+    const int nwg = gridDim.x / kNumXcd;
+    const int xlen = info[kInfoXcdLen + xcd];
+    const int my_items = xlen > r ? (xlen - r + nwg - 1) / nwg : 0;   // items r, r + nwg, ...
+    const int total = B * my_items;
+    if (total == 0) return;
+    const int4* items = reinterpret_cast<const int4*>(info + info[kInfoItems]) + info[kInfoXcdOff + xcd];
+    const PieceDesc* pdesc = reinterpret_cast<const PieceDesc*>(info + info[kInfoPieces]);
+
+    for (int c = tid; c < CO; c += kThreads) bias_lds[c] = bias ? bias[c] : 0.0f;
+
     const size_t plane_in = (size_t)nlat_in * nlon_in;
-    const int w_begin = win_ptr[j], w_end = win_ptr[j + 1];
-
-    floatx16 g[MT][NT];
-#pragma unroll
-    for (int a = 0; a < MT; ++a)
-#pragma unroll
-        for (int c = 0; c < NT; ++c)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) g[a][c][e] = 0.0f;
-
+    const size_t plane_out = (size_t)nlat_out * nlon_out;
     const int nchunks = Ci / 32;
-    for (int cc = 0; cc < nchunks; ++cc) {
-        floatx16 acc[NBW];
-#pragma unroll
-        for (int n = 0; n < NBW; ++n)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) acc[n][e] = 0.0f;
-        const bf16_t* xc = x + ((size_t)b * Ci + (size_t)cc * 32) * plane_in;
+    const bool short_rows = 8 * RS > nlon_in;   // a strip may wrap more than once
 
-        for (int wi = w_begin; wi < w_end; ++wi) {
-            const MfmaWin m = wins[wi];
-            const int d0 = m.p_lo & 7;
-            const int nch = max(m.nch0, m.nch1);
-            const int u0 = S * qwave + (m.p_lo & ~7);
-            const bf16_t* xrow = xc + (size_t)m.lat * nlon_in;
-            // fragment slot v(b) of 4-output block b: u_b = 8*floor((d0 + 4*S*b)/8)
-            const bool hi = d0 >= 4;
-            // chunks per staged piece
-            const int vmax = (S == 1) ? (hi ? (NBW) / 2 : (NBW - 1) / 2) : (NBW - 1);
-            const int cpp = 1 + (kXsLen - 16 - 8 * vmax) / 16;
-            for (int c = 0; c < nch; c += cpp) {
-                // ---- stage 32 channels x 128 longitudes starting at u0 + 16c ----
-                lds_fence();
+    // this lane's slot in each of the wave's strip loads: channel offset, 16-byte group
+    int lch[PWC], lgr[PWC];
 #pragma unroll
-                for (int r = 0; r < 8; ++r) {
-                    const int pr = lane + 64 * r;
-                    const int ci = pr >> 4, grp = pr & 15;
-                    const int gx = (u0 + 16 * c + 8 * grp) % nlon_in;
-                    const uint4 v = *reinterpret_cast<const uint4*>(xrow + (size_t)ci * plane_in + gx);
-                    *reinterpret_cast<uint4*>(xs + ci * kXsStride + 8 * grp) = v;
-                }
-                lds_fence();
-                const int cend = min(nch, c + cpp);
-                for (int k = c; k < cend; ++k) {
-                    const int du = 16 * (k - c);
-                    uint4 t0 = make_uint4(0, 0, 0, 0), t1 = make_uint4(0, 0, 0, 0);
-                    if (k < m.nch0) t0 = taps[(size_t)(m.tap0 + k) * 64 + lane];
-                    if ((S & 1) && k < m.nch1) t1 = taps[(size_t)(m.tap1 + k) * 64 + lane];
-                    const bf16x8_t a0 = *reinterpret_cast<const bf16x8_t*>(&t0);
-                    const bf16x8_t a1 = *reinterpret_cast<const bf16x8_t*>(&t1);
-                    if (S == 1) {
-                        constexpr int NV = NBW / 2 + 1;
-                        bf16x8_t f[NV];
-#pragma unroll
-                        for (int v = 0; v < NV; ++v) {
-                            const int u = du + 8 * v + 8 * lg;
-                            f[v] = (u + 8 <= kXsLen)
-                                       ? *reinterpret_cast<const bf16x8_t*>(xs + l32 * kXsStride + u)
-                                       : f[0];
-                        }
-                        if (!hi) {
-#pragma unroll
-                            for (int n = 0; n < NBW; ++n) acc[n] = mfma((n & 1) ? a1 : a0, f[n / 2], acc[n]);
-                        } else {
-#pragma unroll
-                            for (int n = 0; n < NBW; ++n)
-                                acc[n] = mfma((n & 1) ? a1 : a0, f[(n + 1) / 2], acc[n]);
-                        }
-                    } else {
-#pragma unroll
-                        for (int n = 0; n < NBW; ++n) {
-                            const int u = du + 8 * n + 8 * lg;
-                            const bf16x8_t f = *reinterpret_cast<const bf16x8_t*>(xs + l32 * kXsStride + u);
-                            acc[n] = mfma(a0, f, acc[n]);
-                        }
+    for (int m = 0; m < PWC; ++m) {
+        const int sl = 64 * (wave + kWaves * m) + lane;
+        int ci = sl / RS, grp = sl - (sl / RS) * RS;
+        if (ci >= 32) { ci = 0; grp = 1 << 20; }   // padding slot: never valid
+        lch[m] = ci * (int)plane_in;
+        lgr[m] = grp;
+    }
+    const int nload_c = (NCI - wave + kWaves - 1) / kWaves;   // this wave's loads per piece
+
+    auto item_at = [&](int t) -> int4 {
+        const int bb = t / my_items;
+        return items[r + (t - bb * my_items) * nwg];
+    };
+    auto start = [&](Cursor& cu) {
+        cu.t = 0;
+        cu.cc = 0;
+        cu.pi = 0;
+        cu.b = 0;
+        const int4 it = item_at(0);
+        cu.j = it.x; cu.q0 = it.y; cu.pbase = it.z; cu.np = it.w;
+        const int4 nx = item_at(total > 1 ? 1 : 0);
+        cu.nj = nx.x; cu.nq0 = nx.y; cu.npbase = nx.z; cu.nnp = nx.w;
+    };
+    auto advance = [&](Cursor& cu) {
+        if (++cu.pi == cu.np + kNw) {
+            cu.pi = 0;
+            if (++cu.cc == nchunks) {
+                cu.cc = 0;
+                if (++cu.t < total) {
+                    cu.b = cu.t / my_items;
+                    cu.j = cu.nj; cu.q0 = cu.nq0; cu.pbase = cu.npbase; cu.np = cu.nnp;
+                    if (cu.t + 1 < total) {   // prefetch the item after
+                        const int4 nx = item_at(cu.t + 1);
+                        cu.nj = nx.x; cu.nq0 = nx.y; cu.npbase = nx.z; cu.nnp = nx.w;
                     }
                 }
             }
         }
-        // ---- xk tile: lane (ci = l32, lg) holds k = 4*lg + e%4 for qq = e/4 ----
-        __syncthreads();   // previous chunk's GEMM finished reading xk_lds
+    };
+
+    // Issue the DMA loads of the piece at `cu` (descriptor `pd`, loaded one
+    // iteration earlier) into ring slot `slot`; returns how many this wave
+    // issued.  Every load is issued: lanes without work read a valid address
+    // whose data is never used.
+    auto issue = [&](const Cursor& cu, const PieceDesc& pd, int slot) -> int {
+        u32x4* dst = ring[slot];
+        if (cu.pi >= cu.np) {
+            const u32x4* src =
+                wfrag + ((size_t)(cu.cc * 16 + (cu.pi - cu.np) * kGemmSteps) * (CO / 32)) * 64;
 #pragma unroll
-        for (int n = 0; n < NBW; ++n) {
+            for (int m = 0; m < PWG; ++m) {
+                const int i = wave + kWaves * m;
+                dma16(src + 64 * i + lane, dst + 64 * i);
+            }
+            return PWG;
+        }
+        const bf16_t* xrow =
+            x + ((size_t)cu.b * Ci + (size_t)cu.cc * 32) * plane_in + (size_t)pd.xoff;
+        int u0 = S * cu.q0 + pd.uoff;
+        if (u0 >= nlon_in) u0 -= nlon_in;
+        const int ngrp = piece_groups(S, pd.nck);
 #pragma unroll
-            for (int qq = 0; qq < 4; ++qq) {
-                const int ql = wave * QW + 4 * n + qq;
-                uint2 pk;
-                pk.x = (uint32_t)f32_to_bf16(acc[n][4 * qq + 0]) |
-                       ((uint32_t)f32_to_bf16(acc[n][4 * qq + 1]) << 16);
-                pk.y = (uint32_t)f32_to_bf16(acc[n][4 * qq + 2]) |
-                       ((uint32_t)f32_to_bf16(acc[n][4 * qq + 3]) << 16);
-                *reinterpret_cast<uint2*>(xk_lds + ql * XKS + l32 * 8 + 4 * lg) = pk;
+        for (int m = 0; m < PWC; ++m) {
+            const int i = wave + kWaves * m;
+            if (i < NXI) {
+                int gx = u0 + 8 * lgr[m];
+                if (gx >= nlon_in) gx = short_rows ? gx % nlon_in : gx - nlon_in;
+                const bf16_t* src = lgr[m] < ngrp ? xrow + lch[m] + gx : xrow + u0;
+                dma16(src, dst + 64 * i);
+            } else if (i < NCI) {
+                const int f = i - NXI;                  // chunk f / classes, class f % classes
+                const int kk = (S & 1) ? (f >> 1) : f;
+                const int cls = (S & 1) ? (f & 1) : 0;
+                const int nv = cls ? pd.nv1 : pd.nv0;
+                const int fr = kk < nv ? (cls ? pd.tap1 : pd.tap0) + kk : 0;   // 0: zero fragment
+                dma16(taps + (size_t)fr * 64 + lane, dst + 64 * i);
             }
         }
-        __syncthreads();
-        // ---- channel/basis GEMM over this chunk's 256 (ci, k) pairs ----
-        const uint4* wf = wfrag + (size_t)cc * 16 * (CO / 32) * 64;
-#pragma unroll 4
-        for (int ks = 0; ks < 16; ++ks) {
-            bf16x8_t af[MT], bf[NT];
+        return nload_c;
+    };
+    auto fetch = [&](const Cursor& cu, PieceDesc& pd) {
+        if (cu.t < total && cu.pi < cu.np) pd = pdesc[cu.pbase + cu.pi];
+    };
+    // per-piece metadata for the compute side: chunks | window starts in the upper 8-group half
+    auto meta = [&](const Cursor& cu, const PieceDesc& pd) -> int {
+        return cu.pi < cu.np ? (pd.nck | ((pd.d0 >= 4 ? 1 : 0) << 4)) : 0;
+    };
+
+    floatx16 g[NT];
 #pragma unroll
-            for (int a = 0; a < MT; ++a) {
-                const uint4 v = wf[((size_t)ks * (CO / 32) + wm * MT + a) * 64 + lane];
-                af[a] = *reinterpret_cast<const bf16x8_t*>(&v);
-            }
+    for (int c = 0; c < NT; ++c)
 #pragma unroll
-            for (int c = 0; c < NT; ++c) {
-                const int ql = wn * (Q / WN) + c * 32 + l32;
-                bf[c] = *reinterpret_cast<const bf16x8_t*>(xk_lds + ql * XKS + ks * 16 + 8 * lg);
-            }
+        for (int e = 0; e < 16; ++e) g[c][e] = 0.0f;
+    floatx16 acc[NBW];
 #pragma unroll
-            for (int a = 0; a < MT; ++a)
+    for (int n = 0; n < NBW; ++n)
 #pragma unroll
-                for (int c = 0; c < NT; ++c) g[a][c] = mfma(af[a], bf[c], g[a][c]);
-        }
+        for (int e = 0; e < 16; ++e) acc[n][e] = 0.0f;
+
+    Cursor ic;   // issue position: three pieces ahead of the compute position
+    start(ic);
+    Cursor cu = ic;
+    PieceDesc pdn;
+    pdn.nck = 1; pdn.d0 = 0; pdn.xoff = 0; pdn.uoff = 0; pdn.tap0 = 0; pdn.tap1 = 0; pdn.nv0 = 0; pdn.nv1 = 0;
+    fetch(ic, pdn);
+    // after_k: loads (and stores) this wave issued after the k-th piece in flight;
+    // mq_k: metadata of the k-th piece in flight
+    int after0 = 0, after1 = 0, after2 = 0;
+    int mq0 = 0, mq1 = 0, mq2 = 0;
+    int nissued = 0;
+    for (int k = 0; k < kRing - 1 && ic.t < total; ++k) {
+        const int n = issue(ic, pdn, nissued);
+        const int mt = meta(ic, pdn);
+        if (k == 0) mq0 = mt; else if (k == 1) mq1 = mt; else mq2 = mt;
+        if (k >= 1) after0 += n;
+        if (k >= 2) after1 += n;
+        ++nissued;
+        advance(ic);
+        fetch(ic, pdn);
     }
-    // ---- epilogue ----
-    TY* yb = y + (size_t)b * CO * nlat_out * nlon_out + (size_t)j * nlon_out;
+    __syncthreads();   // bias_lds
+
+    for (int seq = 0; cu.t < total; ++seq) {
+        wait_vm(after0);
+        barrier();   // piece seq is in LDS for every wave; slot (seq + 3) % 4 is free
+        int after3 = 0, mq3 = 0;
+        if (ic.t < total) {
+            const int n = issue(ic, pdn, nissued % kRing);
+            mq3 = meta(ic, pdn);
+            after1 += n;
+            after2 += n;
+            ++nissued;
+            advance(ic);
+            fetch(ic, pdn);   // used at the next iteration
+        }
+        const int slot = seq % kRing;
+        if (cu.pi < cu.np) {
+            // ---- contraction piece ----
+            const bf16_t* xs = reinterpret_cast<const bf16_t*>(ring[slot]);
+            const u32x4* ts = ring[slot] + XSL;
+            const int row = l32 * RS + (S * QW * wave) / 8 + lg;
+            const int nck = mq0 & 15;
+            // S = 1: block n of chunk kk reads staged group 2*kk + n/2, one more for
+            // odd n when the window starts in the upper half of its 8-group; class-0
+            // taps for even blocks, class 1 for odd.  S = 2: group 2*kk + n, class 0.
+            // Chunks beyond a class's band hold the zero fragment.
+            const uint32_t hm = (mq0 >> 4) & 1 ? 0xffffffffu : 0u;
+            for (int kk = 0; kk < nck; ++kk) {
+                constexpr int NV = S == 1 ? NBW / 2 + 1 : NBW;
+                u32x4 f[NV];
 #pragma unroll
-    for (int c = 0; c < NT; ++c) {
-        const int q = q0 + wn * (Q / WN) + c * 32 + l32;
-        if (q >= nlon_out) continue;
+                for (int v = 0; v < NV; ++v)
+                    f[v] = *reinterpret_cast<const u32x4*>(xs + 8 * (row + 2 * kk + v));
+                const int f0 = (S & 1) ? 2 * kk : kk;
+                const bf16x8_t a0 = as_bf16x8(ts[64 * f0 + lane]);
+                if (S == 1) {
+                    const bf16x8_t a1 = as_bf16x8(ts[64 * (f0 + 1) + lane]);
 #pragma unroll
-        for (int a = 0; a < MT; ++a) {
+                    for (int m = 0; m < NBW / 2; ++m) {
+                        acc[2 * m] = mfma(a0, as_bf16x8(f[m]), acc[2 * m]);
+                        acc[2 * m + 1] =
+                            mfma(a1, as_bf16x8(bit_select(hm, f[m + 1], f[m])), acc[2 * m + 1]);
+                    }
+                } else {
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int co = wm * (CO / WM) + a * 32 + 8 * (e >> 2) + 4 * lg + (e & 3);
-                const float bv = bias ? bias[co] : 0.0f;
-                store_f(yb, (size_t)co * nlat_out * nlon_out + q, g[a][c][e] + bv);
+                    for (int n = 0; n < NBW; ++n) acc[n] = mfma(a0, as_bf16x8(f[n]), acc[n]);
+                }
+            }
+            if (cu.pi == cu.np - 1) {
+                // the chunk's contraction is complete: xk tile (bf16) -> LDS
+#pragma unroll
+                for (int n = 0; n < NBW; ++n) {
+#pragma unroll
+                    for (int qq = 0; qq < 4; ++qq) {
+                        const int ql = wave * QW + 4 * n + qq;
+                        const float4v v4 = {acc[n][4 * qq + 0], acc[n][4 * qq + 1],
+                                            acc[n][4 * qq + 2], acc[n][4 * qq + 3]};
+                        const u32x2 pk =
+                            __builtin_bit_cast(u32x2, __builtin_convertvector(v4, bf16x4_t));
+                        *reinterpret_cast<u32x2*>(xk_lds + ql * kXkStride + l32 * 8 + 4 * lg) = pk;
+                    }
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) acc[n][e] = 0.0f;
+                }
+            }
+        } else {
+            // ---- weight piece: kGemmSteps k-steps of the channel/basis GEMM ----
+            const int wp = cu.pi - cu.np;
+            const u32x4* ws = ring[slot];
+#pragma unroll
+            for (int ks = 0; ks < kGemmSteps; ++ks) {
+                const int kg = wp * kGemmSteps + ks;
+                const bf16x8_t af = as_bf16x8(ws[(ks * (CO / 32) + wm) * 64 + lane]);
+#pragma unroll
+                for (int c = 0; c < NT; ++c) {
+                    const int ql = wn * (Q / WN) + c * 32 + l32;
+                    const bf16x8_t bf =
+                        *reinterpret_cast<const bf16x8_t*>(xk_lds + ql * kXkStride + kg * 16 + 8 * lg);
+                    g[c] = mfma(af, bf, g[c]);
+                }
+            }
+            if (wp == kNw - 1 && cu.cc == nchunks - 1) {
+                // ---- epilogue: the item's output tile, transposed through LDS ----
+                barrier();   // every wave is done reading the xk tile
+                // lane base pointers; every element below is a compile-time offset
+                TY* ot = reinterpret_cast<TY*>(xk_lds) + (wm * 32 + 4 * lg) * OS + wn * (Q / WN) + l32;
+                const float* bl = bias_lds + wm * 32 + 4 * lg;
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int cr = 8 * (e >> 2) + (e & 3);   // row within the lane base
+                    const float bv = bl[cr];
+#pragma unroll
+                    for (int c = 0; c < NT; ++c) {
+                        const float v = g[c][e] + bv;
+                        if constexpr (sizeof(TY) == 4) ot[cr * OS + c * 32] = v;
+                        else ot[cr * OS + c * 32] = f32_to_bf16(v);
+                        g[c][e] = 0.0f;
+                    }
+                }
+                barrier();
+                // thread tid stores 16-byte column group tid % CPR of rows
+                // tid / CPR + k * (kThreads / CPR); columns past the end rewrite the
+                // row's last valid 16 bytes with the same data
+                const int qc = min((tid % CPR) * EPC, ((nlon_out - cu.q0 - 1) / EPC) * EPC);
+                const TY* os = reinterpret_cast<const TY*>(xk_lds) + (tid / CPR) * OS + qc;
+                TY* yb = y + ((size_t)cu.b * CO + tid / CPR) * plane_out +
+                         (size_t)cu.j * nlon_out + cu.q0 + qc;
+#pragma unroll
+                for (int st = 0; st < NST; ++st)
+                    *reinterpret_cast<u32x4*>(yb + (size_t)st * (kThreads / CPR) * plane_out) =
+                        *reinterpret_cast<const u32x4*>(os + st * (kThreads / CPR) * OS);
+                after1 += NST;
+                after2 += NST;
+                after3 += NST;
             }
         }
+        after0 = after1;
+        after1 = after2;
+        after2 = after3;
+        mq0 = mq1;
+        mq1 = mq2;
+        mq2 = mq3;
+        advance(cu);
     }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 }  // namespace
@@ -393,47 +661,52 @@ int try_launch_fused_mfma(const disco_psi* psi, const void* x, const void* w, co
                           int* rc) {
     const DevPsi& d = psi->dev;
     const HostPsi& h = psi->host;
+    const disco_psi_desc& D = h.desc;
     if (!d.mfma_ok || groups != 1 || Ci % 32 != 0 || (Co != 128 && Co != 64) || h.K > 8) return 0;
-    if ((reinterpret_cast<uintptr_t>(x) & 15) != 0) return 0;
     const int S = h.stride;
     if (S != 1 && S != 2) return 0;
-    const int* hi = d.mfma_info_host.data();
-    const int nqt = hi[kInfoNqt];
-    const int woff = hi[kInfoWork];
-    const int wstride = hi[kInfoStride];
+    // 16-byte loads of x and 16-byte stores of y rows
+    const int epc = y_dtype == DISCO_F32 ? 4 : 8;
+    if ((reinterpret_cast<uintptr_t>(x) & 15) != 0 || (reinterpret_cast<uintptr_t>(y) & 15) != 0 ||
+        D.nlon_out % epc != 0)
+        return 0;
+    // channel offsets of one 32-channel chunk are 32-bit
+    if ((int64_t)D.nlat_in * D.nlon_in * 32 >= ((int64_t)1 << 31)) return 0;
+    if (B <= 0) return 0;
     const int32_t* dinfo = d.mfma_row_info;
-    const MfmaWin* wins = reinterpret_cast<const MfmaWin*>(dinfo + hi[kInfoWins]);
-    const int32_t* win_ptr = dinfo + hi[kInfoWinPtr];
-    const int32_t* work = dinfo + woff;
-    const uint4* taps = static_cast<const uint4*>(d.mfma_taps);
+    const u32x4* taps = static_cast<const u32x4*>(d.mfma_taps);
 
     // weight fragments (stream-ordered workspace)
     const size_t nfrag = (size_t)(Ci / 32) * 16 * (Co / 32) * 64;
     void* wsp = nullptr;
-    hipError_t e = hipMallocAsync(&wsp, nfrag * sizeof(uint4), st);
+    hipError_t e = hipMallocAsync(&wsp, nfrag * sizeof(u32x4), st);
     if (e != hipSuccess) {
         (void)hipGetLastError();
         *rc = set_error(e == hipErrorOutOfMemory ? DISCO_ENOMEM : DISCO_EHIP,
                         "hipMallocAsync for the weight fragments failed: %s", hipGetErrorString(e));
         return 1;
     }
-    uint4* wf = static_cast<uint4*>(wsp);
+    u32x4* wf = static_cast<u32x4*>(wsp);
     hipLaunchKernelGGL(prep_weight_frags, dim3((unsigned)((nfrag + 255) / 256)), dim3(256), 0, st,
                        static_cast<const bf16_t*>(w), wf, Ci, Co, h.K);
     const bf16_t* X = static_cast<const bf16_t*>(x);
-    const disco_psi_desc& D = h.desc;
-    dim3 grid((unsigned)(kNumXcd * wstride), (unsigned)B);
-#define DISCO_FM(SS, CC, QQ, WMM, WNN, TT)                                                         \
-    hipLaunchKernelGGL((fused_mfma<SS, CC, QQ, WMM, WNN, TT>), grid, dim3(256), 0, st, X, wf, bias, \
-                       (TT*)y, wins, win_ptr, taps, work, wstride, nqt, Ci, D.nlat_in, D.nlon_in,   \
-                       D.nlat_out, D.nlon_out)
+    // one persistent workgroup per CU: 32 per XCD
+    int dev = 0, ncu = 256;
+    if (hipGetDevice(&dev) == hipSuccess)
+        (void)hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+    (void)hipGetLastError();
+    const int per_xcd = std::max(1, ncu / kNumXcd);
+    dim3 grid((unsigned)(kNumXcd * per_xcd));
+#define DISCO_FM(SS, CC, TT)                                                                 \
+    hipLaunchKernelGGL((fused_mfma<SS, CC, TT>), grid, dim3(kThreads), 0, st, X, wf, bias, (TT*)y, \
+                       dinfo, taps, B, Ci, D.nlat_in, D.nlon_in, D.nlat_out, D.nlon_out)
     const bool f32 = y_dtype == DISCO_F32;
     if (Co == 128) {
-        if (S == 1) { if (f32) DISCO_FM(1, 128, 128, 2, 2, float); else DISCO_FM(1, 128, 128, 2, 2, bf16_t); }
-        else        { if (f32) DISCO_FM(2, 128, 128, 2, 2, float); else DISCO_FM(2, 128, 128, 2, 2, bf16_t); }
+        if (S == 1) { if (f32) DISCO_FM(1, 128, float); else DISCO_FM(1, 128, bf16_t); }
+        else        { if (f32) DISCO_FM(2, 128, float); else DISCO_FM(2, 128, bf16_t); }
     } else {
-        if (S == 1) { if (f32) DISCO_FM(1, 64, 128, 2, 2, float); else DISCO_FM(1, 64, 128, 2, 2, bf16_t); }
-        else        { if (f32) DISCO_FM(2, 64, 128, 2, 2, float); else DISCO_FM(2, 64, 128, 2, 2, bf16_t); }
+        if (S == 1) { if (f32) DISCO_FM(1, 64, float); else DISCO_FM(1, 64, bf16_t); }
+        else        { if (f32) DISCO_FM(2, 64, float); else DISCO_FM(2, 64, bf16_t); }
     }
 #undef DISCO_FM
     hipError_t le = hipGetLastError();

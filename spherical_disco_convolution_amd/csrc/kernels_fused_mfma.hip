@@ -319,32 +319,30 @@ typedef __attribute__((address_space(3))) void lds_void;
 // serialise the ring.  These transfers are ordered explicitly instead: wait_vm
 // on this wave's outstanding count, then a barrier.  The statement has no
 // register outputs; M0 holds the LDS address.
-__device__ __forceinline__ void dma16(const void* src, const void* lds_dst) {
-    const uint32_t la = __builtin_amdgcn_readfirstlane(
-        (uint32_t)(uintptr_t)(const lds_void*)lds_dst);
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds_addr) {
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                  :
-                 : "v"(src), "s"(la)
+                 : "v"(src), "s"(lds_addr)
                  : "memory", "m0");
 }
 
-// Position in the stream of pieces a workgroup walks: for each batch entry,
-// each of its work items, each 32-channel chunk: the contraction pieces of the
-// item's output row, then kNw weight pieces (the chunk's channel/basis GEMM).
-struct Cursor {
-    int t;        // work item counter (batch-major); t == total: past the end
-    int cc;       // channel chunk
-    int pi;       // piece within the chunk: < np contraction, else weight piece pi - np
-    int j, q0, pbase, np, b;
-    int nj, nq0, npbase, nnp;   // the next work item (prefetched)
-};
-
 constexpr int kWaves = 8;   // two waves per SIMD
 constexpr int kThreads = 64 * kWaves;
+constexpr int kDmaWaves = 4;   // waves 0-3 issue the DMA; waves 4-7 write the output
 
 __device__ __forceinline__ u32x4 bit_select(uint32_t m, const u32x4& a, const u32x4& b) {
     return (a & m) | (b & ~m);   // v_bfi_b32 per dword
 }
+
+// Record of one piece in the ring, written by the DMA waves when they issue it
+// and read by every wave when it is consumed.
+enum : int {
+    kRecNck = 0xf,          // chunks (contraction piece)
+    kRecHi = 1 << 4,        // window starts in the upper half of its 8-group (S = 1)
+    kRecWeight = 1 << 5,    // weight piece; its index within the chunk in bits 6-7
+    kRecLastC = 1 << 8,     // last contraction piece of the chunk: write the xk tile
+    kRecEpi = 1 << 9,       // last weight piece of the work item: write the output tile
+};
 
 template <int S, int CO, typename TY>
 __global__ __launch_bounds__(512, 1) void fused_mfma(
@@ -357,35 +355,39 @@ __global__ __launch_bounds__(512, 1) void fused_mfma(
     constexpr int RS = row_stride(S);
     constexpr int NXI = x_instr(S);
     constexpr int NCI = NXI + tap_instr(S);        // DMA loads of a contraction piece
-    constexpr int PWC = (NCI + kWaves - 1) / kWaves;
+    constexpr int PWD = (NCI + kDmaWaves - 1) / kDmaWaves;   // loads per DMA wave per piece
     constexpr int SLOT = slot_size(S);
     constexpr int XSL = NXI * 64;
     constexpr int WM = CO / 32;                    // GEMM wave grid WM x WN, wave tile 32 x (Q/WN)
     constexpr int WN = kWaves / WM;
     constexpr int NT = Q / WN / 32;
     constexpr int NWI = kGemmSteps * (CO / 32);    // DMA loads of a weight piece
-    constexpr int PWG = NWI / kWaves;
     constexpr int kNw = 16 / kGemmSteps;           // weight pieces per channel chunk
     constexpr int OS = sizeof(TY) == 4 ? 132 : 136;   // output tile row stride (elements)
     constexpr int EPC = 16 / (int)sizeof(TY);         // output elements per 16-byte store
     constexpr int CPR = Q / EPC;                      // 16-byte stores per output row
-    constexpr int NST = CO * CPR / kThreads;          // stores per thread per item
-    static_assert(NWI % kWaves == 0 && NWI * 64 <= SLOT, "weight piece layout");
+    constexpr int kStoreThreads = kThreads - 64 * kDmaWaves;
+    constexpr int NST = CO * CPR / kStoreThreads;     // stores per store thread per item
+    static_assert(NWI <= kDmaWaves * PWD && NWI * 64 <= SLOT, "weight piece layout");
     static_assert(WM * WN == kWaves && NT >= 1, "GEMM wave grid");
     static_assert(CO * OS * (int)sizeof(TY) <= Q * kXkStride * 2, "output tile fits the xk tile");
     static_assert(QW % 8 == 0 && NBW % 2 == 0, "wave output range keeps 8-alignment");
-    static_assert(NST * kThreads == CO * CPR, "store split");
+    static_assert(NST * kStoreThreads == CO * CPR, "store split");
+    static_assert(2 * PWD <= 63, "vmcnt range");
+    static_assert(kDmaWaves * PWD == NCI || NCI - kDmaWaves >= NXI, "repeated loads are tap loads");
 
     __shared__ __attribute__((aligned(16))) bf16_t xk_lds[Q * kXkStride];
     __shared__ __attribute__((aligned(16))) u32x4 ring[kRing][SLOT];
+    __shared__ int4 rec_lds[kRing];
     __shared__ float bias_lds[CO];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     const int lg = lane >> 5;
     const int l32 = lane & 31;
     const int wm = wave / WN, wn = wave % WN;
+    const bool dma_wave = wave < kDmaWaves;
 
     const int xcd = blockIdx.x % kNumXcd;
     const int r = blockIdx.x / kNumXcd;
@@ -394,106 +396,11 @@ __global__ __launch_bounds__(512, 1) void fused_mfma(
     const int my_items = xlen > r ? (xlen - r + nwg - 1) / nwg : 0;   // items r, r + nwg, ...
     const int total = B * my_items;
     if (total == 0) return;
-    const int4* items = reinterpret_cast<const int4*>(info + info[kInfoItems]) + info[kInfoXcdOff + xcd];
-    const PieceDesc* pdesc = reinterpret_cast<const PieceDesc*>(info + info[kInfoPieces]);
-
-    for (int c = tid; c < CO; c += kThreads) bias_lds[c] = bias ? bias[c] : 0.0f;
-
+    const int nchunks = Ci / 32;
     const size_t plane_in = (size_t)nlat_in * nlon_in;
     const size_t plane_out = (size_t)nlat_out * nlon_out;
-    const int nchunks = Ci / 32;
-    const bool short_rows = 8 * RS > nlon_in;   // a strip may wrap more than once
 
-    // this lane's slot in each of the wave's strip loads: channel offset, 16-byte group
-    int lch[PWC], lgr[PWC];
-#pragma unroll
-    for (int m = 0; m < PWC; ++m) {
-        const int sl = 64 * (wave + kWaves * m) + lane;
-        int ci = sl / RS, grp = sl - (sl / RS) * RS;
-        if (ci >= 32) { ci = 0; grp = 1 << 20; }   // padding slot: never valid
-        lch[m] = ci * (int)plane_in;
-        lgr[m] = grp;
-    }
-    const int nload_c = (NCI - wave + kWaves - 1) / kWaves;   // this wave's loads per piece
-
-    auto item_at = [&](int t) -> int4 {
-        const int bb = t / my_items;
-        return items[r + (t - bb * my_items) * nwg];
-    };
-    auto start = [&](Cursor& cu) {
-        cu.t = 0;
-        cu.cc = 0;
-        cu.pi = 0;
-        cu.b = 0;
-        const int4 it = item_at(0);
-        cu.j = it.x; cu.q0 = it.y; cu.pbase = it.z; cu.np = it.w;
-        const int4 nx = item_at(total > 1 ? 1 : 0);
-        cu.nj = nx.x; cu.nq0 = nx.y; cu.npbase = nx.z; cu.nnp = nx.w;
-    };
-    auto advance = [&](Cursor& cu) {
-        if (++cu.pi == cu.np + kNw) {
-            cu.pi = 0;
-            if (++cu.cc == nchunks) {
-                cu.cc = 0;
-                if (++cu.t < total) {
-                    cu.b = cu.t / my_items;
-                    cu.j = cu.nj; cu.q0 = cu.nq0; cu.pbase = cu.npbase; cu.np = cu.nnp;
-                    if (cu.t + 1 < total) {   // prefetch the item after
-                        const int4 nx = item_at(cu.t + 1);
-                        cu.nj = nx.x; cu.nq0 = nx.y; cu.npbase = nx.z; cu.nnp = nx.w;
-                    }
-                }
-            }
-        }
-    };
-
-    // Issue the DMA loads of the piece at `cu` (descriptor `pd`, loaded one
-    // iteration earlier) into ring slot `slot`; returns how many this wave
-    // issued.  Every load is issued: lanes without work read a valid address
-    // whose data is never used.
-    auto issue = [&](const Cursor& cu, const PieceDesc& pd, int slot) -> int {
-        u32x4* dst = ring[slot];
-        if (cu.pi >= cu.np) {
-            const u32x4* src =
-                wfrag + ((size_t)(cu.cc * 16 + (cu.pi - cu.np) * kGemmSteps) * (CO / 32)) * 64;
-#pragma unroll
-            for (int m = 0; m < PWG; ++m) {
-                const int i = wave + kWaves * m;
-                dma16(src + 64 * i + lane, dst + 64 * i);
-            }
-            return PWG;
-        }
-        const bf16_t* xrow =
-            x + ((size_t)cu.b * Ci + (size_t)cu.cc * 32) * plane_in + (size_t)pd.xoff;
-        int u0 = S * cu.q0 + pd.uoff;
-        if (u0 >= nlon_in) u0 -= nlon_in;
-        const int ngrp = piece_groups(S, pd.nck);
-#pragma unroll
-        for (int m = 0; m < PWC; ++m) {
-            const int i = wave + kWaves * m;
-            if (i < NXI) {
-                int gx = u0 + 8 * lgr[m];
-                if (gx >= nlon_in) gx = short_rows ? gx % nlon_in : gx - nlon_in;
-                const bf16_t* src = lgr[m] < ngrp ? xrow + lch[m] + gx : xrow + u0;
-                dma16(src, dst + 64 * i);
-            } else if (i < NCI) {
-                const int f = i - NXI;                  // chunk f / classes, class f % classes
-                const int kk = (S & 1) ? (f >> 1) : f;
-                const int cls = (S & 1) ? (f & 1) : 0;
-                const int nv = cls ? pd.nv1 : pd.nv0;
-                const int fr = kk < nv ? (cls ? pd.tap1 : pd.tap0) + kk : 0;   // 0: zero fragment
-                dma16(taps + (size_t)fr * 64 + lane, dst + 64 * i);
-            }
-        }
-        return nload_c;
-    };
-    auto fetch = [&](const Cursor& cu, PieceDesc& pd) {
-        if (cu.t < total && cu.pi < cu.np) pd = pdesc[cu.pbase + cu.pi];
-    };
-    // per-piece metadata for the compute side: chunks | window starts in the upper 8-group half
-    auto meta = [&](const Cursor& cu, const PieceDesc& pd) -> int {
-        return cu.pi < cu.np ? (pd.nck | ((pd.d0 >= 4 ? 1 : 0) << 4)) : 0;
-    };
+    for (int c = tid; c < CO; c += kThreads) bias_lds[c] = bias ? bias[c] : 0.0f;
 
     floatx16 g[NT];
 #pragma unroll
@@ -506,54 +413,133 @@ __global__ __launch_bounds__(512, 1) void fused_mfma(
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[n][e] = 0.0f;
 
-    Cursor ic;   // issue position: three pieces ahead of the compute position
-    start(ic);
-    Cursor cu = ic;
-    PieceDesc pdn;
-    pdn.nck = 1; pdn.d0 = 0; pdn.xoff = 0; pdn.uoff = 0; pdn.tap0 = 0; pdn.tap1 = 0; pdn.nv0 = 0; pdn.nv1 = 0;
-    fetch(ic, pdn);
-    // after_k: loads (and stores) this wave issued after the k-th piece in flight;
-    // mq_k: metadata of the k-th piece in flight
-    int after0 = 0, after1 = 0, after2 = 0;
-    int mq0 = 0, mq1 = 0, mq2 = 0;
-    int nissued = 0;
-    for (int k = 0; k < kRing - 1 && ic.t < total; ++k) {
-        const int n = issue(ic, pdn, nissued);
-        const int mt = meta(ic, pdn);
-        if (k == 0) mq0 = mt; else if (k == 1) mq1 = mt; else mq2 = mt;
-        if (k >= 1) after0 += n;
-        if (k >= 2) after1 += n;
-        ++nissued;
-        advance(ic);
-        fetch(ic, pdn);
+    // ---------------- DMA waves: the issue cursor ----------------
+    // (all of its state is wave-uniform; only waves 0-3 touch it)
+    const int4* items = reinterpret_cast<const int4*>(info + info[kInfoItems]) + info[kInfoXcdOff + xcd];
+    const PieceDesc* pdesc = reinterpret_cast<const PieceDesc*>(info + info[kInfoPieces]);
+    const uint32_t ring_base =
+        __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_void*)&ring[0][0]);
+    const bool short_rows = 8 * RS > nlon_in;   // a strip may wrap more than once
+    int lch[PWD], lgr[PWD];                     // this lane's slot in the wave's strip loads
+#pragma unroll
+    for (int m = 0; m < PWD; ++m) {
+        const int sl = 64 * (wave + kDmaWaves * m) + lane;
+        int ci = sl / RS, grp = sl - (sl / RS) * RS;
+        if (ci >= 32) { ci = 0; grp = 1 << 20; }   // padding slot: never valid
+        lch[m] = ci * (int)plane_in;
+        lgr[m] = grp;
     }
-    __syncthreads();   // bias_lds
-
-    for (int seq = 0; cu.t < total; ++seq) {
-        wait_vm(after0);
-        barrier();   // piece seq is in LDS for every wave; slot (seq + 3) % 4 is free
-        int after3 = 0, mq3 = 0;
-        if (ic.t < total) {
-            const int n = issue(ic, pdn, nissued % kRing);
-            mq3 = meta(ic, pdn);
-            after1 += n;
-            after2 += n;
-            ++nissued;
-            advance(ic);
-            fetch(ic, pdn);   // used at the next iteration
+    // cursor: item k of this workgroup's list, batch entry b, chunk cc, piece pi
+    int c_k = 0, c_b = 0, c_cc = 0, c_pi = 0, c_t = 0;
+    int4 c_it = items[r];                           // (j, q0, first piece, pieces)
+    int4 c_nx = items[r + (my_items > 1 ? nwg : 0)];   // the next item (prefetched)
+    const bf16_t* c_xb = x;                         // channel chunk base of (b, cc)
+    PieceDesc pdn;                                  // descriptor of the piece at the cursor
+    pdn = pdesc[c_it.z];
+    auto advance = [&]() {
+        if (++c_pi == c_it.w + kNw) {
+            c_pi = 0;
+            if (++c_cc == nchunks) {
+                c_cc = 0;
+                ++c_t;
+                if (++c_k == my_items) { c_k = 0; ++c_b; }
+                c_it = c_nx;
+                int k2 = c_k + 1, b2 = c_b;
+                if (k2 == my_items) { k2 = 0; ++b2; }
+                if (b2 < B) c_nx = items[r + k2 * nwg];
+            }
+            c_xb = x + ((size_t)c_b * Ci + (size_t)c_cc * 32) * plane_in;
         }
-        const int slot = seq % kRing;
-        if (cu.pi < cu.np) {
+        if (c_t < total && c_pi < c_it.w) pdn = pdesc[c_it.z + c_pi];   // used at the next issue
+    };
+    // issue the piece at the cursor into ring slot `slot` (PWD loads per DMA
+    // wave; loads without work repeat a valid load) and publish its record
+    auto issue = [&](int slot) {
+        const uint32_t dst = ring_base + (uint32_t)slot * (SLOT * 16);
+        int rec;
+        if (c_pi >= c_it.w) {
+            const int wp = c_pi - c_it.w;
+            const u32x4* src = wfrag + ((size_t)(c_cc * 16 + wp * kGemmSteps) * (CO / 32)) * 64;
+#pragma unroll
+            for (int m = 0; m < PWD; ++m) {
+                int i = wave + kDmaWaves * m;
+                if (i >= NWI) i = wave + kDmaWaves * ((NWI - 1 - wave) / kDmaWaves);   // repeat
+                dma16(src + 64 * i + lane, dst + i * 1024);
+            }
+            rec = kRecWeight | (wp << 6) |
+                  (wp == kNw - 1 && c_cc == nchunks - 1 ? kRecEpi : 0);
+        } else {
+            const bf16_t* xrow = c_xb + pdn.xoff;
+            int u0 = S * c_it.y + pdn.uoff;
+            if (u0 >= nlon_in) u0 -= nlon_in;
+            const int ngrp = piece_groups(S, pdn.nck);
+#pragma unroll
+            for (int m = 0; m < PWD; ++m) {
+                const int i0 = wave + kDmaWaves * m;
+                if (i0 < NXI) {
+                    int gx = u0 + 8 * lgr[m];
+                    if (short_rows) gx %= nlon_in;
+                    else gx -= gx >= nlon_in ? nlon_in : 0;
+                    const bf16_t* src = lgr[m] < ngrp ? xrow + lch[m] + gx : xrow + u0;
+                    dma16(src, dst + i0 * 1024);
+                } else {
+                    // loads past the piece's end repeat this wave's previous tap load
+                    const int i = i0 >= NCI ? i0 - kDmaWaves : i0;
+                    const int f = i - NXI;              // chunk f / classes, class f % classes
+                    const int kk = (S & 1) ? (f >> 1) : f;
+                    const int cls = (S & 1) ? (f & 1) : 0;
+                    const int nv = cls ? pdn.nv1 : pdn.nv0;
+                    const int fr = kk < nv ? (cls ? pdn.tap1 : pdn.tap0) + kk : 0;   // 0: zero fragment
+                    dma16(taps + (size_t)fr * 64 + lane, dst + i * 1024);
+                }
+            }
+            rec = pdn.nck | (pdn.d0 >= 4 ? kRecHi : 0) | (c_pi == c_it.w - 1 ? kRecLastC : 0);
+        }
+        if (wave == 0 && lane == 0) rec_lds[slot] = make_int4(rec, c_b, c_it.x, c_it.y);
+    };
+
+    // prologue: three pieces in flight (every item has at least 1 + kNw pieces)
+    bool more = false;   // the issue cursor has pieces left (DMA waves)
+    if (dma_wave) {
+        for (int k = 0; k < kRing - 1; ++k) {
+            issue(k);
+            advance();
+        }
+        more = c_t < total;
+    }
+    __syncthreads();   // bias_lds, rec_lds of the first pieces
+
+    // The compute side walks the same stream through the records; it ends with
+    // the epilogue of the last work item.
+    int done = 0;
+    for (int seq = 0;; ++seq) {
+        // DMA waves: piece seq is complete once only the two later pieces' loads remain
+        if (dma_wave) {
+            if (more) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * PWD) : "memory");
+            else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        }
+        barrier();   // piece seq is in LDS for every wave; slot (seq + 3) % 4 is free
+        const int slot = seq & (kRing - 1);
+        const int4 rq = rec_lds[slot];
+        const int rf = __builtin_amdgcn_readfirstlane(rq.x);
+        if (dma_wave && more) {
+            if (c_t < total) {
+                issue((seq + kRing - 1) & (kRing - 1));
+                advance();
+            }
+            more = c_t < total;
+        }
+        if (!(rf & kRecWeight)) {
             // ---- contraction piece ----
             const bf16_t* xs = reinterpret_cast<const bf16_t*>(ring[slot]);
             const u32x4* ts = ring[slot] + XSL;
             const int row = l32 * RS + (S * QW * wave) / 8 + lg;
-            const int nck = mq0 & 15;
+            const int nck = rf & kRecNck;
             // S = 1: block n of chunk kk reads staged group 2*kk + n/2, one more for
             // odd n when the window starts in the upper half of its 8-group; class-0
             // taps for even blocks, class 1 for odd.  S = 2: group 2*kk + n, class 0.
             // Chunks beyond a class's band hold the zero fragment.
-            const uint32_t hm = (mq0 >> 4) & 1 ? 0xffffffffu : 0u;
+            const uint32_t hm = (rf & kRecHi) ? 0xffffffffu : 0u;
             for (int kk = 0; kk < nck; ++kk) {
                 constexpr int NV = S == 1 ? NBW / 2 + 1 : NBW;
                 u32x4 f[NV];
@@ -575,7 +561,7 @@ __global__ __launch_bounds__(512, 1) void fused_mfma(
                     for (int n = 0; n < NBW; ++n) acc[n] = mfma(a0, as_bf16x8(f[n]), acc[n]);
                 }
             }
-            if (cu.pi == cu.np - 1) {
+            if (rf & kRecLastC) {
                 // the chunk's contraction is complete: xk tile (bf16) -> LDS
 #pragma unroll
                 for (int n = 0; n < NBW; ++n) {
@@ -594,7 +580,7 @@ __global__ __launch_bounds__(512, 1) void fused_mfma(
             }
         } else {
             // ---- weight piece: kGemmSteps k-steps of the channel/basis GEMM ----
-            const int wp = cu.pi - cu.np;
+            const int wp = (rf >> 6) & 3;
             const u32x4* ws = ring[slot];
 #pragma unroll
             for (int ks = 0; ks < kGemmSteps; ++ks) {
@@ -608,8 +594,11 @@ __global__ __launch_bounds__(512, 1) void fused_mfma(
                     g[c] = mfma(af, bf, g[c]);
                 }
             }
-            if (wp == kNw - 1 && cu.cc == nchunks - 1) {
+            if (rf & kRecEpi) {
                 // ---- epilogue: the item's output tile, transposed through LDS ----
+                const int eb = __builtin_amdgcn_readfirstlane(rq.y);
+                const int ej = __builtin_amdgcn_readfirstlane(rq.z);
+                const int eq0 = __builtin_amdgcn_readfirstlane(rq.w);
                 barrier();   // every wave is done reading the xk tile
                 // lane base pointers; every element below is a compile-time offset
                 TY* ot = reinterpret_cast<TY*>(xk_lds) + (wm * 32 + 4 * lg) * OS + wn * (Q / WN) + l32;
@@ -627,29 +616,23 @@ __global__ __launch_bounds__(512, 1) void fused_mfma(
                     }
                 }
                 barrier();
-                // thread tid stores 16-byte column group tid % CPR of rows
-                // tid / CPR + k * (kThreads / CPR); columns past the end rewrite the
-                // row's last valid 16 bytes with the same data
-                const int qc = min((tid % CPR) * EPC, ((nlon_out - cu.q0 - 1) / EPC) * EPC);
-                const TY* os = reinterpret_cast<const TY*>(xk_lds) + (tid / CPR) * OS + qc;
-                TY* yb = y + ((size_t)cu.b * CO + tid / CPR) * plane_out +
-                         (size_t)cu.j * nlon_out + cu.q0 + qc;
+                if (!dma_wave) {
+                    // store thread st stores 16-byte column group st % CPR of rows
+                    // st / CPR + k * (kStoreThreads / CPR); columns past the end
+                    // rewrite the row's last valid 16 bytes with the same data
+                    const int st = tid - 64 * kDmaWaves;
+                    const int qc = min((st % CPR) * EPC, ((nlon_out - eq0 - 1) / EPC) * EPC);
+                    const TY* os = reinterpret_cast<const TY*>(xk_lds) + (st / CPR) * OS + qc;
+                    TY* yb = y + ((size_t)eb * CO + st / CPR) * plane_out + (size_t)ej * nlon_out +
+                             eq0 + qc;
 #pragma unroll
-                for (int st = 0; st < NST; ++st)
-                    *reinterpret_cast<u32x4*>(yb + (size_t)st * (kThreads / CPR) * plane_out) =
-                        *reinterpret_cast<const u32x4*>(os + st * (kThreads / CPR) * OS);
-                after1 += NST;
-                after2 += NST;
-                after3 += NST;
+                    for (int k = 0; k < NST; ++k)
+                        *reinterpret_cast<u32x4*>(yb + (size_t)k * (kStoreThreads / CPR) * plane_out) =
+                            *reinterpret_cast<const u32x4*>(os + k * (kStoreThreads / CPR) * OS);
+                }
+                if (++done == total) break;
             }
         }
-        after0 = after1;
-        after1 = after2;
-        after2 = after3;
-        mq0 = mq1;
-        mq1 = mq2;
-        mq2 = mq3;
-        advance(cu);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }

@@ -326,9 +326,9 @@ __device__ __forceinline__ void dma16(const void* src, uint32_t lds_addr) {
                  : "memory", "m0");
 }
 
-constexpr int kWaves = 8;   // two waves per SIMD
-constexpr int kThreads = 64 * kWaves;
-constexpr int kDmaWaves = 4;   // waves 0-3 issue the DMA; waves 4-7 write the output
+constexpr int kDmaWaves = 4;       // waves 0-3 only issue the DMA (one per SIMD)
+constexpr int kWaves = 8;          // compute waves 4-11 (two per SIMD)
+constexpr int kThreads = 64 * (kDmaWaves + kWaves);
 
 __device__ __forceinline__ u32x4 bit_select(uint32_t m, const u32x4& a, const u32x4& b) {
     return (a & m) | (b & ~m);   // v_bfi_b32 per dword
@@ -345,7 +345,7 @@ enum : int {
 };
 
 template <int S, int CO, typename TY>
-__global__ __launch_bounds__(512, 1) void fused_mfma(
+__global__ __launch_bounds__(768, 1) void fused_mfma(
     const bf16_t* __restrict__ x, const u32x4* __restrict__ wfrag, const float* __restrict__ bias,
     TY* __restrict__ y, const int32_t* __restrict__ info, const u32x4* __restrict__ taps, int B,
     int Ci, int nlat_in, int nlon_in, int nlat_out, int nlon_out) {
@@ -366,7 +366,7 @@ __global__ __launch_bounds__(512, 1) void fused_mfma(
     constexpr int OS = sizeof(TY) == 4 ? 132 : 136;   // output tile row stride (elements)
     constexpr int EPC = 16 / (int)sizeof(TY);         // output elements per 16-byte store
     constexpr int CPR = Q / EPC;                      // 16-byte stores per output row
-    constexpr int kStoreThreads = kThreads - 64 * kDmaWaves;
+    constexpr int kStoreThreads = 64 * kWaves;
     constexpr int NST = CO * CPR / kStoreThreads;     // stores per store thread per item
     static_assert(NWI <= kDmaWaves * PWD && NWI * 64 <= SLOT, "weight piece layout");
     static_assert(WM * WN == kWaves && NT >= 1, "GEMM wave grid");
@@ -383,11 +383,12 @@ __global__ __launch_bounds__(512, 1) void fused_mfma(
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+    const bool dma_wave = wv < kDmaWaves;
+    const int wave = dma_wave ? wv : wv - kDmaWaves;   // index among the DMA / compute waves
     const int lg = lane >> 5;
     const int l32 = lane & 31;
     const int wm = wave / WN, wn = wave % WN;
-    const bool dma_wave = wave < kDmaWaves;
 
     const int xcd = blockIdx.x % kNumXcd;
     const int r = blockIdx.x / kNumXcd;
@@ -454,7 +455,7 @@ __global__ __launch_bounds__(512, 1) void fused_mfma(
     };
     // issue the piece at the cursor into ring slot `slot` (PWD loads per DMA
     // wave; loads without work repeat a valid load) and publish its record
-    auto issue = [&](int slot) {
+    auto issue = [&](int slot) -> int {
         const uint32_t dst = ring_base + (uint32_t)slot * (SLOT * 16);
         int rec;
         if (c_pi >= c_it.w) {
@@ -496,40 +497,55 @@ __global__ __launch_bounds__(512, 1) void fused_mfma(
             rec = pdn.nck | (pdn.d0 >= 4 ? kRecHi : 0) | (c_pi == c_it.w - 1 ? kRecLastC : 0);
         }
         if (wave == 0 && lane == 0) rec_lds[slot] = make_int4(rec, c_b, c_it.x, c_it.y);
+        return rec;
     };
 
-    // prologue: three pieces in flight (every item has at least 1 + kNw pieces)
-    bool more = false;   // the issue cursor has pieces left (DMA waves)
     if (dma_wave) {
+        // ================= DMA waves =================
+        // prologue: three pieces in flight (every item has at least 1 + kNw pieces)
+        uint32_t epi_mask = 0;   // ring slots whose piece ends a work item
         for (int k = 0; k < kRing - 1; ++k) {
-            issue(k);
+            if (issue(k) & kRecEpi) epi_mask |= 1u << k;
             advance();
         }
-        more = c_t < total;
-    }
-    __syncthreads();   // bias_lds, rec_lds of the first pieces
-
-    // The compute side walks the same stream through the records; it ends with
-    // the epilogue of the last work item.
-    int done = 0;
-    for (int seq = 0;; ++seq) {
-        // DMA waves: piece seq is complete once only the two later pieces' loads remain
-        if (dma_wave) {
+        bool more = c_t < total;
+        __syncthreads();   // bias_lds, rec_lds of the first pieces
+        int done = 0;
+        for (int seq = 0;; ++seq) {
+            // piece seq is complete once only the two later pieces' loads remain
             if (more) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * PWD) : "memory");
             else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            barrier();   // piece seq is in LDS for every wave; slot (seq + 3) % 4 is free
+            const int slot = seq & (kRing - 1);
+            if (more) {
+                const int ns = (seq + kRing - 1) & (kRing - 1);
+                if (issue(ns) & kRecEpi) epi_mask |= 1u << ns;
+                advance();
+                more = c_t < total;
+            }
+            if (epi_mask & (1u << slot)) {
+                // the compute waves write the output tile between two barriers
+                epi_mask &= ~(1u << slot);
+                barrier();
+                barrier();
+                if (++done == total) break;
+            }
         }
-        barrier();   // piece seq is in LDS for every wave; slot (seq + 3) % 4 is free
+        return;
+    }
+
+    // ================= compute waves =================
+    __syncthreads();   // bias_lds, rec_lds of the first pieces
+    // The compute side walks the stream through the records; it ends with the
+    // epilogue of the last work item.
+    int done = 0;
+    for (int seq = 0;; ++seq) {
+        barrier();   // piece seq is in LDS for every wave
         const int slot = seq & (kRing - 1);
         const int4 rq = rec_lds[slot];
         const int rf = __builtin_amdgcn_readfirstlane(rq.x);
-        if (dma_wave && more) {
-            if (c_t < total) {
-                issue((seq + kRing - 1) & (kRing - 1));
-                advance();
-            }
-            more = c_t < total;
-        }
         if (!(rf & kRecWeight)) {
+            // ---- contraction piece ----        } else if (!(rf & kRecWeight)) {
             // ---- contraction piece ----
             const bf16_t* xs = reinterpret_cast<const bf16_t*>(ring[slot]);
             const u32x4* ts = ring[slot] + XSL;
@@ -616,7 +632,7 @@ __global__ __launch_bounds__(512, 1) void fused_mfma(
                     }
                 }
                 barrier();
-                if (!dma_wave) {
+                {
                     // store thread st stores 16-byte column group st % CPR of rows
                     // st / CPR + k * (kStoreThreads / CPR); columns past the end
                     // rewrite the row's last valid 16 bytes with the same data

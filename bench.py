@@ -1,6 +1,8 @@
 """Benchmark of the forward DISCO convolution on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c4] [--no-cpu-baseline]
+    python bench.py --copy-calibration      (one plain device copy of known size, for
+                                             calibrating rocprofv3 FETCH_SIZE / WRITE_SIZE)
 
 A step is one forward pass (the fused kernel: contraction and channel/basis
 contraction in one launch) over one batch of seeded synthetic input that is
@@ -14,7 +16,14 @@ Prints one JSON line.  `value` is output points x output channels per second.
 plus 2 FLOPs per non-zero Psi entry, channel and output longitude) against
 the MI355X dense bf16 matrix peak (2.5 PFLOP/s) or, for float32 workloads,
 the float32 peak (157.3 TFLOP/s).  `cpu_baseline` is the float64 CPU oracle
-timed on a bounded sample of output rows of the same workload.
+timed on a bounded sample of output rows of the same workload, single-threaded,
+and extrapolated to the whole workload by support-point weighting (the oracle's
+time is linear in the support size of the rows it evaluates).
+
+The timed unit of the fused forward is one disco_fused_fwd call: a small kernel
+that tiles the weights into matrix-core operand fragments, then the fused
+kernel.  `roofline.achieved` divides the algorithmic work by that call's
+average HIP-event time, so it slightly understates the fused kernel itself.
 """
 from __future__ import annotations
 
@@ -32,10 +41,29 @@ if ROOT not in sys.path:
 PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
 HBM_PEAK_GBS = 8000.0
 
+METRIC = "DISCO fwd output-points\u00b7Cout/s at 721x1440 C=128 K=7; % HBM/MFMA roofline"
+
 # rocprofv3 HBM counters of the fused kernel at the headline workload, per
-# launch (FETCH_SIZE + WRITE_SIZE, scaled by the copy-kernel calibration);
-# None until measured for the current kernel.
-MEASURED_TRAFFIC_BYTES = {}
+# launch: FETCH_SIZE x 2.000 + WRITE_SIZE x 1.000 (factors from a 512 MiB
+# device copy, see profiles/).  Keyed by the SHA-1 of the kernel source the
+# counters were taken with: when the source has changed the figure is stale
+# and `traffic` is reported as null.
+MEASURED_TRAFFIC_BYTES = {
+    "c4": {"bytes": 1412312510, "kernel_source_sha1": "e093aba13d7165fa88be6f6ffb4b7929d010f071"},
+}
+FUSED_SOURCE = os.path.join(ROOT, "spherical_disco_convolution_amd", "csrc", "kernels_fused_mfma.hip")
+
+
+def measured_traffic(key):
+    import hashlib
+    m = MEASURED_TRAFFIC_BYTES.get(key)
+    if m is None or not os.path.exists(FUSED_SOURCE):
+        return None
+    with open(FUSED_SOURCE, "rb") as f:
+        sha = hashlib.sha1(f.read()).hexdigest()
+    return m["bytes"] if sha == m["kernel_source_sha1"] else None
+
+COPY_CALIBRATION_BYTES = 512 << 20
 
 
 def parse():
@@ -47,7 +75,24 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-unfused", action="store_true")
     ap.add_argument("--fused-only", action="store_true", help="time only the fused kernel (profiling)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run one device-to-device copy of %d MiB and exit" % (COPY_CALIBRATION_BYTES >> 20))
     return ap.parse_args()
+
+
+def copy_calibration():
+    """One plain copy of known size: FETCH_SIZE and WRITE_SIZE of its kernel
+    divided into COPY_CALIBRATION_BYTES give the counters' scale factors."""
+    import torch
+    n = COPY_CALIBRATION_BYTES // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": COPY_CALIBRATION_BYTES,
+                      "read_bytes": COPY_CALIBRATION_BYTES, "write_bytes": COPY_CALIBRATION_BYTES}),
+          flush=True)
 
 
 def algorithmic_flops(wl, nnz_nonzero):
@@ -82,33 +127,42 @@ def time_region(fn, steps, torch):
 
 
 def cpu_baseline(wl, x, w):
-    import numpy as np
     import oracle
+    from threadpoolctl import threadpool_limits
     d = oracle.Desc(wl.nlat_in, wl.nlon_in, wl.nlat_out, wl.nlon_out, wl.kernel_shape,
                     wl.theta_cutoff)
     csr = oracle.psi(d)
     # systematic sample of output rows, all longitudes, batches and channels
-    step = max(1, wl.nlat_out // 12)
+    step = max(1, wl.nlat_out // 60)
     rows = list(range(step // 2, wl.nlat_out, step))
     sup = sum(int(csr.row_ptr[j + 1] - csr.row_ptr[j]) for j in rows)
-    t0 = time.perf_counter()
-    oracle.forward(d, x, w, wl.groups, csr=csr, rows=rows)
-    dt = time.perf_counter() - t0
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        oracle.forward(d, x, w, wl.groups, csr=csr, rows=rows)
+        dt = time.perf_counter() - t0
     pts = wl.B * len(rows) * wl.nlon_out * wl.Co
+    # the oracle's time is linear in the support it evaluates: extrapolate the
+    # sample to the whole workload by support weighting
+    t_all = dt * csr.nnz / sup
+    total_pts = wl.B * wl.nlat_out * wl.nlon_out * wl.Co
     return {
-        "value": pts / dt,
-        "unit": "output-points*Cout/s",
+        "value": total_pts / t_all,
+        "unit": "output-points\u00b7Cout/s",
         "cores": 1,
         "kind": "oracle",
         "sample": (f"{len(rows)} of {wl.nlat_out} output rows (every {step}th from {step // 2}), "
-                   f"all longitudes, batches and channels; {sup / len(rows):.0f} support points "
-                   f"per sampled row vs {csr.nnz / wl.nlat_out:.0f} over all rows; "
-                   f"float64 numpy, single thread; {dt:.1f} s"),
+                   f"all longitudes, batches and channels, {sup} of {csr.nnz} support points; "
+                   f"float64 numpy, BLAS limited to 1 thread; {dt:.1f} s, i.e. {pts / dt:.3g} "
+                   f"output-points\u00b7Cout/s on the sample, extrapolated by support to "
+                   f"{t_all:.0f} s for the whole workload"),
     }
 
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 "
                           "(multi-GPU sharding is described, not implemented)"}), flush=True)
@@ -164,7 +218,7 @@ def main():
     dsize = 2 if wl.dtype == "bf16" else 4
     peak = PEAK_TFLOPS[wl.dtype]
     achieved = f_alg / kernel_s / 1e12
-    traffic = MEASURED_TRAFFIC_BYTES.get(key)
+    traffic = measured_traffic(key)
     roofline = {"bound": "mfma" if wl.dtype == "bf16" else "alu", "achieved": round(achieved, 3),
                 "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                 "traffic": traffic}
@@ -191,9 +245,9 @@ def main():
         extra["unfused_ms"] = round((t_c + t_e) / n * 1000, 4)
         del xk
     line = {
-        "metric": "DISCO fwd output-points*Cout/s at 721x1440 C=128 K=7",
+        "metric": METRIC,
         "value": value,
-        "unit": "output-points*Cout/s",
+        "unit": "output-points\u00b7Cout/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,

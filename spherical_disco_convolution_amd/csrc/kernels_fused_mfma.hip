@@ -158,7 +158,10 @@ int build_mfma_tables(disco_psi* psi, std::vector<char>& taps, std::vector<int32
     std::vector<PieceDesc> pieces;
     std::vector<double> cost(nlat_out, 0.0);
     for (int j = 0; j < nlat_out; ++j) {
-        double c = 4 * (2048.0 + 400.0) + 3000.0;   // weight pieces + epilogue (cycles)
+        // relative cost of one work item of this row: a fixed part (weight
+        // pieces, epilogue) plus per contraction piece and per chunk; the
+        // weights are a least-squares fit of measured item times at 721x1440
+        double c = 17.17;
         for (int64_t n = h.win_ptr[j]; n < h.win_ptr[j + 1]; ++n) {
             const MfmaWin& m = wins[n];
             const int nch = std::max(m.nch0, m.nch1);
@@ -173,13 +176,13 @@ int build_mfma_tables(disco_psi* psi, std::vector<char>& taps, std::vector<int32
                 pd.tap0 = pd.nv0 > 0 ? m.tap0 + c0 : 0;
                 pd.tap1 = pd.nv1 > 0 ? m.tap1 + c0 : 0;
                 pieces.push_back(pd);
-                c += 8.0 * 32.0 * pd.nck + 400.0;
+                c += 1.779 + 0.461 * pd.nck;
             }
         }
         if ((int)pieces.size() == piece_ptr[j]) {
             PieceDesc pd{0, 0, 0, 0, 1, 0, 0, 0};
             pieces.push_back(pd);
-            c += 8.0 * 32.0 + 400.0;
+            c += 1.779 + 0.461;
         }
         piece_ptr[j + 1] = (int32_t)pieces.size();
         cost[j] = c;

@@ -58,6 +58,7 @@ constexpr int kQ = 128;             // output longitudes per work item
 constexpr int kNbw = kQ / 16;       // 4-output blocks per wave
 constexpr int kRing = 4;            // LDS ring slots: three pieces in flight while one is consumed
 constexpr int kXkStride = 264;      // xk tile row: 256 (ci, k) pairs + 8 pad
+constexpr int kXkTStride = 136;     // transposed xk tile row (k, ci): 128 outputs + 8 pad
 constexpr int kGemmSteps = 4;       // GEMM k-steps (16 kappa each) per streamed weight piece
 // Chunks of 16 input longitudes per contraction piece.
 constexpr int cp_max(int S) { return S == 1 ? 4 : 2; }
@@ -321,11 +322,13 @@ typedef __attribute__((address_space(3))) void lds_void;
 // waits for all of them (vmcnt(0)) before every later LDS read, which would
 // serialise the ring.  These transfers are ordered explicitly instead: wait_vm
 // on this wave's outstanding count, then a barrier.  The statement has no
-// register outputs; M0 holds the LDS address.
+// register outputs; M0 holds the LDS address, which is uniform across the
+// wave (readfirstlane keeps it in a scalar register where the compiler's
+// uniformity analysis loses track of that).
 __device__ __forceinline__ void dma16(const void* src, uint32_t lds_addr) {
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                  :
-                 : "v"(src), "s"(lds_addr)
+                 : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_addr))
                  : "memory", "m0");
 }
 
@@ -344,14 +347,18 @@ enum : int {
     kRecHi = 1 << 4,        // window starts in the upper half of its 8-group (S = 1)
     kRecWeight = 1 << 5,    // weight piece; its index within the chunk in bits 6-7
     kRecLastC = 1 << 8,     // last contraction piece of the chunk: write the xk tile
-    kRecEpi = 1 << 9,       // last weight piece of the work item: write the output tile
+    kRecEpi = 1 << 9,       // last piece of the work item (fused: write the output tile)
+    kRecChunkShift = 16,    // channel chunk index in bits 16 and up
 };
 
-template <int S, int CO, typename TY>
+// XK = true: the contraction alone.  No weight pieces are streamed; the last
+// piece of a channel chunk stores the chunk's xk tile (bf16) to
+// y = xk[B, Ci, K, nlat_out, nlon_out] instead of feeding the GEMM.
+template <int S, int CO, typename TY, bool XK = false>
 __global__ __launch_bounds__(768, 1) void fused_mfma(
     const bf16_t* __restrict__ x, const u32x4* __restrict__ wfrag, const float* __restrict__ bias,
     TY* __restrict__ y, const int32_t* __restrict__ info, const u32x4* __restrict__ taps, int B,
-    int Ci, int nlat_in, int nlon_in, int nlat_out, int nlon_out) {
+    int Ci, int K, int nlat_in, int nlon_in, int nlat_out, int nlon_out) {
     constexpr int Q = kQ;
     constexpr int QW = Q / kWaves;                 // outputs per wave in the contraction
     constexpr int NBW = QW / 4;                    // 4-output blocks per wave
@@ -378,8 +385,10 @@ __global__ __launch_bounds__(768, 1) void fused_mfma(
     static_assert(NST * kStoreThreads == CO * CPR, "store split");
     static_assert(2 * PWD <= 63, "vmcnt range");
     static_assert(kDmaWaves * PWD == NCI || NCI - kDmaWaves >= NXI, "repeated loads are tap loads");
+    static_assert(!XK || (sizeof(TY) == 2 && 32 * 16 == 64 * kWaves), "xk store split");
 
-    __shared__ __attribute__((aligned(16))) bf16_t xk_lds[Q * kXkStride];
+    // fused: xk tile [q][(ci, k)]; XK: transposed tile [(k, ci)][q]
+    __shared__ __attribute__((aligned(16))) bf16_t xk_lds[XK ? 256 * kXkTStride : Q * kXkStride];
     __shared__ __attribute__((aligned(16))) u32x4 ring[kRing][SLOT];
     __shared__ int4 rec_lds[kRing];
     __shared__ float bias_lds[CO];
@@ -441,7 +450,7 @@ __global__ __launch_bounds__(768, 1) void fused_mfma(
     PieceDesc pdn;                                  // descriptor of the piece at the cursor
     pdn = pdesc[c_it.z];
     auto advance = [&]() {
-        if (++c_pi == c_it.w + kNw) {
+        if (++c_pi == c_it.w + (XK ? 0 : kNw)) {
             c_pi = 0;
             if (++c_cc == nchunks) {
                 c_cc = 0;
@@ -461,7 +470,7 @@ __global__ __launch_bounds__(768, 1) void fused_mfma(
     auto issue = [&](int slot) -> int {
         const uint32_t dst = ring_base + (uint32_t)slot * (SLOT * 16);
         int rec;
-        if (c_pi >= c_it.w) {
+        if (!XK && c_pi >= c_it.w) {
             const int wp = c_pi - c_it.w;
             const u32x4* src = wfrag + ((size_t)(c_cc * 16 + wp * kGemmSteps) * (CO / 32)) * 64;
 #pragma unroll
@@ -497,7 +506,9 @@ __global__ __launch_bounds__(768, 1) void fused_mfma(
                     dma16(taps + (size_t)fr * 64 + lane, dst + i * 1024);
                 }
             }
-            rec = pdn.nck | (pdn.d0 >= 4 ? kRecHi : 0) | (c_pi == c_it.w - 1 ? kRecLastC : 0);
+            const bool last = c_pi == c_it.w - 1;
+            rec = pdn.nck | (pdn.d0 >= 4 ? kRecHi : 0) | (last ? kRecLastC : 0) |
+                  (XK && last && c_cc == nchunks - 1 ? kRecEpi : 0) | (c_cc << kRecChunkShift);
         }
         if (wave == 0 && lane == 0) rec_lds[slot] = make_int4(rec, c_b, c_it.x, c_it.y);
         return rec;
@@ -505,10 +516,14 @@ __global__ __launch_bounds__(768, 1) void fused_mfma(
 
     if (dma_wave) {
         // ================= DMA waves =================
-        // prologue: three pieces in flight (every item has at least 1 + kNw pieces)
-        uint32_t epi_mask = 0;   // ring slots whose piece ends a work item
-        for (int k = 0; k < kRing - 1; ++k) {
-            if (issue(k) & kRecEpi) epi_mask |= 1u << k;
+        // prologue: three pieces in flight (a fused work item has at least
+        // 1 + kNw pieces; XK: up to three)
+        uint32_t epi_mask = 0;     // ring slots whose piece ends a work item
+        uint32_t lastc_mask = 0;   // XK: ring slots whose piece ends a channel chunk
+        for (int k = 0; k < kRing - 1 && (!XK || c_t < total); ++k) {
+            const int rec = issue(k);
+            if (rec & kRecEpi) epi_mask |= 1u << k;
+            if (XK && (rec & kRecLastC)) lastc_mask |= 1u << k;
             advance();
         }
         bool more = c_t < total;
@@ -522,15 +537,25 @@ __global__ __launch_bounds__(768, 1) void fused_mfma(
             const int slot = seq & (kRing - 1);
             if (more) {
                 const int ns = (seq + kRing - 1) & (kRing - 1);
-                if (issue(ns) & kRecEpi) epi_mask |= 1u << ns;
+                const int rec = issue(ns);
+                if (rec & kRecEpi) epi_mask |= 1u << ns;
+                if (XK && (rec & kRecLastC)) lastc_mask |= 1u << ns;
                 advance();
                 more = c_t < total;
             }
+            if (XK && (lastc_mask & (1u << slot))) {
+                // the compute waves write the xk tile before this barrier and
+                // store it after
+                lastc_mask &= ~(1u << slot);
+                barrier();
+            }
             if (epi_mask & (1u << slot)) {
-                // the compute waves write the output tile between two barriers
+                // fused: the compute waves write the output tile between two barriers
                 epi_mask &= ~(1u << slot);
-                barrier();
-                barrier();
+                if (!XK) {
+                    barrier();
+                    barrier();
+                }
                 if (++done == total) break;
             }
         }
@@ -580,7 +605,43 @@ __global__ __launch_bounds__(768, 1) void fused_mfma(
                     for (int n = 0; n < NBW; ++n) acc[n] = mfma(a0, as_bf16x8(f[n]), acc[n]);
                 }
             }
-            if (rf & kRecLastC) {
+            if (XK && (rf & kRecLastC)) {
+                // the chunk's contraction is complete: transposed xk tile
+                // (bf16) -> LDS, row k * 32 + ci, 4 outputs per 8-byte write
+#pragma unroll
+                for (int n = 0; n < NBW; ++n) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float4v v4 = {acc[n][e], acc[n][4 + e], acc[n][8 + e], acc[n][12 + e]};
+                        const u32x2 pk =
+                            __builtin_bit_cast(u32x2, __builtin_convertvector(v4, bf16x4_t));
+                        *reinterpret_cast<u32x2*>(xk_lds + ((4 * lg + e) * 32 + l32) * kXkTStride +
+                                                  wave * QW + 4 * n) = pk;
+                    }
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) acc[n][e] = 0.0f;
+                }
+                barrier();   // the tile is complete
+                // store thread st writes 16 bytes (8 outputs) of row (k, st / 16)
+                // per k; outputs past the row's end are not written
+                const int eb = __builtin_amdgcn_readfirstlane(rq.y);
+                const int ej = __builtin_amdgcn_readfirstlane(rq.z);
+                const int eq0 = __builtin_amdgcn_readfirstlane(rq.w);
+                const int cc = rf >> kRecChunkShift;
+                const int st = tid - 64 * kDmaWaves;
+                const int ci = st >> 4, q = eq0 + 8 * (st & 15);
+                const bf16_t* os = xk_lds + ci * kXkTStride + 8 * (st & 15);
+                TY* ob = y + ((size_t)(eb * Ci + cc * 32 + ci) * K) * plane_out +
+                         (size_t)ej * nlon_out + q;
+                if (q < nlon_out) {
+                    for (int k = 0; k < K; ++k)
+                        *reinterpret_cast<u32x4*>(ob + (size_t)k * plane_out) =
+                            *reinterpret_cast<const u32x4*>(os + k * 32 * kXkTStride);
+                }
+                if (rf & kRecEpi) {
+                    if (++done == total) break;
+                }
+            } else if (!XK && (rf & kRecLastC)) {
                 // the chunk's contraction is complete: xk tile (bf16) -> LDS
 #pragma unroll
                 for (int n = 0; n < NBW; ++n) {
@@ -701,7 +762,7 @@ int try_launch_fused_mfma(const disco_psi* psi, const void* x, const void* w, co
     dim3 grid((unsigned)(kNumXcd * per_xcd));
 #define DISCO_FM(SS, CC, TT)                                                                 \
     hipLaunchKernelGGL((fused_mfma<SS, CC, TT>), grid, dim3(kThreads), 0, st, X, wf, bias, (TT*)y, \
-                       dinfo, taps, B, Ci, D.nlat_in, D.nlon_in, D.nlat_out, D.nlon_out)
+                       dinfo, taps, B, Ci, h.K, D.nlat_in, D.nlon_in, D.nlat_out, D.nlon_out)
     const bool f32 = y_dtype == DISCO_F32;
     if (Co == 128) {
         if (S == 1) { if (f32) DISCO_FM(1, 128, float); else DISCO_FM(1, 128, bf16_t); }
@@ -720,6 +781,47 @@ int try_launch_fused_mfma(const disco_psi* psi, const void* x, const void* w, co
     if (fe != hipSuccess) {
         (void)hipGetLastError();
         *rc = set_error(DISCO_EHIP, "hipFreeAsync failed: %s", hipGetErrorString(fe));
+        return 1;
+    }
+    *rc = DISCO_OK;
+    return 1;
+}
+
+int try_launch_contract_mfma(const disco_psi* psi, const void* x, void* xk, int B, int C,
+                             hipStream_t st, int* rc) {
+    const DevPsi& d = psi->dev;
+    const HostPsi& h = psi->host;
+    const disco_psi_desc& D = h.desc;
+    if (!d.mfma_ok || C % 32 != 0 || h.K > 8 || B <= 0) return 0;
+    const int S = h.stride;
+    if (S != 1 && S != 2) return 0;
+    // 16-byte loads of x rows and 16-byte stores of xk rows
+    if ((reinterpret_cast<uintptr_t>(x) & 15) != 0 || (reinterpret_cast<uintptr_t>(xk) & 15) != 0 ||
+        D.nlon_out % 8 != 0)
+        return 0;
+    // channel offsets of one 32-channel chunk are 32-bit
+    if ((int64_t)D.nlat_in * D.nlon_in * 32 >= ((int64_t)1 << 31)) return 0;
+    int dev = 0, ncu = 256;
+    if (hipGetDevice(&dev) == hipSuccess)
+        (void)hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+    (void)hipGetLastError();
+    const int per_xcd = std::max(1, ncu / kNumXcd);
+    dim3 grid((unsigned)(kNumXcd * per_xcd));
+    const bf16_t* X = static_cast<const bf16_t*>(x);
+    bf16_t* XK = static_cast<bf16_t*>(xk);
+    const int32_t* dinfo = d.mfma_row_info;
+    const u32x4* taps = static_cast<const u32x4*>(d.mfma_taps);
+#define DISCO_CM(SS)                                                                             \
+    hipLaunchKernelGGL((fused_mfma<SS, 128, bf16_t, true>), grid, dim3(kThreads), 0, st, X,       \
+                       nullptr, nullptr, XK, dinfo, taps, B, C, h.K, D.nlat_in, D.nlon_in,         \
+                       D.nlat_out, D.nlon_out)
+    if (S == 1) DISCO_CM(1);
+    else DISCO_CM(2);
+#undef DISCO_CM
+    hipError_t le = hipGetLastError();
+    if (le != hipSuccess) {
+        *rc = set_error(DISCO_EHIP, "contraction (matrix cores) launch failed: %s",
+                        hipGetErrorString(le));
         return 1;
     }
     *rc = DISCO_OK;

@@ -304,9 +304,18 @@ int contract_dispatch(const disco_psi* psi, const void* x, void* xk, int B, int 
 
 }  // namespace
 
+// defined in kernels_fused_mfma.hip: the matrix-core contraction (bf16 x and
+// xk); returns 0 when the shape is not one it takes
+int try_launch_contract_mfma(const disco_psi* psi, const void* x, void* xk, int B, int C,
+                             hipStream_t st, int* rc);
+
 int launch_contract(const disco_psi* psi, const void* x, int x_dtype, void* xk, int xk_dtype,
                     int B, int C, void* stream) {
     hipStream_t st = static_cast<hipStream_t>(stream);
+    int rc = DISCO_OK;
+    if (x_dtype == DISCO_BF16 && xk_dtype == DISCO_BF16 &&
+        try_launch_contract_mfma(psi, x, xk, B, C, st, &rc))
+        return rc;
     if (x_dtype == DISCO_F32 && xk_dtype == DISCO_F32)
         return contract_dispatch<float, float>(psi, x, xk, B, C, st);
     if (x_dtype == DISCO_F32 && xk_dtype == DISCO_BF16)

@@ -49,19 +49,27 @@ METRIC = "DISCO fwd output-points\u00b7Cout/s at 721x1440 C=128 K=7; % HBM/MFMA 
 # counters were taken with: when the source has changed the figure is stale
 # and `traffic` is reported as null.
 MEASURED_TRAFFIC_BYTES = {
-    "c4": {"bytes": 1412312510, "kernel_source_sha1": "e093aba13d7165fa88be6f6ffb4b7929d010f071"},
+    ("c4", "fused"): {"bytes": 1385536054, "source": "kernels_fused_mfma.hip",
+                      "sha1": "085750d43f6ea11b9542c528c622dee7a36cc62c"},
+    ("c4", "contract"): {"bytes": 2868086133, "source": "kernels_fused_mfma.hip",
+                         "sha1": "085750d43f6ea11b9542c528c622dee7a36cc62c"},
+    ("c4", "einsum"): {"bytes": 2640528958, "source": "kernels_einsum_mfma.hip",
+                       "sha1": "664722963bc48f17bb18c1dc6c32a5e442abc321"},
 }
-FUSED_SOURCE = os.path.join(ROOT, "spherical_disco_convolution_amd", "csrc", "kernels_fused_mfma.hip")
+CSRC = os.path.join(ROOT, "spherical_disco_convolution_amd", "csrc")
 
 
-def measured_traffic(key):
+def measured_traffic(key, kernel):
+    """HBM bytes per launch from rocprofv3 FETCH_SIZE + WRITE_SIZE (copy-calibrated),
+    or None when there is no figure or the kernel source changed since it was taken."""
     import hashlib
-    m = MEASURED_TRAFFIC_BYTES.get(key)
-    if m is None or not os.path.exists(FUSED_SOURCE):
+    m = MEASURED_TRAFFIC_BYTES.get((key, kernel))
+    src = os.path.join(CSRC, m["source"]) if m else None
+    if m is None or not os.path.exists(src):
         return None
-    with open(FUSED_SOURCE, "rb") as f:
+    with open(src, "rb") as f:
         sha = hashlib.sha1(f.read()).hexdigest()
-    return m["bytes"] if sha == m["kernel_source_sha1"] else None
+    return m["bytes"] if sha == m["sha1"] else None
 
 COPY_CALIBRATION_BYTES = 512 << 20
 
@@ -218,7 +226,7 @@ def main():
     dsize = 2 if wl.dtype == "bf16" else 4
     peak = PEAK_TFLOPS[wl.dtype]
     achieved = f_alg / kernel_s / 1e12
-    traffic = measured_traffic(key)
+    traffic = measured_traffic(key, "fused")
     roofline = {"bound": "mfma" if wl.dtype == "bf16" else "alu", "achieved": round(achieved, 3),
                 "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                 "traffic": traffic}
@@ -243,6 +251,18 @@ def main():
         extra["contract_ms"] = round(t_c / n * 1000, 4)
         extra["einsum_ms"] = round(t_e / n * 1000, 4)
         extra["unfused_ms"] = round((t_c + t_e) / n * 1000, 4)
+        # both are HBM-bound: algorithmic bytes per launch over the launch time
+        xk_bytes = wl.B * wl.Ci * wl.K * wl.nlat_out * wl.nlon_out * dsize
+        a_bytes = algorithmic_bytes(wl, psi.nnz, dsize)
+        x_psi = a_bytes - (wl.Co * cig * wl.K * dsize) - wl.B * wl.Co * wl.nlat_out * wl.nlon_out * 4
+        b_contract = x_psi + xk_bytes
+        b_einsum = xk_bytes + (a_bytes - x_psi)
+        for name, nb, t in (("contract", b_contract, t_c / n), ("einsum", b_einsum, t_e / n)):
+            gbps = nb / t / 1e9
+            extra[name + "_roofline"] = {"bound": "hbm", "achieved": round(gbps, 1),
+                                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                         "frac": round(gbps / HBM_PEAK_GBS, 4),
+                                         "traffic": measured_traffic(key, name)}
         del xk
     line = {
         "metric": METRIC,

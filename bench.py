@@ -238,6 +238,16 @@ def main():
         "psi_build_s": round(psi_build_s, 3),
         "psi_upload_s": round(psi_upload_s, 3),
     }
+    if not args.fused_only and sdc.fused_is_spectral_optin(psi, tdt, wl.Ci, wl.Co, wl.groups):
+        # the opt-in longitude-spectral algorithm on the same inputs
+        os.environ["DISCO_FUSED_PATH"] = "spectral"
+        try:
+            for _ in range(2):
+                fused()
+            _, t_s = time_region(fused, args.steps, torch)
+            extra["spectral_fused_ms"] = round(t_s / args.steps * 1000, 4)
+        finally:
+            del os.environ["DISCO_FUSED_PATH"]
     if not args.no_unfused and not args.fused_only:
         xk = torch.empty((wl.B, wl.Ci, wl.K, wl.nlat_out, wl.nlon_out), dtype=tdt, device="cuda")
         contract = lambda: sdc.contract(psi, xd, xk=xk)

@@ -122,11 +122,28 @@ int disco_einsum(const void* xk, int xk_dtype, const void* w, int w_dtype,
 
 /* Fused forward (DiscreteContinuousConvS2 page, `fused` parameter): the same
  * result as disco_contract followed by disco_einsum, without storing xk in
- * device memory.  x_dtype and w_dtype must be equal. */
+ * device memory.  x_dtype and w_dtype must be equal.
+ *
+ * With the environment variable DISCO_FUSED_PATH=spectral, stride-1 layers
+ * (nlon_in == nlon_out, even, N/2 a product of 2, 3 and 5, N <= 2048) with
+ * bf16 x and w, groups == 1, Ci a multiple of 32, Co 64 or 128, K <= 8 and at
+ * most 8 input rows per output row run in the longitude-spectral form: the
+ * forward equation's longitude shift makes each window a circular
+ * correlation, so it is evaluated with real DFTs along longitude (three
+ * kernels, a stream-ordered workspace of B*Ci*nlat_in*MP*4 +
+ * B*Co*nlat_out*MP*8 bytes with MP = N/2 + 1 rounded up to 32).  Otherwise
+ * the direct kernels run. */
 int disco_fused_fwd(const disco_psi* psi, const void* x, int x_dtype,
                     const void* w, int w_dtype, const float* bias,
                     void* y, int y_dtype, int32_t B, int32_t Ci, int32_t Co,
                     int32_t groups, void* stream);
+
+/* 1 if disco_fused_fwd with these arguments takes the longitude-spectral
+ * path described above, 0 if it takes a direct kernel, negative on error
+ * (NULL handle or handle not uploaded).  Reads DISCO_FUSED_PATH like the call
+ * itself. */
+int disco_fused_is_spectral(const disco_psi* psi, int x_dtype, int32_t Ci, int32_t Co,
+                            int32_t groups);
 
 /* Message for the last failed call on this thread ("" if none). */
 const char* disco_last_error(void);

@@ -74,6 +74,7 @@ def _load():
                                         I32, I32, I32, I32, I32, I32, I32, P]),
         "disco_fused_fwd": (ctypes.c_int, [P, P, ctypes.c_int, P, ctypes.c_int, P, P,
                                            ctypes.c_int, I32, I32, I32, I32, P]),
+        "disco_fused_is_spectral": (ctypes.c_int, [P, ctypes.c_int, I32, I32, I32]),
         "disco_last_error": (ctypes.c_char_p, []),
         "disco_version": (ctypes.c_char_p, []),
     }
@@ -87,7 +88,7 @@ def _load():
 _lib = _load()
 EXPORTED = ("disco_psi_build", "disco_psi_query", "disco_psi_export", "disco_psi_to_device",
             "disco_psi_free", "disco_contract", "disco_einsum", "disco_fused_fwd",
-            "disco_last_error", "disco_version")
+            "disco_fused_is_spectral", "disco_last_error", "disco_version")
 
 
 def version() -> str:
@@ -269,6 +270,31 @@ def einsum(xk, w, groups: int = 1, bias=None, y=None, out_dtype=None, stream=Non
                              y.data_ptr(), _dtype_code(y), B, Ci, Co, groups, K, H, W,
                              _stream(stream)), "einsum")
     return y
+
+
+def fused_is_spectral(psi: Psi, x_dtype, Ci: int, Co: int, groups: int = 1) -> bool:
+    """Whether fused_fwd takes the longitude-spectral path for these arguments
+    (x_dtype: a torch dtype)."""
+    torch = _torch()
+    code = BF16 if x_dtype == torch.bfloat16 else F32
+    rc = _lib.disco_fused_is_spectral(psi.handle, code, Ci, Co, groups)
+    if rc < 0:
+        _check(rc, "fused_is_spectral")
+    return rc == 1
+
+
+def fused_is_spectral_optin(psi: Psi, x_dtype, Ci: int, Co: int, groups: int = 1) -> bool:
+    """Whether fused_fwd would take the longitude-spectral path for these
+    arguments under DISCO_FUSED_PATH=spectral."""
+    old = os.environ.get("DISCO_FUSED_PATH")
+    os.environ["DISCO_FUSED_PATH"] = "spectral"
+    try:
+        return fused_is_spectral(psi, x_dtype, Ci, Co, groups)
+    finally:
+        if old is None:
+            del os.environ["DISCO_FUSED_PATH"]
+        else:
+            os.environ["DISCO_FUSED_PATH"] = old
 
 
 def fused_fwd(psi: Psi, x, w, groups: int = 1, bias=None, y=None, out_dtype=None, stream=None):

@@ -24,6 +24,8 @@ SOURCES = [
     "kernels_generic.hip",
     "kernels_einsum_mfma.hip",
     "kernels_fused_mfma.hip",
+    "kernels_spectral.hip",
+    "spectral_host.cpp",
 ]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -208,6 +208,9 @@ int disco_psi_to_device(disco_psi* psi) {
     std::vector<int32_t> info;
     rc = build_mfma_tables(psi, taps, info);
     if (rc != DISCO_OK) return rc;
+    std::vector<float> spec_psih;
+    rc = build_spectral_tables(h, spec_psih, d.spec_radix, &d.spec_nrad, &d.spec_mp);
+    if (rc != DISCO_OK) return rc;
 
     void* p = nullptr;
     if ((rc = dev_alloc(d, &p, wptr.size() * sizeof(int32_t))) != DISCO_OK) goto fail;
@@ -229,6 +232,12 @@ int disco_psi_to_device(disco_psi* psi) {
         if ((rc = dev_copy(p, info.data(), info.size() * sizeof(int32_t))) != DISCO_OK) goto fail;
         d.mfma_info_host = info;
         d.mfma_ok = 1;
+    }
+    if (d.spec_mp > 0) {
+        if ((rc = dev_alloc(d, &p, spec_psih.size() * sizeof(float))) != DISCO_OK) goto fail;
+        d.spec_psih = p;
+        if ((rc = dev_copy(p, spec_psih.data(), spec_psih.size() * sizeof(float))) != DISCO_OK)
+            goto fail;
     }
     d.device = dev;
     psi->dev = d;
@@ -306,6 +315,14 @@ int disco_einsum(const void* xk, int xk_dtype, const void* w, int w_dtype, const
         return set_error(DISCO_EINVAL, "y overlaps an input");
     return launch_einsum(xk, xk_dtype, w, w_dtype, bias, y, y_dtype, B, Ci, Co, groups, K,
                          nlat_out, nlon_out, stream);
+}
+
+int disco_fused_is_spectral(const disco_psi* psi, int x_dtype, int32_t Ci, int32_t Co,
+                            int32_t groups) {
+    clear_error();
+    if (psi == nullptr) return set_error(DISCO_EINVAL, "psi handle is NULL");
+    if (psi->dev.device < 0) return set_error(DISCO_EINVAL, "psi is not on a device");
+    return fused_spectral_eligible(psi, x_dtype, Ci, Co, groups);
 }
 
 int disco_fused_fwd(const disco_psi* psi, const void* x, int x_dtype, const void* w, int w_dtype,

@@ -47,6 +47,17 @@ struct HostPsi {
 // error code (message recorded).
 int build_host_psi(const disco_psi_desc& desc, HostPsi& out);
 
+// Longitude-spectral tables (spectral_host.cpp), built for stride-1 layers
+// whose longitude count N is even, at most kSpecMaxN, with N/2 a product of
+// 2, 3 and 5, and K <= 8.  psih: float32 pairs [nwin][K][MP], Psi_hat of each
+// window; radix: the plan of the N/2-point transform.  *mp = 0 when the layer
+// does not qualify.
+constexpr int kSpecMaxN = 2048;   // four rows of two N/2-point float2 buffers: 64 KB LDS
+constexpr int kSpecMaxRadix = 12;
+int spectral_plan(int n, int32_t* radix, int32_t* nrad);
+int build_spectral_tables(const HostPsi& h, std::vector<float>& psih, int32_t* radix,
+                          int32_t* nrad, int32_t* mp);
+
 // ---------------------------------------------------------------------------
 // Device form of Psi
 // ---------------------------------------------------------------------------
@@ -72,6 +83,11 @@ struct DevPsi {
     int32_t* mfma_row_info = nullptr;     // device copy of the info block
     std::vector<int32_t> mfma_info_host;  // host copy (offsets, tile options)
     int32_t mfma_ok = 0;
+    // longitude-spectral tables for the spectral fused path (stride 1)
+    void* spec_psih = nullptr;    // float2 [nwin][K][spec_mp]
+    int32_t spec_mp = 0;          // padded frequency count; 0 = no tables
+    int32_t spec_radix[kSpecMaxRadix] = {0};
+    int32_t spec_nrad = 0;
     std::vector<void*> allocations;
 };
 
@@ -93,5 +109,7 @@ int launch_einsum(const void* xk, int xk_dtype, const void* w, int w_dtype, cons
 int launch_fused(const disco_psi* psi, const void* x, int dtype, const void* w,
                  const float* bias, void* y, int y_dtype, int B, int Ci, int Co, int groups,
                  void* stream);
+// 1 if disco_fused_fwd takes the longitude-spectral path for these arguments
+int fused_spectral_eligible(const disco_psi* psi, int x_dtype, int Ci, int Co, int groups);
 
 }  // namespace disco

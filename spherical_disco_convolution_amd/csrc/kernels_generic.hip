@@ -451,10 +451,18 @@ int try_launch_fused_mfma(const disco_psi* psi, const void* x, const void* w, co
                           void* y, int y_dtype, int B, int Ci, int Co, int groups, hipStream_t st,
                           int* rc);
 
+// defined in kernels_spectral.hip; returns 1 if it handled the call
+int try_launch_fused_spectral(const disco_psi* psi, const void* x, const void* w,
+                              const float* bias, void* y, int y_dtype, int B, int Ci, int Co,
+                              int groups, hipStream_t st, int* rc);
+
 int launch_fused(const disco_psi* psi, const void* x, int dtype, const void* w, const float* bias,
                  void* y, int y_dtype, int B, int Ci, int Co, int groups, void* stream) {
     hipStream_t st = static_cast<hipStream_t>(stream);
     int rc = DISCO_OK;
+    if (dtype == DISCO_BF16 &&
+        try_launch_fused_spectral(psi, x, w, bias, y, y_dtype, B, Ci, Co, groups, st, &rc))
+        return rc;
     if (dtype == DISCO_BF16 &&
         try_launch_fused_mfma(psi, x, w, bias, y, y_dtype, B, Ci, Co, groups, st, &rc))
         return rc;

@@ -1,0 +1,573 @@
+// Spectral evaluation of the fused DISCO forward pass for stride-1 layers.
+//
+// Along longitude the forward equation's inner sum is, per (output row,
+// input row) window, a circular correlation (the p-shift of the
+// DiscreteContinuousConvS2 page).  With the real DFT over longitude,
+//   X_hat[b,ci,k,j,m] = sum_windows x_hat[b,ci,i,m] * conj(Psi_hat[k,j,i,m])
+//   y_hat[b,co,j,m]   = sum_{ci,k} w[co,ci,k] * X_hat[b,ci,k,j,m]
+//   y[b,co,j,:]       = inverse real DFT of y_hat[b,co,j,:] (+ bias)
+// (the channel and basis sums of the forward equation commute with the DFT).
+// Psi_hat comes from spectral_host.cpp.  Three kernels:
+//   spec_rfft   x rows -> x_hat, stored as bf16 (re, im) pairs;
+//   spec_mfma   per (batch, output row, 32 frequencies): the window sum on
+//               the vector ALUs into a bf16 [frequency, re/im][(ci, k)] LDS
+//               tile per 32-channel chunk, then the channel/basis GEMM on
+//               v_mfma_f32_32x32x16_bf16 into y_hat (float32 pairs);
+//   spec_irfft  y_hat rows -> y rows (+ bias).
+// The real transforms run an N/2-point complex transform in LDS: iterative
+// Stockham passes of radix 4, 2, 3 and 5 (Govindaraju et al., "High
+// performance discrete Fourier transforms on graphics processors", SC 2008),
+// with the usual packing of even and odd samples into one complex sequence.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdlib>
+#include <cstring>
+
+#include "disco_internal.h"
+#include "kernels_common.h"
+
+namespace disco {
+
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+struct SpecPlan {
+    int32_t n;
+    int32_t r[kSpecMaxRadix];
+};
+
+__device__ __forceinline__ float2 cadd(float2 a, float2 b) { return make_float2(a.x + b.x, a.y + b.y); }
+__device__ __forceinline__ float2 csub(float2 a, float2 b) { return make_float2(a.x - b.x, a.y - b.y); }
+__device__ __forceinline__ float2 cscale(float2 a, float s) { return make_float2(a.x * s, a.y * s); }
+__device__ __forceinline__ float2 cmul(float2 a, float2 b) {
+    return make_float2(a.x * b.x - a.y * b.y, a.x * b.y + a.y * b.x);
+}
+__device__ __forceinline__ float2 cconj(float2 a) { return make_float2(a.x, -a.y); }
+// i * s * a for s = +-1
+__device__ __forceinline__ float2 cimul(float2 a, float s) { return make_float2(-s * a.y, s * a.x); }
+
+// In-place DFT of length R: a[u] <- sum_t a[t] exp(s * 2 pi i u t / R).
+template <int R>
+__device__ __forceinline__ void butterfly(float2 (&a)[R], float s);
+
+template <>
+__device__ __forceinline__ void butterfly<2>(float2 (&a)[2], float) {
+    const float2 t = a[0];
+    a[0] = cadd(t, a[1]);
+    a[1] = csub(t, a[1]);
+}
+
+template <>
+__device__ __forceinline__ void butterfly<4>(float2 (&a)[4], float s) {
+    const float2 p0 = cadd(a[0], a[2]), p1 = cadd(a[1], a[3]);
+    const float2 t1 = csub(a[0], a[2]), t2 = cimul(csub(a[1], a[3]), s);
+    a[0] = cadd(p0, p1);
+    a[1] = cadd(t1, t2);
+    a[2] = csub(p0, p1);
+    a[3] = csub(t1, t2);
+}
+
+template <>
+__device__ __forceinline__ void butterfly<3>(float2 (&a)[3], float s) {
+    const float2 t = cadd(a[1], a[2]), d = csub(a[1], a[2]);
+    const float2 m = csub(a[0], cscale(t, 0.5f));
+    const float2 e = cimul(cscale(d, 0.86602540378443865f), s);
+    a[0] = cadd(a[0], t);
+    a[1] = cadd(m, e);
+    a[2] = csub(m, e);
+}
+
+template <>
+__device__ __forceinline__ void butterfly<5>(float2 (&a)[5], float s) {
+    const float c1 = 0.30901699437494742f, c2 = -0.80901699437494742f;
+    const float s1 = 0.95105651629515357f, s2 = 0.58778525229247313f;
+    const float2 t1 = cadd(a[1], a[4]), t2 = cadd(a[2], a[3]);
+    const float2 d1 = csub(a[1], a[4]), d2 = csub(a[2], a[3]);
+    const float2 r1 = cadd(a[0], cadd(cscale(t1, c1), cscale(t2, c2)));
+    const float2 r2 = cadd(a[0], cadd(cscale(t1, c2), cscale(t2, c1)));
+    const float2 i1 = cimul(cadd(cscale(d1, s1), cscale(d2, s2)), s);
+    const float2 i2 = cimul(csub(cscale(d1, s2), cscale(d2, s1)), s);
+    a[0] = cadd(a[0], cadd(t1, t2));
+    a[1] = cadd(r1, i1);
+    a[4] = csub(r1, i1);
+    a[2] = cadd(r2, i2);
+    a[3] = csub(r2, i2);
+}
+
+// exp(s * 2 pi i * e / H), with the hardware sine and cosine (|angle| <= 2 pi)
+__device__ __forceinline__ float2 root(int e, float inv_h, float s) {
+    float sn, cs;
+    __sincosf(6.28318530717958648f * (float)e * inv_h, &sn, &cs);
+    return make_float2(cs, s * sn);
+}
+
+// One Stockham pass of radix R over an H-point sequence whose sub-transforms
+// of length Ns are done, by the 64 lanes of one wave (s = -1 forward, +1
+// inverse).  Quotients by Ns use a float reciprocal: (j + 1/2) / Ns is below
+// H / 2 <= 1024 and at least 1 / (2 Ns) >= 1 / H from an integer, and the
+// float product is within 2 ulp (<= 1.3e-4 at 1024) of it, so truncation
+// gives the exact quotient.
+template <int R>
+__device__ __forceinline__ void stockham_pass(const float2* src, float2* dst, int H, int Ns,
+                                              float inv_h, float s, int lane) {
+    const int HR = H / R;
+    const int ts = H / (Ns * R);
+    const float inv_ns = 1.0f / (float)Ns;
+    for (int j = lane; j < HR; j += 64) {
+        const int q = (int)(((float)j + 0.5f) * inv_ns);
+        const int jj = j - q * Ns;
+        float2 a[R];
+#pragma unroll
+        for (int t = 0; t < R; ++t) a[t] = src[j + t * HR];
+        if (jj != 0) {
+            const float2 w = root(jj * ts, inv_h, s);
+            float2 wt = w;
+#pragma unroll
+            for (int t = 1; t < R; ++t) {
+                a[t] = cmul(a[t], wt);
+                if (t + 1 < R) wt = cmul(wt, w);
+            }
+        }
+        butterfly<R>(a, s);
+        const int base = q * Ns * R + jj;
+#pragma unroll
+        for (int u = 0; u < R; ++u) dst[base + u * Ns] = a[u];
+    }
+}
+
+// H-point complex DFT of buf0 (one wave's LDS), using buf1 as the other
+// Stockham buffer; returns the buffer that holds the result.  Each pass ends
+// with a workgroup barrier (every wave of the workgroup runs the same plan).
+__device__ float2* fft_wave(float2* buf0, float2* buf1, int H, const SpecPlan& pl, float s,
+                            int lane) {
+    float2* src = buf0;
+    float2* dst = buf1;
+    const float inv_h = 1.0f / (float)H;
+    int Ns = 1;
+    for (int p = 0; p < pl.n; ++p) {
+        switch (pl.r[p]) {
+            case 4: stockham_pass<4>(src, dst, H, Ns, inv_h, s, lane); break;
+            case 2: stockham_pass<2>(src, dst, H, Ns, inv_h, s, lane); break;
+            case 3: stockham_pass<3>(src, dst, H, Ns, inv_h, s, lane); break;
+            default: stockham_pass<5>(src, dst, H, Ns, inv_h, s, lane); break;
+        }
+        __syncthreads();
+        Ns *= pl.r[p];
+        float2* t = src;
+        src = dst;
+        dst = t;
+    }
+    return src;
+}
+
+typedef float float2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+
+// two floats -> bf16 pair (round to nearest even, one v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((float2v){lo, hi}, bf16x2v));
+}
+
+constexpr int kFftThreads = 256;
+constexpr int kFftRows = kFftThreads / 64;   // one wave per row
+
+// x rows (N real, bf16) -> x_hat rows (MP bf16 pairs; frequencies past N/2
+// are zero).  One wave per row, four rows per workgroup; LDS: two H-point
+// buffers per row.  Rows past the end compute on row 0 and store nothing.
+__global__ __launch_bounds__(kFftThreads) void spec_rfft(const bf16_t* __restrict__ x,
+                                                         uint32_t* __restrict__ xh, int N, int MP,
+                                                         int64_t nrows, SpecPlan pl) {
+    extern __shared__ float2 sm[];
+    const int H = N / 2;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * kFftRows + wave;
+    const bool live = row < nrows;
+    float2* b0 = sm + (size_t)wave * 2 * H;
+    float2* b1 = b0 + H;
+    const uint32_t* xr = reinterpret_cast<const uint32_t*>(x + (live ? row : 0) * (size_t)N);
+    for (int n = lane; n < H; n += 64) {
+        const uint32_t v = xr[n];   // samples 2n (low half) and 2n + 1
+        b0[n] = make_float2(__uint_as_float(v << 16), __uint_as_float(v & 0xffff0000u));
+    }
+    __syncthreads();
+    const float2* z = fft_wave(b0, b1, H, pl, -1.0f, lane);
+    if (!live) return;
+    // X[m] = (a + b)/2 - i W^m (a - b)/2, a = Z[m mod H], b = conj(Z[(H - m) mod H]),
+    // W = exp(-2 pi i / N)
+    uint32_t* out = xh + row * (size_t)MP;
+    const float inv_n = 0.5f / (float)H;
+    for (int m = lane; m < MP; m += 64) {
+        float2 X = make_float2(0.0f, 0.0f);
+        if (m <= H) {
+            const float2 a = z[m == H ? 0 : m];
+            const float2 b = cconj(z[m == 0 ? 0 : H - m]);
+            const float2 e = cmul(root(m, inv_n, -1.0f), csub(a, b));
+            X = cadd(cscale(cadd(a, b), 0.5f), cscale(make_float2(e.y, -e.x), 0.5f));
+        }
+        out[m] = pack_bf16x2(X.x, X.y);
+    }
+}
+
+// y_hat rows (MP float pairs, frequencies 0..N/2 used) -> y rows (N) + bias,
+// one wave per row.  The imaginary parts of the zero and N/2 frequencies are
+// dropped (a real row's spectrum has none).
+template <typename TY>
+__global__ __launch_bounds__(kFftThreads) void spec_irfft(const float2* __restrict__ yh,
+                                                          TY* __restrict__ y,
+                                                          const float* __restrict__ bias, int N,
+                                                          int MP, int Co, int nlat_out,
+                                                          int64_t nrows, SpecPlan pl) {
+    extern __shared__ float2 sm[];
+    const int H = N / 2;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * kFftRows + wave;
+    const bool live = row < nrows;
+    float2* b0 = sm + (size_t)wave * 2 * H;
+    float2* b1 = b0 + H;
+    const float2* src = yh + (live ? row : 0) * (size_t)MP;
+    // Z[m] = (a + b)/2 + i conj(W^m) (a - b)/2, a = X[m], b = conj(X[H - m]), m < H
+    const float inv_n = 0.5f / (float)H;
+    for (int m = lane; m < H; m += 64) {
+        float2 a = src[m];
+        float2 b = cconj(src[H - m]);
+        if (m == 0) {
+            a.y = 0.0f;
+            b.y = 0.0f;
+        }
+        const float2 e = cmul(root(m, inv_n, 1.0f), csub(a, b));
+        b0[m] = cadd(cscale(cadd(a, b), 0.5f), cscale(make_float2(-e.y, e.x), 0.5f));
+    }
+    __syncthreads();
+    const float2* z = fft_wave(b0, b1, H, pl, 1.0f, lane);
+    if (!live) return;
+    const float bv = bias ? bias[(row / nlat_out) % Co] : 0.0f;
+    const float sc = 1.0f / (float)H;
+    TY* out = y + row * (size_t)N;
+    for (int n = lane; n < H; n += 64) {
+        const float2 v = z[n];
+        if constexpr (sizeof(TY) == 4) {
+            *reinterpret_cast<float2*>(out + 2 * n) = make_float2(v.x * sc + bv, v.y * sc + bv);
+        } else {
+            *reinterpret_cast<uint32_t*>(out + 2 * n) = pack_bf16x2(v.x * sc + bv, v.y * sc + bv);
+        }
+    }
+}
+
+// w [Co][Ci][K] bf16 -> the GEMM's A operands in fragment order:
+// wp[chunk][k-step][co / 32][lane][8], lane (l32, lg) holding row co = 32 * tile
+// + l32 and pairs kappa = 16 k-step + 8 lg .. + 7 of the chunk, where a chunk's
+// 256 pairs are ordered kappa = k * 32 + ci (basis index padded to 8 with
+// zeros).  One wave's fragment is 1 KB of contiguous memory.
+__global__ void spec_prep_w(const bf16_t* __restrict__ w, bf16_t* __restrict__ wp, int Co, int Ci,
+                            int K) {
+    const size_t n = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const size_t total = (size_t)Co * Ci * 8;
+    if (n >= total) return;
+    const int e = (int)(n & 7);
+    const int lane = (int)((n >> 3) & 63);
+    const size_t f = n >> 9;                  // (chunk * 16 + k-step) * (Co / 32) + tile
+    const int tile = (int)(f % (Co / 32));
+    const size_t cs = f / (Co / 32);
+    const int ks = (int)(cs % 16), cc = (int)(cs / 16);
+    const int co = tile * 32 + (lane & 31);
+    const int kap = 16 * ks + 8 * (lane >> 5) + e;   // k * 32 + ci
+    const int k = kap >> 5, ci = kap & 31;
+    wp[n] = k < K ? w[((size_t)co * Ci + cc * 32 + ci) * K + k] : (bf16_t)0;
+}
+
+constexpr int kMt = 32;              // frequencies per work item (64 GEMM columns)
+constexpr int kBts = 264;            // B tile row: 256 (k, ci) pairs + 8 pad (bf16)
+constexpr int kSpecThreads = 256;
+constexpr int kSpecMaxWin = 8;       // windows per output row (one 16-deep MFMA step)
+
+// Per (batch b, output row j, 32 frequencies m0 ..): both sums on the matrix
+// cores, per 32-channel chunk.
+//  * Window sum.  For one frequency, X_hat[ci, (k, re/im)] is the product of
+//    x_hat[ci, (r, re/im)] (32 x 16: up to 8 windows) with the real 2 x 2
+//    block form of conj(Psi_hat[k, r]) (16 x 32, columns (k, re/im), k < 8):
+//    one v_mfma_f32_32x32x16_bf16.  The A operand is the bf16 (re, im) words
+//    of x_hat as stored (lane = channel, four windows per lane half), read
+//    from the chunk's spectra block in LDS, which is filled with coalesced
+//    loads one chunk ahead (eight lanes per 128-byte row); its 16-byte pieces
+//    are XOR-swizzled by channel so that the lanes' reads hit distinct banks.
+//    Each wave owns 8 of the 32 frequencies and builds their B operands once
+//    per item from the Psi_hat slice in LDS.  Results go to the bf16 LDS tile
+//    bt[(m, re/im)][k * 32 + ci].
+//  * Channel/basis GEMM: y_hat[co, (m, re/im)] += wp[co, (k, ci)] bt[(k, ci),
+//    (m, re/im)], 4 waves, wave tile 32 x 64 (CO = 128) or 32 x 32 (CO = 64),
+//    16 k-steps per chunk.  Each weight fragment is requested for the next
+//    chunk right after its use, so it arrives while other work runs.
+template <int CO, int KT>
+__global__ __launch_bounds__(kSpecThreads) __attribute__((amdgpu_waves_per_eu(2))) void spec_mfma(
+    const uint32_t* __restrict__ xh, const bf16_t* __restrict__ wp,
+    const float2* __restrict__ psih, const int32_t* __restrict__ win_ptr,
+    const DevWindow* __restrict__ wins, float* __restrict__ yh, int Ci, int nlat_in,
+    int nlat_out, int MP) {
+    __shared__ __attribute__((aligned(16))) bf16_t bt[64 * kBts];
+    __shared__ __attribute__((aligned(16))) u32x4 xs[kSpecMaxWin * 32 * 8];   // [r][ci][piece]
+    __shared__ float2 ps[kSpecMaxWin * KT * kMt];
+    constexpr int WGM = CO / 32;          // waves along the output channels
+    constexpr int WGN = 4 / WGM;          // waves along the columns
+    constexpr int NTW = 2 / WGN;          // 32-column MFMA tiles per wave
+
+    const int m0 = blockIdx.x * kMt;
+    const int j = blockIdx.y;
+    const int b = blockIdx.z;
+    const int w0 = uniform(win_ptr[j]);
+    const int nw = uniform(win_ptr[j + 1]) - w0;   // <= kSpecMaxWin (checked on the host)
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = uniform(tid >> 6);
+    const int l32 = lane & 31, lg = lane >> 5;
+    const int wm = wave % WGM, wn = wave / WGM;
+    const int nchunks = Ci / 32;
+
+    // the row's Psi_hat slice ps[(r KT + k) kMt + ml]; basis columns past KT
+    // of the tile are zero for the whole item
+    for (int idx = tid; idx < nw * KT * kMt; idx += kSpecThreads) {
+        const int rk = idx / kMt, ml = idx - rk * kMt;
+        ps[idx] = psih[(size_t)(w0 * KT + rk) * MP + m0 + ml];
+    }
+    if (KT < 8) {
+        for (int idx = tid; idx < 64 * (8 - KT) * 4; idx += kSpecThreads) {
+            const int row = idx / ((8 - KT) * 4), q = idx - row * ((8 - KT) * 4);
+            *reinterpret_cast<u32x4*>(bt + row * kBts + KT * 32 + q * 8) = u32x4{0, 0, 0, 0};
+        }
+    }
+
+    // input spectra of one chunk: thread (piece p = tid % 8, channel tid / 8)
+    // loads the 16-byte piece p (4 frequencies) of every window's row; LDS
+    // slot ((r * 32 + ci) * 8 + (p ^ (ci & 7)))
+    const int f0 = wave * 8;
+    const int sp = tid & 7, sci = tid >> 3;
+    const size_t cstride = (size_t)32 * nlat_in * MP;   // one 32-channel chunk
+    size_t soff[kSpecMaxWin];
+#pragma unroll
+    for (int r = 0; r < kSpecMaxWin; ++r) {
+        const int lat = wins[w0 + (r < nw ? r : 0)].lat;
+        soff[r] = ((size_t)(b * Ci + sci) * nlat_in + lat) * MP + m0 + 4 * sp;
+    }
+    u32x4 xn[kSpecMaxWin];
+    auto load_x = [&](int cc) {
+#pragma unroll
+        for (int r = 0; r < kSpecMaxWin; ++r)   // rows past nw repeat window 0's (valid)
+            xn[r] = *reinterpret_cast<const u32x4*>(xh + soff[r] + cc * cstride);
+    };
+    auto store_x = [&]() {
+#pragma unroll
+        for (int r = 0; r < kSpecMaxWin; ++r) xs[(r * 32 + sci) * 8 + (sp ^ (sci & 7))] = xn[r];
+    };
+    load_x(0);
+    u32x4 wq[16];
+    // fragment (chunk, k-step) of this wave's 32 rows: wf[(chunk * 16 + k-step) * WGM * 64]
+    const u32x4* wf = reinterpret_cast<const u32x4*>(wp) + wm * 64 + lane;
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks) wq[ks] = wf[(size_t)ks * WGM * 64];
+    store_x();
+    load_x(nchunks > 1 ? 1 : 0);
+    // A-operand reads: lane (channel l32, windows 4 lg + u, clamped to window 0
+    // past the row's windows: finite data against zero B rows), pieces
+    // 2 wave and 2 wave + 1 (the wave's frequencies)
+    int xrd[4][2];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int r = 4 * lg + u < nw ? 4 * lg + u : 0;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) xrd[u][h] = (r * 32 + l32) * 8 + ((2 * wave + h) ^ (l32 & 7));
+    }
+    __syncthreads();   // ps, zero columns, first spectra block
+
+    // B operands of the window sum: lane column n = 2 k + c (c: real, imaginary
+    // part of X_hat), rows (r, re/im) for r = 4 lg .. 4 lg + 3
+    u32x4 bq[8];
+    {
+        const int n = l32, k = n >> 1, c = n & 1;
+#pragma unroll
+        for (int f = 0; f < 8; ++f) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int r = 4 * lg + u;
+                float2 P = make_float2(0.0f, 0.0f);
+                if (n < 2 * KT && r < nw) P = ps[(r * KT + k) * kMt + f0 + f];
+                // real column: (Pr, Pi); imaginary column: (-Pi, Pr)
+                bq[f][u] = c ? pack_bf16x2(-P.y, P.x) : pack_bf16x2(P.x, P.y);
+            }
+        }
+    }
+
+    floatx16 acc[NTW];
+#pragma unroll
+    for (int t = 0; t < NTW; ++t)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[t][e] = 0.0f;
+
+    for (int cc = 0; cc < nchunks; ++cc) {
+        // ---- window sum, one MFMA per frequency ----
+        u32x4 xa[4][2];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) xa[u][h] = xs[xrd[u][h]];
+#pragma unroll
+        for (int f = 0; f < 8; ++f) {
+            const u32x4 a = {xa[0][f >> 2][f & 3], xa[1][f >> 2][f & 3], xa[2][f >> 2][f & 3],
+                             xa[3][f >> 2][f & 3]};
+            floatx16 d;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) d[e] = 0.0f;
+            d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                        __builtin_bit_cast(bf16x8_t, bq[f]), d,
+                                                        0, 0, 0);
+            if (l32 < 2 * KT) {
+                // column (k, c) -> tile row 2 (f0 + f) + c, pairs k * 32 + ci,
+                // ci = 8 q + 4 lg + (0..3)
+                bf16_t* dst = bt + (2 * (f0 + f) + (l32 & 1)) * kBts + (l32 >> 1) * 32 + 4 * lg;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const uint2 pk = make_uint2(pack_bf16x2(d[4 * q], d[4 * q + 1]),
+                                                pack_bf16x2(d[4 * q + 2], d[4 * q + 3]));
+                    *reinterpret_cast<uint2*>(dst + 8 * q) = pk;
+                }
+            }
+        }
+        __syncthreads();   // tile complete; every wave is done with the spectra block
+        // next chunk's spectra into LDS, the one after into registers (chunks
+        // past the end reload the last one)
+        const int cn = cc + 1 < nchunks ? cc + 1 : cc;
+        store_x();
+        load_x(cc + 2 < nchunks ? cc + 2 : nchunks - 1);
+        // ---- channel/basis GEMM over this chunk's 256 (k, ci) pairs ----
+        const bf16_t* bb = bt + (wn * (64 / WGN) + l32) * kBts + 8 * lg;
+        const u32x4* wnext = wf + (size_t)cn * 16 * WGM * 64;
+#pragma unroll
+        for (int ks = 0; ks < 16; ++ks) {
+            const bf16x8_t af = __builtin_bit_cast(bf16x8_t, wq[ks]);
+#pragma unroll
+            for (int t = 0; t < NTW; ++t) {
+                const bf16x8_t bf =
+                    *reinterpret_cast<const bf16x8_t*>(bb + t * 32 * kBts + 16 * ks);
+                acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf, acc[t], 0, 0, 0);
+            }
+            wq[ks] = wnext[(size_t)ks * WGM * 64];
+        }
+        __syncthreads();
+    }
+    // ---- y_hat: lane holds GEMM column n (frequency m0 + n/2, real part for
+    // even n), rows 8*(e/4) + 4*lg + e%4 of its 32-row tile ----
+#pragma unroll
+    for (int t = 0; t < NTW; ++t) {
+        const int n = wn * (64 / WGN) + t * 32 + l32;
+        const size_t col = (size_t)(m0 + (n >> 1)) * 2 + (n & 1);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int co = wm * 32 + 8 * (e >> 2) + 4 * lg + (e & 3);
+            yh[((size_t)(b * CO + co) * nlat_out + j) * MP * 2 + col] = acc[t][e];
+        }
+    }
+}
+
+}  // namespace
+
+// Which fused algorithm disco_fused_fwd takes for these arguments.
+int fused_spectral_eligible(const disco_psi* psi, int x_dtype, int Ci, int Co, int groups) {
+    const DevPsi& d = psi->dev;
+    const HostPsi& h = psi->host;
+    if (d.spec_mp <= 0 || x_dtype != DISCO_BF16 || groups != 1 || Ci % 32 != 0 ||
+        (Co != 128 && Co != 64) || h.K > 8)
+        return 0;
+    if (d.max_windows > kSpecMaxWin) return 0;
+    // opt-in: the direct matrix-core kernel is the faster one at the sizes measured
+    const char* e = std::getenv("DISCO_FUSED_PATH");
+    return e != nullptr && std::strcmp(e, "spectral") == 0;
+}
+
+int try_launch_fused_spectral(const disco_psi* psi, const void* x, const void* w,
+                              const float* bias, void* y, int y_dtype, int B, int Ci, int Co,
+                              int groups, hipStream_t st, int* rc) {
+    if (!fused_spectral_eligible(psi, DISCO_BF16, Ci, Co, groups) || B <= 0) return 0;
+    const DevPsi& d = psi->dev;
+    const HostPsi& h = psi->host;
+    const disco_psi_desc& D = h.desc;
+    const int N = D.nlon_in, H = N / 2, MP = d.spec_mp, K = h.K;
+    SpecPlan pl;
+    pl.n = d.spec_nrad;
+    for (int i = 0; i < kSpecMaxRadix; ++i) pl.r[i] = d.spec_radix[i];
+
+    auto up = [](size_t v) { return (v + 255) / 256 * 256; };
+    const size_t xh_bytes = up((size_t)B * Ci * D.nlat_in * MP * 4);
+    const size_t yh_bytes = up((size_t)B * Co * D.nlat_out * MP * 8);
+    const size_t wp_bytes = up((size_t)Co * Ci * 8 * 2);
+    void* ws = nullptr;
+    hipError_t e = hipMallocAsync(&ws, xh_bytes + yh_bytes + wp_bytes, st);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        *rc = set_error(e == hipErrorOutOfMemory ? DISCO_ENOMEM : DISCO_EHIP,
+                        "hipMallocAsync for the spectral workspace failed: %s",
+                        hipGetErrorString(e));
+        return 1;
+    }
+    uint32_t* xh = static_cast<uint32_t*>(ws);
+    float* yh = reinterpret_cast<float*>(static_cast<char*>(ws) + xh_bytes);
+    bf16_t* wpd = reinterpret_cast<bf16_t*>(static_cast<char*>(ws) + xh_bytes + yh_bytes);
+    const float2* psih = static_cast<const float2*>(d.spec_psih);
+
+    const size_t nwp = (size_t)Co * Ci * 8;
+    hipLaunchKernelGGL(spec_prep_w, dim3((unsigned)((nwp + 255) / 256)), dim3(256), 0, st,
+                       static_cast<const bf16_t*>(w), wpd, Co, Ci, K);
+    const size_t fft_lds = (size_t)kFftRows * 2 * H * sizeof(float2);
+    const int64_t xrows = (int64_t)B * Ci * D.nlat_in;
+    hipLaunchKernelGGL(spec_rfft, dim3((unsigned)((xrows + kFftRows - 1) / kFftRows)),
+                       dim3(kFftThreads), fft_lds, st, static_cast<const bf16_t*>(x), xh, N, MP,
+                       xrows, pl);
+    dim3 grid((unsigned)(MP / kMt), (unsigned)D.nlat_out, (unsigned)B);
+#define DISCO_SM(CC, KK)                                                                     \
+    hipLaunchKernelGGL((spec_mfma<CC, KK>), grid, dim3(kSpecThreads), 0, st, xh, wpd,         \
+                       psih, d.win_ptr, d.windows, yh, Ci, D.nlat_in, D.nlat_out, MP)
+#define DISCO_SM_K(CC)                                                                       \
+    switch (K) {                                                                             \
+        case 1: DISCO_SM(CC, 1); break;                                                      \
+        case 2: DISCO_SM(CC, 2); break;                                                      \
+        case 3: DISCO_SM(CC, 3); break;                                                      \
+        case 4: DISCO_SM(CC, 4); break;                                                      \
+        case 5: DISCO_SM(CC, 5); break;                                                      \
+        case 6: DISCO_SM(CC, 6); break;                                                      \
+        case 7: DISCO_SM(CC, 7); break;                                                      \
+        default: DISCO_SM(CC, 8); break;                                                     \
+    }
+    if (Co == 128) {
+        DISCO_SM_K(128)
+    } else {
+        DISCO_SM_K(64)
+    }
+#undef DISCO_SM_K
+#undef DISCO_SM
+    const int64_t yrows = (int64_t)B * Co * D.nlat_out;
+    const dim3 igrid((unsigned)((yrows + kFftRows - 1) / kFftRows));
+    if (y_dtype == DISCO_F32)
+        hipLaunchKernelGGL(spec_irfft<float>, igrid, dim3(kFftThreads), fft_lds, st,
+                           reinterpret_cast<const float2*>(yh), static_cast<float*>(y), bias, N,
+                           MP, Co, D.nlat_out, yrows, pl);
+    else
+        hipLaunchKernelGGL(spec_irfft<bf16_t>, igrid, dim3(kFftThreads), fft_lds, st,
+                           reinterpret_cast<const float2*>(yh), static_cast<bf16_t*>(y), bias, N,
+                           MP, Co, D.nlat_out, yrows, pl);
+    hipError_t le = hipGetLastError();
+    hipError_t fe = hipFreeAsync(ws, st);
+    if (le != hipSuccess) {
+        *rc = set_error(DISCO_EHIP, "spectral fused launch failed: %s", hipGetErrorString(le));
+        return 1;
+    }
+    if (fe != hipSuccess) {
+        (void)hipGetLastError();
+        *rc = set_error(DISCO_EHIP, "hipFreeAsync failed: %s", hipGetErrorString(fe));
+        return 1;
+    }
+    *rc = DISCO_OK;
+    return 1;
+}
+
+}  // namespace disco

@@ -1,0 +1,99 @@
+// Longitude-spectral form of Psi, for layers with equal input and output
+// longitude counts (stride 1).
+//
+// With stride 1 the forward equation's inner sum over one output row j and
+// one input row i is a circular correlation along longitude (the p-shift of
+// the DiscreteContinuousConvS2 page): with the window's values v[k, t] at
+// longitudes p = p_lo + t,
+//   X_K[k, q] = sum_t v[k, t] * x[(q + p_lo + t) mod N].
+// Its discrete Fourier transform over q is conj(Psi_hat[k, m]) * x_hat[m]
+// with Psi_hat[k, m] = sum_t v[k, t] * exp(-2 pi i m (p_lo + t) / N).  x is
+// real, so frequencies m = 0 .. N/2 carry everything.
+//
+// This file tabulates, in float64 and stored as float32 pairs:
+//   * Psi_hat per window for m < N/2 + 1, zero up to the padded count MP
+//     (a multiple of 32);
+//   * the radix plan (4, 2, 3, 5) of the N/2-point complex transform the
+//     real transforms are built on.
+#include <algorithm>
+#include <cmath>
+#include <thread>
+#include <vector>
+
+#include "disco_internal.h"
+
+namespace disco {
+
+int spectral_plan(int n, int32_t* radix, int32_t* nrad) {
+    int cnt = 0;
+    for (int r : {4, 2, 3, 5}) {
+        while (n % r == 0 && cnt < kSpecMaxRadix) {
+            radix[cnt++] = r;
+            n /= r;
+        }
+    }
+    *nrad = cnt;
+    return n == 1;
+}
+
+int build_spectral_tables(const HostPsi& h, std::vector<float>& psih, int32_t* radix,
+                          int32_t* nrad, int32_t* mp) {
+    *mp = 0;
+    *nrad = 0;
+    const int N = h.desc.nlon_in;
+    if (h.stride != 1 || h.desc.nlon_out != N || N % 2 != 0 || N < 4 || N > kSpecMaxN ||
+        h.K > 8 || !spectral_plan(N / 2, radix, nrad))
+        return DISCO_OK;   // not eligible: no tables
+    const int M = N / 2 + 1;
+    const int MP = (M + 31) / 32 * 32;
+    const int K = h.K;
+    const size_t nwin = h.windows.size();
+    std::vector<double> c(N), s(N);
+    for (int n = 0; n < N; ++n) {
+        const double a = 2.0 * M_PI * (double)n / (double)N;
+        c[n] = std::cos(a);
+        s[n] = std::sin(a);
+    }
+    try {
+        psih.assign(nwin * (size_t)K * MP * 2, 0.0f);
+    } catch (const std::bad_alloc&) {
+        return set_error(DISCO_ENOMEM, "host allocation for the spectral tables failed");
+    }
+    auto work = [&](size_t w0, size_t w1) {
+        std::vector<double> re(K), im(K);
+        for (size_t w = w0; w < w1; ++w) {
+            const Window& wd = h.windows[w];
+            const double* v = h.win_vals.data() + (size_t)wd.val_off * K;
+            for (int m = 0; m < M; ++m) {
+                std::fill(re.begin(), re.end(), 0.0);
+                std::fill(im.begin(), im.end(), 0.0);
+                for (int t = 0; t < wd.width; ++t) {
+                    int p = (wd.p_lo + t) % N;
+                    if (p < 0) p += N;
+                    const int e = (int)(((int64_t)m * p) % N);
+                    for (int k = 0; k < K; ++k) {
+                        re[k] += v[(size_t)t * K + k] * c[e];
+                        im[k] -= v[(size_t)t * K + k] * s[e];
+                    }
+                }
+                for (int k = 0; k < K; ++k) {
+                    float* o = psih.data() + (((w * K + k) * (size_t)MP) + m) * 2;
+                    o[0] = (float)re[k];
+                    o[1] = (float)im[k];
+                }
+            }
+        }
+    };
+    const unsigned hw = std::max(1u, std::min(16u, std::thread::hardware_concurrency()));
+    const size_t per = (nwin + hw - 1) / hw;
+    std::vector<std::thread> pool;
+    for (unsigned t = 0; t < hw; ++t) {
+        const size_t a = t * per, b = std::min(nwin, a + per);
+        if (a < b) pool.emplace_back(work, a, b);
+    }
+    for (auto& th : pool) th.join();
+    *mp = MP;
+    return DISCO_OK;
+}
+
+}  // namespace disco

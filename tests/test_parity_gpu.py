@@ -201,6 +201,10 @@ def test_roll_equivariance_gpu(sdc, which):
     if wl.dtype == "f32":
         # vector-ALU paths sum every output in the same order: exact
         assert diff == 0.0
+    elif sdc.fused_is_spectral(psi, torch.bfloat16, wl.Ci, wl.Co, wl.groups):
+        # longitude-spectral path: the shift is a phase rotation of the input
+        # spectrum, which is rounded to bf16, so equal up to that rounding
+        assert rel_l2(yr, np.roll(y, -1, axis=-1)) <= 1e-2
     else:
         # the matrix-core path sums within MFMA tiles in an order that depends
         # on the output's position in its 4-output block, and then rounds the

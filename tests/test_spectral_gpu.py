@@ -1,0 +1,182 @@
+"""GPU parity of the longitude-spectral fused path (and of the direct matrix-core
+path on the same shapes), through the C ABI, against the CPU oracle.
+
+The spectral path evaluates each window's circular correlation along
+longitude with real DFTs (the p-shift of the DiscreteContinuousConvS2 page).
+Its spectra and the (frequency, (ci, k)) tile are rounded to bf16, so the bar is
+the bf16 one: relative L2 <= 2e-2 against the float64 oracle on the same
+bf16-rounded inputs.  The shapes below cover every radix of the transform
+plans (2, 3, 4, 5), K from 1 to 8, both output-channel tiles, a batch of two,
+and isotropic and anisotropic bases.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from disco_workloads import WORKLOADS, Workload, draw_inputs, round_bf16
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+TOL_BF16 = 2e-2
+
+
+def _say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module")
+def sdc():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import spherical_disco_convolution_amd as m
+    return m
+
+
+def rel_l2(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+def W(name, B, Ci, Co, nlat, nlon, ks, cut, seed=21):
+    return Workload(name, seed, B, Ci, Co, 1, nlat, nlon, nlat, nlon, ks, oracle.num_basis(ks), cut,
+                    "bf16")
+
+
+# nlon / 2 = 60 (4,3,5), 50 (2,5,5), 36 (4,3,3), 30 (2,3,5), 8 (4,2)
+SPECTRAL = [
+    W("c4_like", 1, 128, 128, 61, 120, (3, 3), 4 * math.pi / 60),
+    W("b2_ci64_co128", 2, 64, 128, 25, 100, (3, 3), 0.45),
+    W("iso_k4_co64", 1, 32, 64, 19, 72, (4,), 0.6),
+    W("k8_co64", 1, 32, 64, 21, 60, (2, 7), 0.5),
+    W("k1_tiny", 1, 32, 64, 9, 16, (1,), 0.7),
+]
+
+
+def _prepare(wl):
+    x, w = draw_inputs(wl)
+    return round_bf16(x), round_bf16(w)
+
+
+def _dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda").to(torch.bfloat16)
+
+
+def _psi(sdc, wl):
+    return sdc.psi_build(wl.nlat_in, wl.nlon_in, wl.nlat_out, wl.nlon_out, wl.kernel_shape,
+                         wl.theta_cutoff).to_device()
+
+
+def _desc(wl):
+    return oracle.Desc(wl.nlat_in, wl.nlon_in, wl.nlat_out, wl.nlon_out, wl.kernel_shape,
+                       wl.theta_cutoff)
+
+
+def test_path_selection(sdc, monkeypatch):
+    wl = SPECTRAL[0]
+    psi = _psi(sdc, wl)
+    monkeypatch.delenv("DISCO_FUSED_PATH", raising=False)
+    assert not sdc.fused_is_spectral(psi, torch.bfloat16, 128, 128, 1)   # opt-in
+    monkeypatch.setenv("DISCO_FUSED_PATH", "spectral")
+    assert sdc.fused_is_spectral(psi, torch.bfloat16, 128, 128, 1)
+    assert sdc.fused_is_spectral(psi, torch.bfloat16, 64, 64, 1)
+    assert not sdc.fused_is_spectral(psi, torch.float32, 128, 128, 1)    # bf16 only
+    assert not sdc.fused_is_spectral(psi, torch.bfloat16, 128, 96, 1)    # Co tile
+    assert not sdc.fused_is_spectral(psi, torch.bfloat16, 40, 64, 1)     # 32-channel chunks
+    assert not sdc.fused_is_spectral(psi, torch.bfloat16, 128, 128, 2)   # groups
+    # stride 2 has no spectral tables
+    p2 = sdc.psi_build(33, 64, 17, 32, (3, 3), 4 * math.pi / 16).to_device()
+    assert not sdc.fused_is_spectral(p2, torch.bfloat16, 128, 128, 1)
+    # N / 2 = 7 is not a product of 2, 3 and 5
+    p7 = sdc.psi_build(9, 14, 9, 14, (3,), 0.7).to_device()
+    assert not sdc.fused_is_spectral(p7, torch.bfloat16, 128, 128, 1)
+
+
+@pytest.mark.parametrize("path", ["spectral", "toeplitz"])
+@pytest.mark.parametrize("wl", SPECTRAL, ids=[w.name for w in SPECTRAL])
+def test_fused_paths_small(sdc, wl, path, monkeypatch):
+    if path == "toeplitz":
+        monkeypatch.delenv("DISCO_FUSED_PATH", raising=False)
+    else:
+        monkeypatch.setenv("DISCO_FUSED_PATH", "spectral")
+    _say("fused", path, wl.name)
+    x, w = _prepare(wl)
+    psi = _psi(sdc, wl)
+    assert sdc.fused_is_spectral(psi, torch.bfloat16, wl.Ci, wl.Co, 1) == (path == "spectral")
+    bias = np.linspace(-1, 1, wl.Co).astype(np.float32)
+    ref = oracle.forward(_desc(wl), x, w, 1)
+    refb = oracle.forward(_desc(wl), x, w, 1, bias=bias)
+    xd, wd = _dev(x), _dev(w)
+    y = sdc.fused_fwd(psi, xd, wd).cpu().numpy()
+    err = rel_l2(y, ref)
+    _say(f"  rel-L2 {err:.3e}")
+    assert err <= TOL_BF16
+    bd = torch.from_numpy(bias).cuda()
+    for out_dtype in (torch.float32, torch.bfloat16):
+        yb = sdc.fused_fwd(psi, xd, wd, bias=bd, out_dtype=out_dtype).float().cpu().numpy()
+        assert rel_l2(yb, refb) <= TOL_BF16
+
+
+def test_spectral_roll_equivariance(sdc, monkeypatch):
+    # a longitude shift of x is a phase rotation of its spectrum, which is then
+    # rounded to bf16: the rolled output agrees up to that rounding (a wrong
+    # shift or index would be off by O(1))
+    monkeypatch.setenv("DISCO_FUSED_PATH", "spectral")
+    wl = SPECTRAL[1]
+    x, w = _prepare(wl)
+    psi = _psi(sdc, wl)
+    xd, wd = _dev(x), _dev(w)
+    y = sdc.fused_fwd(psi, xd, wd).cpu().numpy()
+    yr = sdc.fused_fwd(psi, torch.roll(xd, -1, dims=-1).contiguous(), wd).cpu().numpy()
+    err = rel_l2(yr, np.roll(y, -1, axis=-1))
+    _say(f"spectral roll equivariance rel-L2 {err:.3e}")
+    assert err <= 1e-2
+
+
+def test_spectral_determinism(sdc, monkeypatch):
+    monkeypatch.setenv("DISCO_FUSED_PATH", "spectral")
+    wl = SPECTRAL[1]
+    x, w = _prepare(wl)
+    psi = _psi(sdc, wl)
+    xd, wd = _dev(x), _dev(w)
+    a = sdc.fused_fwd(psi, xd, wd).cpu().numpy()
+    b = sdc.fused_fwd(psi, xd, wd).cpu().numpy()
+    assert np.array_equal(a, b)
+
+
+def _sample_rows(nlat):
+    rows = {0, 1, 2, 5, nlat // 7, nlat // 3, nlat // 2, (2 * nlat) // 3, nlat - 6, nlat - 2, nlat - 1}
+    return sorted(r for r in rows if 0 <= r < nlat)
+
+
+def _sample_cols(nlon, seed=0):
+    rng = np.random.default_rng(seed)
+    cols = {0, 1, nlon - 1, nlon // 2} | set(rng.choice(nlon, size=min(nlon, 28), replace=False).tolist())
+    return sorted(cols)
+
+
+@pytest.mark.parametrize("path", ["spectral", "toeplitz"])
+def test_full_size_c4_paths(sdc, path, monkeypatch):
+    """721x1440, 128 -> 128 channels, K = 7, bf16: both fused algorithms (the
+    benchmark times the direct one, the default)."""
+    if path == "toeplitz":
+        monkeypatch.delenv("DISCO_FUSED_PATH", raising=False)
+    else:
+        monkeypatch.setenv("DISCO_FUSED_PATH", "spectral")
+    wl = WORKLOADS["c4"]
+    _say("full size c4", path)
+    x, w = _prepare(wl)
+    psi = _psi(sdc, wl)
+    assert sdc.fused_is_spectral(psi, torch.bfloat16, wl.Ci, wl.Co, 1) == (path == "spectral")
+    y = sdc.fused_fwd(psi, _dev(x), _dev(w))
+    torch.cuda.synchronize()
+    rows, cols = _sample_rows(wl.nlat_out), _sample_cols(wl.nlon_out)
+    ref = oracle.forward(_desc(wl), x, w, 1, rows=rows, cols_out=cols)
+    got = y[:, :, rows][:, :, :, cols].cpu().numpy()
+    err = rel_l2(got, ref)
+    _say(f"  c4 {path} rel-L2 {err:.3e}")
+    assert err <= TOL_BF16

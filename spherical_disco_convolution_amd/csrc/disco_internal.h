@@ -52,7 +52,7 @@ int build_host_psi(const disco_psi_desc& desc, HostPsi& out);
 // 2, 3 and 5, and K <= 8.  psih: float32 pairs [nwin][K][MP], Psi_hat of each
 // window; radix: the plan of the N/2-point transform.  *mp = 0 when the layer
 // does not qualify.
-constexpr int kSpecMaxN = 2048;   // four rows of two N/2-point float2 buffers: 64 KB LDS
+constexpr int kSpecMaxN = 1800;   // N/2 <= 900 bounds the transform butterflies per lane
 constexpr int kSpecMaxRadix = 12;
 int spectral_plan(int n, int32_t* radix, int32_t* nrad);
 int build_spectral_tables(const HostPsi& h, std::vector<float>& psih, int32_t* radix,

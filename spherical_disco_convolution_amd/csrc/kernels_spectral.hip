@@ -12,7 +12,7 @@
 //   spec_mfma   per (batch, output row, 32 frequencies): the window sum on
 //               the vector ALUs into a bf16 [frequency, re/im][(ci, k)] LDS
 //               tile per 32-channel chunk, then the channel/basis GEMM on
-//               v_mfma_f32_32x32x16_bf16 into y_hat (float32 pairs);
+//               v_mfma_f32_32x32x16_bf16 into y_hat (bf16 pairs);
 //   spec_irfft  y_hat rows -> y rows (+ bias).
 // The real transforms run an N/2-point complex transform in LDS: iterative
 // Stockham passes of radix 4, 2, 3 and 5 (Govindaraju et al., "High
@@ -105,63 +105,75 @@ __device__ __forceinline__ float2 root(int e, float inv_h, float s) {
     return make_float2(cs, s * sn);
 }
 
-// One Stockham pass of radix R over an H-point sequence whose sub-transforms
-// of length Ns are done, by the 64 lanes of one wave (s = -1 forward, +1
-// inverse).  Quotients by Ns use a float reciprocal: (j + 1/2) / Ns is below
-// H / 2 <= 1024 and at least 1 / (2 Ns) >= 1 / H from an integer, and the
-// float product is within 2 ulp (<= 1.3e-4 at 1024) of it, so truncation
-// gives the exact quotient.
-template <int R>
-__device__ __forceinline__ void stockham_pass(const float2* src, float2* dst, int H, int Ns,
-                                              float inv_h, float s, int lane) {
+// The wave's LDS accesses are complete (and the compiler keeps later LDS
+// accesses after this point): enough between the steps of a transform that
+// one wave owns.
+__device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// One in-place Stockham pass of radix R over an H-point sequence whose
+// sub-transforms of length Ns are done, by the 64 lanes of one wave (s = -1
+// forward, +1 inverse).  The lane's butterflies j = lane + 64 it (at most MAXIT)
+// first read all their inputs into registers, then wait for those reads, then
+// write: so one buffer per row suffices.  Quotients by Ns use a float
+// reciprocal: (j + 1/2) / Ns is below H / 2 and at least 1 / (2 Ns) >= 1 / H
+// from an integer, and the float product is within 2 ulp of it (H <= 900), so
+// truncation gives the exact quotient.
+template <int R, int MAXIT>
+__device__ __forceinline__ void stockham_pass(float2* buf, int H, int Ns, const float2* twl,
+                                              float s, int lane) {
     const int HR = H / R;
     const int ts = H / (Ns * R);
     const float inv_ns = 1.0f / (float)Ns;
-    for (int j = lane; j < HR; j += 64) {
-        const int q = (int)(((float)j + 0.5f) * inv_ns);
-        const int jj = j - q * Ns;
-        float2 a[R];
+    float2 a[MAXIT][R];
 #pragma unroll
-        for (int t = 0; t < R; ++t) a[t] = src[j + t * HR];
-        if (jj != 0) {
-            const float2 w = root(jj * ts, inv_h, s);
-            float2 wt = w;
+    for (int it = 0; it < MAXIT; ++it) {
+        const int j = lane + 64 * it;
+        if (j < HR) {
 #pragma unroll
-            for (int t = 1; t < R; ++t) {
-                a[t] = cmul(a[t], wt);
-                if (t + 1 < R) wt = cmul(wt, w);
-            }
+            for (int t = 0; t < R; ++t) a[it][t] = buf[j + t * HR];
         }
-        butterfly<R>(a, s);
-        const int base = q * Ns * R + jj;
-#pragma unroll
-        for (int u = 0; u < R; ++u) dst[base + u * Ns] = a[u];
     }
+    wave_lds_sync();
+#pragma unroll
+    for (int it = 0; it < MAXIT; ++it) {
+        const int j = lane + 64 * it;
+        if (j < HR) {
+            const int q = (int)(((float)j + 0.5f) * inv_ns);
+            const int jj = j - q * Ns;
+            if (jj != 0) {
+                // twl[e] = exp(-2 pi i e / H); e = jj * t * ts < H
+#pragma unroll
+                for (int t = 1; t < R; ++t) {
+                    float2 w = twl[jj * t * ts];
+                    if (s > 0.0f) w.y = -w.y;
+                    a[it][t] = cmul(a[it][t], w);
+                }
+            }
+            butterfly<R>(a[it], s);
+            const int base = q * Ns * R + jj;
+#pragma unroll
+            for (int u = 0; u < R; ++u) buf[base + u * Ns] = a[it][u];
+        }
+    }
+    wave_lds_sync();
 }
 
-// H-point complex DFT of buf0 (one wave's LDS), using buf1 as the other
-// Stockham buffer; returns the buffer that holds the result.  Each pass ends
-// with a workgroup barrier (every wave of the workgroup runs the same plan).
-__device__ float2* fft_wave(float2* buf0, float2* buf1, int H, const SpecPlan& pl, float s,
-                            int lane) {
-    float2* src = buf0;
-    float2* dst = buf1;
-    const float inv_h = 1.0f / (float)H;
+// H-point complex DFT, in place in buf (one wave's LDS row), with the
+// workgroup's twiddle table twl[e] = exp(-2 pi i e / H).  The transform
+// belongs to one wave, so passes are separated by wave-level waits.
+// H <= kSpecMaxN / 2 = 900 bounds the butterflies per lane (MAXIT).
+__device__ void fft_wave(float2* buf, int H, const SpecPlan& pl, const float2* twl, float s,
+                         int lane) {
     int Ns = 1;
     for (int p = 0; p < pl.n; ++p) {
         switch (pl.r[p]) {
-            case 4: stockham_pass<4>(src, dst, H, Ns, inv_h, s, lane); break;
-            case 2: stockham_pass<2>(src, dst, H, Ns, inv_h, s, lane); break;
-            case 3: stockham_pass<3>(src, dst, H, Ns, inv_h, s, lane); break;
-            default: stockham_pass<5>(src, dst, H, Ns, inv_h, s, lane); break;
+            case 4: stockham_pass<4, 4>(buf, H, Ns, twl, s, lane); break;
+            case 2: stockham_pass<2, 8>(buf, H, Ns, twl, s, lane); break;
+            case 3: stockham_pass<3, 5>(buf, H, Ns, twl, s, lane); break;
+            default: stockham_pass<5, 3>(buf, H, Ns, twl, s, lane); break;
         }
-        __syncthreads();
         Ns *= pl.r[p];
-        float2* t = src;
-        src = dst;
-        dst = t;
     }
-    return src;
 }
 
 typedef float float2v __attribute__((ext_vector_type(2)));
@@ -175,9 +187,16 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 constexpr int kFftThreads = 256;
 constexpr int kFftRows = kFftThreads / 64;   // one wave per row
 
+// Twiddle table of the workgroup: twl[e] = exp(-2 pi i e / H), e < H.
+__device__ __forceinline__ void fill_twiddles(float2* twl, int H) {
+    const float inv_h = 1.0f / (float)H;
+    for (int e = threadIdx.x; e < H; e += blockDim.x) twl[e] = root(e, inv_h, -1.0f);
+}
+
 // x rows (N real, bf16) -> x_hat rows (MP bf16 pairs; frequencies past N/2
-// are zero).  One wave per row, four rows per workgroup; LDS: two H-point
-// buffers per row.  Rows past the end compute on row 0 and store nothing.
+// are zero).  One wave per row, four rows per workgroup; LDS: one H-point
+// buffer per row and the H-point twiddle table.  Waves past the last row
+// leave after the table is built.
 __global__ __launch_bounds__(kFftThreads) void spec_rfft(const bf16_t* __restrict__ x,
                                                          uint32_t* __restrict__ xh, int N, int MP,
                                                          int64_t nrows, SpecPlan pl) {
@@ -186,16 +205,18 @@ __global__ __launch_bounds__(kFftThreads) void spec_rfft(const bf16_t* __restric
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int64_t row = (int64_t)blockIdx.x * kFftRows + wave;
     const bool live = row < nrows;
-    float2* b0 = sm + (size_t)wave * 2 * H;
-    float2* b1 = b0 + H;
+    float2* b0 = sm + (size_t)wave * H;
+    float2* twl = sm + (size_t)kFftRows * H;
+    fill_twiddles(twl, H);
     const uint32_t* xr = reinterpret_cast<const uint32_t*>(x + (live ? row : 0) * (size_t)N);
     for (int n = lane; n < H; n += 64) {
         const uint32_t v = xr[n];   // samples 2n (low half) and 2n + 1
         b0[n] = make_float2(__uint_as_float(v << 16), __uint_as_float(v & 0xffff0000u));
     }
-    __syncthreads();
-    const float2* z = fft_wave(b0, b1, H, pl, -1.0f, lane);
+    __syncthreads();   // the twiddle table
     if (!live) return;
+    fft_wave(b0, H, pl, twl, -1.0f, lane);
+    const float2* z = b0;
     // X[m] = (a + b)/2 - i W^m (a - b)/2, a = Z[m mod H], b = conj(Z[(H - m) mod H]),
     // W = exp(-2 pi i / N)
     uint32_t* out = xh + row * (size_t)MP;
@@ -212,11 +233,11 @@ __global__ __launch_bounds__(kFftThreads) void spec_rfft(const bf16_t* __restric
     }
 }
 
-// y_hat rows (MP float pairs, frequencies 0..N/2 used) -> y rows (N) + bias,
-// one wave per row.  The imaginary parts of the zero and N/2 frequencies are
+// y_hat rows (MP bf16 pairs, frequencies 0..N/2 used) -> y rows (N) + bias,
+// one wave per row (LDS as for spec_rfft).  The imaginary parts of the zero and N/2 frequencies are
 // dropped (a real row's spectrum has none).
 template <typename TY>
-__global__ __launch_bounds__(kFftThreads) void spec_irfft(const float2* __restrict__ yh,
+__global__ __launch_bounds__(kFftThreads) void spec_irfft(const uint32_t* __restrict__ yh,
                                                           TY* __restrict__ y,
                                                           const float* __restrict__ bias, int N,
                                                           int MP, int Co, int nlat_out,
@@ -226,14 +247,19 @@ __global__ __launch_bounds__(kFftThreads) void spec_irfft(const float2* __restri
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int64_t row = (int64_t)blockIdx.x * kFftRows + wave;
     const bool live = row < nrows;
-    float2* b0 = sm + (size_t)wave * 2 * H;
-    float2* b1 = b0 + H;
-    const float2* src = yh + (live ? row : 0) * (size_t)MP;
+    float2* b0 = sm + (size_t)wave * H;
+    float2* twl = sm + (size_t)kFftRows * H;
+    fill_twiddles(twl, H);
+    const uint32_t* src = yh + (live ? row : 0) * (size_t)MP;
+    auto spec = [&](int m) {
+        const uint32_t v = src[m];
+        return make_float2(__uint_as_float(v << 16), __uint_as_float(v & 0xffff0000u));
+    };
     // Z[m] = (a + b)/2 + i conj(W^m) (a - b)/2, a = X[m], b = conj(X[H - m]), m < H
     const float inv_n = 0.5f / (float)H;
     for (int m = lane; m < H; m += 64) {
-        float2 a = src[m];
-        float2 b = cconj(src[H - m]);
+        float2 a = spec(m);
+        float2 b = cconj(spec(H - m));
         if (m == 0) {
             a.y = 0.0f;
             b.y = 0.0f;
@@ -241,9 +267,10 @@ __global__ __launch_bounds__(kFftThreads) void spec_irfft(const float2* __restri
         const float2 e = cmul(root(m, inv_n, 1.0f), csub(a, b));
         b0[m] = cadd(cscale(cadd(a, b), 0.5f), cscale(make_float2(-e.y, e.x), 0.5f));
     }
-    __syncthreads();
-    const float2* z = fft_wave(b0, b1, H, pl, 1.0f, lane);
+    __syncthreads();   // the twiddle table, b0
     if (!live) return;
+    fft_wave(b0, H, pl, twl, 1.0f, lane);
+    const float2* z = b0;
     const float bv = bias ? bias[(row / nlat_out) % Co] : 0.0f;
     const float sc = 1.0f / (float)H;
     TY* out = y + row * (size_t)N;
@@ -305,7 +332,7 @@ template <int CO, int KT>
 __global__ __launch_bounds__(kSpecThreads) __attribute__((amdgpu_waves_per_eu(2))) void spec_mfma(
     const uint32_t* __restrict__ xh, const bf16_t* __restrict__ wp,
     const float2* __restrict__ psih, const int32_t* __restrict__ win_ptr,
-    const DevWindow* __restrict__ wins, float* __restrict__ yh, int Ci, int nlat_in,
+    const DevWindow* __restrict__ wins, bf16_t* __restrict__ yh, int Ci, int nlat_in,
     int nlat_out, int MP) {
     __shared__ __attribute__((aligned(16))) bf16_t bt[64 * kBts];
     __shared__ __attribute__((aligned(16))) u32x4 xs[kSpecMaxWin * 32 * 8];   // [r][ci][piece]
@@ -456,16 +483,17 @@ __global__ __launch_bounds__(kSpecThreads) __attribute__((amdgpu_waves_per_eu(2)
         }
         __syncthreads();
     }
-    // ---- y_hat: lane holds GEMM column n (frequency m0 + n/2, real part for
-    // even n), rows 8*(e/4) + 4*lg + e%4 of its 32-row tile ----
+    // ---- y_hat (bf16 (re, im) pairs): lane holds GEMM column n (frequency
+    // m0 + n/2, real part for even n), rows 8*(e/4) + 4*lg + e%4 of its 32-row
+    // tile; element 2 m0 + n of the row ----
 #pragma unroll
     for (int t = 0; t < NTW; ++t) {
         const int n = wn * (64 / WGN) + t * 32 + l32;
-        const size_t col = (size_t)(m0 + (n >> 1)) * 2 + (n & 1);
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
             const int co = wm * 32 + 8 * (e >> 2) + 4 * lg + (e & 3);
-            yh[((size_t)(b * CO + co) * nlat_out + j) * MP * 2 + col] = acc[t][e];
+            yh[((size_t)(b * CO + co) * nlat_out + j) * MP * 2 + 2 * m0 + n] =
+                __builtin_bit_cast(bf16_t, (__bf16)acc[t][e]);
         }
     }
 }
@@ -499,7 +527,7 @@ int try_launch_fused_spectral(const disco_psi* psi, const void* x, const void* w
 
     auto up = [](size_t v) { return (v + 255) / 256 * 256; };
     const size_t xh_bytes = up((size_t)B * Ci * D.nlat_in * MP * 4);
-    const size_t yh_bytes = up((size_t)B * Co * D.nlat_out * MP * 8);
+    const size_t yh_bytes = up((size_t)B * Co * D.nlat_out * MP * 4);
     const size_t wp_bytes = up((size_t)Co * Ci * 8 * 2);
     void* ws = nullptr;
     hipError_t e = hipMallocAsync(&ws, xh_bytes + yh_bytes + wp_bytes, st);
@@ -511,14 +539,14 @@ int try_launch_fused_spectral(const disco_psi* psi, const void* x, const void* w
         return 1;
     }
     uint32_t* xh = static_cast<uint32_t*>(ws);
-    float* yh = reinterpret_cast<float*>(static_cast<char*>(ws) + xh_bytes);
+    bf16_t* yh = reinterpret_cast<bf16_t*>(static_cast<char*>(ws) + xh_bytes);
     bf16_t* wpd = reinterpret_cast<bf16_t*>(static_cast<char*>(ws) + xh_bytes + yh_bytes);
     const float2* psih = static_cast<const float2*>(d.spec_psih);
 
     const size_t nwp = (size_t)Co * Ci * 8;
     hipLaunchKernelGGL(spec_prep_w, dim3((unsigned)((nwp + 255) / 256)), dim3(256), 0, st,
                        static_cast<const bf16_t*>(w), wpd, Co, Ci, K);
-    const size_t fft_lds = (size_t)kFftRows * 2 * H * sizeof(float2);
+    const size_t fft_lds = (size_t)(kFftRows + 1) * H * sizeof(float2);
     const int64_t xrows = (int64_t)B * Ci * D.nlat_in;
     hipLaunchKernelGGL(spec_rfft, dim3((unsigned)((xrows + kFftRows - 1) / kFftRows)),
                        dim3(kFftThreads), fft_lds, st, static_cast<const bf16_t*>(x), xh, N, MP,
@@ -549,11 +577,11 @@ int try_launch_fused_spectral(const disco_psi* psi, const void* x, const void* w
     const dim3 igrid((unsigned)((yrows + kFftRows - 1) / kFftRows));
     if (y_dtype == DISCO_F32)
         hipLaunchKernelGGL(spec_irfft<float>, igrid, dim3(kFftThreads), fft_lds, st,
-                           reinterpret_cast<const float2*>(yh), static_cast<float*>(y), bias, N,
+                           reinterpret_cast<const uint32_t*>(yh), static_cast<float*>(y), bias, N,
                            MP, Co, D.nlat_out, yrows, pl);
     else
         hipLaunchKernelGGL(spec_irfft<bf16_t>, igrid, dim3(kFftThreads), fft_lds, st,
-                           reinterpret_cast<const float2*>(yh), static_cast<bf16_t*>(y), bias, N,
+                           reinterpret_cast<const uint32_t*>(yh), static_cast<bf16_t*>(y), bias, N,
                            MP, Co, D.nlat_out, yrows, pl);
     hipError_t le = hipGetLastError();
     hipError_t fe = hipFreeAsync(ws, st);

@@ -311,28 +311,34 @@ constexpr int kBts = 264;            // B tile row: 256 (k, ci) pairs + 8 pad (b
 constexpr int kSpecThreads = 256;
 constexpr int kSpecMaxWin = 8;       // windows per output row (one 16-deep MFMA step)
 
-// Per (batch b, output row j, 32 frequencies m0 ..): both sums on the matrix
-// cores, per 32-channel chunk.
+// Both sums of the forward equation for work items (batch b, output row j,
+// 32 frequencies m0 ..), on the matrix cores, per 32-channel chunk.
 //  * Window sum.  For one frequency, X_hat[ci, (k, re/im)] is the product of
 //    x_hat[ci, (r, re/im)] (32 x 16: up to 8 windows) with the real 2 x 2
 //    block form of conj(Psi_hat[k, r]) (16 x 32, columns (k, re/im), k < 8):
 //    one v_mfma_f32_32x32x16_bf16.  The A operand is the bf16 (re, im) words
 //    of x_hat as stored (lane = channel, four windows per lane half), read
 //    from the chunk's spectra block in LDS, which is filled with coalesced
-//    loads one chunk ahead (eight lanes per 128-byte row); its 16-byte pieces
-//    are XOR-swizzled by channel so that the lanes' reads hit distinct banks.
-//    Each wave owns 8 of the 32 frequencies and builds their B operands once
-//    per item from the Psi_hat slice in LDS.  Results go to the bf16 LDS tile
-//    bt[(m, re/im)][k * 32 + ci].
+//    loads (eight lanes per 128-byte row); its 16-byte pieces are
+//    XOR-swizzled by channel so that the lanes' reads hit distinct banks.
+//    Each wave owns 8 of the 32 frequencies and builds their B operands at
+//    the start of an item from the Psi_hat slice in LDS.  Results go to the
+//    bf16 LDS tile bt[(m, re/im)][k * 32 + ci].
 //  * Channel/basis GEMM: y_hat[co, (m, re/im)] += wp[co, (k, ci)] bt[(k, ci),
 //    (m, re/im)], 4 waves, wave tile 32 x 64 (CO = 128) or 32 x 32 (CO = 64),
-//    16 k-steps per chunk.  Each weight fragment is requested for the next
-//    chunk right after its use, so it arrives while other work runs.
+//    16 k-steps per chunk, weights in fragment order.
+// Persistent: workgroup g takes items g, g + G, ... (G = gridDim.x), items
+// ordered (b, j, tile).  Its (item, chunk) pairs form one stream, pipelined
+// across item boundaries: the spectra of stream position p + 1 are in LDS and
+// those of p + 2 in flight while p is computed (their window rows fetched
+// one position earlier), each weight fragment is reloaded for the next chunk
+// right after its use (the weights do not depend on the item), and the next
+// item's Psi_hat slice is loaded during the current item.
 template <int CO, int KT>
 __global__ __launch_bounds__(kSpecThreads) __attribute__((amdgpu_waves_per_eu(2))) void spec_mfma(
     const uint32_t* __restrict__ xh, const bf16_t* __restrict__ wp,
     const float2* __restrict__ psih, const int32_t* __restrict__ win_ptr,
-    const DevWindow* __restrict__ wins, bf16_t* __restrict__ yh, int Ci, int nlat_in,
+    const DevWindow* __restrict__ wins, bf16_t* __restrict__ yh, int B, int Ci, int nlat_in,
     int nlat_out, int MP) {
     __shared__ __attribute__((aligned(16))) bf16_t bt[64 * kBts];
     __shared__ __attribute__((aligned(16))) u32x4 xs[kSpecMaxWin * 32 * 8];   // [r][ci][piece]
@@ -340,161 +346,224 @@ __global__ __launch_bounds__(kSpecThreads) __attribute__((amdgpu_waves_per_eu(2)
     constexpr int WGM = CO / 32;          // waves along the output channels
     constexpr int WGN = 4 / WGM;          // waves along the columns
     constexpr int NTW = 2 / WGN;          // 32-column MFMA tiles per wave
+    constexpr int PSN = (kSpecMaxWin * KT * kMt + kSpecThreads - 1) / kSpecThreads;
 
-    const int m0 = blockIdx.x * kMt;
-    const int j = blockIdx.y;
-    const int b = blockIdx.z;
-    const int w0 = uniform(win_ptr[j]);
-    const int nw = uniform(win_ptr[j + 1]) - w0;   // <= kSpecMaxWin (checked on the host)
+    const int ntiles = MP / kMt;
+    const int nitems = B * nlat_out * ntiles;
+    const int G = gridDim.x;
+    const int nmine = (nitems - (int)blockIdx.x + G - 1) / G;   // >= 1 (grid <= items)
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = uniform(tid >> 6);
     const int l32 = lane & 31, lg = lane >> 5;
     const int wm = wave % WGM, wn = wave / WGM;
     const int nchunks = Ci / 32;
+    const int f0 = wave * 8;
+    const int sp = tid & 7, sci = tid >> 3;
+    const size_t cstride = (size_t)32 * nlat_in * MP;   // one 32-channel chunk
+    const size_t plane = (size_t)nlat_in * MP;
 
-    // the row's Psi_hat slice ps[(r KT + k) kMt + ml]; basis columns past KT
-    // of the tile are zero for the whole item
-    for (int idx = tid; idx < nw * KT * kMt; idx += kSpecThreads) {
-        const int rk = idx / kMt, ml = idx - rk * kMt;
-        ps[idx] = psih[(size_t)(w0 * KT + rk) * MP + m0 + ml];
-    }
+    // item n of this workgroup (clamped to its last): global index, (b, j, m0)
+    auto item_of = [&](int n) { return (int)blockIdx.x + (n < nmine ? n : nmine - 1) * G; };
+
+    // ---- spectra stream: position p = (item p / nchunks, chunk p % nchunks).
+    // Thread (piece p = tid % 8, channel tid / 8) loads the 16-byte piece (4
+    // frequencies) of every window's row; LDS slot ((r * 32 + ci) * 8 +
+    // (piece ^ (ci & 7))).  Window slots past the row's windows repeat window
+    // 0 (valid, finite; their B rows are zero).
+    size_t src_base = 0;            // this lane's element offset of the position fetched next
+    int src_row[kSpecMaxWin];       // its window rows' offsets (lat * MP, wave-uniform)
+    int lat_req[kSpecMaxWin];       // window rows of the position after it (requested)
+    int req_m0 = 0, req_chunk = 0, req_b = 0;
+    auto request_rows = [&](int p) {   // vector loads of position p's window rows
+        const int it = item_of(p / nchunks);
+        const int mt = it % ntiles, jb = it / ntiles;
+        const int j = jb % nlat_out;
+        req_b = jb / nlat_out;
+        req_m0 = mt * kMt;
+        req_chunk = p % nchunks;
+        const int w0 = win_ptr[j], nw = win_ptr[j + 1] - w0;
+#pragma unroll
+        for (int r = 0; r < kSpecMaxWin; ++r) lat_req[r] = wins[w0 + (r < nw ? r : 0)].lat;
+    };
+    auto resolve_rows = [&]() {   // addresses from the requested rows
+        src_base = ((size_t)(req_b * Ci + req_chunk * 32 + sci)) * plane + req_m0 + 4 * sp;
+#pragma unroll
+        for (int r = 0; r < kSpecMaxWin; ++r) src_row[r] = uniform(lat_req[r]) * MP;
+    };
+    u32x4 xn[kSpecMaxWin];
+    auto load_x = [&]() {
+        const uint32_t* base = xh + src_base;
+#pragma unroll
+        for (int r = 0; r < kSpecMaxWin; ++r)
+            xn[r] = *reinterpret_cast<const u32x4*>(base + src_row[r]);
+    };
+    auto store_x = [&]() {
+#pragma unroll
+        for (int r = 0; r < kSpecMaxWin; ++r) xs[(r * 32 + sci) * 8 + (sp ^ (sci & 7))] = xn[r];
+    };
+
+    // ---- Psi_hat slice of an item: ps[(r KT + k) kMt + ml]; slots past the
+    // row's windows are zero
+    float2 pn[PSN];
+    auto load_ps = [&](int n) {
+        const int it = item_of(n);
+        const int mt = it % ntiles, j = (it / ntiles) % nlat_out;
+        const int w0 = win_ptr[j], nw = win_ptr[j + 1] - w0;
+#pragma unroll
+        for (int q = 0; q < PSN; ++q) {
+            const int idx = tid + q * kSpecThreads;
+            const int rk = idx / kMt, ml = idx - rk * kMt;
+            pn[q] = make_float2(0.0f, 0.0f);
+            if (rk < nw * KT) pn[q] = psih[(size_t)(w0 * KT + rk) * MP + mt * kMt + ml];
+        }
+    };
+    auto store_ps = [&]() {
+#pragma unroll
+        for (int q = 0; q < PSN; ++q) {
+            const int idx = tid + q * kSpecThreads;
+            if (idx < kSpecMaxWin * KT * kMt) ps[idx] = pn[q];
+        }
+    };
+
+    // ---- prologue: basis columns past KT are zero for the whole kernel
     if (KT < 8) {
         for (int idx = tid; idx < 64 * (8 - KT) * 4; idx += kSpecThreads) {
             const int row = idx / ((8 - KT) * 4), q = idx - row * ((8 - KT) * 4);
             *reinterpret_cast<u32x4*>(bt + row * kBts + KT * 32 + q * 8) = u32x4{0, 0, 0, 0};
         }
     }
-
-    // input spectra of one chunk: thread (piece p = tid % 8, channel tid / 8)
-    // loads the 16-byte piece p (4 frequencies) of every window's row; LDS
-    // slot ((r * 32 + ci) * 8 + (p ^ (ci & 7)))
-    const int f0 = wave * 8;
-    const int sp = tid & 7, sci = tid >> 3;
-    const size_t cstride = (size_t)32 * nlat_in * MP;   // one 32-channel chunk
-    size_t soff[kSpecMaxWin];
-#pragma unroll
-    for (int r = 0; r < kSpecMaxWin; ++r) {
-        const int lat = wins[w0 + (r < nw ? r : 0)].lat;
-        soff[r] = ((size_t)(b * Ci + sci) * nlat_in + lat) * MP + m0 + 4 * sp;
-    }
-    u32x4 xn[kSpecMaxWin];
-    auto load_x = [&](int cc) {
-#pragma unroll
-        for (int r = 0; r < kSpecMaxWin; ++r)   // rows past nw repeat window 0's (valid)
-            xn[r] = *reinterpret_cast<const u32x4*>(xh + soff[r] + cc * cstride);
-    };
-    auto store_x = [&]() {
-#pragma unroll
-        for (int r = 0; r < kSpecMaxWin; ++r) xs[(r * 32 + sci) * 8 + (sp ^ (sci & 7))] = xn[r];
-    };
-    load_x(0);
+    const int npos = nmine * nchunks;
+    load_ps(0);
+    request_rows(0);
+    resolve_rows();
+    load_x();                          // position 0
     u32x4 wq[16];
     // fragment (chunk, k-step) of this wave's 32 rows: wf[(chunk * 16 + k-step) * WGM * 64]
     const u32x4* wf = reinterpret_cast<const u32x4*>(wp) + wm * 64 + lane;
 #pragma unroll
     for (int ks = 0; ks < 16; ++ks) wq[ks] = wf[(size_t)ks * WGM * 64];
-    store_x();
-    load_x(nchunks > 1 ? 1 : 0);
-    // A-operand reads: lane (channel l32, windows 4 lg + u, clamped to window 0
-    // past the row's windows: finite data against zero B rows), pieces
-    // 2 wave and 2 wave + 1 (the wave's frequencies)
-    int xrd[4][2];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int r = 4 * lg + u < nw ? 4 * lg + u : 0;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) xrd[u][h] = (r * 32 + l32) * 8 + ((2 * wave + h) ^ (l32 & 7));
-    }
+    store_ps();
+    store_x();                         // xs: position 0
+    request_rows(npos > 1 ? 1 : 0);
+    resolve_rows();
+    load_x();                          // xn: position 1
+    request_rows(npos > 2 ? 2 : npos - 1);   // rows of position 2
     __syncthreads();   // ps, zero columns, first spectra block
 
-    // B operands of the window sum: lane column n = 2 k + c (c: real, imaginary
-    // part of X_hat), rows (r, re/im) for r = 4 lg .. 4 lg + 3
-    u32x4 bq[8];
-    {
-        const int n = l32, k = n >> 1, c = n & 1;
-#pragma unroll
-        for (int f = 0; f < 8; ++f) {
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int r = 4 * lg + u;
-                float2 P = make_float2(0.0f, 0.0f);
-                if (n < 2 * KT && r < nw) P = ps[(r * KT + k) * kMt + f0 + f];
-                // real column: (Pr, Pi); imaginary column: (-Pi, Pr)
-                bq[f][u] = c ? pack_bf16x2(-P.y, P.x) : pack_bf16x2(P.x, P.y);
-            }
-        }
-    }
+    for (int n = 0; n < nmine; ++n) {
+        const int it = item_of(n);
+        const int mt = it % ntiles, jb = it / ntiles;
+        const int j = jb % nlat_out, b = jb / nlat_out;
+        const int m0 = mt * kMt;
+        const int w0 = uniform(win_ptr[j]);
+        const int nw = uniform(win_ptr[j + 1]) - w0;   // <= kSpecMaxWin (checked on the host)
 
-    floatx16 acc[NTW];
+        // B operands of the window sum: lane column n = 2 k + c (c: real,
+        // imaginary part of X_hat), rows (r, re/im) for r = 4 lg .. 4 lg + 3
+        u32x4 bq[8];
+        {
+            const int nn = l32, k = nn >> 1, c = nn & 1;
 #pragma unroll
-    for (int t = 0; t < NTW; ++t)
+            for (int f = 0; f < 8; ++f) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) acc[t][e] = 0.0f;
-
-    for (int cc = 0; cc < nchunks; ++cc) {
-        // ---- window sum, one MFMA per frequency ----
-        u32x4 xa[4][2];
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-#pragma unroll
-            for (int h = 0; h < 2; ++h) xa[u][h] = xs[xrd[u][h]];
-#pragma unroll
-        for (int f = 0; f < 8; ++f) {
-            const u32x4 a = {xa[0][f >> 2][f & 3], xa[1][f >> 2][f & 3], xa[2][f >> 2][f & 3],
-                             xa[3][f >> 2][f & 3]};
-            floatx16 d;
-#pragma unroll
-            for (int e = 0; e < 16; ++e) d[e] = 0.0f;
-            d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                        __builtin_bit_cast(bf16x8_t, bq[f]), d,
-                                                        0, 0, 0);
-            if (l32 < 2 * KT) {
-                // column (k, c) -> tile row 2 (f0 + f) + c, pairs k * 32 + ci,
-                // ci = 8 q + 4 lg + (0..3)
-                bf16_t* dst = bt + (2 * (f0 + f) + (l32 & 1)) * kBts + (l32 >> 1) * 32 + 4 * lg;
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const uint2 pk = make_uint2(pack_bf16x2(d[4 * q], d[4 * q + 1]),
-                                                pack_bf16x2(d[4 * q + 2], d[4 * q + 3]));
-                    *reinterpret_cast<uint2*>(dst + 8 * q) = pk;
+                for (int u = 0; u < 4; ++u) {
+                    const int r = 4 * lg + u;
+                    float2 P = make_float2(0.0f, 0.0f);
+                    if (nn < 2 * KT && r < nw) P = ps[(r * KT + k) * kMt + f0 + f];
+                    // real column: (Pr, Pi); imaginary column: (-Pi, Pr)
+                    bq[f][u] = c ? pack_bf16x2(-P.y, P.x) : pack_bf16x2(P.x, P.y);
                 }
             }
         }
-        __syncthreads();   // tile complete; every wave is done with the spectra block
-        // next chunk's spectra into LDS, the one after into registers (chunks
-        // past the end reload the last one)
-        const int cn = cc + 1 < nchunks ? cc + 1 : cc;
-        store_x();
-        load_x(cc + 2 < nchunks ? cc + 2 : nchunks - 1);
-        // ---- channel/basis GEMM over this chunk's 256 (k, ci) pairs ----
-        const bf16_t* bb = bt + (wn * (64 / WGN) + l32) * kBts + 8 * lg;
-        const u32x4* wnext = wf + (size_t)cn * 16 * WGM * 64;
+        load_ps(n + 1);   // the next item's slice, stored after this item
+        // A-operand reads: lane (channel l32, windows 4 lg + u, clamped to
+        // window 0 past the row's windows), pieces 2 wave and 2 wave + 1
+        int xrd[4][2];
 #pragma unroll
-        for (int ks = 0; ks < 16; ++ks) {
-            const bf16x8_t af = __builtin_bit_cast(bf16x8_t, wq[ks]);
+        for (int u = 0; u < 4; ++u) {
+            const int r = 4 * lg + u < nw ? 4 * lg + u : 0;
 #pragma unroll
-            for (int t = 0; t < NTW; ++t) {
-                const bf16x8_t bf =
-                    *reinterpret_cast<const bf16x8_t*>(bb + t * 32 * kBts + 16 * ks);
-                acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf, acc[t], 0, 0, 0);
+            for (int h = 0; h < 2; ++h)
+                xrd[u][h] = (r * 32 + l32) * 8 + ((2 * wave + h) ^ (l32 & 7));
+        }
+
+        floatx16 acc[NTW];
+#pragma unroll
+        for (int t = 0; t < NTW; ++t)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[t][e] = 0.0f;
+
+        for (int cc = 0; cc < nchunks; ++cc) {
+            const int p = n * nchunks + cc;   // stream position in xs
+            // ---- window sum, one MFMA per frequency ----
+            u32x4 xa[4][2];
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) xa[u][h] = xs[xrd[u][h]];
+#pragma unroll
+            for (int f = 0; f < 8; ++f) {
+                const u32x4 a = {xa[0][f >> 2][f & 3], xa[1][f >> 2][f & 3], xa[2][f >> 2][f & 3],
+                                 xa[3][f >> 2][f & 3]};
+                floatx16 d;
+#pragma unroll
+                for (int e = 0; e < 16; ++e) d[e] = 0.0f;
+                d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                            __builtin_bit_cast(bf16x8_t, bq[f]), d,
+                                                            0, 0, 0);
+                if (l32 < 2 * KT) {
+                    // column (k, c) -> tile row 2 (f0 + f) + c, pairs k * 32 + ci,
+                    // ci = 8 q + 4 lg + (0..3)
+                    bf16_t* dst =
+                        bt + (2 * (f0 + f) + (l32 & 1)) * kBts + (l32 >> 1) * 32 + 4 * lg;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const uint2 pk = make_uint2(pack_bf16x2(d[4 * q], d[4 * q + 1]),
+                                                    pack_bf16x2(d[4 * q + 2], d[4 * q + 3]));
+                        *reinterpret_cast<uint2*>(dst + 8 * q) = pk;
+                    }
+                }
             }
-            wq[ks] = wnext[(size_t)ks * WGM * 64];
+            __syncthreads();   // tile complete; every wave is done with the spectra block
+            // stream: position p + 1 into LDS, p + 2 in flight, rows of p + 3
+            // requested (positions past the end repeat the last)
+            store_x();
+            resolve_rows();
+            load_x();
+            request_rows(p + 3 < npos ? p + 3 : npos - 1);
+            // ---- channel/basis GEMM over this chunk's 256 (k, ci) pairs ----
+            const int cn = cc + 1 < nchunks ? cc + 1 : 0;   // weights of the next chunk
+            const bf16_t* bb = bt + (wn * (64 / WGN) + l32) * kBts + 8 * lg;
+            const u32x4* wnext = wf + (size_t)cn * 16 * WGM * 64;
+#pragma unroll
+            for (int ks = 0; ks < 16; ++ks) {
+                const bf16x8_t af = __builtin_bit_cast(bf16x8_t, wq[ks]);
+#pragma unroll
+                for (int t = 0; t < NTW; ++t) {
+                    const bf16x8_t bf =
+                        *reinterpret_cast<const bf16x8_t*>(bb + t * 32 * kBts + 16 * ks);
+                    acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf, acc[t], 0, 0, 0);
+                }
+                wq[ks] = wnext[(size_t)ks * WGM * 64];
+            }
+            __syncthreads();
         }
+        // ---- y_hat (bf16 (re, im) pairs): lane holds GEMM column nn (frequency
+        // m0 + nn/2, real part for even nn), rows 8*(e/4) + 4*lg + e%4 of its
+        // 32-row tile; element 2 m0 + nn of the row ----
+#pragma unroll
+        for (int t = 0; t < NTW; ++t) {
+            const int nn = wn * (64 / WGN) + t * 32 + l32;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int co = wm * 32 + 8 * (e >> 2) + 4 * lg + (e & 3);
+                yh[((size_t)(b * CO + co) * nlat_out + j) * MP * 2 + 2 * m0 + nn] =
+                    __builtin_bit_cast(bf16_t, (__bf16)acc[t][e]);
+            }
+        }
+        store_ps();      // the next item's slice (every wave built its B operands)
         __syncthreads();
-    }
-    // ---- y_hat (bf16 (re, im) pairs): lane holds GEMM column n (frequency
-    // m0 + n/2, real part for even n), rows 8*(e/4) + 4*lg + e%4 of its 32-row
-    // tile; element 2 m0 + n of the row ----
-#pragma unroll
-    for (int t = 0; t < NTW; ++t) {
-        const int n = wn * (64 / WGN) + t * 32 + l32;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int co = wm * 32 + 8 * (e >> 2) + 4 * lg + (e & 3);
-            yh[((size_t)(b * CO + co) * nlat_out + j) * MP * 2 + 2 * m0 + n] =
-                __builtin_bit_cast(bf16_t, (__bf16)acc[t][e]);
-        }
     }
 }
 
@@ -551,10 +620,16 @@ int try_launch_fused_spectral(const disco_psi* psi, const void* x, const void* w
     hipLaunchKernelGGL(spec_rfft, dim3((unsigned)((xrows + kFftRows - 1) / kFftRows)),
                        dim3(kFftThreads), fft_lds, st, static_cast<const bf16_t*>(x), xh, N, MP,
                        xrows, pl);
-    dim3 grid((unsigned)(MP / kMt), (unsigned)D.nlat_out, (unsigned)B);
+    // persistent: two workgroups per CU (their registers and LDS allow two)
+    int dev = 0, ncu = 256;
+    if (hipGetDevice(&dev) == hipSuccess)
+        (void)hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+    (void)hipGetLastError();
+    const int64_t nitems = (int64_t)B * D.nlat_out * (MP / kMt);
+    dim3 grid((unsigned)std::min<int64_t>(nitems, 2 * (int64_t)ncu));
 #define DISCO_SM(CC, KK)                                                                     \
     hipLaunchKernelGGL((spec_mfma<CC, KK>), grid, dim3(kSpecThreads), 0, st, xh, wpd,         \
-                       psih, d.win_ptr, d.windows, yh, Ci, D.nlat_in, D.nlat_out, MP)
+                       psih, d.win_ptr, d.windows, yh, B, Ci, D.nlat_in, D.nlat_out, MP)
 #define DISCO_SM_K(CC)                                                                       \
     switch (K) {                                                                             \
         case 1: DISCO_SM(CC, 1); break;                                                      \

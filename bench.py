@@ -4,9 +4,10 @@
     python bench.py --copy-calibration      (one plain device copy of known size, for
                                              calibrating rocprofv3 FETCH_SIZE / WRITE_SIZE)
 
-A step is one forward pass (the fused kernel: contraction and channel/basis
-contraction in one launch) over one batch of seeded synthetic input that is
-resident in device memory before timing starts.  Psi is built once before
+A step is one forward pass (one disco_fused_fwd call: contraction and
+channel/basis contraction without storing the K-expanded tensor) over one
+batch of seeded synthetic input that is resident in device memory before
+timing starts.  Psi is built once before
 the timed region (it is a precomputed tensor of the layer).  The unfused pair
 (contraction writing the K-expanded tensor, then the channel/basis GEMM) is
 timed alongside and reported as extra fields.
@@ -20,10 +21,14 @@ timed on a bounded sample of output rows of the same workload, single-threaded,
 and extrapolated to the whole workload by support-point weighting (the oracle's
 time is linear in the support size of the rows it evaluates).
 
-The timed unit of the fused forward is one disco_fused_fwd call: a small kernel
-that tiles the weights into matrix-core operand fragments, then the fused
-kernel.  `roofline.achieved` divides the algorithmic work by that call's
-average HIP-event time, so it slightly understates the fused kernel itself.
+The timed unit of the fused forward is one disco_fused_fwd call.  For layers
+the longitude-spectral algorithm takes (the headline workload is one) a call is
+four launches: weight tiling, the forward real DFT of x, the per-frequency
+window and channel/basis matrix-core kernel, and the inverse real DFT; for
+others it is the weight tiling and the direct fused kernel.  `roofline.achieved`
+divides the algorithmic work by that call's average HIP-event time, and
+`roofline.traffic` sums the HBM counters of the call's launches.  The direct
+kernel's time on the same inputs is reported as `direct_fused_ms`.
 """
 from __future__ import annotations
 
@@ -43,17 +48,19 @@ HBM_PEAK_GBS = 8000.0
 
 METRIC = "DISCO fwd output-points\u00b7Cout/s at 721x1440 C=128 K=7; % HBM/MFMA roofline"
 
-# rocprofv3 HBM counters of the fused kernel at the headline workload, per
-# launch: FETCH_SIZE x 2.000 + WRITE_SIZE x 1.000 (factors from a 512 MiB
-# device copy, see profiles/).  Keyed by the SHA-1 of the kernel source the
-# counters were taken with: when the source has changed the figure is stale
-# and `traffic` is reported as null.
+# rocprofv3 HBM counters at the headline workload, per call (summed over the
+# call's launches): FETCH_SIZE x 2.000 + WRITE_SIZE x 1.000 (factors from a
+# 512 MiB device copy, see profiles/).  Keyed by the SHA-1 of the kernel source
+# the counters were taken with: when the source has changed the figure is
+# stale and `traffic` is reported as null.
 MEASURED_TRAFFIC_BYTES = {
-    ("c4", "fused"): {"bytes": 1385536054, "source": "kernels_fused_mfma.hip",
+    ("c4", "fused_spectral"): {"bytes": 3764698465, "source": "kernels_spectral.hip",
+                               "sha1": "42ca2c8f2f75e096c4c5ce5919ed5f523242b0c6"},
+    ("c4", "fused"): {"bytes": 1398957116, "source": "kernels_fused_mfma.hip",
                       "sha1": "085750d43f6ea11b9542c528c622dee7a36cc62c"},
-    ("c4", "contract"): {"bytes": 2868086133, "source": "kernels_fused_mfma.hip",
+    ("c4", "contract"): {"bytes": 2869686387, "source": "kernels_fused_mfma.hip",
                          "sha1": "085750d43f6ea11b9542c528c622dee7a36cc62c"},
-    ("c4", "einsum"): {"bytes": 2640528958, "source": "kernels_einsum_mfma.hip",
+    ("c4", "einsum"): {"bytes": 2640377027, "source": "kernels_einsum_mfma.hip",
                        "sha1": "664722963bc48f17bb18c1dc6c32a5e442abc321"},
 }
 CSRC = os.path.join(ROOT, "spherical_disco_convolution_amd", "csrc")
@@ -203,6 +210,7 @@ def main():
     psi.to_device()
     torch.cuda.synchronize()
     psi_upload_s = time.perf_counter() - t0
+    spectral = sdc.fused_is_spectral(psi, tdt, wl.Ci, wl.Co, wl.groups)
 
     y = torch.empty((wl.B, wl.Co, wl.nlat_out, wl.nlon_out), dtype=torch.float32, device="cuda")
     fused = lambda: sdc.fused_fwd(psi, xd, wd, groups=wl.groups, y=y)
@@ -226,7 +234,7 @@ def main():
     dsize = 2 if wl.dtype == "bf16" else 4
     peak = PEAK_TFLOPS[wl.dtype]
     achieved = f_alg / kernel_s / 1e12
-    traffic = measured_traffic(key, "fused")
+    traffic = measured_traffic(key, "fused_spectral" if spectral else "fused")
     roofline = {"bound": "mfma" if wl.dtype == "bf16" else "alu", "achieved": round(achieved, 3),
                 "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                 "traffic": traffic}
@@ -238,14 +246,15 @@ def main():
         "psi_build_s": round(psi_build_s, 3),
         "psi_upload_s": round(psi_upload_s, 3),
     }
-    if not args.fused_only and sdc.fused_is_spectral_optin(psi, tdt, wl.Ci, wl.Co, wl.groups):
-        # the opt-in longitude-spectral algorithm on the same inputs
-        os.environ["DISCO_FUSED_PATH"] = "spectral"
+    extra["fused_algorithm"] = "spectral" if spectral else "direct"
+    if not args.fused_only and spectral:
+        # the direct matrix-core kernel on the same inputs, for comparison
+        os.environ["DISCO_FUSED_PATH"] = "toeplitz"
         try:
             for _ in range(2):
                 fused()
             _, t_s = time_region(fused, args.steps, torch)
-            extra["spectral_fused_ms"] = round(t_s / args.steps * 1000, 4)
+            extra["direct_fused_ms"] = round(t_s / args.steps * 1000, 4)
         finally:
             del os.environ["DISCO_FUSED_PATH"]
     if not args.no_unfused and not args.fused_only:

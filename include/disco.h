@@ -124,15 +124,16 @@ int disco_einsum(const void* xk, int xk_dtype, const void* w, int w_dtype,
  * result as disco_contract followed by disco_einsum, without storing xk in
  * device memory.  x_dtype and w_dtype must be equal.
  *
- * With the environment variable DISCO_FUSED_PATH=spectral, stride-1 layers
- * (nlon_in == nlon_out, even, N/2 a product of 2, 3 and 5, N <= 1800) with
- * bf16 x and w, groups == 1, Ci a multiple of 32, Co 64 or 128, K <= 8 and at
- * most 8 input rows per output row run in the longitude-spectral form: the
- * forward equation's longitude shift makes each window a circular
- * correlation, so it is evaluated with real DFTs along longitude (three
- * kernels, a stream-ordered workspace of B*Ci*nlat_in*MP*4 +
- * B*Co*nlat_out*MP*4 bytes with MP = N/2 + 1 rounded up to 32).  Otherwise
- * the direct kernels run. */
+ * Stride-1 layers (nlon_in == nlon_out, even, N/2 a product of 2, 3 and 5,
+ * N <= 1800) with bf16 x and w, groups == 1, Ci a multiple of 32, Co 64 or
+ * 128, K <= 8 and at most 8 input rows per output row run in the
+ * longitude-spectral form: the forward equation's longitude shift makes each
+ * window a circular correlation, so it is evaluated with real DFTs along
+ * longitude (three kernels, a stream-ordered workspace of
+ * B*Ci*nlat_in*MP*4 + B*Co*nlat_out*MP*4 bytes with MP = N/2 + 1 rounded up
+ * to 32).  The environment variable DISCO_FUSED_PATH=toeplitz selects the
+ * direct matrix-core kernel for them instead.  Other layers run the direct
+ * kernels. */
 int disco_fused_fwd(const disco_psi* psi, const void* x, int x_dtype,
                     const void* w, int w_dtype, const float* bias,
                     void* y, int y_dtype, int32_t B, int32_t Ci, int32_t Co,

@@ -283,20 +283,6 @@ def fused_is_spectral(psi: Psi, x_dtype, Ci: int, Co: int, groups: int = 1) -> b
     return rc == 1
 
 
-def fused_is_spectral_optin(psi: Psi, x_dtype, Ci: int, Co: int, groups: int = 1) -> bool:
-    """Whether fused_fwd would take the longitude-spectral path for these
-    arguments under DISCO_FUSED_PATH=spectral."""
-    old = os.environ.get("DISCO_FUSED_PATH")
-    os.environ["DISCO_FUSED_PATH"] = "spectral"
-    try:
-        return fused_is_spectral(psi, x_dtype, Ci, Co, groups)
-    finally:
-        if old is None:
-            del os.environ["DISCO_FUSED_PATH"]
-        else:
-            os.environ["DISCO_FUSED_PATH"] = old
-
-
 def fused_fwd(psi: Psi, x, w, groups: int = 1, bias=None, y=None, out_dtype=None, stream=None):
     """The forward DISCO convolution without storing the K-expanded tensor."""
     torch = _torch()

@@ -577,9 +577,9 @@ int fused_spectral_eligible(const disco_psi* psi, int x_dtype, int Ci, int Co, i
         (Co != 128 && Co != 64) || h.K > 8)
         return 0;
     if (d.max_windows > kSpecMaxWin) return 0;
-    // opt-in: the direct matrix-core kernel is the faster one at the sizes measured
+    // DISCO_FUSED_PATH=toeplitz selects the direct matrix-core kernel instead
     const char* e = std::getenv("DISCO_FUSED_PATH");
-    return e != nullptr && std::strcmp(e, "spectral") == 0;
+    return e == nullptr || std::strcmp(e, "toeplitz") != 0;
 }
 
 int try_launch_fused_spectral(const disco_psi* psi, const void* x, const void* w,

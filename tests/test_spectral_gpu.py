@@ -79,10 +79,10 @@ def _desc(wl):
 def test_path_selection(sdc, monkeypatch):
     wl = SPECTRAL[0]
     psi = _psi(sdc, wl)
-    monkeypatch.delenv("DISCO_FUSED_PATH", raising=False)
-    assert not sdc.fused_is_spectral(psi, torch.bfloat16, 128, 128, 1)   # opt-in
-    monkeypatch.setenv("DISCO_FUSED_PATH", "spectral")
-    assert sdc.fused_is_spectral(psi, torch.bfloat16, 128, 128, 1)
+    monkeypatch.setenv("DISCO_FUSED_PATH", "toeplitz")
+    assert not sdc.fused_is_spectral(psi, torch.bfloat16, 128, 128, 1)   # direct kernel asked for
+    monkeypatch.delenv("DISCO_FUSED_PATH")
+    assert sdc.fused_is_spectral(psi, torch.bfloat16, 128, 128, 1)       # the default
     assert sdc.fused_is_spectral(psi, torch.bfloat16, 64, 64, 1)
     assert not sdc.fused_is_spectral(psi, torch.float32, 128, 128, 1)    # bf16 only
     assert not sdc.fused_is_spectral(psi, torch.bfloat16, 128, 96, 1)    # Co tile
@@ -100,9 +100,9 @@ def test_path_selection(sdc, monkeypatch):
 @pytest.mark.parametrize("wl", SPECTRAL, ids=[w.name for w in SPECTRAL])
 def test_fused_paths_small(sdc, wl, path, monkeypatch):
     if path == "toeplitz":
-        monkeypatch.delenv("DISCO_FUSED_PATH", raising=False)
+        monkeypatch.setenv("DISCO_FUSED_PATH", "toeplitz")
     else:
-        monkeypatch.setenv("DISCO_FUSED_PATH", "spectral")
+        monkeypatch.delenv("DISCO_FUSED_PATH", raising=False)
     _say("fused", path, wl.name)
     x, w = _prepare(wl)
     psi = _psi(sdc, wl)
@@ -125,7 +125,7 @@ def test_spectral_roll_equivariance(sdc, monkeypatch):
     # a longitude shift of x is a phase rotation of its spectrum, which is then
     # rounded to bf16: the rolled output agrees up to that rounding (a wrong
     # shift or index would be off by O(1))
-    monkeypatch.setenv("DISCO_FUSED_PATH", "spectral")
+    monkeypatch.delenv("DISCO_FUSED_PATH", raising=False)
     wl = SPECTRAL[1]
     x, w = _prepare(wl)
     psi = _psi(sdc, wl)
@@ -138,7 +138,7 @@ def test_spectral_roll_equivariance(sdc, monkeypatch):
 
 
 def test_spectral_determinism(sdc, monkeypatch):
-    monkeypatch.setenv("DISCO_FUSED_PATH", "spectral")
+    monkeypatch.delenv("DISCO_FUSED_PATH", raising=False)
     wl = SPECTRAL[1]
     x, w = _prepare(wl)
     psi = _psi(sdc, wl)
@@ -162,11 +162,11 @@ def _sample_cols(nlon, seed=0):
 @pytest.mark.parametrize("path", ["spectral", "toeplitz"])
 def test_full_size_c4_paths(sdc, path, monkeypatch):
     """721x1440, 128 -> 128 channels, K = 7, bf16: both fused algorithms (the
-    benchmark times the direct one, the default)."""
+    benchmark times the spectral one, the default)."""
     if path == "toeplitz":
-        monkeypatch.delenv("DISCO_FUSED_PATH", raising=False)
+        monkeypatch.setenv("DISCO_FUSED_PATH", "toeplitz")
     else:
-        monkeypatch.setenv("DISCO_FUSED_PATH", "spectral")
+        monkeypatch.delenv("DISCO_FUSED_PATH", raising=False)
     wl = WORKLOADS["c4"]
     _say("full size c4", path)
     x, w = _prepare(wl)

@@ -208,7 +208,7 @@ int disco_psi_to_device(disco_psi* psi) {
     std::vector<int32_t> info;
     rc = build_mfma_tables(psi, taps, info);
     if (rc != DISCO_OK) return rc;
-    std::vector<float> spec_psih;
+    std::vector<uint32_t> spec_psih;
     rc = build_spectral_tables(h, spec_psih, d.spec_radix, &d.spec_nrad, &d.spec_mp);
     if (rc != DISCO_OK) return rc;
 
@@ -234,9 +234,9 @@ int disco_psi_to_device(disco_psi* psi) {
         d.mfma_ok = 1;
     }
     if (d.spec_mp > 0) {
-        if ((rc = dev_alloc(d, &p, spec_psih.size() * sizeof(float))) != DISCO_OK) goto fail;
+        if ((rc = dev_alloc(d, &p, spec_psih.size() * sizeof(uint32_t))) != DISCO_OK) goto fail;
         d.spec_psih = p;
-        if ((rc = dev_copy(p, spec_psih.data(), spec_psih.size() * sizeof(float))) != DISCO_OK)
+        if ((rc = dev_copy(p, spec_psih.data(), spec_psih.size() * sizeof(uint32_t))) != DISCO_OK)
             goto fail;
     }
     d.device = dev;

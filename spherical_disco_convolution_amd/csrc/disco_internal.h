@@ -49,13 +49,14 @@ int build_host_psi(const disco_psi_desc& desc, HostPsi& out);
 
 // Longitude-spectral tables (spectral_host.cpp), built for stride-1 layers
 // whose longitude count N is even, at most kSpecMaxN, with N/2 a product of
-// 2, 3 and 5, and K <= 8.  psih: float32 pairs [nwin][K][MP], Psi_hat of each
-// window; radix: the plan of the N/2-point transform.  *mp = 0 when the layer
+// 2, 3 and 5, and K <= 8.  psih: [nwin][K][MP] bf16 (re, im) pairs in 32-bit
+// words (real part low), Psi_hat of each window; radix: the plan of the
+// N/2-point transform.  *mp = 0 when the layer
 // does not qualify.
 constexpr int kSpecMaxN = 1800;   // N/2 <= 900 bounds the transform butterflies per lane
 constexpr int kSpecMaxRadix = 12;
 int spectral_plan(int n, int32_t* radix, int32_t* nrad);
-int build_spectral_tables(const HostPsi& h, std::vector<float>& psih, int32_t* radix,
+int build_spectral_tables(const HostPsi& h, std::vector<uint32_t>& psih, int32_t* radix,
                           int32_t* nrad, int32_t* mp);
 
 // ---------------------------------------------------------------------------
@@ -84,7 +85,7 @@ struct DevPsi {
     std::vector<int32_t> mfma_info_host;  // host copy (offsets, tile options)
     int32_t mfma_ok = 0;
     // longitude-spectral tables for the spectral fused path (stride 1)
-    void* spec_psih = nullptr;    // float2 [nwin][K][spec_mp]
+    void* spec_psih = nullptr;    // bf16 (re, im) words [nwin][K][spec_mp]
     int32_t spec_mp = 0;          // padded frequency count; 0 = no tables
     int32_t spec_radix[kSpecMaxRadix] = {0};
     int32_t spec_nrad = 0;

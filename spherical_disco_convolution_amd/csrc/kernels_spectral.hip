@@ -10,7 +10,7 @@
 // Psi_hat comes from spectral_host.cpp.  Three kernels:
 //   spec_rfft   x rows -> x_hat, stored as bf16 (re, im) pairs;
 //   spec_mfma   per (batch, output row, 32 frequencies): the window sum on
-//               the vector ALUs into a bf16 [frequency, re/im][(ci, k)] LDS
+//               the matrix cores into a bf16 [frequency, re/im][(ci, k)] LDS
 //               tile per 32-channel chunk, then the channel/basis GEMM on
 //               v_mfma_f32_32x32x16_bf16 into y_hat (bf16 pairs);
 //   spec_irfft  y_hat rows -> y rows (+ bias).
@@ -310,6 +310,7 @@ constexpr int kMt = 32;              // frequencies per work item (64 GEMM colum
 constexpr int kBts = 264;            // B tile row: 256 (k, ci) pairs + 8 pad (bf16)
 constexpr int kSpecThreads = 256;
 constexpr int kSpecMaxWin = 8;       // windows per output row (one 16-deep MFMA step)
+constexpr int kXcds = 8;             // accelerator dies of the chip (L2 domains)
 
 // Both sums of the forward equation for work items (batch b, output row j,
 // 32 frequencies m0 ..), on the matrix cores, per 32-channel chunk.
@@ -327,8 +328,13 @@ constexpr int kSpecMaxWin = 8;       // windows per output row (one 16-deep MFMA
 //  * Channel/basis GEMM: y_hat[co, (m, re/im)] += wp[co, (k, ci)] bt[(k, ci),
 //    (m, re/im)], 4 waves, wave tile 32 x 64 (CO = 128) or 32 x 32 (CO = 64),
 //    16 k-steps per chunk, weights in fragment order.
-// Persistent: workgroup g takes items g, g + G, ... (G = gridDim.x), items
-// ordered (b, j, tile).  Its (item, chunk) pairs form one stream, pipelined
+// Persistent, in NX bands of the flattened output rows (b, j): workgroup g
+// serves band g % NX (workgroups are dispatched to the XCDs round-robin, so a
+// band stays on one XCD when NX is their count) and takes that band's items
+// slot, slot + GX, ... (slot = g / NX, GX = gridDim.x / NX), where the band's
+// items run tile-major: every row of the band for frequency tile 0, then tile
+// 1, ...  The items in flight on an XCD then share their input rows' spectra
+// in its L2.  A workgroup's (item, chunk) pairs form one stream, pipelined
 // across item boundaries: the spectra of stream position p + 1 are in LDS and
 // those of p + 2 in flight while p is computed (their window rows fetched
 // one position earlier), each weight fragment is reloaded for the next chunk
@@ -337,21 +343,25 @@ constexpr int kSpecMaxWin = 8;       // windows per output row (one 16-deep MFMA
 template <int CO, int KT>
 __global__ __launch_bounds__(kSpecThreads) __attribute__((amdgpu_waves_per_eu(2))) void spec_mfma(
     const uint32_t* __restrict__ xh, const bf16_t* __restrict__ wp,
-    const float2* __restrict__ psih, const int32_t* __restrict__ win_ptr,
+    const uint32_t* __restrict__ psih, const int32_t* __restrict__ win_ptr,
     const DevWindow* __restrict__ wins, bf16_t* __restrict__ yh, int B, int Ci, int nlat_in,
-    int nlat_out, int MP) {
+    int nlat_out, int MP, int NX) {
     __shared__ __attribute__((aligned(16))) bf16_t bt[64 * kBts];
     __shared__ __attribute__((aligned(16))) u32x4 xs[kSpecMaxWin * 32 * 8];   // [r][ci][piece]
-    __shared__ float2 ps[kSpecMaxWin * KT * kMt];
+    __shared__ uint32_t ps[kSpecMaxWin * KT * kMt];
     constexpr int WGM = CO / 32;          // waves along the output channels
     constexpr int WGN = 4 / WGM;          // waves along the columns
     constexpr int NTW = 2 / WGN;          // 32-column MFMA tiles per wave
     constexpr int PSN = (kSpecMaxWin * KT * kMt + kSpecThreads - 1) / kSpecThreads;
 
     const int ntiles = MP / kMt;
-    const int nitems = B * nlat_out * ntiles;
-    const int G = gridDim.x;
-    const int nmine = (nitems - (int)blockIdx.x + G - 1) / G;   // >= 1 (grid <= items)
+    const int GX = (int)gridDim.x / NX;   // workgroups per band (the grid is NX * GX)
+    const int band = (int)blockIdx.x % NX, slot = (int)blockIdx.x / NX;
+    const int nrows_all = B * nlat_out;
+    const int r0 = (int)((int64_t)band * nrows_all / NX);
+    const int brows = (int)((int64_t)(band + 1) * nrows_all / NX) - r0;
+    // >= 1: slot < GX, and the host keeps GX <= (rows of the smallest band) * ntiles
+    const int nmine = (brows * ntiles - slot + GX - 1) / GX;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = uniform(tid >> 6);
@@ -363,8 +373,13 @@ __global__ __launch_bounds__(kSpecThreads) __attribute__((amdgpu_waves_per_eu(2)
     const size_t cstride = (size_t)32 * nlat_in * MP;   // one 32-channel chunk
     const size_t plane = (size_t)nlat_in * MP;
 
-    // item n of this workgroup (clamped to its last): global index, (b, j, m0)
-    auto item_of = [&](int n) { return (int)blockIdx.x + (n < nmine ? n : nmine - 1) * G; };
+    // item n of this workgroup (clamped to its last): index (b * nlat_out + j)
+    // * ntiles + tile
+    auto item_of = [&](int n) {
+        const int l = slot + (n < nmine ? n : nmine - 1) * GX;
+        const int mt = l / brows;
+        return (r0 + (l - mt * brows)) * ntiles + mt;
+    };
 
     // ---- spectra stream: position p = (item p / nchunks, chunk p % nchunks).
     // Thread (piece p = tid % 8, channel tid / 8) loads the 16-byte piece (4
@@ -405,7 +420,7 @@ __global__ __launch_bounds__(kSpecThreads) __attribute__((amdgpu_waves_per_eu(2)
 
     // ---- Psi_hat slice of an item: ps[(r KT + k) kMt + ml]; slots past the
     // row's windows are zero
-    float2 pn[PSN];
+    uint32_t pn[PSN];
     auto load_ps = [&](int n) {
         const int it = item_of(n);
         const int mt = it % ntiles, j = (it / ntiles) % nlat_out;
@@ -414,7 +429,7 @@ __global__ __launch_bounds__(kSpecThreads) __attribute__((amdgpu_waves_per_eu(2)
         for (int q = 0; q < PSN; ++q) {
             const int idx = tid + q * kSpecThreads;
             const int rk = idx / kMt, ml = idx - rk * kMt;
-            pn[q] = make_float2(0.0f, 0.0f);
+            pn[q] = 0u;
             if (rk < nw * KT) pn[q] = psih[(size_t)(w0 * KT + rk) * MP + mt * kMt + ml];
         }
     };
@@ -469,10 +484,10 @@ __global__ __launch_bounds__(kSpecThreads) __attribute__((amdgpu_waves_per_eu(2)
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
                     const int r = 4 * lg + u;
-                    float2 P = make_float2(0.0f, 0.0f);
+                    uint32_t P = 0u;   // bf16 (Pr, Pi), real part low
                     if (nn < 2 * KT && r < nw) P = ps[(r * KT + k) * kMt + f0 + f];
                     // real column: (Pr, Pi); imaginary column: (-Pi, Pr)
-                    bq[f][u] = c ? pack_bf16x2(-P.y, P.x) : pack_bf16x2(P.x, P.y);
+                    bq[f][u] = c ? (__builtin_rotateleft32(P, 16) ^ 0x8000u) : P;
                 }
             }
         }
@@ -610,7 +625,7 @@ int try_launch_fused_spectral(const disco_psi* psi, const void* x, const void* w
     uint32_t* xh = static_cast<uint32_t*>(ws);
     bf16_t* yh = reinterpret_cast<bf16_t*>(static_cast<char*>(ws) + xh_bytes);
     bf16_t* wpd = reinterpret_cast<bf16_t*>(static_cast<char*>(ws) + xh_bytes + yh_bytes);
-    const float2* psih = static_cast<const float2*>(d.spec_psih);
+    const uint32_t* psih = static_cast<const uint32_t*>(d.spec_psih);
 
     const size_t nwp = (size_t)Co * Ci * 8;
     hipLaunchKernelGGL(spec_prep_w, dim3((unsigned)((nwp + 255) / 256)), dim3(256), 0, st,
@@ -625,11 +640,16 @@ int try_launch_fused_spectral(const disco_psi* psi, const void* x, const void* w
     if (hipGetDevice(&dev) == hipSuccess)
         (void)hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
     (void)hipGetLastError();
-    const int64_t nitems = (int64_t)B * D.nlat_out * (MP / kMt);
-    dim3 grid((unsigned)std::min<int64_t>(nitems, 2 * (int64_t)ncu));
+    // bands of output rows, one per XCD; GX workgroups per band, at most the
+    // smallest band's item count
+    const int64_t nrows_all = (int64_t)B * D.nlat_out;
+    const int NX = (int)std::min<int64_t>(kXcds, nrows_all);
+    const int64_t min_items = nrows_all / NX * (MP / kMt);
+    const int GX = (int)std::max<int64_t>(1, std::min<int64_t>(min_items, 2 * (int64_t)ncu / NX));
+    dim3 grid((unsigned)(NX * GX));
 #define DISCO_SM(CC, KK)                                                                     \
     hipLaunchKernelGGL((spec_mfma<CC, KK>), grid, dim3(kSpecThreads), 0, st, xh, wpd,         \
-                       psih, d.win_ptr, d.windows, yh, B, Ci, D.nlat_in, D.nlat_out, MP)
+                       psih, d.win_ptr, d.windows, yh, B, Ci, D.nlat_in, D.nlat_out, MP, NX)
 #define DISCO_SM_K(CC)                                                                       \
     switch (K) {                                                                             \
         case 1: DISCO_SM(CC, 1); break;                                                      \

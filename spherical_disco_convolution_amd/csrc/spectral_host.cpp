@@ -10,19 +10,42 @@
 // with Psi_hat[k, m] = sum_t v[k, t] * exp(-2 pi i m (p_lo + t) / N).  x is
 // real, so frequencies m = 0 .. N/2 carry everything.
 //
-// This file tabulates, in float64 and stored as float32 pairs:
+// This file tabulates, in float64:
 //   * Psi_hat per window for m < N/2 + 1, zero up to the padded count MP
-//     (a multiple of 32);
+//     (a multiple of 32), stored as bf16 (re, im) pairs in one 32-bit word
+//     (real part in the low half): the matrix-core operand type it feeds;
 //   * the radix plan (4, 2, 3, 5) of the N/2-point complex transform the
 //     real transforms are built on.
 #include <algorithm>
 #include <cmath>
+#include <cstring>
 #include <thread>
 #include <vector>
 
 #include "disco_internal.h"
 
 namespace disco {
+
+namespace {
+
+// double -> bf16, round to nearest even.  The intermediate float is rounded to
+// odd (inexact results get their lowest bit set), so the second rounding sees
+// the sticky information of the first and the result is the correctly rounded
+// bf16 of the double.
+uint32_t bf16_of(double v) {
+    float f = (float)v;
+    uint32_t u;
+    std::memcpy(&u, &f, 4);
+    if ((double)f != v && std::isfinite(f)) {
+        // back to round-toward-zero, then set the sticky bit
+        if (std::fabs((double)f) > std::fabs(v)) u -= 1;
+        u |= 1u;
+    }
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+}  // namespace
 
 int spectral_plan(int n, int32_t* radix, int32_t* nrad) {
     int cnt = 0;
@@ -36,7 +59,7 @@ int spectral_plan(int n, int32_t* radix, int32_t* nrad) {
     return n == 1;
 }
 
-int build_spectral_tables(const HostPsi& h, std::vector<float>& psih, int32_t* radix,
+int build_spectral_tables(const HostPsi& h, std::vector<uint32_t>& psih, int32_t* radix,
                           int32_t* nrad, int32_t* mp) {
     *mp = 0;
     *nrad = 0;
@@ -55,7 +78,7 @@ int build_spectral_tables(const HostPsi& h, std::vector<float>& psih, int32_t* r
         s[n] = std::sin(a);
     }
     try {
-        psih.assign(nwin * (size_t)K * MP * 2, 0.0f);
+        psih.assign(nwin * (size_t)K * MP, 0u);
     } catch (const std::bad_alloc&) {
         return set_error(DISCO_ENOMEM, "host allocation for the spectral tables failed");
     }
@@ -76,11 +99,8 @@ int build_spectral_tables(const HostPsi& h, std::vector<float>& psih, int32_t* r
                         im[k] -= v[(size_t)t * K + k] * s[e];
                     }
                 }
-                for (int k = 0; k < K; ++k) {
-                    float* o = psih.data() + (((w * K + k) * (size_t)MP) + m) * 2;
-                    o[0] = (float)re[k];
-                    o[1] = (float)im[k];
-                }
+                for (int k = 0; k < K; ++k)
+                    psih[(w * K + k) * (size_t)MP + m] = bf16_of(re[k]) | (bf16_of(im[k]) << 16);
             }
         }
     };

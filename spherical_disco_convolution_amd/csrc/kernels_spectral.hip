@@ -23,6 +23,7 @@
 #include <algorithm>
 #include <cstdlib>
 #include <cstring>
+#include <type_traits>
 
 #include "disco_internal.h"
 #include "kernels_common.h"
@@ -280,6 +281,309 @@ __global__ __launch_bounds__(kFftThreads) void spec_irfft(const uint32_t* __rest
             *reinterpret_cast<float2*>(out + 2 * n) = make_float2(v.x * sc + bv, v.y * sc + bv);
         } else {
             *reinterpret_cast<uint32_t*>(out + 2 * n) = pack_bf16x2(v.x * sc + bv, v.y * sc + bv);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Register-resident transforms for N/2 = H1 * H2 (a four-step split of the
+// complex transform, each step's short DFTs unrolled in registers).
+
+// Compile-time cosine and sine: Taylor series after reduction to [-pi, pi]
+// (through degree 31, far below float rounding there).
+constexpr double kPiD = 3.14159265358979323846;
+constexpr double ct_reduce(double x) {
+    while (x > kPiD) x -= 2.0 * kPiD;
+    while (x < -kPiD) x += 2.0 * kPiD;
+    return x;
+}
+constexpr double ct_sin(double x) {
+    x = ct_reduce(x);
+    double term = x, sum = x;
+    for (int n = 1; n < 16; ++n) {
+        term *= -x * x / ((2.0 * n) * (2.0 * n + 1.0));
+        sum += term;
+    }
+    return sum;
+}
+constexpr double ct_cos(double x) {
+    x = ct_reduce(x);
+    double term = 1.0, sum = 1.0;
+    for (int n = 1; n < 16; ++n) {
+        term *= -x * x / ((2.0 * n - 1.0) * (2.0 * n));
+        sum += term;
+    }
+    return sum;
+}
+
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for<I + 1, N>(f);
+    }
+}
+
+// v * exp(S * 2 pi i * E / N) for a compile-time exponent E
+template <int N, int S, int E>
+__device__ __forceinline__ float2 rot_ct(float2 v) {
+    constexpr int e = ((E % N) + N) % N;
+    if constexpr (e == 0) {
+        return v;
+    } else if constexpr (2 * e == N) {
+        return make_float2(-v.x, -v.y);
+    } else if constexpr (4 * e == N) {
+        return cimul(v, (float)S);
+    } else if constexpr (4 * e == 3 * N) {
+        return cimul(v, (float)-S);
+    } else {
+        constexpr float c = (float)ct_cos(2.0 * kPiD * e / N);
+        constexpr float sn = (float)(S * ct_sin(2.0 * kPiD * e / N));
+        return cmul(v, make_float2(c, sn));
+    }
+}
+
+// In-place DFT of length N in registers, a[u] <- sum_t a[t] exp(S 2 pi i u t / N):
+// mixed-radix decimation in time (radix 4, 2, 3, 5 first), every index and
+// root compile-time.
+template <int N, int S>
+__device__ __forceinline__ void reg_dft(float2 (&a)[N]) {
+    if constexpr (N == 1) {
+    } else if constexpr (N <= 5) {
+        butterfly<N>(a, (float)S);
+    } else {
+        constexpr int R = N % 4 == 0 ? 4 : N % 2 == 0 ? 2 : N % 3 == 0 ? 3 : 5;
+        constexpr int M = N / R;
+        static_assert(R * M == N && N % R == 0, "N must be a product of 2, 3 and 5");
+        float2 y[R][M];
+        static_for<0, R>([&](auto r) {
+            static_for<0, M>([&](auto m) { y[r][m] = a[R * m + r]; });
+            reg_dft<M, S>(y[r]);
+        });
+        // X[k1 + M k2] = sum_r exp(S 2 pi i r k1 / N) exp(S 2 pi i r k2 / R) Y_r[k1]
+        static_for<0, M>([&](auto k1) {
+            float2 t[R];
+            static_for<0, R>([&](auto r) {
+                t[r] = rot_ct<N, S, decltype(r)::value * decltype(k1)::value>(y[r][k1]);
+            });
+            butterfly<R>(t, (float)S);
+            static_for<0, R>([&](auto k2) { a[k1 + M * k2] = t[k2]; });
+        });
+    }
+}
+
+__device__ __forceinline__ float2 unpack_bf16x2(uint32_t v) {
+    return make_float2(__uint_as_float(v << 16), __uint_as_float(v & 0xffff0000u));
+}
+
+constexpr int kRegThreads = 64;   // one wave per workgroup
+
+constexpr int spec_mp_of(int H) { return (H + 32) / 32 * 32; }   // (H + 1) rounded up to 32
+
+// x rows (N = 2 H real bf16 samples, H = H1 H2) -> x_hat rows (MP bf16 pairs),
+// RW rows per wave and step.  The H-point transform of z[n] = x[2n] + i x[2n+1]
+// is split with n = H2 a + b and k = c + H1 d:
+//   step A, tasks (row, b): A[b, c] = w_H^{b c} sum_a z[H2 a + b] w_H1^{a c};
+//   step B, tasks (row, c): Z[c + H1 d] = sum_b A[b, c] w_H2^{b d};
+// w_L = exp(-2 pi i / L).  Step A reads its samples from memory (lanes b
+// consecutive), A passes through LDS with a row stride P2 (odd, so step B's
+// strided reads spread over the banks), Z returns to LDS in natural order for
+// the even/odd split, which writes four frequencies per 16-byte store.
+// Workgroup g transforms rows g RW .. g RW + RW - 1.  (A persistent form that
+// loads the next group during the current one needs more than 256 registers
+// and is slower.)
+template <int H1, int H2, int RW>
+__global__ __launch_bounds__(kRegThreads) void spec_rfft_reg(const uint32_t* __restrict__ x,
+                                                             uint32_t* __restrict__ xh,
+                                                             int64_t nrows) {
+    constexpr int H = H1 * H2, MP = spec_mp_of(H);
+    constexpr int P2 = H2 | 1, LP = H1 * P2;
+    constexpr int TA = RW * H2, ITA = (TA + 63) / 64;
+    constexpr int TB = RW * H1, ITB = (TB + 63) / 64;
+    constexpr int NQ = MP / 4, TQ = RW * NQ;
+    static_assert(LP >= H, "the split needs H entries per row");
+    __shared__ float2 buf[RW * LP];
+    const int lane = threadIdx.x;
+    const int64_t g = blockIdx.x;   // the grid is the row-group count
+
+    uint32_t raw[ITA][H1];
+#pragma unroll
+    for (int i = 0; i < ITA; ++i) {
+        const int t = min(lane + 64 * i, TA - 1);
+        const int r = t / H2, b = t - r * H2;
+        const int64_t row = min(g * RW + r, nrows - 1);
+        const uint32_t* src = x + row * H + b;
+#pragma unroll
+        for (int a = 0; a < H1; ++a) raw[i][a] = src[H2 * a];
+    }
+    {
+        // ---- step A ----
+#pragma unroll
+        for (int i = 0; i < ITA; ++i) {
+            const int t = lane + 64 * i;
+            const int tc = min(t, TA - 1);
+            const int r = tc / H2, b = tc - r * H2;
+            float2 v[H1];
+#pragma unroll
+            for (int a = 0; a < H1; ++a) v[a] = unpack_bf16x2(raw[i][a]);
+            reg_dft<H1, -1>(v);
+            const float2 w = root(b, 1.0f / (float)H, -1.0f);
+            float2 p = w;
+#pragma unroll
+            for (int c = 1; c < H1; ++c) {
+                v[c] = cmul(v[c], p);
+                p = cmul(p, w);
+            }
+            if (t < TA) {
+#pragma unroll
+                for (int c = 0; c < H1; ++c) buf[r * LP + c * P2 + b] = v[c];
+            }
+        }
+        wave_lds_sync();
+        // ---- step B ----
+        float2 v[ITB][H2];
+#pragma unroll
+        for (int i = 0; i < ITB; ++i) {
+            const int t = min(lane + 64 * i, TB - 1);
+            const int r = t / H1, c = t - r * H1;
+#pragma unroll
+            for (int b = 0; b < H2; ++b) v[i][b] = buf[r * LP + c * P2 + b];
+        }
+        wave_lds_sync();
+#pragma unroll
+        for (int i = 0; i < ITB; ++i) {
+            const int t = lane + 64 * i;
+            const int r = min(t, TB - 1) / H1, c = min(t, TB - 1) - r * H1;
+            reg_dft<H2, -1>(v[i]);
+            if (t < TB) {
+#pragma unroll
+                for (int d = 0; d < H2; ++d) buf[r * LP + c + H1 * d] = v[i][d];
+            }
+        }
+        wave_lds_sync();
+        // ---- even/odd split: X[m] = (a + b)/2 - i W^m (a - b)/2 with
+        // a = Z[m mod H], b = conj(Z[(H - m) mod H]), W = exp(-2 pi i / N);
+        // frequencies past H are zero ----
+        for (int t = lane; t < TQ; t += 64) {
+            const int r = t / NQ, q = t - r * NQ;
+            const int64_t row = g * RW + r;
+            const int m0 = 4 * q;
+            const float2 w0 = root(m0, 0.5f / (float)H, -1.0f);
+            const float2* z = buf + r * LP;
+            u32x4 o;
+            static_for<0, 4>([&](auto u) {
+                const int m = m0 + u;
+                float2 X = make_float2(0.0f, 0.0f);
+                if (m <= H) {
+                    const float2 a = z[m == H ? 0 : m];
+                    const float2 bb = cconj(z[m == 0 ? 0 : H - m]);
+                    const float2 e = cmul(rot_ct<2 * H, -1, decltype(u)::value>(w0), csub(a, bb));
+                    X = cadd(cscale(cadd(a, bb), 0.5f), cscale(make_float2(e.y, -e.x), 0.5f));
+                }
+                o[decltype(u)::value] = pack_bf16x2(X.x, X.y);
+            });
+            if (row < nrows) *reinterpret_cast<u32x4*>(xh + row * MP + m0) = o;
+        }
+    }
+}
+
+// y_hat rows (MP bf16 pairs) -> y rows (N = 2 H) + bias, RW rows per wave and
+// step.  Z[k] = (a + b)/2 + i W^-k (a - b)/2 with a = X[k], b = conj(X[H - k])
+// (the imaginary parts of X[0] and X[H] dropped: a real row's spectrum has
+// none), W = exp(-2 pi i / N); z[n] = sum_k Z[k] w_H^{-n k} by the same split
+// (k = H2 a + b, n = c + H1 d); y[2n] = Re z[n] / H, y[2n+1] = Im z[n] / H.
+// Step A forms Z from its loads of y_hat, step B stores y (lanes c
+// consecutive).  Workgroup g transforms rows g RW .. g RW + RW - 1.
+template <int H1, int H2, int RW, typename TY>
+__global__ __launch_bounds__(kRegThreads) void spec_irfft_reg(const uint32_t* __restrict__ yh,
+                                                              TY* __restrict__ y,
+                                                              const float* __restrict__ bias,
+                                                              int Co, int nlat_out,
+                                                              int64_t nrows) {
+    constexpr int H = H1 * H2, N = 2 * H, MP = spec_mp_of(H);
+    constexpr int P2 = H2 | 1, LP = H1 * P2;
+    constexpr int TA = RW * H2, ITA = (TA + 63) / 64;
+    constexpr int TB = RW * H1, ITB = (TB + 63) / 64;
+    __shared__ float2 buf[RW * LP];
+    const int lane = threadIdx.x;
+    const int64_t g = blockIdx.x;   // the grid is the row-group count
+    constexpr float sc = 1.0f / (float)H;
+
+    uint32_t ra[ITA][H1], rb[ITA][H1];   // X[k], X[H - k] for k = H2 a + b
+#pragma unroll
+    for (int i = 0; i < ITA; ++i) {
+        const int t = min(lane + 64 * i, TA - 1);
+        const int r = t / H2, b = t - r * H2;
+        const int64_t row = min(g * RW + r, nrows - 1);
+        const uint32_t* src = yh + row * MP;
+#pragma unroll
+        for (int a = 0; a < H1; ++a) {
+            ra[i][a] = src[H2 * a + b];
+            rb[i][a] = src[H - H2 * a - b];
+        }
+    }
+    {
+        // ---- step A ----
+#pragma unroll
+        for (int i = 0; i < ITA; ++i) {
+            const int t = lane + 64 * i;
+            const int tc = min(t, TA - 1);
+            const int r = tc / H2, b = tc - r * H2;
+            const float2 wb = root(b, 1.0f / (float)N, 1.0f);   // W^-b
+            float2 v[H1];
+            static_for<0, H1>([&](auto a) {
+                float2 A = unpack_bf16x2(ra[i][a]);
+                float2 Bc = cconj(unpack_bf16x2(rb[i][a]));
+                if (decltype(a)::value == 0 && b == 0) {
+                    A.y = 0.0f;
+                    Bc.y = 0.0f;
+                }
+                const float2 e = cmul(rot_ct<N, 1, H2 * decltype(a)::value>(wb), csub(A, Bc));
+                v[a] = cadd(cscale(cadd(A, Bc), 0.5f), cscale(make_float2(-e.y, e.x), 0.5f));
+            });
+            reg_dft<H1, 1>(v);
+            const float2 w = root(b, 1.0f / (float)H, 1.0f);
+            float2 p = w;
+#pragma unroll
+            for (int c = 1; c < H1; ++c) {
+                v[c] = cmul(v[c], p);
+                p = cmul(p, w);
+            }
+            if (t < TA) {
+#pragma unroll
+                for (int c = 0; c < H1; ++c) buf[r * LP + c * P2 + b] = v[c];
+            }
+        }
+        wave_lds_sync();
+        // ---- step B ----
+        float2 v[ITB][H2];
+#pragma unroll
+        for (int i = 0; i < ITB; ++i) {
+            const int t = min(lane + 64 * i, TB - 1);
+            const int r = t / H1, c = t - r * H1;
+#pragma unroll
+            for (int b = 0; b < H2; ++b) v[i][b] = buf[r * LP + c * P2 + b];
+        }
+        wave_lds_sync();
+#pragma unroll
+        for (int i = 0; i < ITB; ++i) {
+            const int t = lane + 64 * i;
+            const int r = min(t, TB - 1) / H1, c = min(t, TB - 1) - r * H1;
+            const int64_t row = g * RW + r;
+            reg_dft<H2, 1>(v[i]);
+            if (t < TB && row < nrows) {
+                const float bv = bias ? bias[(row / nlat_out) % Co] : 0.0f;
+                TY* out = y + row * N;
+#pragma unroll
+                for (int d = 0; d < H2; ++d) {
+                    const int n = c + H1 * d;
+                    const float2 o = make_float2(v[i][d].x * sc + bv, v[i][d].y * sc + bv);
+                    if constexpr (sizeof(TY) == 4)
+                        *reinterpret_cast<float2*>(out + 2 * n) = o;
+                    else
+                        *reinterpret_cast<uint32_t*>(out + 2 * n) = pack_bf16x2(o.x, o.y);
+                }
+            }
         }
     }
 }
@@ -627,19 +931,38 @@ int try_launch_fused_spectral(const disco_psi* psi, const void* x, const void* w
     bf16_t* wpd = reinterpret_cast<bf16_t*>(static_cast<char*>(ws) + xh_bytes + yh_bytes);
     const uint32_t* psih = static_cast<const uint32_t*>(d.spec_psih);
 
+    int dev = 0, ncu = 256;
+    if (hipGetDevice(&dev) == hipSuccess)
+        (void)hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+    (void)hipGetLastError();
+    // the register-resident transforms cover these half lengths (their MP is
+    // the table's)
+    const bool reg = (H == 720 || H == 360 || H == 180) && MP == spec_mp_of(H);
+    // one-wave workgroups, one group of rw rows each
+    auto reg_grid = [](int64_t rows, int rw) { return dim3((unsigned)((rows + rw - 1) / rw)); };
+
     const size_t nwp = (size_t)Co * Ci * 8;
     hipLaunchKernelGGL(spec_prep_w, dim3((unsigned)((nwp + 255) / 256)), dim3(256), 0, st,
                        static_cast<const bf16_t*>(w), wpd, Co, Ci, K);
     const size_t fft_lds = (size_t)(kFftRows + 1) * H * sizeof(float2);
     const int64_t xrows = (int64_t)B * Ci * D.nlat_in;
-    hipLaunchKernelGGL(spec_rfft, dim3((unsigned)((xrows + kFftRows - 1) / kFftRows)),
-                       dim3(kFftThreads), fft_lds, st, static_cast<const bf16_t*>(x), xh, N, MP,
-                       xrows, pl);
-    // persistent: two workgroups per CU (their registers and LDS allow two)
-    int dev = 0, ncu = 256;
-    if (hipGetDevice(&dev) == hipSuccess)
-        (void)hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
-    (void)hipGetLastError();
+    const uint32_t* x32 = static_cast<const uint32_t*>(x);
+#define DISCO_RF(H1, H2, RW)                                                                   \
+    hipLaunchKernelGGL((spec_rfft_reg<H1, H2, RW>),                                            \
+                       reg_grid(xrows, RW),                                                    \
+                       dim3(kRegThreads), 0, st, x32, xh, xrows)
+    if (reg && H == 720) {
+        DISCO_RF(16, 45, 4);
+    } else if (reg && H == 360) {
+        DISCO_RF(8, 45, 8);
+    } else if (reg && H == 180) {
+        DISCO_RF(4, 45, 16);
+    } else {
+        hipLaunchKernelGGL(spec_rfft, dim3((unsigned)((xrows + kFftRows - 1) / kFftRows)),
+                           dim3(kFftThreads), fft_lds, st, static_cast<const bf16_t*>(x), xh, N,
+                           MP, xrows, pl);
+    }
+#undef DISCO_RF
     // bands of output rows, one per XCD; GX workgroups per band, at most the
     // smallest band's item count
     const int64_t nrows_all = (int64_t)B * D.nlat_out;
@@ -670,7 +993,25 @@ int try_launch_fused_spectral(const disco_psi* psi, const void* x, const void* w
 #undef DISCO_SM
     const int64_t yrows = (int64_t)B * Co * D.nlat_out;
     const dim3 igrid((unsigned)((yrows + kFftRows - 1) / kFftRows));
-    if (y_dtype == DISCO_F32)
+    const uint32_t* yh32 = reinterpret_cast<const uint32_t*>(yh);
+#define DISCO_IR(H1, H2, RW, TY)                                                               \
+    hipLaunchKernelGGL((spec_irfft_reg<H1, H2, RW, TY>),                                       \
+                       reg_grid(yrows, RW),                                                    \
+                       dim3(kRegThreads), 0, st, yh32, static_cast<TY*>(y), bias, Co,          \
+                       D.nlat_out, yrows)
+#define DISCO_IR_T(H1, H2, RW)                 \
+    if (y_dtype == DISCO_F32) {                \
+        DISCO_IR(H1, H2, RW, float);           \
+    } else {                                   \
+        DISCO_IR(H1, H2, RW, bf16_t);          \
+    }
+    if (reg && H == 720) {
+        DISCO_IR_T(16, 45, 4)
+    } else if (reg && H == 360) {
+        DISCO_IR_T(8, 45, 8)
+    } else if (reg && H == 180) {
+        DISCO_IR_T(4, 45, 16)
+    } else if (y_dtype == DISCO_F32)
         hipLaunchKernelGGL(spec_irfft<float>, igrid, dim3(kFftThreads), fft_lds, st,
                            reinterpret_cast<const uint32_t*>(yh), static_cast<float*>(y), bias, N,
                            MP, Co, D.nlat_out, yrows, pl);
@@ -678,6 +1019,8 @@ int try_launch_fused_spectral(const disco_psi* psi, const void* x, const void* w
         hipLaunchKernelGGL(spec_irfft<bf16_t>, igrid, dim3(kFftThreads), fft_lds, st,
                            reinterpret_cast<const uint32_t*>(yh), static_cast<bf16_t*>(y), bias, N,
                            MP, Co, D.nlat_out, yrows, pl);
+#undef DISCO_IR_T
+#undef DISCO_IR
     hipError_t le = hipGetLastError();
     hipError_t fe = hipFreeAsync(ws, st);
     if (le != hipSuccess) {

@@ -180,3 +180,34 @@ def test_full_size_c4_paths(sdc, path, monkeypatch):
     err = rel_l2(got, ref)
     _say(f"  c4 {path} rel-L2 {err:.3e}")
     assert err <= TOL_BF16
+
+
+# half lengths with register-resident transforms: 720 = 16 x 45 (0.25 degree
+# grids), 360 = 8 x 45, 180 = 4 x 45; outputs compared at sampled longitudes
+REG = [
+    W("n1440", 1, 32, 64, 13, 1440, (3, 3), 0.5),
+    W("n720_b2", 2, 32, 128, 11, 720, (3,), 0.6),
+    W("n360", 1, 64, 64, 19, 360, (2, 2), 0.4),
+]
+
+
+@pytest.mark.parametrize("wl", REG, ids=[w.name for w in REG])
+def test_register_transforms(sdc, wl, monkeypatch):
+    monkeypatch.delenv("DISCO_FUSED_PATH", raising=False)
+    _say("register transforms", wl.name)
+    x, w = _prepare(wl)
+    psi = _psi(sdc, wl)
+    assert sdc.fused_is_spectral(psi, torch.bfloat16, wl.Ci, wl.Co, 1)
+    cols = _sample_cols(wl.nlon_out, seed=3)
+    bias = np.linspace(-1, 1, wl.Co).astype(np.float32)
+    ref = oracle.forward(_desc(wl), x, w, 1, cols_out=cols)
+    refb = oracle.forward(_desc(wl), x, w, 1, cols_out=cols, bias=bias)
+    xd, wd = _dev(x), _dev(w)
+    y = sdc.fused_fwd(psi, xd, wd)[..., cols].cpu().numpy()
+    err = rel_l2(y, ref)
+    _say(f"  rel-L2 {err:.3e}")
+    assert err <= TOL_BF16
+    bd = torch.from_numpy(bias).cuda()
+    for out_dtype in (torch.float32, torch.bfloat16):
+        yb = sdc.fused_fwd(psi, xd, wd, bias=bd, out_dtype=out_dtype)[..., cols].float().cpu().numpy()
+        assert rel_l2(yb, refb) <= TOL_BF16

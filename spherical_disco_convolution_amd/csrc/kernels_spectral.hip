@@ -611,7 +611,12 @@ __global__ void spec_prep_w(const bf16_t* __restrict__ w, bf16_t* __restrict__ w
 }
 
 constexpr int kMt = 32;              // frequencies per work item (64 GEMM columns)
-constexpr int kBts = 264;            // B tile row: 256 (k, ci) pairs + 8 pad (bf16)
+// B tile row of spec_mfma: pair (k, ci) at 40 k + ci (each 32-pair block padded by
+// 8), 312 bf16 = 624 bytes per row (an odd multiple of 16 bytes).  The window
+// sum's 8-byte writes (lanes differing in k) then fall into distinct banks, as
+// do the GEMM's 16-byte reads (lanes differing in the row).
+constexpr int kBts = 312;
+constexpr int kBkb = 40;             // bf16 per k block of a tile row
 constexpr int kSpecThreads = 256;
 constexpr int kSpecMaxWin = 8;       // windows per output row (one 16-deep MFMA step)
 constexpr int kXcds = 8;             // accelerator dies of the chip (L2 domains)
@@ -628,10 +633,11 @@ constexpr int kXcds = 8;             // accelerator dies of the chip (L2 domains
 //    XOR-swizzled by channel so that the lanes' reads hit distinct banks.
 //    Each wave owns 8 of the 32 frequencies and builds their B operands at
 //    the start of an item from the Psi_hat slice in LDS.  Results go to the
-//    bf16 LDS tile bt[(m, re/im)][k * 32 + ci].
+//    bf16 LDS tile bt[(m, re/im)][40 k + ci].
 //  * Channel/basis GEMM: y_hat[co, (m, re/im)] += wp[co, (k, ci)] bt[(k, ci),
 //    (m, re/im)], 4 waves, wave tile 32 x 64 (CO = 128) or 32 x 32 (CO = 64),
-//    16 k-steps per chunk, weights in fragment order.
+//    2 KT k-steps per chunk (the pairs of basis columns past KT are zero and
+//    skipped), weights in fragment order.
 // Persistent, in NX bands of the flattened output rows (b, j): workgroup g
 // serves band g % NX (workgroups are dispatched to the XCDs round-robin, so a
 // band stays on one XCD when NX is their count) and takes that band's items
@@ -677,36 +683,70 @@ __global__ __launch_bounds__(kSpecThreads) __attribute__((amdgpu_waves_per_eu(2)
     const size_t cstride = (size_t)32 * nlat_in * MP;   // one 32-channel chunk
     const size_t plane = (size_t)nlat_in * MP;
 
-    // item n of this workgroup (clamped to its last): index (b * nlat_out + j)
-    // * ntiles + tile
-    auto item_of = [&](int n) {
-        const int l = slot + (n < nmine ? n : nmine - 1) * GX;
-        const int mt = l / brows;
-        return (r0 + (l - mt * brows)) * ntiles + mt;
+    // Item cursor: item n of this workgroup is l = slot + n GX of its band,
+    // frequency tile mt = l / brows and band row ro = l % brows.  Cursors step
+    // through the items in order (stopping at the last), so no item is decoded
+    // by division more than once.
+    struct Cur {
+        int n, mt, ro;
+    };
+    auto cur_first = [&]() {
+        Cur c;
+        c.n = 0;
+        c.mt = slot / brows;
+        c.ro = slot - c.mt * brows;
+        return c;
+    };
+    auto cur_next = [&](Cur& c) {
+        if (c.n + 1 < nmine) {
+            ++c.n;
+            c.ro += GX;
+            while (c.ro >= brows) {
+                c.ro -= brows;
+                ++c.mt;
+            }
+        }
+    };
+    auto cur_bj = [&](const Cur& c, int& b, int& j) {   // batch entry and output row
+        j = r0 + c.ro;
+        b = 0;
+        if (B > 1) {
+            b = j / nlat_out;
+            j -= b * nlat_out;
+        }
     };
 
     // ---- spectra stream: position p = (item p / nchunks, chunk p % nchunks).
+    // The request cursor walks the positions in order (staying at the last).
     // Thread (piece p = tid % 8, channel tid / 8) loads the 16-byte piece (4
     // frequencies) of every window's row; LDS slot ((r * 32 + ci) * 8 +
     // (piece ^ (ci & 7))).  Window slots past the row's windows repeat window
     // 0 (valid, finite; their B rows are zero).
     size_t src_base = 0;            // this lane's element offset of the position fetched next
     int src_row[kSpecMaxWin];       // its window rows' offsets (lat * MP, wave-uniform)
-    int lat_req[kSpecMaxWin];       // window rows of the position after it (requested)
-    int req_m0 = 0, req_chunk = 0, req_b = 0;
-    auto request_rows = [&](int p) {   // vector loads of position p's window rows
-        const int it = item_of(p / nchunks);
-        const int mt = it % ntiles, jb = it / ntiles;
-        const int j = jb % nlat_out;
-        req_b = jb / nlat_out;
-        req_m0 = mt * kMt;
-        req_chunk = p % nchunks;
+    int lat_req[kSpecMaxWin];       // window rows of the requested position's item
+    int req_pos = 0, req_chunk = 0, req_b = 0;
+    const int npos = nmine * nchunks;
+    Cur rq = cur_first();
+    auto request_item = [&]() {   // the window rows of the request cursor's item
+        int j;
+        cur_bj(rq, req_b, j);
         const int w0 = win_ptr[j], nw = win_ptr[j + 1] - w0;
 #pragma unroll
         for (int r = 0; r < kSpecMaxWin; ++r) lat_req[r] = wins[w0 + (r < nw ? r : 0)].lat;
     };
+    auto request_next = [&]() {   // the next position
+        if (req_pos + 1 < npos) {
+            ++req_pos;
+            if (++req_chunk == nchunks) {
+                req_chunk = 0;
+                cur_next(rq);
+                request_item();
+            }
+        }
+    };
     auto resolve_rows = [&]() {   // addresses from the requested rows
-        src_base = ((size_t)(req_b * Ci + req_chunk * 32 + sci)) * plane + req_m0 + 4 * sp;
+        src_base = ((size_t)(req_b * Ci + req_chunk * 32 + sci)) * plane + rq.mt * kMt + 4 * sp;
 #pragma unroll
         for (int r = 0; r < kSpecMaxWin; ++r) src_row[r] = uniform(lat_req[r]) * MP;
     };
@@ -725,9 +765,10 @@ __global__ __launch_bounds__(kSpecThreads) __attribute__((amdgpu_waves_per_eu(2)
     // ---- Psi_hat slice of an item: ps[(r KT + k) kMt + ml]; slots past the
     // row's windows are zero
     uint32_t pn[PSN];
-    auto load_ps = [&](int n) {
-        const int it = item_of(n);
-        const int mt = it % ntiles, j = (it / ntiles) % nlat_out;
+    auto load_ps = [&](const Cur& c) {
+        int b, j;
+        cur_bj(c, b, j);
+        const int mt = c.mt;
         const int w0 = win_ptr[j], nw = win_ptr[j + 1] - w0;
 #pragma unroll
         for (int q = 0; q < PSN; ++q) {
@@ -749,32 +790,35 @@ __global__ __launch_bounds__(kSpecThreads) __attribute__((amdgpu_waves_per_eu(2)
     if (KT < 8) {
         for (int idx = tid; idx < 64 * (8 - KT) * 4; idx += kSpecThreads) {
             const int row = idx / ((8 - KT) * 4), q = idx - row * ((8 - KT) * 4);
-            *reinterpret_cast<u32x4*>(bt + row * kBts + KT * 32 + q * 8) = u32x4{0, 0, 0, 0};
+            *reinterpret_cast<u32x4*>(bt + row * kBts + (KT + (q >> 2)) * kBkb + (q & 3) * 8) =
+                u32x4{0, 0, 0, 0};
         }
     }
-    const int npos = nmine * nchunks;
-    load_ps(0);
-    request_rows(0);
+    Cur cur = cur_first();   // item n
+    Cur nxt = cur;           // item n + 1 (the last item past the end)
+    cur_next(nxt);
+    load_ps(cur);
+    request_item();          // position 0
     resolve_rows();
     load_x();                          // position 0
-    u32x4 wq[16];
+    constexpr int NKS = 2 * KT;   // k-steps with non-zero basis columns
+    u32x4 wq[NKS];
     // fragment (chunk, k-step) of this wave's 32 rows: wf[(chunk * 16 + k-step) * WGM * 64]
     const u32x4* wf = reinterpret_cast<const u32x4*>(wp) + wm * 64 + lane;
 #pragma unroll
-    for (int ks = 0; ks < 16; ++ks) wq[ks] = wf[(size_t)ks * WGM * 64];
+    for (int ks = 0; ks < NKS; ++ks) wq[ks] = wf[(size_t)ks * WGM * 64];
     store_ps();
     store_x();                         // xs: position 0
-    request_rows(npos > 1 ? 1 : 0);
+    request_next();
     resolve_rows();
     load_x();                          // xn: position 1
-    request_rows(npos > 2 ? 2 : npos - 1);   // rows of position 2
+    request_next();                    // rows of position 2
     __syncthreads();   // ps, zero columns, first spectra block
 
     for (int n = 0; n < nmine; ++n) {
-        const int it = item_of(n);
-        const int mt = it % ntiles, jb = it / ntiles;
-        const int j = jb % nlat_out, b = jb / nlat_out;
-        const int m0 = mt * kMt;
+        int b, j;
+        cur_bj(cur, b, j);
+        const int m0 = cur.mt * kMt;
         const int w0 = uniform(win_ptr[j]);
         const int nw = uniform(win_ptr[j + 1]) - w0;   // <= kSpecMaxWin (checked on the host)
 
@@ -795,7 +839,7 @@ __global__ __launch_bounds__(kSpecThreads) __attribute__((amdgpu_waves_per_eu(2)
                 }
             }
         }
-        load_ps(n + 1);   // the next item's slice, stored after this item
+        load_ps(nxt);   // the next item's slice, stored after this item
         // A-operand reads: lane (channel l32, windows 4 lg + u, clamped to
         // window 0 past the row's windows), pieces 2 wave and 2 wave + 1
         int xrd[4][2];
@@ -814,7 +858,6 @@ __global__ __launch_bounds__(kSpecThreads) __attribute__((amdgpu_waves_per_eu(2)
             for (int e = 0; e < 16; ++e) acc[t][e] = 0.0f;
 
         for (int cc = 0; cc < nchunks; ++cc) {
-            const int p = n * nchunks + cc;   // stream position in xs
             // ---- window sum, one MFMA per frequency ----
             u32x4 xa[4][2];
 #pragma unroll
@@ -832,10 +875,10 @@ __global__ __launch_bounds__(kSpecThreads) __attribute__((amdgpu_waves_per_eu(2)
                                                             __builtin_bit_cast(bf16x8_t, bq[f]), d,
                                                             0, 0, 0);
                 if (l32 < 2 * KT) {
-                    // column (k, c) -> tile row 2 (f0 + f) + c, pairs k * 32 + ci,
+                    // column (k, c) -> tile row 2 (f0 + f) + c, pairs (k, ci),
                     // ci = 8 q + 4 lg + (0..3)
                     bf16_t* dst =
-                        bt + (2 * (f0 + f) + (l32 & 1)) * kBts + (l32 >> 1) * 32 + 4 * lg;
+                        bt + (2 * (f0 + f) + (l32 & 1)) * kBts + (l32 >> 1) * kBkb + 4 * lg;
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
                         const uint2 pk = make_uint2(pack_bf16x2(d[4 * q], d[4 * q + 1]),
@@ -850,39 +893,48 @@ __global__ __launch_bounds__(kSpecThreads) __attribute__((amdgpu_waves_per_eu(2)
             store_x();
             resolve_rows();
             load_x();
-            request_rows(p + 3 < npos ? p + 3 : npos - 1);
+            request_next();   // rows of position p + 3
             // ---- channel/basis GEMM over this chunk's 256 (k, ci) pairs ----
             const int cn = cc + 1 < nchunks ? cc + 1 : 0;   // weights of the next chunk
             const bf16_t* bb = bt + (wn * (64 / WGN) + l32) * kBts + 8 * lg;
             const u32x4* wnext = wf + (size_t)cn * 16 * WGM * 64;
 #pragma unroll
-            for (int ks = 0; ks < 16; ++ks) {
+            for (int ks = 0; ks < NKS; ++ks) {
                 const bf16x8_t af = __builtin_bit_cast(bf16x8_t, wq[ks]);
 #pragma unroll
                 for (int t = 0; t < NTW; ++t) {
                     const bf16x8_t bf =
-                        *reinterpret_cast<const bf16x8_t*>(bb + t * 32 * kBts + 16 * ks);
-                    acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf, acc[t], 0, 0, 0);
+                        *reinterpret_cast<const bf16x8_t*>(bb + t * 32 * kBts +
+                                                           (ks >> 1) * kBkb + 16 * (ks & 1));
+                    // transposed product: lane column = output channel, rows =
+                    // the tile's columns (frequency, re/im)
+                    acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf, af, acc[t], 0, 0, 0);
                 }
                 wq[ks] = wnext[(size_t)ks * WGM * 64];
             }
             __syncthreads();
         }
-        // ---- y_hat (bf16 (re, im) pairs): lane holds GEMM column nn (frequency
-        // m0 + nn/2, real part for even nn), rows 8*(e/4) + 4*lg + e%4 of its
-        // 32-row tile; element 2 m0 + nn of the row ----
+        // ---- y_hat (bf16 (re, im) pairs): lane holds channel co = 32 wm + l32
+        // and columns 8 g + 4 lg + (0..3) of its 32-column tile (g = e / 4),
+        // i.e. four consecutive elements 2 m0 + column of the channel's row
+        // (the two lane halves write 16 contiguous bytes) ----
+        {
+            bf16_t* yrow = yh + ((size_t)(b * CO + wm * 32 + l32) * nlat_out + j) * MP * 2 + 2 * m0;
 #pragma unroll
-        for (int t = 0; t < NTW; ++t) {
-            const int nn = wn * (64 / WGN) + t * 32 + l32;
+            for (int t = 0; t < NTW; ++t) {
+                const int c0 = wn * (64 / WGN) + t * 32 + 4 * lg;
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int co = wm * 32 + 8 * (e >> 2) + 4 * lg + (e & 3);
-                yh[((size_t)(b * CO + co) * nlat_out + j) * MP * 2 + 2 * m0 + nn] =
-                    __builtin_bit_cast(bf16_t, (__bf16)acc[t][e]);
+                for (int g = 0; g < 4; ++g) {
+                    const uint2 pk = make_uint2(pack_bf16x2(acc[t][4 * g], acc[t][4 * g + 1]),
+                                                pack_bf16x2(acc[t][4 * g + 2], acc[t][4 * g + 3]));
+                    *reinterpret_cast<uint2*>(yrow + c0 + 8 * g) = pk;
+                }
             }
         }
         store_ps();      // the next item's slice (every wave built its B operands)
-        __syncthreads();
+        __syncthreads();   // ps for the next item
+        cur = nxt;
+        cur_next(nxt);
     }
 }
 

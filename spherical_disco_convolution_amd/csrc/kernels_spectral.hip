@@ -400,8 +400,8 @@ __global__ __launch_bounds__(kRegThreads) void spec_rfft_reg(const uint32_t* __r
     constexpr int P2 = H2 | 1, LP = H1 * P2;
     constexpr int TA = RW * H2, ITA = (TA + 63) / 64;
     constexpr int TB = RW * H1, ITB = (TB + 63) / 64;
-    constexpr int NQ = MP / 4, TQ = RW * NQ;
     static_assert(LP >= H, "the split needs H entries per row");
+    static_assert(MP - H - 1 <= 64, "one lane per padding word");
     __shared__ float2 buf[RW * LP];
     const int lane = threadIdx.x;
     const int64_t g = blockIdx.x;   // the grid is the row-group count
@@ -461,28 +461,37 @@ __global__ __launch_bounds__(kRegThreads) void spec_rfft_reg(const uint32_t* __r
             }
         }
         wave_lds_sync();
-        // ---- even/odd split: X[m] = (a + b)/2 - i W^m (a - b)/2 with
-        // a = Z[m mod H], b = conj(Z[(H - m) mod H]), W = exp(-2 pi i / N);
-        // frequencies past H are zero ----
-        for (int t = lane; t < TQ; t += 64) {
-            const int r = t / NQ, q = t - r * NQ;
-            const int64_t row = g * RW + r;
-            const int m0 = 4 * q;
-            const float2 w0 = root(m0, 0.5f / (float)H, -1.0f);
-            const float2* z = buf + r * LP;
-            u32x4 o;
-            static_for<0, 4>([&](auto u) {
-                const int m = m0 + u;
-                float2 X = make_float2(0.0f, 0.0f);
-                if (m <= H) {
-                    const float2 a = z[m == H ? 0 : m];
-                    const float2 bb = cconj(z[m == 0 ? 0 : H - m]);
-                    const float2 e = cmul(rot_ct<2 * H, -1, decltype(u)::value>(w0), csub(a, bb));
-                    X = cadd(cscale(cadd(a, bb), 0.5f), cscale(make_float2(e.y, -e.x), 0.5f));
-                }
-                o[decltype(u)::value] = pack_bf16x2(X.x, X.y);
-            });
-            if (row < nrows) *reinterpret_cast<u32x4*>(xh + row * MP + m0) = o;
+        // ---- even/odd split, frequencies m and H - m together: with
+        // a = Z[m], b = conj(Z[H - m]) (Z[H] = Z[0]) and e = W^m (a - b),
+        // W = exp(-2 pi i / N):  X[m] = (a + b)/2 - i e/2 and
+        // X[H - m] = conj((a + b)/2 + i e/2).  Lane pairs m = lane + 64 i,
+        // m <= H/2; words past H are zero ----
+        {
+            constexpr int NPI = (H / 2 + 1 + 63) / 64;   // pair iterations per row
+            const float2 wl = root(lane, 0.5f / (float)H, -1.0f);   // W^lane
+#pragma unroll
+            for (int r = 0; r < RW; ++r) {
+                const int64_t row = g * RW + r;
+                const float2* z = buf + r * LP;
+                uint32_t* out = xh + (row < nrows ? row : 0) * MP;
+                static_for<0, NPI>([&](auto ii) {
+                    constexpr int I = decltype(ii)::value;
+                    const int m = lane + 64 * I;
+                    if (m <= H / 2 && row < nrows) {
+                        const float2 a = z[m];
+                        const float2 bb = cconj(z[m == 0 ? 0 : H - m]);
+                        const float2 e = cmul(rot_ct<2 * H, -1, 64 * I>(wl), csub(a, bb));
+                        const float2 sm = cadd(a, bb);
+                        // -i e = (e.y, -e.x)
+                        out[m] = pack_bf16x2(0.5f * (sm.x + e.y), 0.5f * (sm.y - e.x));
+                        if (m != 0 && 2 * m != H)
+                            out[H - m] = pack_bf16x2(0.5f * (sm.x - e.y), -0.5f * (sm.y + e.x));
+                        else if (m == 0)
+                            out[H] = pack_bf16x2(0.5f * (sm.x - e.y), -0.5f * (sm.y + e.x));
+                    }
+                });
+                if (lane < MP - H - 1 && row < nrows) out[H + 1 + lane] = 0u;
+            }
         }
     }
 }
@@ -492,8 +501,9 @@ __global__ __launch_bounds__(kRegThreads) void spec_rfft_reg(const uint32_t* __r
 // (the imaginary parts of X[0] and X[H] dropped: a real row's spectrum has
 // none), W = exp(-2 pi i / N); z[n] = sum_k Z[k] w_H^{-n k} by the same split
 // (k = H2 a + b, n = c + H1 d); y[2n] = Re z[n] / H, y[2n+1] = Im z[n] / H.
-// Step A forms Z from its loads of y_hat, step B stores y (lanes c
-// consecutive).  Workgroup g transforms rows g RW .. g RW + RW - 1.
+// The merge fills Z in LDS (k and H - k together), step A reads it there,
+// step B stores y (lanes c consecutive).  Workgroup g transforms rows
+// g RW .. g RW + RW - 1.
 template <int H1, int H2, int RW, typename TY>
 __global__ __launch_bounds__(kRegThreads) void spec_irfft_reg(const uint32_t* __restrict__ yh,
                                                               TY* __restrict__ y,
@@ -509,49 +519,78 @@ __global__ __launch_bounds__(kRegThreads) void spec_irfft_reg(const uint32_t* __
     const int64_t g = blockIdx.x;   // the grid is the row-group count
     constexpr float sc = 1.0f / (float)H;
 
-    uint32_t ra[ITA][H1], rb[ITA][H1];   // X[k], X[H - k] for k = H2 a + b
+    // ---- merge, frequencies m and H - m together: with A = X[m],
+    // B = conj(X[H - m]) (imaginary parts of X[0] and X[H] dropped),
+    // s = A + B and e = W^-m (A - B):  Z[m] = (s + i e)/2 and
+    // Z[H - m] = conj((s - i e)/2).  Z goes to LDS in natural order.
+    {
+        constexpr int NPI = (H / 2 + 1 + 63) / 64;   // pair iterations per row
+        // every load first (addresses clamped to valid frequencies), so that
+        // all are in flight together
+        uint32_t la[RW][NPI], lb[RW][NPI];
 #pragma unroll
-    for (int i = 0; i < ITA; ++i) {
-        const int t = min(lane + 64 * i, TA - 1);
-        const int r = t / H2, b = t - r * H2;
-        const int64_t row = min(g * RW + r, nrows - 1);
-        const uint32_t* src = yh + row * MP;
+        for (int r = 0; r < RW; ++r) {
+            const uint32_t* src = yh + min(g * RW + r, nrows - 1) * MP;
 #pragma unroll
-        for (int a = 0; a < H1; ++a) {
-            ra[i][a] = src[H2 * a + b];
-            rb[i][a] = src[H - H2 * a - b];
+            for (int I = 0; I < NPI; ++I) {
+                const int m = min(lane + 64 * I, H / 2);
+                la[r][I] = src[m];
+                lb[r][I] = src[H - m];
+            }
+        }
+        const float2 wl = root(lane, 1.0f / (float)N, 1.0f);   // W^-lane
+#pragma unroll
+        for (int r = 0; r < RW; ++r) {
+            float2* z = buf + r * LP;
+            static_for<0, NPI>([&](auto ii) {
+                constexpr int I = decltype(ii)::value;
+                const int m = lane + 64 * I;
+                if (m <= H / 2) {
+                    float2 A = unpack_bf16x2(la[r][I]);
+                    float2 Bc = cconj(unpack_bf16x2(lb[r][I]));
+                    if (m == 0) {
+                        A.y = 0.0f;
+                        Bc.y = 0.0f;
+                    }
+                    const float2 e = cmul(rot_ct<N, 1, 64 * I>(wl), csub(A, Bc));
+                    const float2 sm = cadd(A, Bc);
+                    // i e = (-e.y, e.x)
+                    z[m] = make_float2(0.5f * (sm.x - e.y), 0.5f * (sm.y + e.x));
+                    if (m != 0 && 2 * m != H)
+                        z[H - m] = make_float2(0.5f * (sm.x + e.y), 0.5f * (e.x - sm.y));
+                }
+            });
         }
     }
+    wave_lds_sync();
     {
-        // ---- step A ----
+        // ---- step A: every lane reads its Z values, then the buffer is
+        // rewritten in the exchange layout ----
+        float2 va[ITA][H1];
+#pragma unroll
+        for (int i = 0; i < ITA; ++i) {
+            const int t = min(lane + 64 * i, TA - 1);
+            const int r = t / H2, b = t - r * H2;
+#pragma unroll
+            for (int a = 0; a < H1; ++a) va[i][a] = buf[r * LP + H2 * a + b];
+        }
+        wave_lds_sync();
 #pragma unroll
         for (int i = 0; i < ITA; ++i) {
             const int t = lane + 64 * i;
             const int tc = min(t, TA - 1);
             const int r = tc / H2, b = tc - r * H2;
-            const float2 wb = root(b, 1.0f / (float)N, 1.0f);   // W^-b
-            float2 v[H1];
-            static_for<0, H1>([&](auto a) {
-                float2 A = unpack_bf16x2(ra[i][a]);
-                float2 Bc = cconj(unpack_bf16x2(rb[i][a]));
-                if (decltype(a)::value == 0 && b == 0) {
-                    A.y = 0.0f;
-                    Bc.y = 0.0f;
-                }
-                const float2 e = cmul(rot_ct<N, 1, H2 * decltype(a)::value>(wb), csub(A, Bc));
-                v[a] = cadd(cscale(cadd(A, Bc), 0.5f), cscale(make_float2(-e.y, e.x), 0.5f));
-            });
-            reg_dft<H1, 1>(v);
+            reg_dft<H1, 1>(va[i]);
             const float2 w = root(b, 1.0f / (float)H, 1.0f);
             float2 p = w;
 #pragma unroll
             for (int c = 1; c < H1; ++c) {
-                v[c] = cmul(v[c], p);
+                va[i][c] = cmul(va[i][c], p);
                 p = cmul(p, w);
             }
             if (t < TA) {
 #pragma unroll
-                for (int c = 0; c < H1; ++c) buf[r * LP + c * P2 + b] = v[c];
+                for (int c = 0; c < H1; ++c) buf[r * LP + c * P2 + b] = va[i][c];
             }
         }
         wave_lds_sync();

@@ -880,15 +880,9 @@ __global__ __launch_bounds__(kSpecThreads) __attribute__((amdgpu_waves_per_eu(2)
         }
         load_ps(nxt);   // the next item's slice, stored after this item
         // A-operand reads: lane (channel l32, windows 4 lg + u, clamped to
-        // window 0 past the row's windows), pieces 2 wave and 2 wave + 1
-        int xrd[4][2];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int r = 4 * lg + u < nw ? 4 * lg + u : 0;
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-                xrd[u][h] = (r * 32 + l32) * 8 + ((2 * wave + h) ^ (l32 & 7));
-        }
+        // window 0 past the row's windows), pieces 2 wave + h (swizzled by
+        // the channel; 2 wave is even, so the h = 1 piece is the other's ^ 1)
+        const int xsw = (2 * wave) ^ (l32 & 7);
 
         floatx16 acc[NTW];
 #pragma unroll
@@ -902,7 +896,10 @@ __global__ __launch_bounds__(kSpecThreads) __attribute__((amdgpu_waves_per_eu(2)
 #pragma unroll
             for (int u = 0; u < 4; ++u)
 #pragma unroll
-                for (int h = 0; h < 2; ++h) xa[u][h] = xs[xrd[u][h]];
+                for (int h = 0; h < 2; ++h) {
+                    const int r = 4 * lg + u < nw ? 4 * lg + u : 0;
+                    xa[u][h] = xs[(r * 32 + l32) * 8 + (xsw ^ h)];
+                }
 #pragma unroll
             for (int f = 0; f < 8; ++f) {
                 const u32x4 a = {xa[0][f >> 2][f & 3], xa[1][f >> 2][f & 3], xa[2][f >> 2][f & 3],

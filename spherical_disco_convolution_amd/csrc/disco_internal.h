@@ -50,8 +50,8 @@ int build_host_psi(const disco_psi_desc& desc, HostPsi& out);
 // Longitude-spectral tables (spectral_host.cpp), built for stride-1 layers
 // whose longitude count N is even, at most kSpecMaxN, with N/2 a product of
 // 2, 3 and 5, and K <= 8.  psih: [nwin][K][MP] bf16 (re, im) pairs in 32-bit
-// words (real part low), Psi_hat of each window; radix: the plan of the
-// N/2-point transform.  *mp = 0 when the layer
+// words (real part low), Psi_hat of each window, followed by 32 zero words;
+// radix: the plan of the N/2-point transform.  *mp = 0 when the layer
 // does not qualify.
 constexpr int kSpecMaxN = 1800;   // N/2 <= 900 bounds the transform butterflies per lane
 constexpr int kSpecMaxRadix = 12;

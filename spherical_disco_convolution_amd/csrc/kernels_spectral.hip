@@ -372,6 +372,25 @@ __device__ __forceinline__ void reg_dft(float2 (&a)[N]) {
     }
 }
 
+typedef __attribute__((address_space(3))) void lds_void;
+
+// 16 bytes per lane from global memory straight into LDS: lane L writes
+// lds_addr + 16 L (global_load_lds_dwordx4, LDS address in M0).  No register
+// results: completion is tracked by the caller's vmcnt waits.
+__device__ __forceinline__ void dma_lds16(const void* src, uint32_t lds_addr) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_addr))
+                 : "memory", "m0");
+}
+
+// Wait until at most N vector memory operations of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 __device__ __forceinline__ float2 unpack_bf16x2(uint32_t v) {
     return make_float2(__uint_as_float(v << 16), __uint_as_float(v & 0xffff0000u));
 }
@@ -684,24 +703,25 @@ constexpr int kXcds = 8;             // accelerator dies of the chip (L2 domains
 // items run tile-major: every row of the band for frequency tile 0, then tile
 // 1, ...  The items in flight on an XCD then share their input rows' spectra
 // in its L2.  A workgroup's (item, chunk) pairs form one stream, pipelined
-// across item boundaries: the spectra of stream position p + 1 are in LDS and
-// those of p + 2 in flight while p is computed (their window rows fetched
-// one position earlier), each weight fragment is reloaded for the next chunk
-// right after its use (the weights do not depend on the item), and the next
+// across item boundaries: once the window sum of position p has read its
+// spectra, the block of p + 1 is loaded into the same LDS by DMA (its window
+// rows fetched one position earlier) while p is computed, each weight
+// fragment is reloaded for the next chunk right after its use (the weights
+// do not depend on the item), and the next
 // item's Psi_hat slice is loaded during the current item.
 template <int CO, int KT>
 __global__ __launch_bounds__(kSpecThreads) __attribute__((amdgpu_waves_per_eu(2))) void spec_mfma(
     const uint32_t* __restrict__ xh, const bf16_t* __restrict__ wp,
     const uint32_t* __restrict__ psih, const int32_t* __restrict__ win_ptr,
     const DevWindow* __restrict__ wins, bf16_t* __restrict__ yh, int B, int Ci, int nlat_in,
-    int nlat_out, int MP, int NX) {
+    int nlat_out, int MP, int NX, int64_t psih_zero) {
     __shared__ __attribute__((aligned(16))) bf16_t bt[64 * kBts];
     __shared__ __attribute__((aligned(16))) u32x4 xs[kSpecMaxWin * 32 * 8];   // [r][ci][piece]
-    __shared__ uint32_t ps[kSpecMaxWin * KT * kMt];
+    __shared__ __attribute__((aligned(16))) uint32_t ps[kSpecMaxWin * KT * kMt];
+    __shared__ __attribute__((aligned(16))) bf16_t dump[32];   // 4 writes of 8 bytes, 8 apart
     constexpr int WGM = CO / 32;          // waves along the output channels
     constexpr int WGN = 4 / WGM;          // waves along the columns
     constexpr int NTW = 2 / WGN;          // 32-column MFMA tiles per wave
-    constexpr int PSN = (kSpecMaxWin * KT * kMt + kSpecThreads - 1) / kSpecThreads;
 
     const int ntiles = MP / kMt;
     const int GX = (int)gridDim.x / NX;   // workgroups per band (the grid is NX * GX)
@@ -718,7 +738,6 @@ __global__ __launch_bounds__(kSpecThreads) __attribute__((amdgpu_waves_per_eu(2)
     const int wm = wave % WGM, wn = wave / WGM;
     const int nchunks = Ci / 32;
     const int f0 = wave * 8;
-    const int sp = tid & 7, sci = tid >> 3;
     const size_t cstride = (size_t)32 * nlat_in * MP;   // one 32-channel chunk
     const size_t plane = (size_t)nlat_in * MP;
 
@@ -757,13 +776,12 @@ __global__ __launch_bounds__(kSpecThreads) __attribute__((amdgpu_waves_per_eu(2)
 
     // ---- spectra stream: position p = (item p / nchunks, chunk p % nchunks).
     // The request cursor walks the positions in order (staying at the last).
-    // Thread (piece p = tid % 8, channel tid / 8) loads the 16-byte piece (4
-    // frequencies) of every window's row; LDS slot ((r * 32 + ci) * 8 +
-    // (piece ^ (ci & 7))).  Window slots past the row's windows repeat window
-    // 0 (valid, finite; their B rows are zero).
-    size_t src_base = 0;            // this lane's element offset of the position fetched next
-    int src_row[kSpecMaxWin];       // its window rows' offsets (lat * MP, wave-uniform)
-    int lat_req[kSpecMaxWin];       // window rows of the requested position's item
+    // A position's spectra block goes straight to LDS by DMA: wave w fills
+    // windows 2w and 2w + 1.  LDS slot ((r * 32 + ci) * 8 + pos) holds the
+    // 16-byte piece pos ^ (ci & 7) (4 frequencies) of channel ci's row in
+    // window r.  Window slots past the row's windows repeat window 0 (valid,
+    // finite; their B rows are zero).
+    int lat_lo = 0, lat_hi = 0;     // input rows of windows 2w, 2w + 1 of the requested item
     int req_pos = 0, req_chunk = 0, req_b = 0;
     const int npos = nmine * nchunks;
     Cur rq = cur_first();
@@ -771,8 +789,8 @@ __global__ __launch_bounds__(kSpecThreads) __attribute__((amdgpu_waves_per_eu(2)
         int j;
         cur_bj(rq, req_b, j);
         const int w0 = win_ptr[j], nw = win_ptr[j + 1] - w0;
-#pragma unroll
-        for (int r = 0; r < kSpecMaxWin; ++r) lat_req[r] = wins[w0 + (r < nw ? r : 0)].lat;
+        lat_lo = wins[w0 + (2 * wave < nw ? 2 * wave : 0)].lat;
+        lat_hi = wins[w0 + (2 * wave + 1 < nw ? 2 * wave + 1 : 0)].lat;
     };
     auto request_next = [&]() {   // the next position
         if (req_pos + 1 < npos) {
@@ -784,74 +802,63 @@ __global__ __launch_bounds__(kSpecThreads) __attribute__((amdgpu_waves_per_eu(2)
             }
         }
     };
-    auto resolve_rows = [&]() {   // addresses from the requested rows
-        src_base = ((size_t)(req_b * Ci + req_chunk * 32 + sci)) * plane + rq.mt * kMt + 4 * sp;
+    const uint32_t xs_lds =
+        __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_void*)&xs[0]);
+    // DMA of the requested position: 8 instructions per wave, instruction i
+    // covering channels 8 (i % 4) .. + 7 of window 2w + i / 4 (64 slots)
+    // this lane's source offsets (channel within the chunk and piece) of
+    // instructions i and i + 4: constant over the stream
+    size_t dma_off[4];
 #pragma unroll
-        for (int r = 0; r < kSpecMaxWin; ++r) src_row[r] = uniform(lat_req[r]) * MP;
-    };
-    u32x4 xn[kSpecMaxWin];
-    auto load_x = [&]() {
-        const uint32_t* base = xh + src_base;
+    for (int q = 0; q < 4; ++q) {
+        const int ci = 8 * q + (lane >> 3);
+        dma_off[q] = (size_t)ci * plane + 4 * ((lane & 7) ^ (ci & 7));
+    }
+    auto dma_x = [&]() {
+        const size_t cb = (size_t)(req_b * Ci + req_chunk * 32) * plane + rq.mt * kMt;
+        const uint32_t* blo = xh + cb + (size_t)uniform(lat_lo) * MP;
+        const uint32_t* bhi = xh + cb + (size_t)uniform(lat_hi) * MP;
 #pragma unroll
-        for (int r = 0; r < kSpecMaxWin; ++r)
-            xn[r] = *reinterpret_cast<const u32x4*>(base + src_row[r]);
-    };
-    auto store_x = [&]() {
-#pragma unroll
-        for (int r = 0; r < kSpecMaxWin; ++r) xs[(r * 32 + sci) * 8 + (sp ^ (sci & 7))] = xn[r];
+        for (int i = 0; i < 8; ++i) {
+            const int r = 2 * wave + (i >> 2);
+            dma_lds16((i < 4 ? blo : bhi) + dma_off[i & 3],
+                      xs_lds + (uint32_t)((r * 32 + 8 * (i & 3)) * 8 * 16));
+        }
     };
 
-    // ---- Psi_hat slice of an item: ps[(r KT + k) kMt + ml]; slots past the
-    // row's windows are zero
-    uint32_t pn[PSN];
-    auto load_ps = [&](const Cur& c) {
+    // ---- Psi_hat slice of an item, ps[(r KT + k) kMt + ml], by DMA: KT
+    // instructions of 64 16-byte slots (4 frequencies each), spread over the
+    // waves; slots past the row's windows copy the table's zero block
+    const uint32_t ps_lds =
+        __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_void*)&ps[0]);
+    auto dma_ps = [&](const Cur& c) {
         int b, j;
         cur_bj(c, b, j);
-        const int mt = c.mt;
         const int w0 = win_ptr[j], nw = win_ptr[j + 1] - w0;
-#pragma unroll
-        for (int q = 0; q < PSN; ++q) {
-            const int idx = tid + q * kSpecThreads;
-            const int rk = idx / kMt, ml = idx - rk * kMt;
-            pn[q] = 0u;
-            if (rk < nw * KT) pn[q] = psih[(size_t)(w0 * KT + rk) * MP + mt * kMt + ml];
-        }
-    };
-    auto store_ps = [&]() {
-#pragma unroll
-        for (int q = 0; q < PSN; ++q) {
-            const int idx = tid + q * kSpecThreads;
-            if (idx < kSpecMaxWin * KT * kMt) ps[idx] = pn[q];
+        for (int i = wave; i < KT; i += 4) {
+            const int slot = 64 * i + lane;
+            const int rk = slot >> 3, ml0 = (slot & 7) * 4;
+            const uint32_t* src = rk < nw * KT
+                                      ? psih + (size_t)(w0 * KT + rk) * MP + c.mt * kMt + ml0
+                                      : psih + psih_zero;
+            dma_lds16(src, ps_lds + (uint32_t)(i * 1024));
         }
     };
 
-    // ---- prologue: basis columns past KT are zero for the whole kernel
-    if (KT < 8) {
-        for (int idx = tid; idx < 64 * (8 - KT) * 4; idx += kSpecThreads) {
-            const int row = idx / ((8 - KT) * 4), q = idx - row * ((8 - KT) * 4);
-            *reinterpret_cast<u32x4*>(bt + row * kBts + (KT + (q >> 2)) * kBkb + (q & 3) * 8) =
-                u32x4{0, 0, 0, 0};
-        }
-    }
     Cur cur = cur_first();   // item n
     Cur nxt = cur;           // item n + 1 (the last item past the end)
     cur_next(nxt);
-    load_ps(cur);
+    dma_ps(cur);
     request_item();          // position 0
-    resolve_rows();
-    load_x();                          // position 0
+    dma_x();
     constexpr int NKS = 2 * KT;   // k-steps with non-zero basis columns
     u32x4 wq[NKS];
     // fragment (chunk, k-step) of this wave's 32 rows: wf[(chunk * 16 + k-step) * WGM * 64]
     const u32x4* wf = reinterpret_cast<const u32x4*>(wp) + wm * 64 + lane;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) wq[ks] = wf[(size_t)ks * WGM * 64];
-    store_ps();
-    store_x();                         // xs: position 0
-    request_next();
-    resolve_rows();
-    load_x();                          // xn: position 1
-    request_next();                    // rows of position 2
+    request_next();                    // rows of position 1
+    wait_vmcnt<0>();
     __syncthreads();   // ps, zero columns, first spectra block
 
     for (int n = 0; n < nmine; ++n) {
@@ -863,22 +870,25 @@ __global__ __launch_bounds__(kSpecThreads) __attribute__((amdgpu_waves_per_eu(2)
 
         // B operands of the window sum: lane column n = 2 k + c (c: real,
         // imaginary part of X_hat), rows (r, re/im) for r = 4 lg .. 4 lg + 3
+        // (windows past the row's are zero in ps; basis columns k >= KT are
+        // never read by the GEMM, so their lanes take column KT - 1's values)
         u32x4 bq[8];
         {
-            const int nn = l32, k = nn >> 1, c = nn & 1;
+            const int k = min(l32 >> 1, KT - 1), c = l32 & 1;
 #pragma unroll
-            for (int f = 0; f < 8; ++f) {
+            for (int u = 0; u < 4; ++u) {
+                // the wave's 8 frequencies of (window 4 lg + u, basis k): 32 bytes
+                const u32x4* src =
+                    reinterpret_cast<const u32x4*>(ps + ((4 * lg + u) * KT + k) * kMt + f0);
+                const u32x4 lo = src[0], hi = src[1];
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const int r = 4 * lg + u;
-                    uint32_t P = 0u;   // bf16 (Pr, Pi), real part low
-                    if (nn < 2 * KT && r < nw) P = ps[(r * KT + k) * kMt + f0 + f];
+                for (int f = 0; f < 8; ++f) {
+                    const uint32_t P = f < 4 ? lo[f] : hi[f - 4];   // bf16 (Pr, Pi), real low
                     // real column: (Pr, Pi); imaginary column: (-Pi, Pr)
                     bq[f][u] = c ? (__builtin_rotateleft32(P, 16) ^ 0x8000u) : P;
                 }
             }
         }
-        load_ps(nxt);   // the next item's slice, stored after this item
         // A-operand reads: lane (channel l32, windows 4 lg + u, clamped to
         // window 0 past the row's windows), pieces 2 wave + h (swizzled by
         // the channel; 2 wave is even, so the h = 1 piece is the other's ^ 1)
@@ -900,6 +910,13 @@ __global__ __launch_bounds__(kSpecThreads) __attribute__((amdgpu_waves_per_eu(2)
                     const int r = 4 * lg + u < nw ? 4 * lg + u : 0;
                     xa[u][h] = xs[(r * 32 + l32) * 8 + (xsw ^ h)];
                 }
+            wave_lds_sync();   // this wave's spectra reads are done
+            __syncthreads();   // every wave's: the block may be overwritten
+            // every wave has built its B operands from ps: the next item's
+            // slice may replace it (completed with this position's DMA)
+            if (cc == 0) dma_ps(nxt);
+            dma_x();           // position p + 1 (the last position repeats at the end)
+            request_next();    // rows of position p + 2
 #pragma unroll
             for (int f = 0; f < 8; ++f) {
                 const u32x4 a = {xa[0][f >> 2][f & 3], xa[1][f >> 2][f & 3], xa[2][f >> 2][f & 3],
@@ -910,11 +927,14 @@ __global__ __launch_bounds__(kSpecThreads) __attribute__((amdgpu_waves_per_eu(2)
                 d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                             __builtin_bit_cast(bf16x8_t, bq[f]), d,
                                                             0, 0, 0);
-                if (l32 < 2 * KT) {
+                {
                     // column (k, c) -> tile row 2 (f0 + f) + c, pairs (k, ci),
-                    // ci = 8 q + 4 lg + (0..3)
+                    // ci = 8 q + 4 lg + (0..3).  Columns KT <= k < 8 are written
+                    // but never read; lanes of columns k >= 8 (no tile block)
+                    // write the shared dump instead of branching around it.
                     bf16_t* dst =
-                        bt + (2 * (f0 + f) + (l32 & 1)) * kBts + (l32 >> 1) * kBkb + 4 * lg;
+                        l32 < 16 ? bt + (2 * (f0 + f) + (l32 & 1)) * kBts + (l32 >> 1) * kBkb + 4 * lg
+                                 : dump;
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
                         const uint2 pk = make_uint2(pack_bf16x2(d[4 * q], d[4 * q + 1]),
@@ -923,13 +943,7 @@ __global__ __launch_bounds__(kSpecThreads) __attribute__((amdgpu_waves_per_eu(2)
                     }
                 }
             }
-            __syncthreads();   // tile complete; every wave is done with the spectra block
-            // stream: position p + 1 into LDS, p + 2 in flight, rows of p + 3
-            // requested (positions past the end repeat the last)
-            store_x();
-            resolve_rows();
-            load_x();
-            request_next();   // rows of position p + 3
+            __syncthreads();   // tile complete
             // ---- channel/basis GEMM over this chunk's 256 (k, ci) pairs ----
             const int cn = cc + 1 < nchunks ? cc + 1 : 0;   // weights of the next chunk
             const bf16_t* bb = bt + (wn * (64 / WGN) + l32) * kBts + 8 * lg;
@@ -948,7 +962,10 @@ __global__ __launch_bounds__(kSpecThreads) __attribute__((amdgpu_waves_per_eu(2)
                 }
                 wq[ks] = wnext[(size_t)ks * WGM * 64];
             }
-            __syncthreads();
+            // this wave's DMA of position p + 1 is complete; the NKS weight
+            // reloads issued after it may stay in flight
+            wait_vmcnt<NKS>();
+            __syncthreads();   // spectra of p + 1 in LDS; B tile free
         }
         // ---- y_hat (bf16 (re, im) pairs): lane holds channel co = 32 wm + l32
         // and columns 8 g + 4 lg + (0..3) of its 32-column tile (g = e / 4),
@@ -967,8 +984,6 @@ __global__ __launch_bounds__(kSpecThreads) __attribute__((amdgpu_waves_per_eu(2)
                 }
             }
         }
-        store_ps();      // the next item's slice (every wave built its B operands)
-        __syncthreads();   // ps for the next item
         cur = nxt;
         cur_next(nxt);
     }
@@ -1060,7 +1075,8 @@ int try_launch_fused_spectral(const disco_psi* psi, const void* x, const void* w
     dim3 grid((unsigned)(NX * GX));
 #define DISCO_SM(CC, KK)                                                                     \
     hipLaunchKernelGGL((spec_mfma<CC, KK>), grid, dim3(kSpecThreads), 0, st, xh, wpd,         \
-                       psih, d.win_ptr, d.windows, yh, B, Ci, D.nlat_in, D.nlat_out, MP, NX)
+                       psih, d.win_ptr, d.windows, yh, B, Ci, D.nlat_in, D.nlat_out, MP, NX, \
+                       (int64_t)h.windows.size() * K * MP)
 #define DISCO_SM_K(CC)                                                                       \
     switch (K) {                                                                             \
         case 1: DISCO_SM(CC, 1); break;                                                      \

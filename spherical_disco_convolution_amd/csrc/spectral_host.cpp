@@ -78,7 +78,9 @@ int build_spectral_tables(const HostPsi& h, std::vector<uint32_t>& psih, int32_t
         s[n] = std::sin(a);
     }
     try {
-        psih.assign(nwin * (size_t)K * MP, 0u);
+        // plus a zero block of 32 words at the end (a DMA source for the
+        // slices of windows a row does not have)
+        psih.assign(nwin * (size_t)K * MP + 32, 0u);
     } catch (const std::bad_alloc&) {
         return set_error(DISCO_ENOMEM, "host allocation for the spectral tables failed");
     }

@@ -384,11 +384,13 @@ __device__ __forceinline__ void dma_lds16(const void* src, uint32_t lds_addr) {
                  : "memory", "m0");
 }
 
-// Wait until at most N vector memory operations of this wave are outstanding.
+// Wait until at most N vector memory operations of this wave are outstanding
+// (s_waitcnt with the export and LDS/scalar counts left at their maxima; the
+// builtin, unlike inline asm, is seen by the compiler's own wait placement).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
 __device__ __forceinline__ float2 unpack_bf16x2(uint32_t v) {
@@ -961,6 +963,9 @@ __global__ __launch_bounds__(kSpecThreads) __attribute__((amdgpu_waves_per_eu(2)
                     acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf, af, acc[t], 0, 0, 0);
                 }
                 wq[ks] = wnext[(size_t)ks * WGM * 64];
+                // reloads stay in k-step order right after their use: then the
+                // next GEMM's wait for wq[0] leaves the newer spectra DMA in flight
+                __builtin_amdgcn_sched_barrier(0);
             }
             // this wave's DMA of position p + 1 is complete; the NKS weight
             // reloads issued after it may stay in flight

@@ -343,14 +343,49 @@ __device__ __forceinline__ float2 rot_ct(float2 v) {
     }
 }
 
-// In-place DFT of length N in registers, a[u] <- sum_t a[t] exp(S 2 pi i u t / N):
-// mixed-radix decimation in time (radix 4, 2, 3, 5 first), every index and
-// root compile-time.
+// Prime-factor split of N: the largest power of 2, 3 or 5 dividing N that is
+// not N itself and leaves a cofactor coprime to it (1 if there is none).
+constexpr int pfa_factor(int n) {
+    for (int p : {2, 3, 5}) {
+        int q = 1;
+        while (n % (q * p) == 0) q *= p;
+        if (q > 1 && q < n) return q;
+    }
+    return 1;
+}
+// x with (x * a) % m == 1 (a and m coprime)
+constexpr int inverse_mod(int a, int m) {
+    for (int x = 1; x < m; ++x)
+        if ((x * a) % m == 1) return x;
+    return 1;
+}
+
+// In-place DFT of length N in registers, a[u] <- sum_t a[t] exp(S 2 pi i u t / N),
+// every index and root compile-time.  Coprime factors N = N1 N2 take the
+// prime-factor algorithm (Good 1958, Thomas 1963): input index
+// (N2 n1 + N1 n2) mod N, output index (N2 T1 k1 + N1 T2 k2) mod N with
+// T1 = N2^-1 mod N1, T2 = N1^-1 mod N2, and no twiddle factors between the
+// two sets of short DFTs.  Prime powers use mixed-radix decimation in time
+// (radix 4, 2, 3, 5 first).
 template <int N, int S>
 __device__ __forceinline__ void reg_dft(float2 (&a)[N]) {
     if constexpr (N == 1) {
     } else if constexpr (N <= 5) {
         butterfly<N>(a, (float)S);
+    } else if constexpr (pfa_factor(N) > 1) {
+        constexpr int N1 = pfa_factor(N), N2 = N / N1;
+        constexpr int T1 = inverse_mod(N2 % N1, N1), T2 = inverse_mod(N1 % N2, N2);
+        float2 y[N2][N1];
+        static_for<0, N2>([&](auto n2) {
+            static_for<0, N1>([&](auto n1) { y[n2][n1] = a[(N2 * n1 + N1 * n2) % N]; });
+            reg_dft<N1, S>(y[n2]);
+        });
+        static_for<0, N1>([&](auto k1) {
+            float2 t[N2];
+            static_for<0, N2>([&](auto n2) { t[n2] = y[n2][k1]; });
+            reg_dft<N2, S>(t);
+            static_for<0, N2>([&](auto k2) { a[(N2 * T1 * k1 + N1 * T2 * k2) % N] = t[k2]; });
+        });
     } else {
         constexpr int R = N % 4 == 0 ? 4 : N % 2 == 0 ? 2 : N % 3 == 0 ? 3 : 5;
         constexpr int M = N / R;

@@ -146,6 +146,21 @@ int disco_fused_fwd(const disco_psi* psi, const void* x, int x_dtype,
 int disco_fused_is_spectral(const disco_psi* psi, int x_dtype, int32_t Ci, int32_t Co,
                             int32_t groups);
 
+/* Per-kernel timing, for benchmarks and profiling (not part of the pages'
+ * method).  With enable != 0, every kernel the library launches from then on
+ * is bracketed by a pair of HIP events recorded on its launch stream; with 0,
+ * no further events are recorded.  Always returns DISCO_OK. */
+int disco_kernel_timing(int enable);
+
+/* Drains the recorded event pairs (waiting for each to complete) into totals
+ * per kernel, in order of first launch: kernel i's name is the i-th
+ * NUL-terminated string packed into names[0 .. names_len), total_ms[i] its
+ * summed event time and launches[i] its launch count.  Returns the number of
+ * kernels (0 if nothing was recorded), or DISCO_EINVAL if the buffers are too
+ * small (the records are then discarded), or DISCO_EHIP. */
+int disco_kernel_timing_read(char* names, int32_t names_len, double* total_ms,
+                             int64_t* launches, int32_t max_kernels);
+
 /* Message for the last failed call on this thread ("" if none). */
 const char* disco_last_error(void);
 

@@ -75,6 +75,9 @@ def _load():
         "disco_fused_fwd": (ctypes.c_int, [P, P, ctypes.c_int, P, ctypes.c_int, P, P,
                                            ctypes.c_int, I32, I32, I32, I32, P]),
         "disco_fused_is_spectral": (ctypes.c_int, [P, ctypes.c_int, I32, I32, I32]),
+        "disco_kernel_timing": (ctypes.c_int, [ctypes.c_int]),
+        "disco_kernel_timing_read": (ctypes.c_int, [ctypes.c_char_p, I32, ctypes.POINTER(D),
+                                                    ctypes.POINTER(I64), I32]),
         "disco_last_error": (ctypes.c_char_p, []),
         "disco_version": (ctypes.c_char_p, []),
     }
@@ -88,7 +91,8 @@ def _load():
 _lib = _load()
 EXPORTED = ("disco_psi_build", "disco_psi_query", "disco_psi_export", "disco_psi_to_device",
             "disco_psi_free", "disco_contract", "disco_einsum", "disco_fused_fwd",
-            "disco_fused_is_spectral", "disco_last_error", "disco_version")
+            "disco_fused_is_spectral", "disco_kernel_timing", "disco_kernel_timing_read",
+            "disco_last_error", "disco_version")
 
 
 def version() -> str:
@@ -161,7 +165,9 @@ class Psi:
 
     def __del__(self):
         h = getattr(self, "_h", None)
-        if h is not None and h.value:
+        # at interpreter exit the module's globals may already be cleared:
+        # the process is ending and the handle goes with it
+        if h is not None and h.value and _lib is not None:
             _lib.disco_psi_free(h)
             self._h = ctypes.c_void_p(0)
 
@@ -281,6 +287,30 @@ def fused_is_spectral(psi: Psi, x_dtype, Ci: int, Co: int, groups: int = 1) -> b
     if rc < 0:
         _check(rc, "fused_is_spectral")
     return rc == 1
+
+
+def kernel_timing(enable: bool) -> None:
+    """Start (True) or stop (False) recording a HIP event pair around every
+    kernel the library launches, on its launch stream."""
+    _check(_lib.disco_kernel_timing(1 if enable else 0), "kernel_timing")
+
+
+def kernel_timing_read(max_kernels: int = 64) -> dict:
+    """Drain the recorded events: {kernel name: (total milliseconds, launches)},
+    in order of first launch.  Waits for the recorded launches to finish."""
+    names = ctypes.create_string_buffer(64 * max_kernels)
+    tot = (ctypes.c_double * max_kernels)()
+    cnt = (ctypes.c_int64 * max_kernels)()
+    n = _lib.disco_kernel_timing_read(names, len(names), tot, cnt, max_kernels)
+    if n < 0:
+        _check(n, "kernel_timing_read")
+    out, off = {}, 0
+    raw = names.raw
+    for i in range(n):
+        end = raw.index(b"\0", off)
+        out[raw[off:end].decode()] = (tot[i], cnt[i])
+        off = end + 1
+    return out
 
 
 def fused_fwd(psi: Psi, x, w, groups: int = 1, bias=None, y=None, out_dtype=None, stream=None):

@@ -26,6 +26,7 @@ SOURCES = [
     "kernels_fused_mfma.hip",
     "kernels_spectral.hip",
     "spectral_host.cpp",
+    "kernel_timing.cpp",
 ]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

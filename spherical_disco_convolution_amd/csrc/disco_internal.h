@@ -2,6 +2,8 @@
 // HIP kernel launchers.  Not part of the public ABI.
 #pragma once
 
+#include <hip/hip_runtime_api.h>
+
 #include <cstdint>
 #include <string>
 #include <vector>
@@ -112,5 +114,23 @@ int launch_fused(const disco_psi* psi, const void* x, int dtype, const void* w,
                  void* stream);
 // 1 if disco_fused_fwd takes the longitude-spectral path for these arguments
 int fused_spectral_eligible(const disco_psi* psi, int x_dtype, int Ci, int Co, int groups);
+
+// Scope around one kernel launch: while disco_kernel_timing(1) is in effect,
+// records a HIP event on the launch stream at construction and at
+// destruction, for disco_kernel_timing_read.  The name must be a string
+// literal.
+class KernelTimer {
+  public:
+    KernelTimer(const char* name, hipStream_t st);
+    ~KernelTimer();
+    KernelTimer(const KernelTimer&) = delete;
+    KernelTimer& operator=(const KernelTimer&) = delete;
+
+  private:
+    const char* name_;
+    hipStream_t st_;
+    hipEvent_t start_ = nullptr, stop_ = nullptr;
+    bool armed_ = false;
+};
 
 }  // namespace disco

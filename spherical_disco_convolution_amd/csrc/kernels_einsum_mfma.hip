@@ -314,12 +314,15 @@ int launch_einsum_mfma_bf16(const void* xk, const void* w, const float* bias, vo
 #define DISCO_ES(BMV, TT)                                                                        \
     hipLaunchKernelGGL((einsum_stream_bf16<BMV, TT>), sgrid, dim3(512), 0, st, X, Wt, bias, (TT*)y, \
                        Ci, Co, groups, K, HW)
-        if (cog == 128) {
-            if (y_dtype == DISCO_F32) DISCO_ES(128, float);
-            else DISCO_ES(128, bf16_t);
-        } else {
-            if (y_dtype == DISCO_F32) DISCO_ES(64, float);
-            else DISCO_ES(64, bf16_t);
+        {
+            KernelTimer timer("einsum_stream_bf16", st);
+            if (cog == 128) {
+                if (y_dtype == DISCO_F32) DISCO_ES(128, float);
+                else DISCO_ES(128, bf16_t);
+            } else {
+                if (y_dtype == DISCO_F32) DISCO_ES(64, float);
+                else DISCO_ES(64, bf16_t);
+            }
         }
 #undef DISCO_ES
         hipError_t e = hipGetLastError();
@@ -329,6 +332,7 @@ int launch_einsum_mfma_bf16(const void* xk, const void* w, const float* bias, vo
     }
     const int BM = cog > 64 ? 128 : 64;
     dim3 grid((HW + BN - 1) / BN, (cog + BM - 1) / BM, B * groups);
+    KernelTimer timer("einsum_mfma_bf16", st);
     if (BM == 128) {
         if (y_dtype == DISCO_F32)
             hipLaunchKernelGGL((einsum_mfma_bf16<128, float>), grid, dim3(256), 0, st, X, Wt, bias,

@@ -750,8 +750,11 @@ int try_launch_fused_mfma(const disco_psi* psi, const void* x, const void* w, co
         return 1;
     }
     u32x4* wf = static_cast<u32x4*>(wsp);
-    hipLaunchKernelGGL(prep_weight_frags, dim3((unsigned)((nfrag + 255) / 256)), dim3(256), 0, st,
-                       static_cast<const bf16_t*>(w), wf, Ci, Co, h.K);
+    {
+        KernelTimer timer("prep_weight_frags", st);
+        hipLaunchKernelGGL(prep_weight_frags, dim3((unsigned)((nfrag + 255) / 256)), dim3(256), 0,
+                           st, static_cast<const bf16_t*>(w), wf, Ci, Co, h.K);
+    }
     const bf16_t* X = static_cast<const bf16_t*>(x);
     // one persistent workgroup per CU: 32 per XCD
     int dev = 0, ncu = 256;
@@ -763,6 +766,8 @@ int try_launch_fused_mfma(const disco_psi* psi, const void* x, const void* w, co
 #define DISCO_FM(SS, CC, TT)                                                                 \
     hipLaunchKernelGGL((fused_mfma<SS, CC, TT>), grid, dim3(kThreads), 0, st, X, wf, bias, (TT*)y, \
                        dinfo, taps, B, Ci, h.K, D.nlat_in, D.nlon_in, D.nlat_out, D.nlon_out)
+    {
+    KernelTimer timer("fused_mfma", st);
     const bool f32 = y_dtype == DISCO_F32;
     if (Co == 128) {
         if (S == 1) { if (f32) DISCO_FM(1, 128, float); else DISCO_FM(1, 128, bf16_t); }
@@ -770,6 +775,7 @@ int try_launch_fused_mfma(const disco_psi* psi, const void* x, const void* w, co
     } else {
         if (S == 1) { if (f32) DISCO_FM(1, 64, float); else DISCO_FM(1, 64, bf16_t); }
         else        { if (f32) DISCO_FM(2, 64, float); else DISCO_FM(2, 64, bf16_t); }
+    }
     }
 #undef DISCO_FM
     hipError_t le = hipGetLastError();
@@ -815,8 +821,11 @@ int try_launch_contract_mfma(const disco_psi* psi, const void* x, void* xk, int 
     hipLaunchKernelGGL((fused_mfma<SS, 128, bf16_t, true>), grid, dim3(kThreads), 0, st, X,       \
                        nullptr, nullptr, XK, dinfo, taps, B, C, h.K, D.nlat_in, D.nlon_in,         \
                        D.nlat_out, D.nlon_out)
-    if (S == 1) DISCO_CM(1);
-    else DISCO_CM(2);
+    {
+        KernelTimer timer("contract_mfma", st);
+        if (S == 1) DISCO_CM(1);
+        else DISCO_CM(2);
+    }
 #undef DISCO_CM
     hipError_t le = hipGetLastError();
     if (le != hipSuccess) {

@@ -273,6 +273,7 @@ int contract_kp(const disco_psi* psi, const void* x, void* xk, int B, int C, hip
     hipLaunchKernelGGL((contract_kernel<TX, TO, KP, Q>), grid, dim3(kThreads), lds, st,           \
                        (const TX*)x, (TO*)xk, d.win_ptr, d.windows, d.vals, C, h.K, D.nlat_in,    \
                        D.nlon_in, D.nlat_out, D.nlon_out, h.stride)
+    KernelTimer timer("contract_kernel", st);
     switch (QR) {
         case 1: DISCO_CONTRACT_LAUNCH(1); break;
         case 2: DISCO_CONTRACT_LAUNCH(2); break;
@@ -340,6 +341,7 @@ int einsum_valu_launch(const void* xk, const void* w, const float* bias, void* y
 #define DISCO_EINSUM_LAUNCH(N)                                                                   \
     hipLaunchKernelGGL((einsum_valu<TI, TY, N>), grid, dim3(kThreads), 0, st, (const TI*)xk,     \
                        (const TI*)w, bias, (TY*)y, Ci, Co, groups, K, HW)
+    KernelTimer timer("einsum_valu", st);
     switch (cot) {
         case 16: DISCO_EINSUM_LAUNCH(16); break;
         case 8: DISCO_EINSUM_LAUNCH(8); break;
@@ -386,6 +388,7 @@ int fused_generic_launch(const disco_psi* psi, const void* x, const void* w, con
     if (lds > 64 * 1024)
         return set_error(DISCO_EUNSUPPORTED, "Ci/groups * K too large for the generic fused kernel");
     dim3 grid((D.nlon_out + QT - 1) / QT, D.nlat_out, B * groups);
+    KernelTimer timer("fused_generic", st);
     hipLaunchKernelGGL((fused_generic<T, TY, KP>), grid, dim3(kThreads), lds, st, (const T*)x,
                        (const T*)w, bias, (TY*)y, d.win_ptr, d.windows, d.vals, Ci, Co, groups,
                        h.K, D.nlat_in, D.nlon_in, D.nlat_out, D.nlon_out, h.stride, QT);
@@ -408,6 +411,7 @@ int fused_depthwise_launch(const disco_psi* psi, const void* x, const void* w, c
                        (const T*)x, (const T*)w, bias, (TY*)y, d.win_ptr, d.windows, d.vals, Ci, \
                        Co, groups, h.K, D.nlat_in, D.nlon_in, D.nlat_out, D.nlon_out, h.stride,  \
                        d.max_width)
+    KernelTimer timer("fused_depthwise", st);
     switch (QR) {
         case 1: DISCO_DW_LAUNCH(1); break;
         case 2: DISCO_DW_LAUNCH(2); break;

@@ -1085,8 +1085,11 @@ int try_launch_fused_spectral(const disco_psi* psi, const void* x, const void* w
     auto reg_grid = [](int64_t rows, int rw) { return dim3((unsigned)((rows + rw - 1) / rw)); };
 
     const size_t nwp = (size_t)Co * Ci * 8;
-    hipLaunchKernelGGL(spec_prep_w, dim3((unsigned)((nwp + 255) / 256)), dim3(256), 0, st,
-                       static_cast<const bf16_t*>(w), wpd, Co, Ci, K);
+    {
+        KernelTimer timer("spec_prep_w", st);
+        hipLaunchKernelGGL(spec_prep_w, dim3((unsigned)((nwp + 255) / 256)), dim3(256), 0, st,
+                           static_cast<const bf16_t*>(w), wpd, Co, Ci, K);
+    }
     const size_t fft_lds = (size_t)(kFftRows + 1) * H * sizeof(float2);
     const int64_t xrows = (int64_t)B * Ci * D.nlat_in;
     const uint32_t* x32 = static_cast<const uint32_t*>(x);
@@ -1094,6 +1097,8 @@ int try_launch_fused_spectral(const disco_psi* psi, const void* x, const void* w
     hipLaunchKernelGGL((spec_rfft_reg<H1, H2, RW>),                                            \
                        reg_grid(xrows, RW),                                                    \
                        dim3(kRegThreads), 0, st, x32, xh, xrows)
+    {
+    KernelTimer timer("spec_rfft", st);
     if (reg && H == 720) {
         DISCO_RF(16, 45, 4);
     } else if (reg && H == 360) {
@@ -1104,6 +1109,7 @@ int try_launch_fused_spectral(const disco_psi* psi, const void* x, const void* w
         hipLaunchKernelGGL(spec_rfft, dim3((unsigned)((xrows + kFftRows - 1) / kFftRows)),
                            dim3(kFftThreads), fft_lds, st, static_cast<const bf16_t*>(x), xh, N,
                            MP, xrows, pl);
+    }
     }
 #undef DISCO_RF
     // bands of output rows, one per XCD; GX workgroups per band, at most the
@@ -1128,10 +1134,13 @@ int try_launch_fused_spectral(const disco_psi* psi, const void* x, const void* w
         case 7: DISCO_SM(CC, 7); break;                                                      \
         default: DISCO_SM(CC, 8); break;                                                     \
     }
-    if (Co == 128) {
-        DISCO_SM_K(128)
-    } else {
-        DISCO_SM_K(64)
+    {
+        KernelTimer timer("spec_mfma", st);
+        if (Co == 128) {
+            DISCO_SM_K(128)
+        } else {
+            DISCO_SM_K(64)
+        }
     }
 #undef DISCO_SM_K
 #undef DISCO_SM
@@ -1149,6 +1158,8 @@ int try_launch_fused_spectral(const disco_psi* psi, const void* x, const void* w
     } else {                                   \
         DISCO_IR(H1, H2, RW, bf16_t);          \
     }
+    {
+    KernelTimer timer("spec_irfft", st);
     if (reg && H == 720) {
         DISCO_IR_T(16, 45, 4)
     } else if (reg && H == 360) {
@@ -1163,6 +1174,7 @@ int try_launch_fused_spectral(const disco_psi* psi, const void* x, const void* w
         hipLaunchKernelGGL(spec_irfft<bf16_t>, igrid, dim3(kFftThreads), fft_lds, st,
                            reinterpret_cast<const uint32_t*>(yh), static_cast<bf16_t*>(y), bias, N,
                            MP, Co, D.nlat_out, yrows, pl);
+    }
 #undef DISCO_IR_T
 #undef DISCO_IR
     hipError_t le = hipGetLastError();

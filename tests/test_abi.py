@@ -149,3 +149,15 @@ def test_handle_without_device_copy_is_rejected_or_no_gpu():
     rc = L.disco_contract(p.handle, fake, 0, fake, 0, 1, 1, None)
     assert rc in (sdc.DISCO_EINVAL, sdc.DISCO_EHIP)
     assert L.disco_last_error().decode()
+
+
+def test_kernel_timing_host_logic():
+    # with nothing launched, a read drains nothing; bad buffers are argument errors
+    assert sdc._lib.disco_kernel_timing(1) == 0
+    assert sdc.kernel_timing_read() == {}
+    assert sdc._lib.disco_kernel_timing(0) == 0
+    tot = (ctypes.c_double * 1)()
+    cnt = (ctypes.c_int64 * 1)()
+    assert sdc._lib.disco_kernel_timing_read(None, 0, tot, cnt, -1) == sdc.DISCO_EINVAL
+    assert sdc._lib.disco_kernel_timing_read(None, 16, tot, cnt, 1) == sdc.DISCO_EINVAL
+    assert sdc._lib.disco_kernel_timing_read(None, 0, None, None, 0) == 0

@@ -211,3 +211,26 @@ def test_register_transforms(sdc, wl, monkeypatch):
     for out_dtype in (torch.float32, torch.bfloat16):
         yb = sdc.fused_fwd(psi, xd, wd, bias=bd, out_dtype=out_dtype)[..., cols].float().cpu().numpy()
         assert rel_l2(yb, refb) <= TOL_BF16
+
+
+def test_kernel_timing_names_the_spectral_kernels(sdc, monkeypatch):
+    monkeypatch.delenv("DISCO_FUSED_PATH", raising=False)
+    wl = SPECTRAL[1]
+    x, w = _prepare(wl)
+    psi = _psi(sdc, wl)
+    xd, wd = _dev(x), _dev(w)
+    sdc.fused_fwd(psi, xd, wd)            # not recorded
+    sdc.kernel_timing(True)
+    try:
+        for _ in range(3):
+            sdc.fused_fwd(psi, xd, wd)
+        t = sdc.kernel_timing_read()
+    finally:
+        sdc.kernel_timing(False)
+    _say("kernel timing", t)
+    assert list(t) == ["spec_prep_w", "spec_rfft", "spec_mfma", "spec_irfft"]
+    for name, (ms, n) in t.items():
+        assert n == 3 and ms > 0.0, name
+    sdc.fused_fwd(psi, xd, wd)            # timing off again: nothing recorded
+    torch.cuda.synchronize()
+    assert sdc.kernel_timing_read() == {}

@@ -16,6 +16,10 @@
 // the 16-byte reads of 16 consecutive rows hit distinct banks.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+#include <cstdlib>
+#include <cstring>
+
 #include "disco_internal.h"
 #include "kernels_common.h"
 
@@ -297,6 +301,242 @@ __global__ __launch_bounds__(512) void einsum_stream_bf16(const bf16_t* __restri
     }
 }
 
+// --------------------------------------------------------------------------
+// Ring-pipelined variant for one channel group of 64 or 128 output channels
+// (Kd % 32 == 0, HW % 8 == 0, HW >= 256): one workgroup per CU walks its
+// output tiles (256 points by every output channel) as a single stream of
+// 32-kappa steps.  Two copy waves move each step's operands -- the weights
+// [BM][32] and the X_K block [32 kappa][256 points] -- from global memory
+// straight into a ring of NS LDS stages (global_load_lds), NS - 1 steps ahead
+// of the eight matrix-core waves and across tile boundaries; one barrier per
+// step hands a stage over.  Only the copy waves wait on vector-memory counts,
+// and they issue nothing else, so every wait is exact; the matrix-core waves
+// only read LDS and store results.
+//
+// The X_K block stays as it is in memory, points contiguous, its 16-byte
+// chunks permuted within a row by chunk ^ 4 (kappa & 3); ds_read_b64_tr_b16
+// then hands each lane four kappa of one point, two such reads one operand
+// fragment.  The weight rows (64 bytes) hold their chunks at chunk ^ ((row >> 2) & 3).
+// Both permutations make the operand reads of a half-wave cover all LDS banks.
+//
+// The last tile of a row of points is shifted back to end at HW, so every
+// tile is whole; its leading points repeat columns of the tile before, and
+// both write the same values.
+// --------------------------------------------------------------------------
+constexpr int RN = 256;                    // output points per tile
+constexpr int RK = 32;                     // kappa per step
+constexpr int RB_BYTES = RK * RN * 2;      // X_K block of a stage: 16 KiB
+constexpr int R_COPY_WAVES = 2;
+constexpr int R_MMA_WAVES = 8;
+constexpr int R_THREADS = 64 * (R_COPY_WAVES + R_MMA_WAVES);
+
+template <int BM>
+struct RingCfg {
+    static constexpr int A_BYTES = BM * RK * 2;           // weight slice: 8 / 4 KiB
+    static constexpr int STAGE = A_BYTES + RB_BYTES;      // 24 / 20 KiB
+    static constexpr int NS = BM == 128 ? 6 : 7;          // 144 / 140 KiB of LDS
+    static constexpr int A_INS = A_BYTES / 1024;          // copy instructions per step
+    static constexpr int B_INS = RB_BYTES / 1024;
+    static constexpr int OPS = (A_INS + B_INS) / R_COPY_WAVES;   // per copy wave
+    static constexpr int WNW = BM == 128 ? 4 : 8;         // matrix-core waves along the points
+    static constexpr int WTN = RN / WNW;                  // 64 / 32 points per wave
+    static constexpr int NT = WTN / 32;
+    static_assert((A_INS + B_INS) % R_COPY_WAVES == 0, "copy split");
+    static_assert(OPS * (NS - 2) < 64, "vmcnt range");
+};
+
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16_t lds_v4i16;
+typedef __attribute__((address_space(3))) bf16x8_t lds_bf16x8;
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
+__device__ __forceinline__ void store4(float* p, float a, float b, float c, float d) {
+    *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
+}
+__device__ __forceinline__ void store4(bf16_t* p, float a, float b, float c, float d) {
+    uint2 v;
+    v.x = (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
+    v.y = (uint32_t)f32_to_bf16(c) | ((uint32_t)f32_to_bf16(d) << 16);
+    *reinterpret_cast<uint2*>(p) = v;
+}
+
+template <int BM, typename TY>
+__global__ __launch_bounds__(R_THREADS) void einsum_ring_bf16(const bf16_t* __restrict__ xk,
+                                                              const bf16_t* __restrict__ w,
+                                                              const float* __restrict__ bias,
+                                                              TY* __restrict__ y, int Kd, int HW,
+                                                              int ntiles) {
+    using C = RingCfg<BM>;
+    constexpr int NS = C::NS;
+    __shared__ __attribute__((aligned(1024))) uint8_t ring[NS * C::STAGE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = uniform(tid >> 6);
+    const int nk = Kd / RK;
+    const int ntn = (HW + RN - 1) / RN;
+    const int G = gridDim.x;
+    const int my_tiles = (int)blockIdx.x < ntiles ? (ntiles - 1 - (int)blockIdx.x) / G + 1 : 0;
+    const int Q = my_tiles * nk;   // steps of this workgroup
+    if (Q == 0) return;
+
+    if (wave >= R_MMA_WAVES) {
+        // ---------------- copy waves ----------------
+        const int cw = wave - R_MMA_WAVES;
+        const uint32_t ring_lds =
+            __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_void*)&ring[0]);
+        // the wave takes copy instructions cw, cw + 2, ...: its first A_INS / 2
+        // move weight rows 16 i .. 16 i + 15, the rest X_K rows 2 j, 2 j + 1
+        // (j = i - A_INS).  This lane's source offsets (elements) and LDS
+        // offsets of each:
+        constexpr int OA = C::A_INS / R_COPY_WAVES;
+        int64_t src_off[C::OPS];
+        uint32_t dst_off[C::OPS];
+#pragma unroll
+        for (int o = 0; o < C::OPS; ++o) {
+            const int i = cw + R_COPY_WAVES * o;
+            if (o < OA) {
+                const int P = 64 * i + lane;   // 16-byte slot of the weight slice
+                const int row = P >> 2, c = (P & 3) ^ ((row >> 2) & 3);
+                src_off[o] = (int64_t)row * Kd + 8 * c;
+                dst_off[o] = (uint32_t)(1024 * i);
+            } else {
+                const int P = 64 * (i - C::A_INS) + lane;   // 16-byte slot of the X_K block
+                const int kap = P >> 5, c = (P & 31) ^ (4 * (kap & 3));
+                src_off[o] = (int64_t)kap * HW + 8 * c;
+                dst_off[o] = (uint32_t)(C::A_BYTES + 1024 * (i - C::A_INS));
+            }
+        }
+        // issue cursor: step ik of tile ti, ring stage iq
+        int ik = 0, ti = blockIdx.x, iq = 0;
+        int64_t xbase = 0;
+        auto tile_base = [&]() {
+            const int bb = ti / ntn, n0 = min((ti % ntn) * RN, HW - RN);
+            xbase = (int64_t)bb * Kd * HW + n0;
+        };
+        tile_base();
+        auto issue = [&]() {
+            const uint32_t st = ring_lds + (uint32_t)(iq * C::STAGE);
+            // past the last step every lane reloads 16 bytes of the weights
+            // (cached), so that every step issues the same number of operations
+            const bool live = ti < ntiles;
+            const bf16_t* pa = live ? w + (int64_t)ik * RK : w;
+            const bf16_t* pb = live ? xk + xbase + (int64_t)ik * RK * HW : w;
+#pragma unroll
+            for (int o = 0; o < C::OPS; ++o) {
+                const int64_t off = live ? src_off[o] : (int64_t)lane * 8;
+                dma_lds16((o < OA ? pa : pb) + off, st + dst_off[o]);
+            }
+            if (++iq == NS) iq = 0;
+            if (++ik == nk) {
+                ik = 0;
+                ti += G;
+                if (ti < ntiles) tile_base();
+            }
+        };
+#pragma unroll 1
+        for (int q = 0; q < NS - 1; ++q) issue();
+#pragma unroll 1
+        for (int q = 0; q < Q; ++q) {
+            wait_vmcnt<C::OPS*(NS - 2)>();   // this wave's part of step q has landed
+            __syncthreads();
+            issue();                         // step q + NS - 1, into the stage read at step q - 1
+        }
+        wait_vmcnt<0>();   // no copy may land after the workgroup ends
+        return;
+    }
+
+    // ---------------- matrix-core waves ----------------
+    const int l32 = lane & 31, lg = lane >> 5;
+    const int wm = wave / C::WNW, wn = wave % C::WNW;
+    // weight fragment (second operand): row m, kappa 8 lg + 16 ks .. + 7
+    uint32_t aoff[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+        const int m = wm * 64 + l32;
+        aoff[ks] = (uint32_t)(m * 64 + 16 * ((2 * ks + lg) ^ ((l32 >> 2) & 3)));
+    }
+    // X_K fragment (first operand) by two transposed reads: within each
+    // 16-lane group, lane s reads kappa row 8 lg + 4 h + s / 4, points
+    // 16 (group & 1) + 4 (s & 3) .. + 3 of the 32-point tile
+    uint32_t boff[C::NT];
+    {
+        const int s = lane & 15, g = lane >> 4;
+        const int kap = 8 * (g >> 1) + (s >> 2);
+#pragma unroll
+        for (int c = 0; c < C::NT; ++c) {
+            const int n = wn * C::WTN + 32 * c + 16 * (g & 1) + 4 * (s & 3);
+            boff[c] = (uint32_t)(C::A_BYTES + kap * 512 + 16 * ((n >> 3) ^ (4 * (kap & 3))) +
+                                 2 * (n & 7));
+        }
+    }
+    float bv[2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a) bv[a] = bias ? bias[wm * 64 + 32 * a + l32] : 0.0f;
+    wait_vmcnt<0>();   // only stores are outstanding from here on
+
+    floatx16 acc[2][C::NT];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int c = 0; c < C::NT; ++c)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[a][c][e] = 0.0f;
+
+    const lds_u8* ring_p = (const lds_u8*)&ring[0];
+    int ck = 0, ti = blockIdx.x;
+#pragma unroll 1
+    for (int q = 0; q < Q; ++q) {
+        __syncthreads();
+        const lds_u8* st = ring_p + (q % NS) * C::STAGE;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            bf16x8_t af[2], bfr[C::NT];
+#pragma unroll
+            for (int a = 0; a < 2; ++a)
+                af[a] = *(const lds_bf16x8*)(st + aoff[ks] + a * 32 * 64);
+#pragma unroll
+            for (int c = 0; c < C::NT; ++c) {
+                const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_v4i16*)(st + boff[c] + (16 * ks) * 512));
+                const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_v4i16*)(st + boff[c] + (16 * ks + 4) * 512));
+                const auto v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                bfr[c] = __builtin_bit_cast(bf16x8_t, v);
+            }
+#pragma unroll
+            for (int a = 0; a < 2; ++a)
+#pragma unroll
+                for (int c = 0; c < C::NT; ++c)
+                    acc[a][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[c], af[a], acc[a][c],
+                                                                       0, 0, 0);
+        }
+        if (++ck == nk) {
+            // lane holds row m = 32 a + lane % 32 and points 8 (e / 4) + 4 (lane / 32) + e % 4
+            const int bb = ti / ntn, n0 = min((ti % ntn) * RN, HW - RN);
+            TY* Y = y + (size_t)bb * BM * HW;
+#pragma unroll
+            for (int a = 0; a < 2; ++a) {
+                const int m = wm * 64 + 32 * a + l32;
+#pragma unroll
+                for (int c = 0; c < C::NT; ++c) {
+#pragma unroll
+                    for (int qd = 0; qd < 4; ++qd) {
+                        const int n = n0 + wn * C::WTN + 32 * c + 8 * qd + 4 * lg;
+                        const float v0 = acc[a][c][4 * qd] + bv[a], v1 = acc[a][c][4 * qd + 1] + bv[a],
+                                    v2 = acc[a][c][4 * qd + 2] + bv[a], v3 = acc[a][c][4 * qd + 3] + bv[a];
+                        store4(Y + (size_t)m * HW + n, v0, v1, v2, v3);
+                    }
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) acc[a][c][e] = 0.0f;
+                }
+            }
+            ck = 0;
+            ti += G;
+        }
+    }
+}
+
 }  // namespace
 
 int launch_einsum_mfma_bf16(const void* xk, const void* w, const float* bias, void* y, int y_dtype,
@@ -308,6 +548,38 @@ int launch_einsum_mfma_bf16(const void* xk, const void* w, const float* bias, vo
                        ((reinterpret_cast<uintptr_t>(xk) & 3) == 0);
     const bf16_t* X = static_cast<const bf16_t*>(xk);
     const bf16_t* Wt = static_cast<const bf16_t*>(w);
+    // DISCO_EINSUM_PATH=stream selects the double-buffered kernel below
+    const char* ev = std::getenv("DISCO_EINSUM_PATH");
+    const bool ring_ok = !(ev && std::strcmp(ev, "stream") == 0);
+    const int ring_ns = cog == 128 ? RingCfg<128>::NS : RingCfg<64>::NS;
+    if (ring_ok && groups == 1 && (cog == 128 || cog == 64) && Kd % RK == 0 &&
+        Kd / RK >= ring_ns - 1 && HW % 8 == 0 && HW >= RN &&
+        (reinterpret_cast<uintptr_t>(w) & 15) == 0 && (reinterpret_cast<uintptr_t>(xk) & 15) == 0 &&
+        (reinterpret_cast<uintptr_t>(y) & 15) == 0) {
+        int dev = 0, ncu = 256;
+        if (hipGetDevice(&dev) == hipSuccess)
+            (void)hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+        const int ntiles = B * ((HW + RN - 1) / RN);
+        const int grid = std::max(1, std::min(ntiles, ncu));   // one workgroup per CU (LDS)
+#define DISCO_ER(BMV, TT)                                                                         \
+    hipLaunchKernelGGL((einsum_ring_bf16<BMV, TT>), dim3(grid), dim3(R_THREADS), 0, st, X, Wt, bias, \
+                       (TT*)y, Kd, HW, ntiles)
+        {
+            KernelTimer timer("einsum_ring_bf16", st);
+            if (cog == 128) {
+                if (y_dtype == DISCO_F32) DISCO_ER(128, float);
+                else DISCO_ER(128, bf16_t);
+            } else {
+                if (y_dtype == DISCO_F32) DISCO_ER(64, float);
+                else DISCO_ER(64, bf16_t);
+            }
+        }
+#undef DISCO_ER
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return set_error(DISCO_EHIP, "einsum_ring launch failed: %s", hipGetErrorString(e));
+        return DISCO_OK;
+    }
     if ((cog == 128 || cog == 64) && Kd % SK == 0 && HW % 8 == 0 &&
         (reinterpret_cast<uintptr_t>(w) & 15) == 0 && (reinterpret_cast<uintptr_t>(xk) & 15) == 0) {
         dim3 sgrid((HW + SN - 1) / SN, B * groups);

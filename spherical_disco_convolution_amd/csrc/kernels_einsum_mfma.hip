@@ -350,14 +350,9 @@ typedef __attribute__((address_space(3))) v4i16_t lds_v4i16;
 typedef __attribute__((address_space(3))) bf16x8_t lds_bf16x8;
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
-__device__ __forceinline__ void store4(float* p, float a, float b, float c, float d) {
-    *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
-}
-__device__ __forceinline__ void store4(bf16_t* p, float a, float b, float c, float d) {
-    uint2 v;
-    v.x = (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
-    v.y = (uint32_t)f32_to_bf16(c) | ((uint32_t)f32_to_bf16(d) << 16);
-    *reinterpret_cast<uint2*>(p) = v;
+__device__ __forceinline__ void store_nt(float* p, float v) { __builtin_nontemporal_store(v, p); }
+__device__ __forceinline__ void store_nt(bf16_t* p, float v) {
+    __builtin_nontemporal_store(f32_to_bf16(v), p);
 }
 
 template <int BM, typename TY>
@@ -369,6 +364,7 @@ __global__ __launch_bounds__(R_THREADS) void einsum_ring_bf16(const bf16_t* __re
     using C = RingCfg<BM>;
     constexpr int NS = C::NS;
     __shared__ __attribute__((aligned(1024))) uint8_t ring[NS * C::STAGE];
+    __shared__ __attribute__((aligned(16))) float bias_s[BM];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -470,10 +466,8 @@ __global__ __launch_bounds__(R_THREADS) void einsum_ring_bf16(const bf16_t* __re
                                  2 * (n & 7));
         }
     }
-    float bv[2];
-#pragma unroll
-    for (int a = 0; a < 2; ++a) bv[a] = bias ? bias[wm * 64 + 32 * a + l32] : 0.0f;
-    wait_vmcnt<0>();   // only stores are outstanding from here on
+    // bias rows in LDS (visible after the first step's barrier)
+    for (int m = tid; m < BM; m += 64 * R_MMA_WAVES) bias_s[m] = bias ? bias[m] : 0.0f;
 
     floatx16 acc[2][C::NT];
 #pragma unroll
@@ -508,28 +502,36 @@ __global__ __launch_bounds__(R_THREADS) void einsum_ring_bf16(const bf16_t* __re
             for (int a = 0; a < 2; ++a)
 #pragma unroll
                 for (int c = 0; c < C::NT; ++c)
-                    acc[a][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[c], af[a], acc[a][c],
+                    acc[a][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[a], bfr[c], acc[a][c],
                                                                        0, 0, 0);
         }
         if (++ck == nk) {
-            // lane holds row m = 32 a + lane % 32 and points 8 (e / 4) + 4 (lane / 32) + e % 4
+            // lane holds point lane % 32 and rows 8 (e / 4) + 4 (lane / 32) + e % 4
+            // of each 32 x 32 tile: a store instruction writes two whole
+            // 128-byte row segments.  Streaming (non-temporal) stores keep the
+            // results from displacing cached operands.
             const int bb = ti / ntn, n0 = min((ti % ntn) * RN, HW - RN);
             TY* Y = y + (size_t)bb * BM * HW;
 #pragma unroll
             for (int a = 0; a < 2; ++a) {
-                const int m = wm * 64 + 32 * a + l32;
 #pragma unroll
-                for (int c = 0; c < C::NT; ++c) {
+                for (int eq = 0; eq < 4; ++eq) {
+                    const int m0 = wm * 64 + 32 * a + 8 * eq + 4 * lg;
+                    const float4 bq = *reinterpret_cast<const float4*>(&bias_s[m0]);
 #pragma unroll
-                    for (int qd = 0; qd < 4; ++qd) {
-                        const int n = n0 + wn * C::WTN + 32 * c + 8 * qd + 4 * lg;
-                        const float v0 = acc[a][c][4 * qd] + bv[a], v1 = acc[a][c][4 * qd + 1] + bv[a],
-                                    v2 = acc[a][c][4 * qd + 2] + bv[a], v3 = acc[a][c][4 * qd + 3] + bv[a];
-                        store4(Y + (size_t)m * HW + n, v0, v1, v2, v3);
+                    for (int c = 0; c < C::NT; ++c) {
+                        const int n = n0 + wn * C::WTN + 32 * c + l32;
+                        TY* p = Y + (size_t)m0 * HW + n;
+                        store_nt(p, acc[a][c][4 * eq] + bq.x);
+                        store_nt(p + HW, acc[a][c][4 * eq + 1] + bq.y);
+                        store_nt(p + 2 * (size_t)HW, acc[a][c][4 * eq + 2] + bq.z);
+                        store_nt(p + 3 * (size_t)HW, acc[a][c][4 * eq + 3] + bq.w);
                     }
+                }
+#pragma unroll
+                for (int c = 0; c < C::NT; ++c)
 #pragma unroll
                     for (int e = 0; e < 16; ++e) acc[a][c][e] = 0.0f;
-                }
             }
             ck = 0;
             ti += G;

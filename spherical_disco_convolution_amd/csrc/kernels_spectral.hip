@@ -754,7 +754,6 @@ __global__ __launch_bounds__(kSpecThreads) __attribute__((amdgpu_waves_per_eu(2)
     const int wm = wave % WGM, wn = wave / WGM;
     const int nchunks = Ci / 32;
     const int f0 = wave * 8;
-    const size_t cstride = (size_t)32 * nlat_in * MP;   // one 32-channel chunk
     const size_t plane = (size_t)nlat_in * MP;
 
     // Item cursor: item n of this workgroup is l = slot + n GX of its band,
@@ -933,31 +932,41 @@ __global__ __launch_bounds__(kSpecThreads) __attribute__((amdgpu_waves_per_eu(2)
             if (cc == 0) dma_ps(nxt);
             dma_x();           // position p + 1 (the last position repeats at the end)
             request_next();    // rows of position p + 2
-#pragma unroll
-            for (int f = 0; f < 8; ++f) {
+            // one MFMA per frequency, pipelined by one: the product of
+            // frequency f + 1 is issued before frequency f's is converted and
+            // written, so the matrix-core latency is hidden behind the writes
+            auto window_mfma = [&](int f) {
                 const u32x4 a = {xa[0][f >> 2][f & 3], xa[1][f >> 2][f & 3], xa[2][f >> 2][f & 3],
                                  xa[3][f >> 2][f & 3]};
                 floatx16 d;
 #pragma unroll
                 for (int e = 0; e < 16; ++e) d[e] = 0.0f;
-                d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                            __builtin_bit_cast(bf16x8_t, bq[f]), d,
-                                                            0, 0, 0);
-                {
-                    // column (k, c) -> tile row 2 (f0 + f) + c, pairs (k, ci),
-                    // ci = 8 q + 4 lg + (0..3).  Columns KT <= k < 8 are written
-                    // but never read; lanes of columns k >= 8 (no tile block)
-                    // write the shared dump instead of branching around it.
-                    bf16_t* dst =
-                        l32 < 16 ? bt + (2 * (f0 + f) + (l32 & 1)) * kBts + (l32 >> 1) * kBkb + 4 * lg
-                                 : dump;
+                return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                               __builtin_bit_cast(bf16x8_t, bq[f]), d,
+                                                               0, 0, 0);
+            };
+            auto window_write = [&](const floatx16& d, int f) {
+                // column (k, c) -> tile row 2 (f0 + f) + c, pairs (k, ci),
+                // ci = 8 q + 4 lg + (0..3).  Columns KT <= k < 8 are written
+                // but never read; lanes of columns k >= 8 (no tile block)
+                // write the shared dump instead of branching around it.
+                bf16_t* dst =
+                    l32 < 16 ? bt + (2 * (f0 + f) + (l32 & 1)) * kBts + (l32 >> 1) * kBkb + 4 * lg
+                             : dump;
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const uint2 pk = make_uint2(pack_bf16x2(d[4 * q], d[4 * q + 1]),
-                                                    pack_bf16x2(d[4 * q + 2], d[4 * q + 3]));
-                        *reinterpret_cast<uint2*>(dst + 8 * q) = pk;
-                    }
+                for (int q = 0; q < 4; ++q) {
+                    const uint2 pk = make_uint2(pack_bf16x2(d[4 * q], d[4 * q + 1]),
+                                                pack_bf16x2(d[4 * q + 2], d[4 * q + 3]));
+                    *reinterpret_cast<uint2*>(dst + 8 * q) = pk;
                 }
+            };
+            floatx16 dcur = window_mfma(0);
+#pragma unroll
+            for (int f = 0; f < 8; ++f) {
+                floatx16 dnext;
+                if (f + 1 < 8) dnext = window_mfma(f + 1);
+                window_write(dcur, f);
+                if (f + 1 < 8) dcur = dnext;
             }
             __syncthreads();   // tile complete
             // ---- channel/basis GEMM over this chunk's 256 (k, ci) pairs ----

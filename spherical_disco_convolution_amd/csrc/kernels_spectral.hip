@@ -995,12 +995,17 @@ __global__ __launch_bounds__(kSpecThreads) __attribute__((amdgpu_waves_per_eu(2)
             wait_vmcnt<NKS>();
             __syncthreads();   // spectra of p + 1 in LDS; B tile free
         }
-        // ---- y_hat (bf16 (re, im) pairs): lane holds channel co = 32 wm + l32
-        // and columns 8 g + 4 lg + (0..3) of its 32-column tile (g = e / 4),
-        // i.e. four consecutive elements 2 m0 + column of the channel's row
-        // (the two lane halves write 16 contiguous bytes) ----
+        // ---- y_hat (bf16 (re, im) pairs), staged through the free B tile so
+        // that each store instruction writes whole 128-byte row segments.  The
+        // lane holds channel co = 32 wm + l32 and columns 8 g + 4 lg + (0..3)
+        // of its 32-column tile (g = e / 4); the staged tile is [co][64
+        // columns] with rows of YS elements.  The next position's window sum
+        // writes the B tile only after its first barrier, which every wave
+        // reaches after its reads here. ----
         {
-            bf16_t* yrow = yh + ((size_t)(b * CO + wm * 32 + l32) * nlat_out + j) * MP * 2 + 2 * m0;
+            constexpr int YS = 72;   // 144-byte rows: 16-byte aligned, spread over the banks
+            static_assert(CO * YS <= 64 * kBts, "staged y_hat tile fits the B tile");
+            const int co = wm * 32 + l32;
 #pragma unroll
             for (int t = 0; t < NTW; ++t) {
                 const int c0 = wn * (64 / WGN) + t * 32 + 4 * lg;
@@ -1008,8 +1013,18 @@ __global__ __launch_bounds__(kSpecThreads) __attribute__((amdgpu_waves_per_eu(2)
                 for (int g = 0; g < 4; ++g) {
                     const uint2 pk = make_uint2(pack_bf16x2(acc[t][4 * g], acc[t][4 * g + 1]),
                                                 pack_bf16x2(acc[t][4 * g + 2], acc[t][4 * g + 3]));
-                    *reinterpret_cast<uint2*>(yrow + c0 + 8 * g) = pk;
+                    *reinterpret_cast<uint2*>(bt + co * YS + c0 + 8 * g) = pk;
                 }
+            }
+            __syncthreads();   // staged tile complete
+            // 16 bytes per lane: eight lanes per channel row of 64 columns
+            bf16_t* ybase = yh + ((size_t)b * CO * nlat_out + j) * MP * 2 + 2 * m0;
+#pragma unroll
+            for (int it = 0; it < CO * 8 / kSpecThreads; ++it) {
+                const int sl = tid + kSpecThreads * it;
+                const int row = sl >> 3, pc = sl & 7;
+                const u32x4 v = *reinterpret_cast<const u32x4*>(bt + row * YS + 8 * pc);
+                *reinterpret_cast<u32x4*>(ybase + (size_t)row * nlat_out * MP * 2 + 8 * pc) = v;
             }
         }
         cur = nxt;

@@ -114,7 +114,12 @@ int disco_contract(const disco_psi* psi, const void* x, int x_dtype,
  *   y[b,co,j,q] = bias[co] + sum_{ci'<Ci/G} sum_k w[co,ci',k] * xk[b, G(co)*Ci/G + ci', k, j, q]
  * with G(co) = co / (Co/G).  EINVAL unless groups divides Ci and Co
  * (DistributedSpectralConvS2 source on the pages raises ValueError for the
- * same condition). */
+ * same condition).  bf16 xk and w with one group of 64 or 128 output
+ * channels, Ci*K a multiple of 32 (at least 160 at Co = 128, 192 at Co = 64)
+ * and nlat_out*nlon_out a multiple of 8 and at least 256 take a persistent
+ * matrix-core kernel that fills one workgroup per compute unit; the
+ * environment variable DISCO_EINSUM_PATH=stream selects the double-buffered
+ * kernel instead (same sums, float32 accumulation in another order). */
 int disco_einsum(const void* xk, int xk_dtype, const void* w, int w_dtype,
                  const float* bias, void* y, int y_dtype,
                  int32_t B, int32_t Ci, int32_t Co, int32_t groups, int32_t K,

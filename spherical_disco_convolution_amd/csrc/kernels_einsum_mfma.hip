@@ -372,7 +372,13 @@ __global__ __launch_bounds__(R_THREADS) void einsum_ring_bf16(const bf16_t* __re
     const int nk = Kd / RK;
     const int ntn = (HW + RN - 1) / RN;
     const int G = gridDim.x;
-    const int my_tiles = (int)blockIdx.x < ntiles ? (ntiles - 1 - (int)blockIdx.x) / G + 1 : 0;
+    // Tiles base, base + G, ...  Workgroups go to the 8 XCDs round-robin; base
+    // gives the G / 8 workgroups of one XCD consecutive tiles, so that the
+    // cache lines two neighbouring tiles share (X_K rows need not start on a
+    // line) are fetched once into that XCD's L2.
+    const int bx = (int)blockIdx.x;
+    const int base = G % 8 == 0 ? (bx % 8) * (G / 8) + bx / 8 : bx;
+    const int my_tiles = base < ntiles ? (ntiles - 1 - base) / G + 1 : 0;
     const int Q = my_tiles * nk;   // steps of this workgroup
     if (Q == 0) return;
 
@@ -404,7 +410,7 @@ __global__ __launch_bounds__(R_THREADS) void einsum_ring_bf16(const bf16_t* __re
             }
         }
         // issue cursor: step ik of tile ti, ring stage iq
-        int ik = 0, ti = blockIdx.x, iq = 0;
+        int ik = 0, ti = base, iq = 0;
         int64_t xbase = 0;
         auto tile_base = [&]() {
             const int bb = ti / ntn, n0 = min((ti % ntn) * RN, HW - RN);
@@ -478,7 +484,7 @@ __global__ __launch_bounds__(R_THREADS) void einsum_ring_bf16(const bf16_t* __re
             for (int e = 0; e < 16; ++e) acc[a][c][e] = 0.0f;
 
     const lds_u8* ring_p = (const lds_u8*)&ring[0];
-    int ck = 0, ti = blockIdx.x;
+    int ck = 0, ti = base;
 #pragma unroll 1
     for (int q = 0; q < Q; ++q) {
         __syncthreads();

@@ -730,7 +730,7 @@ __global__ __launch_bounds__(kSpecThreads) __attribute__((amdgpu_waves_per_eu(2)
     const uint32_t* __restrict__ xh, const bf16_t* __restrict__ wp,
     const uint32_t* __restrict__ psih, const int32_t* __restrict__ win_ptr,
     const DevWindow* __restrict__ wins, bf16_t* __restrict__ yh, int B, int Ci, int nlat_in,
-    int nlat_out, int MP, int NX, int64_t psih_zero) {
+    int nlat_out, int MP, int NX, int64_t psih_zero, int nwmax) {
     __shared__ __attribute__((aligned(16))) bf16_t bt[64 * kBts];
     __shared__ __attribute__((aligned(16))) u32x4 xs[kSpecMaxWin * 32 * 8];   // [r][ci][piece]
     __shared__ __attribute__((aligned(16))) uint32_t ps[kSpecMaxWin * KT * kMt];
@@ -836,8 +836,10 @@ __global__ __launch_bounds__(kSpecThreads) __attribute__((amdgpu_waves_per_eu(2)
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int r = 2 * wave + (i >> 2);
-            dma_lds16((i < 4 ? blo : bhi) + dma_off[i & 3],
-                      xs_lds + (uint32_t)((r * 32 + 8 * (i & 3)) * 8 * 16));
+            // window slots no output row has (r >= nwmax) are never read
+            if (r < nwmax)
+                dma_lds16((i < 4 ? blo : bhi) + dma_off[i & 3],
+                          xs_lds + (uint32_t)((r * 32 + 8 * (i & 3)) * 8 * 16));
         }
     };
 
@@ -1125,7 +1127,7 @@ int try_launch_fused_spectral(const disco_psi* psi, const void* x, const void* w
 #define DISCO_SM(CC, KK)                                                                     \
     hipLaunchKernelGGL((spec_mfma<CC, KK>), grid, dim3(kSpecThreads), 0, st, xh, wpd,         \
                        psih, d.win_ptr, d.windows, yh, B, Ci, D.nlat_in, D.nlat_out, MP, NX, \
-                       (int64_t)h.windows.size() * K * MP)
+                       (int64_t)h.windows.size() * K * MP, (int)d.max_windows)
 #define DISCO_SM_K(CC)                                                                       \
     switch (K) {                                                                             \
         case 1: DISCO_SM(CC, 1); break;                                                      \

@@ -47,13 +47,17 @@ def W(name, B, Ci, Co, nlat, nlon, ks, cut, seed=21):
                     "bf16")
 
 
-# nlon / 2 = 60 (4,3,5), 50 (2,5,5), 36 (4,3,3), 30 (2,3,5), 8 (4,2)
+# nlon / 2 = 60 (4,3,5), 50 (2,5,5), 36 (4,3,3), 30 (2,3,5), 8 (4,2), 40 (2,4,5)
 SPECTRAL = [
     W("c4_like", 1, 128, 128, 61, 120, (3, 3), 4 * math.pi / 60),
     W("b2_ci64_co128", 2, 64, 128, 25, 100, (3, 3), 0.45),
     W("iso_k4_co64", 1, 32, 64, 19, 72, (4,), 0.6),
     W("k8_co64", 1, 32, 64, 21, 60, (2, 7), 0.5),
     W("k1_tiny", 1, 32, 64, 9, 16, (1,), 0.7),
+    # 41 -> 20 latitudes at 80 longitudes: four output rows gather 8 input
+    # rows, the most the spectral kernel takes (equal grids give odd counts)
+    Workload("lat_down_8win", 21, 1, 32, 128, 1, 41, 80, 20, 80, (3, 3), oracle.num_basis((3, 3)),
+             0.2827, "bf16"),
 ]
 
 

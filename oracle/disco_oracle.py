@@ -23,6 +23,13 @@ Points the pages leave open, and the reading taken here:
 * grid: equiangular colatitudes theta_i = pi*i/(nlat-1), both poles included;
   longitudes lambda_p = 2*pi*p/nlon;
 * quadrature: Clenshaw-Curtis weights in cos(theta) times 2*pi/nlon_in;
+* the other latitude grids the pages name for grid_in / grid_out (the
+  DistributedSpectralConvS2 page lists "legendre-gauss", "lobatto" and
+  "equiangular-trapezoidal" beside "equiangular") are read as rules in
+  x = cos(theta) over [-1, 1]: Gauss-Legendre nodes and weights;
+  Gauss-Lobatto-Legendre nodes (both poles) and weights; equiangular nodes
+  with the composite trapezoid rule in x.  The default theta_cutoff formula
+  is the same for every grid;
 * rotation: about the y axis by -theta'_j, so (theta'_j, 0) goes to the pole;
   r is the polar angle after the rotation, alpha its azimuth, alpha = 0 points
   to local south (+theta) and alpha = pi/2 to local east (+lambda);
@@ -56,13 +63,15 @@ TIE_REL = 1e-10
 class Desc:
     """Shapes and basis of one DISCO layer (same fields as the layer's
     constructor on the DiscreteContinuousConvS2 page: in_shape, out_shape,
-    kernel_shape, theta_cutoff; grids are equiangular)."""
+    kernel_shape, theta_cutoff, grid_in, grid_out)."""
     nlat_in: int
     nlon_in: int
     nlat_out: int
     nlon_out: int
     kernel_shape: tuple
     theta_cutoff: float | None = None
+    grid_in: str = "equiangular"
+    grid_out: str = "equiangular"
 
     @property
     def nr(self) -> int:
@@ -99,9 +108,48 @@ def num_basis(kernel_shape) -> int:
 # --------------------------------------------------------------------------
 # Grid and quadrature
 # --------------------------------------------------------------------------
-def colatitudes(nlat: int) -> np.ndarray:
-    """Equiangular colatitudes including both poles."""
-    return np.array([math.pi * i / (nlat - 1) for i in range(nlat)], dtype=np.float64)
+GRIDS = ("equiangular", "legendre-gauss", "lobatto", "equiangular-trapezoidal")
+
+
+def colatitudes(nlat: int, grid: str = "equiangular") -> np.ndarray:
+    """Colatitudes of a latitude grid, ascending from the north pole."""
+    if grid in ("equiangular", "equiangular-trapezoidal"):
+        return np.array([math.pi * i / (nlat - 1) for i in range(nlat)], dtype=np.float64)
+    return np.arccos(grid_rule(nlat, grid)[0])
+
+
+def grid_rule(nlat: int, grid: str):
+    """Nodes x_i = cos(theta_i) (descending, so theta ascends) and weights w_i
+    of the grid's rule for int_{-1}^{1} f(x) dx."""
+    if grid == "equiangular":
+        return np.cos(colatitudes(nlat)), clenshaw_curtis_weights(nlat)
+    if grid == "legendre-gauss":
+        # Gauss-Legendre: the roots of P_nlat and their Christoffel weights
+        # (numpy's Golub-Welsch routine as a library step), nodes descending
+        x, w = np.polynomial.legendre.leggauss(nlat)
+        return x[::-1].copy(), w[::-1].copy()
+    if grid == "lobatto":
+        # Gauss-Lobatto-Legendre with n = nlat nodes: x = +-1 and the roots of
+        # P'_{n-1}; w_i = 2 / (n (n-1) P_{n-1}(x_i)^2)
+        n = nlat
+        if n < 2:
+            raise ValueError("a Lobatto grid needs at least 2 nodes")
+        pn1 = np.polynomial.legendre.Legendre.basis(n - 1)
+        inner = np.sort(pn1.deriv().roots().real)[::-1] if n > 2 else np.zeros(0)
+        x = np.concatenate([[1.0], inner, [-1.0]])
+        w = 2.0 / (n * (n - 1) * pn1(x) ** 2)
+        return x, w
+    if grid == "equiangular-trapezoidal":
+        # composite trapezoid rule in x on the equiangular nodes:
+        # w_i = (x_{i-1} - x_{i+1}) / 2, halves at the two ends
+        x = np.cos(colatitudes(nlat))
+        w = np.zeros(nlat, dtype=np.float64)
+        for i in range(nlat - 1):
+            h = x[i] - x[i + 1]
+            w[i] += 0.5 * h
+            w[i + 1] += 0.5 * h
+        return x, w
+    raise ValueError(f"unknown grid {grid!r} (known: {GRIDS})")
 
 
 def longitudes(nlon: int) -> np.ndarray:
@@ -129,10 +177,11 @@ def clenshaw_curtis_weights(nlat: int) -> np.ndarray:
     return w
 
 
-def quadrature_weights(nlat: int, nlon: int) -> np.ndarray:
+def quadrature_weights(nlat: int, nlon: int, grid: str = "equiangular") -> np.ndarray:
     """Per-point spherical quadrature weight of latitude row i (sums to 4*pi
-    over the whole grid): Clenshaw-Curtis in cos(theta) times 2*pi/nlon."""
-    return clenshaw_curtis_weights(nlat) * (2.0 * math.pi / nlon)
+    over the whole grid): the grid's rule in cos(theta) (Clenshaw-Curtis for
+    the equiangular grid) times 2*pi/nlon."""
+    return grid_rule(nlat, grid)[1] * (2.0 * math.pi / nlon)
 
 
 # --------------------------------------------------------------------------
@@ -223,11 +272,11 @@ def psi_row(desc: Desc, j: int, omega: np.ndarray | None = None):
     """Support points and values of output row j: (in_lat, lon_off, vals).
     `omega` may pass in quadrature_weights(nlat_in, nlon_in) to save time."""
     cutoff = desc.cutoff
-    theta_in = colatitudes(desc.nlat_in)
-    theta_out = colatitudes(desc.nlat_out)[j]
+    theta_in = colatitudes(desc.nlat_in, desc.grid_in)
+    theta_out = colatitudes(desc.nlat_out, desc.grid_out)[j]
     lam = longitudes(desc.nlon_in)
     if omega is None:
-        omega = quadrature_weights(desc.nlat_in, desc.nlon_in)
+        omega = quadrature_weights(desc.nlat_in, desc.nlon_in, desc.grid_in)
     lat_list, lon_list, val_list = [], [], []
     for i in range(desc.nlat_in):
         # r >= |theta_i - theta'_j|, so rows farther away cannot be in the cap
@@ -250,7 +299,7 @@ def psi_row(desc: Desc, j: int, omega: np.ndarray | None = None):
 def psi(desc: Desc) -> PsiCSR:
     """The whole Psi tensor as canonical CSR (sorted by j, then i, then p)."""
     row_ptr = np.zeros(desc.nlat_out + 1, dtype=np.int64)
-    omega = quadrature_weights(desc.nlat_in, desc.nlon_in)
+    omega = quadrature_weights(desc.nlat_in, desc.nlon_in, desc.grid_in)
     lats, lons, vals = [], [], []
     for j in range(desc.nlat_out):
         a, b, v = psi_row(desc, j, omega)
@@ -298,7 +347,8 @@ def contract(desc: Desc, x: np.ndarray, csr: PsiCSR | None = None, rows=None,
     nq = desc.nlon_out if cols_out is None else len(cols_out)
     x = np.asarray(x, dtype=np.float64)
     out = np.zeros((x.shape[0], x.shape[1], desc.K, len(rows), nq))
-    omega = None if csr is not None else quadrature_weights(desc.nlat_in, desc.nlon_in)
+    omega = None if csr is not None else quadrature_weights(desc.nlat_in, desc.nlon_in,
+                                                            desc.grid_in)
     for jj, j in enumerate(rows):
         if csr is not None:
             a, b = int(csr.row_ptr[j]), int(csr.row_ptr[j + 1])

@@ -52,7 +52,14 @@ extern "C" {
 #define DISCO_BF16  1
 
 /* grids (DiscreteContinuousConvS2 page, grid_in / grid_out parameters) */
+/* Every grid is a rule in x = cos(theta) over [-1, 1] (weights sum to 2),
+ * times 2*pi/nlon per point; nodes ordered from the north pole.  The pages
+ * name the last three (DistributedSpectralConvS2 page, grid_in) without
+ * defining them; these are the textbook rules of those names. */
 #define DISCO_GRID_EQUIANGULAR 0  /* theta_i = pi*i/(nlat-1) (both poles), Clenshaw-Curtis weights */
+#define DISCO_GRID_LEGENDRE_GAUSS 1  /* Gauss-Legendre nodes and weights (no poles) */
+#define DISCO_GRID_LOBATTO 2      /* Gauss-Lobatto-Legendre nodes (both poles) and weights */
+#define DISCO_GRID_EQUIANGULAR_TRAPEZOIDAL 3  /* equiangular nodes, composite trapezoid in x */
 
 /* basis (same page, basis_type / basis_norm_mode parameters) */
 #define DISCO_BASIS_PIECEWISE_LINEAR 0
@@ -65,7 +72,7 @@ typedef struct disco_psi disco_psi;   /* opaque, library-owned, immutable after 
 typedef struct disco_psi_desc {
     int32_t nlat_in, nlon_in;       /* input grid */
     int32_t nlat_out, nlon_out;     /* output grid; nlon_in must be a multiple of nlon_out */
-    int32_t grid_in, grid_out;      /* DISCO_GRID_EQUIANGULAR */
+    int32_t grid_in, grid_out;      /* DISCO_GRID_* */
     int32_t basis_type;             /* DISCO_BASIS_PIECEWISE_LINEAR */
     int32_t basis_norm;             /* DISCO_NORM_NONE */
     int32_t kernel_shape[2];        /* {nr, nphi}: nphi = 0 -> isotropic (nr,), K = nr;
@@ -76,7 +83,8 @@ typedef struct disco_psi_desc {
 /* Build Psi on the host in float64 (DiscreteContinuousConvS2 page, Psi
  * paragraph).  No GPU is touched.  On success *out owns a new handle; free it
  * with disco_psi_free.  EINVAL for inconsistent sizes or cutoff, EUNSUPPORTED
- * for other grids/bases/normalisations or K > 64, ENOMEM on allocation failure. */
+ * for unknown grid codes, other bases/normalisations or K > 64, ENOMEM on
+ * allocation failure. */
 int disco_psi_build(const disco_psi_desc* desc, disco_psi** out);
 
 /* Sizes of a built Psi: number of basis functions K, support points nnz (the

@@ -31,7 +31,7 @@ DISCO_EHIP = -4
 F32 = 0
 BF16 = 1
 
-GRIDS = {"equiangular": 0}
+GRIDS = {"equiangular": 0, "legendre-gauss": 1, "lobatto": 2, "equiangular-trapezoidal": 3}
 BASES = {"piecewise linear": 0}
 NORMS = {"none": 0}
 

@@ -10,6 +10,10 @@
 // Conventions where the pages are silent (each is a reading):
 //  * equiangular grid with both poles, theta_i = pi*i/(nlat-1);
 //  * Clenshaw-Curtis weights in cos(theta), times 2*pi/nlon_in;
+//  * the other grids the pages name ("legendre-gauss", "lobatto",
+//    "equiangular-trapezoidal", DistributedSpectralConvS2 page) as rules in
+//    x = cos(theta) over [-1, 1]: Gauss-Legendre; Gauss-Lobatto-Legendre
+//    (both poles); equiangular nodes with the composite trapezoid in x;
 //  * local frame at the output point: alpha = 0 towards +theta (south),
 //    alpha = pi/2 towards +lambda (east); r is the great-circle distance;
 //  * support is r < cutoff*(1 - 1e-10): points at r == cutoff are excluded;
@@ -48,6 +52,108 @@ std::vector<double> clenshaw_curtis(int nlat) {
         w[i] = ci * (1.0 - s) / double(n);
     }
     return w;
+}
+
+// Legendre P_m(x) and P_{m-1}(x) by the three-term recurrence
+// (k P_k = (2k - 1) x P_{k-1} - (k - 1) P_{k-2}).
+void legendre_pair(int m, double x, double& pm, double& pm1) {
+    double a = 1.0, b = x;   // P_0, P_1
+    if (m == 0) {
+        pm = 1.0;
+        pm1 = 0.0;
+        return;
+    }
+    for (int k = 2; k <= m; ++k) {
+        const double c = ((2.0 * k - 1.0) * x * b - (k - 1.0) * a) / double(k);
+        a = b;
+        b = c;
+    }
+    pm = b;
+    pm1 = a;
+}
+
+// Nodes x_i = cos(theta_i), descending (colatitude ascending), and weights of
+// a latitude grid's rule for the integral over [-1, 1]; theta_i as well, exact
+// for the equiangular node sets.  The Gauss and Lobatto nodes are found by
+// Newton's method from the usual cosine estimates, the first half only, and
+// mirrored, so that the rule is exactly symmetric.
+struct LatRule {
+    std::vector<double> x, w, theta;
+};
+
+LatRule lat_rule(int grid, int n) {
+    LatRule R;
+    R.x.assign(n, 0.0);
+    R.w.assign(n, 0.0);
+    R.theta.assign(n, 0.0);
+    if (grid == DISCO_GRID_EQUIANGULAR || grid == DISCO_GRID_EQUIANGULAR_TRAPEZOIDAL) {
+        for (int i = 0; i < n; ++i) {
+            R.theta[i] = kPi * double(i) / double(n - 1);
+            R.x[i] = std::cos(R.theta[i]);
+        }
+        if (grid == DISCO_GRID_EQUIANGULAR) {
+            R.w = clenshaw_curtis(n);
+        } else {
+            for (int i = 0; i + 1 < n; ++i) {   // trapezoid on [x_{i+1}, x_i]
+                const double h = R.x[i] - R.x[i + 1];
+                R.w[i] += 0.5 * h;
+                R.w[i + 1] += 0.5 * h;
+            }
+        }
+        return R;
+    }
+    if (grid == DISCO_GRID_LEGENDRE_GAUSS) {
+        // roots of P_n; w = 2 / ((1 - x^2) P_n'(x)^2), P_n' = n (x P_n - P_{n-1}) / (x^2 - 1)
+        for (int i = 0; i < (n + 1) / 2; ++i) {
+            double x = std::cos(kPi * (i + 0.75) / (n + 0.5));
+            double dp = 1.0;
+            for (int it = 0; it < 100; ++it) {
+                double p, p1;
+                legendre_pair(n, x, p, p1);
+                dp = double(n) * (x * p - p1) / (x * x - 1.0);
+                const double dx = p / dp;
+                x -= dx;
+                if (std::fabs(dx) < 1e-16) break;
+            }
+            {
+                double p, p1;
+                legendre_pair(n, x, p, p1);
+                dp = double(n) * (x * p - p1) / (x * x - 1.0);
+            }
+            if (2 * i + 1 == n) x = 0.0;   // the middle node of an odd rule
+            const double w = 2.0 / ((1.0 - x * x) * dp * dp);
+            R.x[i] = x;
+            R.x[n - 1 - i] = -x;
+            R.w[i] = R.w[n - 1 - i] = w;
+        }
+    } else {   // DISCO_GRID_LOBATTO: x = +-1 and the roots of P_{n-1}'
+        const int m = n - 1;
+        R.x[0] = 1.0;
+        R.x[n - 1] = -1.0;
+        R.w[0] = R.w[n - 1] = 2.0 / (double(n) * double(m));
+        for (int i = 1; i < (n + 1) / 2; ++i) {
+            double x = std::cos(kPi * double(i) / double(m));
+            for (int it = 0; it < 100; ++it) {
+                double p, p1;
+                legendre_pair(m, x, p, p1);
+                const double d1 = double(m) * (x * p - p1) / (x * x - 1.0);   // P_m'
+                // Legendre's equation: (1 - x^2) P_m'' = 2 x P_m' - m (m + 1) P_m
+                const double d2 = (2.0 * x * d1 - double(m) * (m + 1.0) * p) / (1.0 - x * x);
+                const double dx = d1 / d2;
+                x -= dx;
+                if (std::fabs(dx) < 1e-16) break;
+            }
+            if (2 * i + 1 == n) x = 0.0;
+            double p, p1;
+            legendre_pair(m, x, p, p1);
+            const double w = 2.0 / (double(n) * double(m) * p * p);
+            R.x[i] = x;
+            R.x[n - 1 - i] = -x;
+            R.w[i] = R.w[n - 1 - i] = w;
+        }
+    }
+    for (int i = 0; i < n; ++i) R.theta[i] = std::acos(R.x[i]);
+    return R;
 }
 
 inline double hat(double u, double centre, double half_width) {
@@ -102,9 +208,9 @@ int build_host_psi(const disco_psi_desc& d, HostPsi& P) {
         return set_error(DISCO_EUNSUPPORTED, "grid with more than 2^30 points");
     if (d.nlon_in > 65536)
         return set_error(DISCO_EUNSUPPORTED, "nlon_in > 65536");
-    if (d.grid_in != DISCO_GRID_EQUIANGULAR || d.grid_out != DISCO_GRID_EQUIANGULAR)
-        return set_error(DISCO_EUNSUPPORTED, "only equiangular grids are implemented (got %d, %d)",
-                         d.grid_in, d.grid_out);
+    if (d.grid_in < DISCO_GRID_EQUIANGULAR || d.grid_in > DISCO_GRID_EQUIANGULAR_TRAPEZOIDAL ||
+        d.grid_out < DISCO_GRID_EQUIANGULAR || d.grid_out > DISCO_GRID_EQUIANGULAR_TRAPEZOIDAL)
+        return set_error(DISCO_EUNSUPPORTED, "unknown grid (got %d, %d)", d.grid_in, d.grid_out);
     if (d.basis_type != DISCO_BASIS_PIECEWISE_LINEAR)
         return set_error(DISCO_EUNSUPPORTED, "only the piecewise-linear basis is implemented");
     if (d.basis_norm != DISCO_NORM_NONE)
@@ -136,10 +242,12 @@ int build_host_psi(const disco_psi_desc& d, HostPsi& P) {
         const int K = P.K;
         Basis basis{nr, nphi, K, cutoff, nr > 1 ? cutoff / double(nr - 1) : cutoff};
 
-        const std::vector<double> wcc = clenshaw_curtis(d.nlat_in);
-        std::vector<double> th_in(d.nlat_in), cos_in(d.nlat_in), sin_in(d.nlat_in);
+        const LatRule rin = lat_rule(d.grid_in, d.nlat_in);
+        const LatRule rout = lat_rule(d.grid_out, d.nlat_out);
+        const std::vector<double>& wcc = rin.w;
+        const std::vector<double>& th_in = rin.theta;
+        std::vector<double> cos_in(d.nlat_in), sin_in(d.nlat_in);
         for (int i = 0; i < d.nlat_in; ++i) {
-            th_in[i] = kPi * double(i) / double(d.nlat_in - 1);
             cos_in[i] = std::cos(th_in[i]);
             sin_in[i] = std::sin(th_in[i]);
         }
@@ -165,7 +273,7 @@ int build_host_psi(const disco_psi_desc& d, HostPsi& P) {
         std::vector<char> inside(d.nlon_in);
         std::vector<double> bv(K);
         for (int j = 0; j < d.nlat_out; ++j) {
-            const double tho = kPi * double(j) / double(d.nlat_out - 1);
+            const double tho = rout.theta[j];
             // unit vector of the output point and its local south/east axes
             const double ax = std::sin(tho), az = std::cos(tho);
             const double sx = std::cos(tho), sz = -std::sin(tho);   // south; east = (0,1,0)

@@ -72,8 +72,8 @@ def _rc_build(**kw):
     (dict(kernel_shape=(0, 0)), sdc.DISCO_EINVAL),
     (dict(kernel_shape=(3, -1)), sdc.DISCO_EINVAL),
     (dict(kernel_shape=(10, 8)), sdc.DISCO_EUNSUPPORTED),   # K = 73 > 64
-    (dict(grid_in=1), sdc.DISCO_EUNSUPPORTED),
-    (dict(grid_out=2), sdc.DISCO_EUNSUPPORTED),
+    (dict(grid_in=4), sdc.DISCO_EUNSUPPORTED),       # unknown grid codes
+    (dict(grid_out=-1), sdc.DISCO_EUNSUPPORTED),
     (dict(basis_type=1), sdc.DISCO_EUNSUPPORTED),
     (dict(basis_norm=1), sdc.DISCO_EUNSUPPORTED),
 ])
@@ -81,6 +81,13 @@ def test_build_rejects(kw, code):
     rc, msg = _rc_build(**kw)
     assert rc == code
     assert msg
+
+
+@pytest.mark.parametrize("gin,gout", [(1, 1), (2, 2), (3, 3), (1, 0), (0, 2), (2, 3)])
+def test_build_accepts_every_grid_code(gin, gout):
+    # equiangular 0, legendre-gauss 1, lobatto 2, equiangular-trapezoidal 3
+    rc, msg = _rc_build(grid_in=gin, grid_out=gout)
+    assert rc == 0, msg
 
 
 def test_build_null_arguments():
@@ -95,7 +102,7 @@ def test_python_errors():
     with pytest.raises(ValueError):
         sdc.psi_build(33, 64, 33, 48, (3,), 0.3)
     with pytest.raises(NotImplementedError):
-        sdc.psi_build(33, 64, 33, 64, (3,), 0.3, grid_in="legendre-gauss")
+        sdc.psi_build(33, 64, 33, 64, (3,), 0.3, grid_in="healpix")
     with pytest.raises(NotImplementedError):
         sdc.psi_build(33, 64, 33, 64, (3,), 0.3, basis_norm_mode="nodal")
     with pytest.raises(ValueError):

@@ -80,3 +80,31 @@ def test_query_counts():
     p = sdc.psi_build(wl.nlat_in, wl.nlon_in, wl.nlat_out, wl.nlon_out, wl.kernel_shape,
                       wl.theta_cutoff)
     assert (p.K, p.nnz, p.nnz_nonzero) == (7, 156997, 555973)
+
+
+# the other latitude grids (DistributedSpectralConvS2 page, grid_in / grid_out):
+# the builder computes its nodes and weights by its own Newton iterations, the
+# oracle by numpy's Gauss routine and closed forms
+GRID_CASES = [
+    ("legendre-gauss", "legendre-gauss", (32, 64, 32, 64, (3, 3), 0.45)),
+    ("lobatto", "lobatto", (33, 64, 33, 64, (3,), 0.5)),
+    ("equiangular-trapezoidal", "equiangular-trapezoidal", (33, 64, 33, 64, (2, 2), 0.4)),
+    ("legendre-gauss", "equiangular", (48, 96, 25, 48, (3, 3), 0.5)),   # stride 2
+    ("equiangular", "lobatto", (33, 64, 17, 64, (4,), 0.6)),
+    ("lobatto", "legendre-gauss", (21, 40, 20, 40, (3, 3), 3.0)),        # nearly whole sphere
+    ("legendre-gauss", "legendre-gauss", (1 + 64, 128, 64, 128, (5, 4), 0.3)),
+]
+
+
+@pytest.mark.parametrize("gin,gout,case", GRID_CASES,
+                         ids=[f"{a}-{b}-{c[0]}" for a, b, c in GRID_CASES])
+def test_builder_matches_oracle_other_grids(gin, gout, case):
+    nli, nfi, nlo, nfo, ks, cut = case
+    lib = sdc.psi_build(nli, nfi, nlo, nfo, ks, cut, grid_in=gin, grid_out=gout)
+    ref = oracle.psi(oracle.Desc(nli, nfi, nlo, nfo, tuple(ks), cut, grid_in=gin, grid_out=gout))
+    _compare(lib, ref)
+
+
+def test_unknown_grid_is_rejected():
+    with pytest.raises(NotImplementedError):
+        sdc.psi_build(9, 16, 9, 16, (3,), 0.5, grid_in="healpix")

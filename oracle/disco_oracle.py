@@ -48,6 +48,7 @@ Parity pins for every function live in tests/test_oracle_*.py.
 """
 from __future__ import annotations
 
+import functools
 import math
 from dataclasses import dataclass
 
@@ -120,7 +121,13 @@ def colatitudes(nlat: int, grid: str = "equiangular") -> np.ndarray:
 
 def grid_rule(nlat: int, grid: str):
     """Nodes x_i = cos(theta_i) (descending, so theta ascends) and weights w_i
-    of the grid's rule for int_{-1}^{1} f(x) dx."""
+    of the grid's rule for int_{-1}^{1} f(x) dx (fresh copies)."""
+    x, w = _grid_rule_cached(int(nlat), grid)
+    return x.copy(), w.copy()
+
+
+@functools.lru_cache(maxsize=32)
+def _grid_rule_cached(nlat: int, grid: str):
     if grid == "equiangular":
         return np.cos(colatitudes(nlat)), clenshaw_curtis_weights(nlat)
     if grid == "legendre-gauss":
@@ -129,15 +136,25 @@ def grid_rule(nlat: int, grid: str):
         x, w = np.polynomial.legendre.leggauss(nlat)
         return x[::-1].copy(), w[::-1].copy()
     if grid == "lobatto":
-        # Gauss-Lobatto-Legendre with n = nlat nodes: x = +-1 and the roots of
-        # P'_{n-1}; w_i = 2 / (n (n-1) P_{n-1}(x_i)^2)
+        # Gauss-Lobatto-Legendre with n = nlat nodes: x = +-1 and the n - 2
+        # roots of P'_{n-1}, which are the roots of the (1, 1) Jacobi
+        # polynomial of degree n - 2: the eigenvalues of its symmetric Jacobi
+        # matrix (zero diagonal, off-diagonal sqrt(k (k+2) / ((2k+1)(2k+3))),
+        # k = 1 .. n-3); w_i = 2 / (n (n-1) P_{n-1}(x_i)^2)
         n = nlat
         if n < 2:
             raise ValueError("a Lobatto grid needs at least 2 nodes")
-        pn1 = np.polynomial.legendre.Legendre.basis(n - 1)
-        inner = np.sort(pn1.deriv().roots().real)[::-1] if n > 2 else np.zeros(0)
+        m = n - 2
+        if m > 0:
+            k = np.arange(1, m, dtype=np.float64)
+            off = np.sqrt(k * (k + 2.0) / ((2.0 * k + 1.0) * (2.0 * k + 3.0)))
+            jac = np.diag(off, 1) + np.diag(off, -1)
+            inner = np.sort(np.linalg.eigvalsh(jac))[::-1]
+        else:
+            inner = np.zeros(0)
         x = np.concatenate([[1.0], inner, [-1.0]])
-        w = 2.0 / (n * (n - 1) * pn1(x) ** 2)
+        pn1 = np.polynomial.legendre.legval(x, np.eye(n)[n - 1])
+        w = 2.0 / (n * (n - 1) * pn1 ** 2)
         return x, w
     if grid == "equiangular-trapezoidal":
         # composite trapezoid rule in x on the equiangular nodes:

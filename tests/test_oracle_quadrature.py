@@ -166,3 +166,14 @@ def test_psi_uses_the_grid_rule(grid, cutoff):
     assert sorted(set(lat.tolist())) == np.nonzero(inside)[0].tolist()
     assert lat.size == 24 * int(inside.sum())
     assert abs(v.sum() - 2 * math.pi * w[inside].sum()) < 1e-12
+
+
+@pytest.mark.parametrize("grid", ["legendre-gauss", "lobatto"])
+def test_rules_at_full_size(grid):
+    # 721 rows (the 0.25 degree grids): still symmetric, summing to 2 and
+    # integrating low-degree polynomials to rounding
+    x, w = oracle.grid_rule(721, grid)
+    assert abs(w.sum() - 2.0) < 1e-12
+    assert np.allclose(x, -x[::-1], atol=1e-13)
+    for m in range(0, 41):
+        assert abs(np.dot(w, x ** m) - _moment(m)) < 1e-12, m

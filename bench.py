@@ -73,11 +73,11 @@ MEASURED_TRAFFIC_BYTES = {
 CSRC = os.path.join(ROOT, "spherical_disco_convolution_amd", "csrc")
 
 
-def measured_traffic(key, kernel):
+def measured_traffic(key, kernel, grid="equiangular"):
     """HBM bytes per launch from rocprofv3 FETCH_SIZE + WRITE_SIZE (copy-calibrated),
     or None when there is no figure or the kernel source changed since it was taken."""
     import hashlib
-    m = MEASURED_TRAFFIC_BYTES.get((key, kernel))
+    m = MEASURED_TRAFFIC_BYTES.get((key, kernel)) if grid == "equiangular" else None
     src = os.path.join(CSRC, m["source"]) if m else None
     if m is None or not os.path.exists(src):
         return None
@@ -94,6 +94,10 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=None, help="c1..c5 (default: the headline case c4)")
+    ap.add_argument("--grid", default="equiangular",
+                    choices=["equiangular", "legendre-gauss", "lobatto", "equiangular-trapezoidal"],
+                    help="latitude grid of input and output (default: equiangular, the "
+                         "workloads' own)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-unfused", action="store_true")
     ap.add_argument("--fused-only", action="store_true", help="time only the fused kernel (profiling)")
@@ -167,11 +171,11 @@ def time_region(fn, steps, torch):
     return wall, e0.elapsed_time(e1) / 1000.0
 
 
-def cpu_baseline(wl, x, w):
+def cpu_baseline(wl, x, w, grid="equiangular"):
     import oracle
     from threadpoolctl import threadpool_limits
     d = oracle.Desc(wl.nlat_in, wl.nlon_in, wl.nlat_out, wl.nlon_out, wl.kernel_shape,
-                    wl.theta_cutoff)
+                    wl.theta_cutoff, grid_in=grid, grid_out=grid)
     csr = oracle.psi(d)
     # systematic sample of output rows, all longitudes, batches and channels
     step = max(1, wl.nlat_out // 60)
@@ -230,7 +234,7 @@ def main():
 
     t0 = time.perf_counter()
     psi = sdc.psi_build(wl.nlat_in, wl.nlon_in, wl.nlat_out, wl.nlon_out, wl.kernel_shape,
-                        wl.theta_cutoff)
+                        wl.theta_cutoff, grid_in=args.grid, grid_out=args.grid)
     psi_build_s = time.perf_counter() - t0
     t0 = time.perf_counter()
     psi.to_device()
@@ -260,7 +264,7 @@ def main():
     dsize = 2 if wl.dtype == "bf16" else 4
     peak = PEAK_TFLOPS[wl.dtype]
     achieved = f_alg / kernel_s / 1e12
-    traffic = measured_traffic(key, "fused_spectral" if spectral else "fused")
+    traffic = measured_traffic(key, "fused_spectral" if spectral else "fused", args.grid)
     call_roofline = {"bound": "mfma" if wl.dtype == "bf16" else "alu",
                      "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4), "traffic": traffic}
@@ -284,7 +288,7 @@ def main():
     a_dom = f_dom / dom_s / 1e12
     roofline = {"bound": "mfma" if wl.dtype == "bf16" else "alu", "achieved": round(a_dom, 3),
                 "peak": peak, "unit": "TFLOP/s", "frac": round(a_dom / peak, 4),
-                "traffic": measured_traffic(key, dom), "kernel": dom,
+                "traffic": measured_traffic(key, dom, args.grid), "kernel": dom,
                 "kernel_ms": round(dom_s * 1000, 4), "algorithmic_flop": f_dom}
     extra = {
         "fused_kernel_ms": round(kernel_s * 1000, 4),
@@ -331,7 +335,7 @@ def main():
             extra[name + "_roofline"] = {"bound": "hbm", "achieved": round(gbps, 1),
                                          "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                          "frac": round(gbps / HBM_PEAK_GBS, 4),
-                                         "traffic": measured_traffic(key, name)}
+                                         "traffic": measured_traffic(key, name, args.grid)}
         del xk
     line = {
         "metric": METRIC,
@@ -349,13 +353,14 @@ def main():
         "config": {"workload": f"{key}: B={wl.B} Ci={wl.Ci} Co={wl.Co} groups={wl.groups} "
                                f"{wl.nlat_in}x{wl.nlon_in}->{wl.nlat_out}x{wl.nlon_out} "
                                f"kernel_shape={wl.kernel_shape} K={wl.K} "
-                               f"theta_cutoff={wl.theta_cutoff:.6f} {wl.dtype}, fused forward",
+                               f"theta_cutoff={wl.theta_cutoff:.6f} {wl.dtype}, fused forward"
+                               + ("" if args.grid == "equiangular" else f", {args.grid} grid"),
                    "global_batch": wl.B, "parallelism": "single GPU"},
         "roofline": roofline,
     }
     line.update(extra)
     if not args.no_cpu_baseline and not args.fused_only:
-        line["cpu_baseline"] = cpu_baseline(wl, x, w)
+        line["cpu_baseline"] = cpu_baseline(wl, x, w, args.grid)
     print(json.dumps(line), flush=True)
 
 

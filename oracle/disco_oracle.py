@@ -403,3 +403,72 @@ def forward(desc: Desc, x: np.ndarray, w: np.ndarray, groups: int = 1,
     if bias is not None:
         g = g + np.asarray(bias, dtype=np.float64)[None, :, None, None]
     return g
+
+
+# --------------------------------------------------------------------------
+# Backward: the gradients the layer's autograd returns.  The pages give no
+# formulas; they say the layer trains by backpropagation and that its fused
+# mode recomputes X_K in backward instead of saving it (DiscreteContinuousConvS2
+# page, `fused` parameter).  The forward is linear in x and in w, so each
+# gradient is the adjoint of one of its linear maps, written out here from the
+# forward equation.
+# --------------------------------------------------------------------------
+def contract_transpose(desc: Desc, gxk: np.ndarray, csr: PsiCSR | None = None) -> np.ndarray:
+    """Adjoint of `contract`: for every support point (i, p) of every output
+    row j and every output longitude q,
+        gx[b, c, i, (q*s + p) mod nlon_in] += sum_k Psi[k, j, (i, p)] * gxk[b, c, k, j, q].
+    gxk is [B, C, K, nlat_out, nlon_out]; returns gx [B, C, nlat_in, nlon_in]."""
+    gxk = np.asarray(gxk, dtype=np.float64)
+    B, C = gxk.shape[0], gxk.shape[1]
+    if csr is None:
+        csr = psi(desc)
+    gx = np.zeros((B, C, desc.nlat_in, desc.nlon_in), dtype=np.float64)
+    q = np.arange(desc.nlon_out)
+    for j in range(desc.nlat_out):
+        for e in range(int(csr.row_ptr[j]), int(csr.row_ptr[j + 1])):
+            i, p = int(csr.in_lat[e]), int(csr.lon_off[e])
+            cols = (q * desc.stride + p) % desc.nlon_in     # distinct for distinct q
+            gx[:, :, i, cols] += np.einsum("k,bckq->bcq", csr.vals[e], gxk[:, :, :, j, :])
+    return gx
+
+
+def einsum_grad_w(gg: np.ndarray, xk: np.ndarray, groups: int) -> np.ndarray:
+    """Adjoint of `einsum` in w:
+    gw[co, ci', k] = sum_{b, j, q} gg[b, co, j, q] * X_K[b, G(co)*Ci/G + ci', k, j, q]."""
+    gg = np.asarray(gg, dtype=np.float64)
+    xk = np.asarray(xk, dtype=np.float64)
+    Co, Ci = gg.shape[1], xk.shape[1]
+    cig, cog = Ci // groups, Co // groups
+    gw = np.zeros((Co, cig, xk.shape[2]), dtype=np.float64)
+    for grp in range(groups):
+        gw[grp * cog:(grp + 1) * cog] = np.einsum(
+            "bohw,bikhw->oik", gg[:, grp * cog:(grp + 1) * cog], xk[:, grp * cig:(grp + 1) * cig])
+    return gw
+
+
+def einsum_grad_xk(gg: np.ndarray, w: np.ndarray, groups: int) -> np.ndarray:
+    """Adjoint of `einsum` in X_K:
+    gxk[b, G*Ci/G + ci', k, j, q] = sum_{co in group G} w[co, ci', k] * gg[b, co, j, q]."""
+    gg = np.asarray(gg, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    B, Co, H, W = gg.shape
+    cig, K = w.shape[1], w.shape[2]
+    cog = Co // groups
+    gxk = np.zeros((B, cig * groups, K, H, W), dtype=np.float64)
+    for grp in range(groups):
+        gxk[:, grp * cig:(grp + 1) * cig] = np.einsum(
+            "oik,bohw->bikhw", w[grp * cog:(grp + 1) * cog], gg[:, grp * cog:(grp + 1) * cog])
+    return gxk
+
+
+def backward(desc: Desc, x: np.ndarray, w: np.ndarray, gg: np.ndarray, groups: int = 1,
+             csr: PsiCSR | None = None):
+    """Gradients (gx, gw) of sum(gg * forward(x, w)) with respect to x and w
+    (the bias gradient is gg summed over b, j, q).  X_K is recomputed, as the
+    fused mode does."""
+    if csr is None:
+        csr = psi(desc)
+    xk = contract(desc, x, csr=csr)
+    gw = einsum_grad_w(gg, xk, groups)
+    gx = contract_transpose(desc, einsum_grad_xk(gg, w, groups), csr=csr)
+    return gx, gw

@@ -971,7 +971,10 @@ __global__ __launch_bounds__(kSpecThreads) __attribute__((amdgpu_waves_per_eu(2)
                 if (f + 1 < 8) dcur = dnext;
             }
             __syncthreads();   // tile complete
-            // ---- channel/basis GEMM over this chunk's 256 (k, ci) pairs ----
+            // ---- channel/basis GEMM over this chunk's 256 (k, ci) pairs, at a
+            // raised wave priority so that the SIMD keeps issuing its MFMAs
+            // while the other workgroup's wave runs its window sum ----
+            __builtin_amdgcn_s_setprio(2);
             const int cn = cc + 1 < nchunks ? cc + 1 : 0;   // weights of the next chunk
             const bf16_t* bb = bt + (wn * (64 / WGN) + l32) * kBts + 8 * lg;
             const u32x4* wnext = wf + (size_t)cn * 16 * WGM * 64;
@@ -994,6 +997,7 @@ __global__ __launch_bounds__(kSpecThreads) __attribute__((amdgpu_waves_per_eu(2)
             }
             // this wave's DMA of position p + 1 is complete; the NKS weight
             // reloads issued after it may stay in flight
+            __builtin_amdgcn_s_setprio(0);
             wait_vmcnt<NKS>();
             __syncthreads();   // spectra of p + 1 in LDS; B tile free
         }

@@ -249,6 +249,85 @@ __global__ __launch_bounds__(kThreads) void fused_depthwise(
     }
 }
 
+// The same sum with register tiling, for strides S = 1 and 2: thread tid
+// owns the QR consecutive outputs q0 + tid QR + r, whose input samples for
+// taps t0 .. t0 + DT - 1 form one run of (QR - 1) S + DT values.  That run is
+// read from LDS once per tap chunk and kept in registers; the folded taps are
+// LDS broadcasts.  The tap loop is padded to a multiple of DT with zero taps
+// (the samples they meet are real, finite inputs).
+constexpr int kDwTile = 16;   // taps per register chunk
+
+template <typename T, typename TY, int KP, int QR, int S>
+__global__ __launch_bounds__(kThreads) void fused_depthwise_tiled(
+    const T* __restrict__ x, const T* __restrict__ w, const float* __restrict__ bias,
+    TY* __restrict__ y, const int32_t* __restrict__ win_ptr, const DevWindow* __restrict__ wins,
+    const float* __restrict__ vals, int Ci, int Co, int groups, int K, int nlat_in, int nlon_in,
+    int nlat_out, int nlon_out, int max_width_padded) {
+    constexpr int DT = kDwTile;
+    constexpr int NE = (QR - 1) * S + DT;   // samples per chunk
+    extern __shared__ float smem[];
+    float* folded = smem;                           // [max_width_padded]
+    float* ext = smem + max_width_padded;           // [S (kThreads QR - 1) + max_width_padded]
+    const int j = blockIdx.x;
+    const int co = blockIdx.y;
+    const int b = blockIdx.z;
+    const int cog = Co / groups;
+    const int grp = co / cog;
+    const T* xc = x + ((size_t)b * Ci + grp) * nlat_in * nlon_in;
+    float wk[KP];
+#pragma unroll
+    for (int k = 0; k < KP; ++k) wk[k] = k < K ? load_f(w, (size_t)co * K + k) : 0.0f;
+    const int w0 = win_ptr[j], w1 = win_ptr[j + 1];
+    TY* out = y + (((size_t)b * Co + co) * nlat_out + j) * nlon_out;
+    const float bv = bias ? bias[co] : 0.0f;
+    const int tbase = threadIdx.x * QR * S;
+
+    for (int q0 = 0; q0 < nlon_out; q0 += kThreads * QR) {
+        float acc[QR];
+#pragma unroll
+        for (int r = 0; r < QR; ++r) acc[r] = 0.0f;
+        for (int wi = w0; wi < w1; ++wi) {
+            const DevWindow wd = wins[wi];
+            const int wpad = (wd.width + DT - 1) / DT * DT;
+            const int len = S * (kThreads * QR - 1) + wpad;
+            const T* row = xc + (size_t)wd.lat * nlon_in;
+            const int start = (int)(((int64_t)q0 * S + wd.p_lo) % nlon_in);
+            __syncthreads();
+            const float* v = vals + (size_t)wd.val_off * KP;
+            for (int t = threadIdx.x; t < wpad; t += kThreads) {
+                float f = 0.0f;
+                if (t < wd.width) {
+#pragma unroll
+                    for (int k = 0; k < KP; ++k) f = fmaf(wk[k], v[t * KP + k], f);
+                }
+                folded[t] = f;
+            }
+            for (int u = threadIdx.x; u < len; u += kThreads) {
+                int p = start + u;
+                p -= (p / nlon_in) * nlon_in;
+                ext[u] = load_f(row, p);
+            }
+            __syncthreads();
+            for (int t0 = 0; t0 < wpad; t0 += DT) {
+                float e[NE];
+#pragma unroll
+                for (int m = 0; m < NE; ++m) e[m] = ext[tbase + t0 + m];
+#pragma unroll
+                for (int t = 0; t < DT; ++t) {
+                    const float f = folded[t0 + t];
+#pragma unroll
+                    for (int r = 0; r < QR; ++r) acc[r] = fmaf(f, e[r * S + t], acc[r]);
+                }
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < QR; ++r) {
+            const int q = q0 + threadIdx.x * QR + r;
+            if (q < nlon_out) store_f(out, q, acc[r] + bv);
+        }
+    }
+}
+
 int check_launch(const char* what) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return set_error(DISCO_EHIP, "%s launch failed: %s", what, hipGetErrorString(e));
@@ -257,7 +336,8 @@ int check_launch(const char* what) {
 
 int pick_qr(int nlon_out) {
     int qr = (nlon_out + kThreads - 1) / kThreads;
-    return qr <= 1 ? 1 : qr <= 2 ? 2 : qr <= 4 ? 4 : qr <= 6 ? 6 : 8;
+    // every value returned here has a case in each switch that uses it
+    return qr <= 1 ? 1 : qr <= 2 ? 2 : qr <= 3 ? 3 : qr <= 4 ? 4 : qr <= 6 ? 6 : 8;
 }
 
 template <typename TX, typename TO, int KP>
@@ -277,6 +357,7 @@ int contract_kp(const disco_psi* psi, const void* x, void* xk, int B, int C, hip
     switch (QR) {
         case 1: DISCO_CONTRACT_LAUNCH(1); break;
         case 2: DISCO_CONTRACT_LAUNCH(2); break;
+        case 3: DISCO_CONTRACT_LAUNCH(3); break;
         case 4: DISCO_CONTRACT_LAUNCH(4); break;
         case 6: DISCO_CONTRACT_LAUNCH(6); break;
         default: DISCO_CONTRACT_LAUNCH(8); break;
@@ -402,10 +483,39 @@ int fused_depthwise_launch(const disco_psi* psi, const void* x, const void* w, c
     const DevPsi& d = psi->dev;
     const disco_psi_desc& D = h.desc;
     const int QR = pick_qr(D.nlon_out);
+    dim3 grid(D.nlat_out, Co, B);
+    if (h.stride <= 2) {
+        // register-tiled form; LDS holds the padded folded taps and the samples
+        const int wpad = (d.max_width + kDwTile - 1) / kDwTile * kDwTile;
+        const size_t tl = (size_t)(wpad + h.stride * (kThreads * QR - 1) + wpad) * sizeof(float);
+        if (tl <= 64 * 1024) {
+#define DISCO_DWT(Q, SS)                                                                          \
+    hipLaunchKernelGGL((fused_depthwise_tiled<T, TY, KP, Q, SS>), grid, dim3(kThreads), tl, st,   \
+                       (const T*)x, (const T*)w, bias, (TY*)y, d.win_ptr, d.windows, d.vals, Ci,  \
+                       Co, groups, h.K, D.nlat_in, D.nlon_in, D.nlat_out, D.nlon_out, wpad)
+#define DISCO_DWT_S(Q)             \
+    if (h.stride == 1) {           \
+        DISCO_DWT(Q, 1);           \
+    } else {                       \
+        DISCO_DWT(Q, 2);           \
+    }
+            KernelTimer timer("fused_depthwise", st);
+            switch (QR) {
+                case 1: DISCO_DWT_S(1) break;
+                case 2: DISCO_DWT_S(2) break;
+                case 3: DISCO_DWT_S(3) break;
+                case 4: DISCO_DWT_S(4) break;
+                case 6: DISCO_DWT_S(6) break;
+                default: DISCO_DWT_S(8) break;
+            }
+#undef DISCO_DWT_S
+#undef DISCO_DWT
+            return check_launch("fused_depthwise");
+        }
+    }
     const size_t lds =
         (size_t)(d.max_width + h.stride * (kThreads * QR - 1) + d.max_width) * sizeof(float);
     if (lds > 64 * 1024) return set_error(DISCO_EUNSUPPORTED, "row too long for the depthwise kernel");
-    dim3 grid(D.nlat_out, Co, B);
 #define DISCO_DW_LAUNCH(Q)                                                                       \
     hipLaunchKernelGGL((fused_depthwise<T, TY, KP, Q>), grid, dim3(kThreads), lds, st,          \
                        (const T*)x, (const T*)w, bias, (TY*)y, d.win_ptr, d.windows, d.vals, Ci, \
@@ -415,6 +525,7 @@ int fused_depthwise_launch(const disco_psi* psi, const void* x, const void* w, c
     switch (QR) {
         case 1: DISCO_DW_LAUNCH(1); break;
         case 2: DISCO_DW_LAUNCH(2); break;
+        case 3: DISCO_DW_LAUNCH(3); break;
         case 4: DISCO_DW_LAUNCH(4); break;
         case 6: DISCO_DW_LAUNCH(6); break;
         default: DISCO_DW_LAUNCH(8); break;

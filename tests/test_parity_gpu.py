@@ -85,6 +85,10 @@ SMALL = [
     W("k1_f32", 1, 2, 2, 1, 9, 16, 9, 16, (1,), 0.7, "f32"),
     W("nlat2_f32", 1, 2, 3, 1, 2, 8, 2, 4, (2,), 1.0, "f32"),
     W("wide_cap_f32", 1, 2, 2, 1, 17, 32, 17, 32, (3, 3), 2.5, "f32"),
+    # depthwise rows longer than one 256-thread pass: three outputs per thread
+    # at stride 1, two at stride 2 (the register-tiled depthwise kernel)
+    W("depthwise_long_s1_f32", 1, 4, 4, 4, 13, 600, 13, 600, (3, 3), 0.5, "f32"),
+    W("depthwise_long_s2_f32", 2, 3, 3, 3, 17, 1024, 9, 512, (4,), 0.6, "f32"),
 ]
 
 

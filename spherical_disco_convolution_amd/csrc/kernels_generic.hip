@@ -158,7 +158,28 @@ __global__ __launch_bounds__(kThreads) void fused_generic(
                 const T* row = xc + (size_t)wd.lat * nlon_in;
                 const float* v = vals + (size_t)wd.val_off * KP;
                 int p = (int)(((int64_t)q * s + wd.p_lo) % nlon_in);
-                for (int t = 0; t < wd.width; ++t) {
+                int t = 0;
+                if (nlon_in >= 8) {
+                    // eight independent loads in flight, then their taps in the
+                    // same order as the plain loop below
+                    for (; t + 8 <= wd.width; t += 8) {
+                        float xv[8];
+#pragma unroll
+                        for (int u = 0; u < 8; ++u) {
+                            int pu = p + u;
+                            if (pu >= nlon_in) pu -= nlon_in;
+                            xv[u] = load_f(row, pu);
+                        }
+#pragma unroll
+                        for (int u = 0; u < 8; ++u)
+#pragma unroll
+                            for (int k = 0; k < KP; ++k)
+                                acc[k] = fmaf(v[(t + u) * KP + k], xv[u], acc[k]);
+                        p += 8;
+                        if (p >= nlon_in) p -= nlon_in;
+                    }
+                }
+                for (; t < wd.width; ++t) {
                     const float xv = load_f(row, p);
 #pragma unroll
                     for (int k = 0; k < KP; ++k) acc[k] = fmaf(v[t * KP + k], xv, acc[k]);

@@ -133,8 +133,10 @@ __global__ __launch_bounds__(kThreads) void fused_generic(
     const T* __restrict__ x, const T* __restrict__ w, const float* __restrict__ bias,
     TY* __restrict__ y, const int32_t* __restrict__ win_ptr, const DevWindow* __restrict__ wins,
     const float* __restrict__ vals, int Ci, int Co, int groups, int K, int nlat_in, int nlon_in,
-    int nlat_out, int nlon_out, int s, int QT) {
-    extern __shared__ float xt[];   // [cig][KP][QT]
+    int nlat_out, int nlon_out, int s, int QT, int seg) {
+    extern __shared__ float smem[];
+    float* xt = smem;                          // [cig][KP][QT]: X_K of the tile
+    float* xs = smem + (size_t)(Ci / groups) * KP * QT;   // [nslot][seg]: staged samples
     const int q0 = blockIdx.x * QT;
     const int j = blockIdx.y;
     const int bg = blockIdx.z;
@@ -146,49 +148,45 @@ __global__ __launch_bounds__(kThreads) void fused_generic(
     const int nslot = kThreads / QT;
     const int q = q0 + ql;
     const bool qvalid = q < nlon_out;
+    const T* xg = x + ((size_t)b * Ci + (size_t)grp * cig) * nlat_in * nlon_in;
 
-    for (int ci = slot; ci < cig; ci += nslot) {
+    // channels c0 + slot for c0 = 0, nslot, ...: per window, the nslot
+    // channels' samples q0 s + p_lo .. + (QT - 1) s + width - 1 (mod nlon_in)
+    // are staged in LDS once, then each thread runs its taps from there
+    for (int c0 = 0; c0 < cig; c0 += nslot) {
+        const int ci = c0 + slot;
         float acc[KP];
 #pragma unroll
         for (int k = 0; k < KP; ++k) acc[k] = 0.0f;
-        if (qvalid) {
-            const T* xc = x + ((size_t)b * Ci + (size_t)grp * cig + ci) * nlat_in * nlon_in;
-            for (int wi = w0; wi < w1; ++wi) {
-                const DevWindow wd = wins[wi];
-                const T* row = xc + (size_t)wd.lat * nlon_in;
-                const float* v = vals + (size_t)wd.val_off * KP;
-                int p = (int)(((int64_t)q * s + wd.p_lo) % nlon_in);
-                int t = 0;
-                if (nlon_in >= 8) {
-                    // eight independent loads in flight, then their taps in the
-                    // same order as the plain loop below
-                    for (; t + 8 <= wd.width; t += 8) {
-                        float xv[8];
-#pragma unroll
-                        for (int u = 0; u < 8; ++u) {
-                            int pu = p + u;
-                            if (pu >= nlon_in) pu -= nlon_in;
-                            xv[u] = load_f(row, pu);
-                        }
-#pragma unroll
-                        for (int u = 0; u < 8; ++u)
-#pragma unroll
-                            for (int k = 0; k < KP; ++k)
-                                acc[k] = fmaf(v[(t + u) * KP + k], xv[u], acc[k]);
-                        p += 8;
-                        if (p >= nlon_in) p -= nlon_in;
-                    }
+        for (int wi = w0; wi < w1; ++wi) {
+            const DevWindow wd = wins[wi];
+            const int len = (QT - 1) * s + wd.width;   // <= seg
+            const int start = (int)(((int64_t)q0 * s + wd.p_lo) % nlon_in);
+            __syncthreads();   // the previous window's samples are used
+            for (int u = threadIdx.x; u < nslot * len; u += kThreads) {
+                const int cc = u / len, uu = u - cc * len;
+                if (c0 + cc < cig) {
+                    int p = start + uu;
+                    p -= (p / nlon_in) * nlon_in;
+                    xs[cc * seg + uu] =
+                        load_f(xg + ((size_t)(c0 + cc) * nlat_in + wd.lat) * nlon_in, p);
                 }
-                for (; t < wd.width; ++t) {
-                    const float xv = load_f(row, p);
+            }
+            __syncthreads();
+            if (ci < cig && qvalid) {
+                const float* v = vals + (size_t)wd.val_off * KP;
+                const float* xr = xs + slot * seg + ql * s;
+                for (int t = 0; t < wd.width; ++t) {
+                    const float xv = xr[t];
 #pragma unroll
                     for (int k = 0; k < KP; ++k) acc[k] = fmaf(v[t * KP + k], xv, acc[k]);
-                    if (++p == nlon_in) p = 0;
                 }
             }
         }
+        if (ci < cig) {
 #pragma unroll
-        for (int k = 0; k < KP; ++k) xt[((size_t)ci * KP + k) * QT + ql] = acc[k];
+            for (int k = 0; k < KP; ++k) xt[((size_t)ci * KP + k) * QT + ql] = acc[k];
+        }
     }
     __syncthreads();
     if (!qvalid) return;
@@ -483,17 +481,25 @@ int fused_generic_launch(const disco_psi* psi, const void* x, const void* w, con
     const DevPsi& d = psi->dev;
     const disco_psi_desc& D = h.desc;
     const int cig = Ci / groups;
+    // output-tile width QT: the X_K tile [cig][KP][QT] plus the staged samples
+    // [kThreads / QT][(QT - 1) s + max_width] within 64 KiB, at most 256 and
+    // no wider than two rows' worth of outputs
+    auto lds_of = [&](int qt) {
+        const size_t seg = (size_t)(qt - 1) * h.stride + d.max_width;
+        return ((size_t)cig * KP * qt + (size_t)(kThreads / qt) * seg) * sizeof(float);
+    };
     int QT = 256;
-    while (QT > 16 && (size_t)cig * KP * QT * sizeof(float) > 64 * 1024) QT /= 2;
-    while (QT > 16 && QT / 2 >= D.nlon_out) QT /= 2;
-    const size_t lds = (size_t)cig * KP * QT * sizeof(float);
+    while (QT > 8 && lds_of(QT) > 64 * 1024) QT /= 2;
+    while (QT > 8 && QT / 2 >= D.nlon_out) QT /= 2;
+    const size_t lds = lds_of(QT);
     if (lds > 64 * 1024)
         return set_error(DISCO_EUNSUPPORTED, "Ci/groups * K too large for the generic fused kernel");
+    const int seg = (QT - 1) * h.stride + d.max_width;
     dim3 grid((D.nlon_out + QT - 1) / QT, D.nlat_out, B * groups);
     KernelTimer timer("fused_generic", st);
     hipLaunchKernelGGL((fused_generic<T, TY, KP>), grid, dim3(kThreads), lds, st, (const T*)x,
                        (const T*)w, bias, (TY*)y, d.win_ptr, d.windows, d.vals, Ci, Co, groups,
-                       h.K, D.nlat_in, D.nlon_in, D.nlat_out, D.nlon_out, h.stride, QT);
+                       h.K, D.nlat_in, D.nlon_in, D.nlat_out, D.nlon_out, h.stride, QT, seg);
     return check_launch("fused_generic");
 }
 

@@ -177,8 +177,13 @@ def cpu_baseline(wl, x, w, grid="equiangular"):
     d = oracle.Desc(wl.nlat_in, wl.nlon_in, wl.nlat_out, wl.nlon_out, wl.kernel_shape,
                     wl.theta_cutoff, grid_in=grid, grid_out=grid)
     csr = oracle.psi(d)
-    # systematic sample of output rows, all longitudes, batches and channels
-    step = max(1, wl.nlat_out // 60)
+    # systematic sample of output rows, all longitudes, batches and channels:
+    # up to 60 rows, fewer where the oracle's estimated time would pass about
+    # 30 s (its time per support point grows with B * Ci * K * nlon_out; about
+    # 6e8 of those units per second on one core, from the 721x1440 sample)
+    units = wl.B * wl.Ci * wl.K * wl.nlon_out * csr.nnz / wl.nlat_out
+    n_rows = int(max(2, min(60, 30.0 * 6e8 / max(units, 1.0))))
+    step = max(1, wl.nlat_out // n_rows)
     rows = list(range(step // 2, wl.nlat_out, step))
     sup = sum(int(csr.row_ptr[j + 1] - csr.row_ptr[j]) for j in rows)
     with threadpool_limits(limits=1):

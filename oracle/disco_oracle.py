@@ -1,4 +1,5 @@
-"""Plain CPU oracle of the forward DISCO convolution on the 2-sphere.
+"""Plain CPU oracle of the forward DISCO convolution on the 2-sphere, and of
+its gradients (the adjoints of its two linear maps, at the end of the file).
 
 TEST INFRASTRUCTURE.  Only the tests, the package's smoke check and the
 benchmark's CPU-baseline leg may import this module.  The product path (the

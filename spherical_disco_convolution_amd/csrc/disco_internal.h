@@ -5,6 +5,7 @@
 #include <hip/hip_runtime_api.h>
 
 #include <cstdint>
+#include <functional>
 #include <string>
 #include <vector>
 
@@ -48,6 +49,11 @@ struct HostPsi {
 // Validates the description and builds the host form.  Returns DISCO_OK or an
 // error code (message recorded).
 int build_host_psi(const disco_psi_desc& desc, HostPsi& out);
+
+// Runs fn(begin, end) over [0, n) in shares on up to 16 host threads.  A
+// share whose thread cannot be started runs on the calling thread; an
+// exception inside a share is caught.  Returns false if any share threw.
+bool parallel_ranges(size_t n, const std::function<void(size_t, size_t)>& fn);
 
 // Longitude-spectral tables (spectral_host.cpp), built for stride-1 layers
 // whose longitude count N is even, at most kSpecMaxN, with N/2 a product of

@@ -133,7 +133,7 @@ __global__ __launch_bounds__(kThreads) void fused_generic(
     const T* __restrict__ x, const T* __restrict__ w, const float* __restrict__ bias,
     TY* __restrict__ y, const int32_t* __restrict__ win_ptr, const DevWindow* __restrict__ wins,
     const float* __restrict__ vals, int Ci, int Co, int groups, int K, int nlat_in, int nlon_in,
-    int nlat_out, int nlon_out, int s, int QT, int seg) {
+    int nlat_out, int nlon_out, int s, int QT, int TC, int seg) {
     extern __shared__ float smem[];
     float* xt = smem;                          // [cig][KP][QT]: X_K of the tile
     float* xs = smem + (size_t)(Ci / groups) * KP * QT;   // [nslot][seg]: staged samples
@@ -149,10 +149,12 @@ __global__ __launch_bounds__(kThreads) void fused_generic(
     const int q = q0 + ql;
     const bool qvalid = q < nlon_out;
     const T* xg = x + ((size_t)b * Ci + (size_t)grp * cig) * nlat_in * nlon_in;
-
-    // channels c0 + slot for c0 = 0, nslot, ...: per window, the nslot
-    // channels' samples q0 s + p_lo .. + (QT - 1) s + width - 1 (mod nlon_in)
-    // are staged in LDS once, then each thread runs its taps from there
+    // channels c0 + slot for c0 = 0, nslot, ...: per window and chunk of at
+    // most TC taps t0 .. t0 + tw - 1, the nslot channels' samples
+    // q0 s + p_lo + t0 .. + (QT - 1) s + tw - 1 (mod nlon_in) are staged in LDS
+    // once, then each thread runs those taps from there.  The chunking keeps
+    // the staging buffer independent of the widest window (polar rows of fine
+    // grids span the whole ring).
     for (int c0 = 0; c0 < cig; c0 += nslot) {
         const int ci = c0 + slot;
         float acc[KP];
@@ -160,26 +162,29 @@ __global__ __launch_bounds__(kThreads) void fused_generic(
         for (int k = 0; k < KP; ++k) acc[k] = 0.0f;
         for (int wi = w0; wi < w1; ++wi) {
             const DevWindow wd = wins[wi];
-            const int len = (QT - 1) * s + wd.width;   // <= seg
-            const int start = (int)(((int64_t)q0 * s + wd.p_lo) % nlon_in);
-            __syncthreads();   // the previous window's samples are used
-            for (int u = threadIdx.x; u < nslot * len; u += kThreads) {
-                const int cc = u / len, uu = u - cc * len;
-                if (c0 + cc < cig) {
-                    int p = start + uu;
-                    p -= (p / nlon_in) * nlon_in;
-                    xs[cc * seg + uu] =
-                        load_f(xg + ((size_t)(c0 + cc) * nlat_in + wd.lat) * nlon_in, p);
+            for (int t0 = 0; t0 < wd.width; t0 += TC) {
+                const int tw = min(TC, wd.width - t0);
+                const int len = (QT - 1) * s + tw;   // <= seg
+                const int start = (int)(((int64_t)q0 * s + wd.p_lo + t0) % nlon_in);
+                __syncthreads();   // the previous chunk's samples are used
+                for (int u = threadIdx.x; u < nslot * len; u += kThreads) {
+                    const int cc = u / len, uu = u - cc * len;
+                    if (c0 + cc < cig) {
+                        int p = start + uu;
+                        p -= (p / nlon_in) * nlon_in;
+                        xs[cc * seg + uu] =
+                            load_f(xg + ((size_t)(c0 + cc) * nlat_in + wd.lat) * nlon_in, p);
+                    }
                 }
-            }
-            __syncthreads();
-            if (ci < cig && qvalid) {
-                const float* v = vals + (size_t)wd.val_off * KP;
-                const float* xr = xs + slot * seg + ql * s;
-                for (int t = 0; t < wd.width; ++t) {
-                    const float xv = xr[t];
+                __syncthreads();
+                if (ci < cig && qvalid) {
+                    const float* v = vals + ((size_t)wd.val_off + t0) * KP;
+                    const float* xr = xs + slot * seg + ql * s;
+                    for (int t = 0; t < tw; ++t) {
+                        const float xv = xr[t];
 #pragma unroll
-                    for (int k = 0; k < KP; ++k) acc[k] = fmaf(v[t * KP + k], xv, acc[k]);
+                        for (int k = 0; k < KP; ++k) acc[k] = fmaf(v[t * KP + k], xv, acc[k]);
+                    }
                 }
             }
         }
@@ -481,25 +486,36 @@ int fused_generic_launch(const disco_psi* psi, const void* x, const void* w, con
     const DevPsi& d = psi->dev;
     const disco_psi_desc& D = h.desc;
     const int cig = Ci / groups;
-    // output-tile width QT: the X_K tile [cig][KP][QT] plus the staged samples
-    // [kThreads / QT][(QT - 1) s + max_width] within 64 KiB, at most 256 and
-    // no wider than two rows' worth of outputs
-    auto lds_of = [&](int qt) {
-        const size_t seg = (size_t)(qt - 1) * h.stride + d.max_width;
+    // output-tile width QT and tap chunk TC: the X_K tile [cig][KP][QT] plus
+    // the staged samples [kThreads / QT][(QT - 1) s + TC] within 64 KiB.  QT is
+    // at most 256 and no wider than two rows' worth of outputs; TC is the
+    // widest window, or less (down to 16) where that does not fit.
+    auto lds_of = [&](int qt, int tc) {
+        const size_t seg = (size_t)(qt - 1) * h.stride + tc;
         return ((size_t)cig * KP * qt + (size_t)(kThreads / qt) * seg) * sizeof(float);
     };
+    const int tc_max = std::max(1, d.max_width);
     int QT = 256;
-    while (QT > 8 && lds_of(QT) > 64 * 1024) QT /= 2;
     while (QT > 8 && QT / 2 >= D.nlon_out) QT /= 2;
-    const size_t lds = lds_of(QT);
+    int TC = tc_max;
+    // the widest QT whose tile fits with chunks of at least 64 taps (or the
+    // whole widest window), then smaller chunks if even QT = 8 does not fit
+    for (;;) {
+        TC = tc_max;
+        while (TC > 64 && lds_of(QT, TC) > 64 * 1024) TC = std::max(64, TC / 2);
+        if (lds_of(QT, TC) <= 64 * 1024 || QT <= 8) break;
+        QT /= 2;
+    }
+    while (TC > 16 && lds_of(QT, TC) > 64 * 1024) TC = std::max(16, TC / 2);
+    const size_t lds = lds_of(QT, TC);
     if (lds > 64 * 1024)
         return set_error(DISCO_EUNSUPPORTED, "Ci/groups * K too large for the generic fused kernel");
-    const int seg = (QT - 1) * h.stride + d.max_width;
+    const int seg = (QT - 1) * h.stride + TC;
     dim3 grid((D.nlon_out + QT - 1) / QT, D.nlat_out, B * groups);
     KernelTimer timer("fused_generic", st);
     hipLaunchKernelGGL((fused_generic<T, TY, KP>), grid, dim3(kThreads), lds, st, (const T*)x,
                        (const T*)w, bias, (TY*)y, d.win_ptr, d.windows, d.vals, Ci, Co, groups,
-                       h.K, D.nlat_in, D.nlon_in, D.nlat_out, D.nlon_out, h.stride, QT, seg);
+                       h.K, D.nlat_in, D.nlon_in, D.nlat_out, D.nlon_out, h.stride, QT, TC, seg);
     return check_launch("fused_generic");
 }
 

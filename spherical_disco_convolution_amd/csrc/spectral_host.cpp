@@ -19,12 +19,42 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <atomic>
+#include <functional>
 #include <thread>
 #include <vector>
 
 #include "disco_internal.h"
 
 namespace disco {
+
+bool parallel_ranges(size_t n, const std::function<void(size_t, size_t)>& fn) {
+    const unsigned hw = std::max(1u, std::min(16u, std::thread::hardware_concurrency()));
+    const size_t per = (n + hw - 1) / hw;
+    std::atomic<bool> ok{true};
+    auto run = [&](size_t a, size_t b) {
+        try {
+            fn(a, b);
+        } catch (...) {
+            ok = false;
+        }
+    };
+    std::vector<std::thread> pool;
+    std::vector<std::pair<size_t, size_t>> left;   // shares no thread could take
+    for (unsigned t = 0; t < hw; ++t) {
+        const size_t a = t * per, b = std::min(n, a + per);
+        if (a >= b) continue;
+        try {
+            pool.emplace_back(run, a, b);
+        } catch (...) {   // std::system_error (thread limit) or bad_alloc
+            left.emplace_back(a, b);
+        }
+    }
+    for (const auto& r : left) run(r.first, r.second);
+    for (auto& th : pool) th.join();
+    return ok;
+}
+
 
 namespace {
 
@@ -106,14 +136,8 @@ int build_spectral_tables(const HostPsi& h, std::vector<uint32_t>& psih, int32_t
             }
         }
     };
-    const unsigned hw = std::max(1u, std::min(16u, std::thread::hardware_concurrency()));
-    const size_t per = (nwin + hw - 1) / hw;
-    std::vector<std::thread> pool;
-    for (unsigned t = 0; t < hw; ++t) {
-        const size_t a = t * per, b = std::min(nwin, a + per);
-        if (a < b) pool.emplace_back(work, a, b);
-    }
-    for (auto& th : pool) th.join();
+    if (!parallel_ranges(nwin, work))
+        return set_error(DISCO_ENOMEM, "host allocation for the spectral tables failed");
     *mp = MP;
     return DISCO_OK;
 }

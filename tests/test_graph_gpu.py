@@ -53,17 +53,27 @@ def test_fused_forward_in_a_graph(sdc, path, monkeypatch):
         monkeypatch.setenv("DISCO_FUSED_PATH", "toeplitz")
     else:
         monkeypatch.delenv("DISCO_FUSED_PATH", raising=False)
-    wl = Workload("graph", 21, 1, 64, 128, 1, 25, 100, 25, 100, (3, 3), oracle.num_basis((3, 3)),
+    # 96 longitudes: a multiple of 8, so the direct matrix-core kernel has its
+    # tap tables, and 48 = 2^4 3 for the spectral transforms
+    wl = Workload("graph", 21, 1, 64, 128, 1, 25, 96, 25, 96, (3, 3), oracle.num_basis((3, 3)),
                   0.45, "bf16")
     x, w = draw_inputs(wl)
     x, w = round_bf16(x), round_bf16(w)
     xd = torch.from_numpy(x).cuda().to(torch.bfloat16)
     wd = torch.from_numpy(w).cuda().to(torch.bfloat16)
-    psi = sdc.psi_build(25, 100, 25, 100, (3, 3), 0.45).to_device()
+    psi = sdc.psi_build(25, 96, 25, 96, (3, 3), 0.45).to_device()
     assert sdc.fused_is_spectral(psi, torch.bfloat16, 64, 128, 1) == (path == "spectral")
-    y = torch.empty(1, 128, 25, 100, device="cuda")
+    y = torch.empty(1, 128, 25, 96, device="cuda")
+    # the eager call runs the kernel the path names
+    sdc.kernel_timing(True)
+    try:
+        sdc.fused_fwd(psi, xd, wd, y=y)
+        names = set(sdc.kernel_timing_read())
+    finally:
+        sdc.kernel_timing(False)
+    assert ("spec_mfma" if path == "spectral" else "fused_mfma") in names, names
     ref = _capture_and_replay(lambda: sdc.fused_fwd(psi, xd, wd, y=y), y)
-    want = oracle.forward(oracle.Desc(25, 100, 25, 100, (3, 3), 0.45), x, w, 1)
+    want = oracle.forward(oracle.Desc(25, 96, 25, 96, (3, 3), 0.45), x, w, 1)
     err = np.linalg.norm(ref.cpu().numpy() - want) / np.linalg.norm(want)
     assert err <= 2e-2
 
@@ -79,6 +89,14 @@ def test_contract_and_einsum_in_a_graph(sdc):
     psi = sdc.psi_build(33, 64, 33, 64, (3, 3), 0.3).to_device()
     xk = torch.empty(1, 128, wl.K, 33, 64, device="cuda", dtype=torch.bfloat16)
     y = torch.empty(1, 128, 33, 64, device="cuda")
+    sdc.kernel_timing(True)
+    try:
+        sdc.contract(psi, xd, xk=xk)
+        sdc.einsum(xk, wd, y=y)
+        names = set(sdc.kernel_timing_read())
+    finally:
+        sdc.kernel_timing(False)
+    assert {"contract_mfma", "einsum_ring_bf16"} <= names, names
 
     def both():
         sdc.contract(psi, xd, xk=xk)

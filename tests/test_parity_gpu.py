@@ -40,6 +40,19 @@ def rel_l2(a, b):
     return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
 
 
+def max_rel_l2_slices(a, b):
+    """Largest relative L2 error over single output channels (axis 1) and over
+    single output rows (axis 2) of [B, C, rows, cols] arrays: an error confined
+    to one channel or one row shows here even when the global figure hides it."""
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    worst = 0.0
+    for axis in (1, 2):
+        for i in range(a.shape[axis]):
+            worst = max(worst, rel_l2(np.take(a, i, axis=axis), np.take(b, i, axis=axis)))
+    return worst
+
+
 def _tdtype(dt):
     return torch.float32 if dt == "f32" else torch.bfloat16
 
@@ -89,7 +102,29 @@ SMALL = [
     # at stride 1, two at stride 2 (the register-tiled depthwise kernel)
     W("depthwise_long_s1_f32", 1, 4, 4, 4, 13, 600, 13, 600, (3, 3), 0.5, "f32"),
     W("depthwise_long_s2_f32", 2, 3, 3, 3, 17, 1024, 9, 512, (4,), 0.6, "f32"),
+    # grouped bf16 layers on the matrix-core einsum: 64 output channels per
+    # group (the streamed kernel) and 48 per group (the general tiled kernel)
+    W("grouped_stream_bf16", 1, 64, 128, 2, 33, 64, 33, 64, (3, 3), 4 * math.pi / 32, "bf16"),
+    W("grouped_general_bf16", 2, 64, 96, 2, 33, 64, 17, 32, (3, 3), 4 * math.pi / 16, "bf16"),
 ]
+
+# which einsum kernel each grouped bf16 case must run (the dispatch rule of the
+# C ABI: bf16 groups of 64 or 128 output channels with (Ci/G) K a multiple of
+# 32 stream, other bf16 groups of >= 32 output channels use the tiled kernel)
+EINSUM_KERNEL = {"grouped_stream_bf16": "einsum_stream_bf16",
+                 "grouped_general_bf16": "einsum_mfma_bf16"}
+
+
+def kernels_run(sdc, fn):
+    """Run fn() with the library's per-kernel timing on; return (result,
+    names of the kernels it launched)."""
+    sdc.kernel_timing(True)
+    try:
+        out = fn()
+        names = set(sdc.kernel_timing_read())
+    finally:
+        sdc.kernel_timing(False)
+    return out, names
 
 
 @pytest.mark.parametrize("wl", SMALL, ids=[w.name for w in SMALL])
@@ -116,8 +151,13 @@ def test_einsum_small(sdc, wl):
     if wl.dtype == "bf16":
         xk = round_bf16(xk)
     ref = oracle.einsum(xk, w, wl.groups)
-    y = sdc.einsum(_to_dev(xk, wl.dtype), _to_dev(w, wl.dtype), groups=wl.groups).cpu().numpy()
+    xkd, wd = _to_dev(xk, wl.dtype), _to_dev(w, wl.dtype)
+    y, names = kernels_run(sdc, lambda: sdc.einsum(xkd, wd, groups=wl.groups).cpu().numpy())
+    if wl.name in EINSUM_KERNEL:
+        assert EINSUM_KERNEL[wl.name] in names, names
+    # inputs are exact on both sides: only float32 accumulation order differs
     assert rel_l2(y, ref) <= (1e-5 if wl.dtype == "f32" else 1e-5 * 10)
+    assert max_rel_l2_slices(y, ref) <= (1e-5 if wl.dtype == "f32" else 1e-4)
 
 
 @pytest.mark.parametrize("wl", SMALL, ids=[w.name for w in SMALL])
@@ -130,8 +170,13 @@ def test_fused_and_unfused_small(sdc, wl):
     xd, wd = _to_dev(x, wl.dtype), _to_dev(w, wl.dtype)
     yf = sdc.fused_fwd(psi, xd, wd, groups=wl.groups).cpu().numpy()
     assert rel_l2(yf, ref) <= TOL[wl.dtype], "fused"
-    yu = sdc.einsum(sdc.contract(psi, xd), wd, groups=wl.groups).cpu().numpy()
+    assert max_rel_l2_slices(yf, ref) <= TOL[wl.dtype], "fused, per channel / row"
+    yu, names = kernels_run(sdc, lambda: sdc.einsum(sdc.contract(psi, xd), wd,
+                                                    groups=wl.groups).cpu().numpy())
+    if wl.name in EINSUM_KERNEL:
+        assert EINSUM_KERNEL[wl.name] in names, names
     assert rel_l2(yu, ref) <= TOL[wl.dtype], "unfused"
+    assert max_rel_l2_slices(yu, ref) <= TOL[wl.dtype], "unfused, per channel / row"
 
 
 def test_bias_and_bf16_output(sdc):
@@ -259,8 +304,10 @@ def test_full_size_fused(sdc, key):
     ref = oracle.forward(d, x, w, wl.groups, rows=rows, cols_out=cols)
     got = y[:, :, rows][:, :, :, cols].cpu().numpy()
     err = rel_l2(got, ref)
-    _say(f"{key} fused rel-L2 {err:.3e}")
+    worst = max_rel_l2_slices(got, ref)
+    _say(f"{key} fused rel-L2 {err:.3e}, worst channel/row {worst:.3e}")
     assert err <= TOL[wl.dtype]
+    assert worst <= TOL[wl.dtype]
 
 
 @pytest.mark.parametrize("key", ["c1", "c2", "c3", "c4", "c5"])
@@ -285,6 +332,33 @@ def test_full_size_unfused(sdc, key):
     got_xk = xk[:, :, :, rows][:, :, :, :, cols].float().cpu().numpy()
     got = y[:, :, rows][:, :, :, cols].cpu().numpy()
     e1, e2 = rel_l2(got_xk, xk_ref), rel_l2(got, ref)
-    _say(f"{key} unfused rel-L2 xk {e1:.3e} y {e2:.3e}")
+    worst = max_rel_l2_slices(got, ref)
+    _say(f"{key} unfused rel-L2 xk {e1:.3e} y {e2:.3e}, worst channel/row {worst:.3e}")
     assert e1 <= TOL[wl.dtype]
     assert e2 <= TOL[wl.dtype]
+    assert worst <= TOL[wl.dtype]
+
+
+# the generic fused kernel at 721x1440: polar windows span the whole ring of
+# 1440 longitudes, so its staged samples come in bounded tap chunks
+WIDE = [
+    W("wide_f32_c32", 1, 32, 32, 1, 721, 1440, 721, 1440, (3, 3), 4 * math.pi / 720, "f32"),
+    W("wide_bf16_g2", 1, 64, 64, 2, 721, 1440, 721, 1440, (3, 3), 4 * math.pi / 720, "bf16"),
+]
+
+
+@pytest.mark.parametrize("wl", WIDE, ids=[w.name for w in WIDE])
+def test_fused_generic_full_ring_windows(sdc, wl):
+    _say("generic fused, full-ring windows", wl.name)
+    x, w = _prepare(wl)
+    psi = _psi(sdc, wl)
+    xd, wd = _to_dev(x, wl.dtype), _to_dev(w, wl.dtype)
+    y, names = kernels_run(sdc, lambda: sdc.fused_fwd(psi, xd, wd, groups=wl.groups))
+    assert "fused_generic" in names, names
+    rows, cols = _sample_rows(wl.nlat_out), _sample_cols(wl.nlon_out, 2)
+    ref = oracle.forward(_desc(wl), x, w, wl.groups, rows=rows, cols_out=cols)
+    got = y[:, :, rows][:, :, :, cols].cpu().numpy()
+    err, worst = rel_l2(got, ref), max_rel_l2_slices(got, ref)
+    _say(f"  rel-L2 {err:.3e}, worst channel/row {worst:.3e}")
+    assert err <= TOL[wl.dtype]
+    assert worst <= TOL[wl.dtype]

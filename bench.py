@@ -119,6 +119,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-unfused", action="store_true")
     ap.add_argument("--fused-only", action="store_true", help="time only the fused kernel (profiling)")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the peak micro-benchmarks")
     ap.add_argument("--peaks", action="store_true",
                     help="run only the peak micro-benchmarks (HBM, matrix cores, LDS) and exit")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -510,7 +511,7 @@ def main():
                                          "frac": round(gbps / HBM_PEAK_GBS, 4),
                                          "traffic": measured_traffic(key, name, args.grid)}
         del xk
-    if not args.fused_only:
+    if not args.fused_only and not args.no_peaks:
         extra["measured_peaks"] = measure_peaks()
     line = {
         "metric": METRIC,

@@ -159,6 +159,57 @@ int disco_fused_fwd(const disco_psi* psi, const void* x, int x_dtype,
 int disco_fused_is_spectral(const disco_psi* psi, int x_dtype, int32_t Ci, int32_t Co,
                             int32_t groups);
 
+/* ---- Gradients ----------------------------------------------------------
+ * The layer trains by backpropagation, and its fused mode recomputes the
+ * K-expanded intermediate in the backward pass instead of storing it
+ * (DiscreteContinuousConvS2 page, `fused` parameter); with fused=False that
+ * intermediate is saved for backward (DistributedDiscreteContinuousConvS2
+ * page, `fused` parameter).  The forward equation is linear in x and in w, so
+ * the gradients below are the adjoints of its two linear maps.  gy is the
+ * gradient of the loss with respect to y, [B, Co, nlat_out, nlon_out].  All
+ * sums are accumulated in float32; sums over points run in a fixed order, so
+ * results are reproducible.  Work is enqueued on `stream`; the calls that
+ * need scratch memory take it stream-ordered on that stream. */
+
+/* Adjoint of disco_contract:
+ *   gx[b,c,i,n] = sum over (j, q, p) with (q*s + p) mod nlon_in = n of
+ *                 sum_k Psi[k,j,(i,p)] * gxk[b,c,k,j,q]
+ * gxk: [B, C, K, nlat_out, nlon_out] of gxk_dtype; gx: [B, C, nlat_in,
+ * nlon_in] of gx_dtype, overwritten.  Each input row is gathered from the
+ * windows that reach it (no atomics).  EUNSUPPORTED when K rows of one
+ * output row (K * nlon_out floats) exceed 64 KiB. */
+int disco_contract_transpose(const disco_psi* psi, const void* gxk, int gxk_dtype, void* gx,
+                             int gx_dtype, int32_t B, int32_t C, void* stream);
+
+/* Adjoint of disco_einsum in xk:
+ *   gxk[b, G*Ci/G + ci', k, j, q] = sum_{co in group G} w[co,ci',k] * gy[b,co,j,q]
+ * gy [B, Co, nlat_out, nlon_out], w [Co, Ci/groups, K], gxk [B, Ci, K,
+ * nlat_out, nlon_out]; any dtype combination. */
+int disco_einsum_grad_xk(const void* gy, int gy_dtype, const void* w, int w_dtype, void* gxk,
+                         int gxk_dtype, int32_t B, int32_t Ci, int32_t Co, int32_t groups,
+                         int32_t K, int32_t nlat_out, int32_t nlon_out, void* stream);
+
+/* Adjoint of disco_einsum in w:
+ *   gw[co,ci',k] = sum_{b,j,q} gy[b,co,j,q] * xk[b, G(co)*Ci/G + ci', k, j, q]
+ * xk [B, Ci, K, nlat_out, nlon_out] (the saved intermediate), gy [B, Co,
+ * nlat_out, nlon_out]; gw [Co, Ci/groups, K] float32, overwritten (zeros for
+ * B = 0).  Partial sums over chunks of points, then one reduction. */
+int disco_einsum_grad_w(const void* xk, int xk_dtype, const void* gy, int gy_dtype, float* gw,
+                        int32_t B, int32_t Ci, int32_t Co, int32_t groups, int32_t K,
+                        int32_t nlat_out, int32_t nlon_out, void* stream);
+
+/* Fused-mode backward: from x, w and gy, any of
+ *   gx    [B, Ci, nlat_in, nlon_in] of gx_dtype = contract^T(einsum_grad_xk(gy, w)),
+ *   gw    [Co, Ci/groups, K] float32            = einsum_grad_w(contract(x), gy),
+ *   gbias [Co] float32                          = sum_{b,j,q} gy[b,co,j,q],
+ * each overwritten; a NULL pointer skips that gradient (not all three).
+ * X_K is recomputed in float32, in slabs of at most ceil(nlat_out / 8)
+ * output rows (one slab when the layer's two slab tensors take at most
+ * 64 MiB), so neither K-expanded tensor is ever held whole. */
+int disco_fused_bwd(const disco_psi* psi, const void* x, int x_dtype, const void* w, int w_dtype,
+                    const void* gy, int gy_dtype, void* gx, int gx_dtype, float* gw, float* gbias,
+                    int32_t B, int32_t Ci, int32_t Co, int32_t groups, void* stream);
+
 /* Per-kernel timing, for benchmarks and profiling (not part of the pages'
  * method).  With enable != 0, every kernel the library launches from then on
  * is bracketed by a pair of HIP events recorded on its launch stream; with 0,

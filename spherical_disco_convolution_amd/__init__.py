@@ -11,6 +11,11 @@ Entry points (same names as the C ABI, without the ``disco_`` prefix):
     contract(psi, x)    -> xk           [B, C, K, nlat_out, nlon_out]
     einsum(xk, w, ...)  -> y            [B, Co, nlat_out, nlon_out]
     fused_fwd(psi, x, w, ...) -> y      same result without storing xk
+  gradients (gy: gradient of the loss with respect to y):
+    contract_transpose(psi, gxk) -> gx          adjoint of contract
+    einsum_grad_xk(gy, w, ...)   -> gxk         adjoint of einsum in xk
+    einsum_grad_w(xk, gy, ...)   -> gw          adjoint of einsum in w
+    fused_bwd(psi, x, w, gy, ...) -> (gx, gw, gbias)   X_K recomputed, never whole
 """
 from __future__ import annotations
 
@@ -75,6 +80,14 @@ def _load():
         "disco_fused_fwd": (ctypes.c_int, [P, P, ctypes.c_int, P, ctypes.c_int, P, P,
                                            ctypes.c_int, I32, I32, I32, I32, P]),
         "disco_fused_is_spectral": (ctypes.c_int, [P, ctypes.c_int, I32, I32, I32]),
+        "disco_contract_transpose": (ctypes.c_int, [P, P, ctypes.c_int, P, ctypes.c_int, I32, I32,
+                                                    P]),
+        "disco_einsum_grad_xk": (ctypes.c_int, [P, ctypes.c_int, P, ctypes.c_int, P, ctypes.c_int,
+                                                I32, I32, I32, I32, I32, I32, I32, P]),
+        "disco_einsum_grad_w": (ctypes.c_int, [P, ctypes.c_int, P, ctypes.c_int, P, I32, I32, I32,
+                                               I32, I32, I32, I32, P]),
+        "disco_fused_bwd": (ctypes.c_int, [P, P, ctypes.c_int, P, ctypes.c_int, P, ctypes.c_int, P,
+                                           ctypes.c_int, P, P, I32, I32, I32, I32, P]),
         "disco_kernel_timing": (ctypes.c_int, [ctypes.c_int]),
         "disco_kernel_timing_read": (ctypes.c_int, [ctypes.c_char_p, I32, ctypes.POINTER(D),
                                                     ctypes.POINTER(I64), I32]),
@@ -91,7 +104,8 @@ def _load():
 _lib = _load()
 EXPORTED = ("disco_psi_build", "disco_psi_query", "disco_psi_export", "disco_psi_to_device",
             "disco_psi_free", "disco_contract", "disco_einsum", "disco_fused_fwd",
-            "disco_fused_is_spectral", "disco_kernel_timing", "disco_kernel_timing_read",
+            "disco_fused_is_spectral", "disco_contract_transpose", "disco_einsum_grad_xk",
+            "disco_einsum_grad_w", "disco_fused_bwd", "disco_kernel_timing", "disco_kernel_timing_read",
             "disco_last_error", "disco_version")
 
 
@@ -339,3 +353,100 @@ def fused_fwd(psi: Psi, x, w, groups: int = 1, bias=None, y=None, out_dtype=None
                                 groups, _stream(stream)), "fused_fwd")
     return y
 
+
+
+# ----------------------------------------------------------------------------
+# gradients
+# ----------------------------------------------------------------------------
+def contract_transpose(psi: Psi, gxk, gx=None, gx_dtype=None, stream=None):
+    """gx[b,c,i,(q*s+p) mod nlon_in] = sum over windows of Psi[k,j,(i,p)] gxk[b,c,k,j,q]
+    (the adjoint of contract)."""
+    torch = _torch()
+    if gxk.dim() != 5:
+        raise ValueError("gxk must be [B, C, K, nlat_out, nlon_out]")
+    B, C = gxk.shape[:2]
+    _need(gxk, "gxk", (B, C, psi.K, psi.nlat_out, psi.nlon_out))
+    if gx is None:
+        dt = torch.float32 if gx_dtype is None else gx_dtype
+        gx = torch.empty((B, C, psi.nlat_in, psi.nlon_in), dtype=dt, device=gxk.device)
+    _need(gx, "gx", (B, C, psi.nlat_in, psi.nlon_in))
+    _check(_lib.disco_contract_transpose(psi.handle, gxk.data_ptr(), _dtype_code(gxk),
+                                         gx.data_ptr(), _dtype_code(gx), B, C, _stream(stream)),
+           "contract_transpose")
+    return gx
+
+
+def einsum_grad_xk(gy, w, groups: int = 1, gxk=None, out_dtype=None, stream=None):
+    """gxk[b, G*Ci/G+ci', k, j, q] = sum_{co in G} w[co,ci',k] gy[b,co,j,q]."""
+    torch = _torch()
+    if gy.dim() != 4 or w.dim() != 3:
+        raise ValueError("gy must be [B, Co, nlat_out, nlon_out] and w [Co, Ci/groups, K]")
+    B, Co, H, W = gy.shape
+    _need(gy, "gy", (B, Co, H, W))
+    if groups < 1 or Co % groups or w.shape[0] != Co:
+        raise ValueError(f"w must have {Co} rows and groups ({groups}) must divide them")
+    Ci, K = w.shape[1] * groups, w.shape[2]
+    _need(w, "w", (Co, Ci // groups, K))
+    if gxk is None:
+        dt = torch.float32 if out_dtype is None else out_dtype
+        gxk = torch.empty((B, Ci, K, H, W), dtype=dt, device=gy.device)
+    _need(gxk, "gxk", (B, Ci, K, H, W))
+    _check(_lib.disco_einsum_grad_xk(gy.data_ptr(), _dtype_code(gy), w.data_ptr(), _dtype_code(w),
+                                     gxk.data_ptr(), _dtype_code(gxk), B, Ci, Co, groups, K, H, W,
+                                     _stream(stream)), "einsum_grad_xk")
+    return gxk
+
+
+def einsum_grad_w(xk, gy, groups: int = 1, gw=None, stream=None):
+    """gw[co,ci',k] = sum_{b,j,q} gy[b,co,j,q] xk[b, G(co)*Ci/G+ci', k, j, q] (float32)."""
+    torch = _torch()
+    if xk.dim() != 5 or gy.dim() != 4:
+        raise ValueError("xk must be [B, Ci, K, nlat_out, nlon_out] and gy [B, Co, nlat_out, nlon_out]")
+    B, Ci, K, H, W = xk.shape
+    Co = gy.shape[1]
+    _need(xk, "xk", (B, Ci, K, H, W))
+    _need(gy, "gy", (B, Co, H, W))
+    if groups < 1 or Ci % groups or Co % groups:
+        raise ValueError(f"groups ({groups}) must divide in_channels ({Ci}) and out_channels ({Co})")
+    if gw is None:
+        gw = torch.empty((Co, Ci // groups, K), dtype=torch.float32, device=xk.device)
+    _need(gw, "gw", (Co, Ci // groups, K))
+    if gw.dtype != torch.float32:
+        raise ValueError("gw must be float32")
+    _check(_lib.disco_einsum_grad_w(xk.data_ptr(), _dtype_code(xk), gy.data_ptr(), _dtype_code(gy),
+                                    gw.data_ptr(), B, Ci, Co, groups, K, H, W, _stream(stream)),
+           "einsum_grad_w")
+    return gw
+
+
+def fused_bwd(psi: Psi, x, w, gy, groups: int = 1, need_gx: bool = True, need_gw: bool = True,
+              need_gbias: bool = False, gx_dtype=None, stream=None):
+    """Gradients (gx, gw, gbias) of sum(gy * fused_fwd(psi, x, w)) with X_K
+    recomputed slab by slab; entries not asked for are None."""
+    torch = _torch()
+    if x.dim() != 4 or w.dim() != 3 or gy.dim() != 4:
+        raise ValueError("x must be [B, Ci, nlat_in, nlon_in], w [Co, Ci/groups, K] and gy "
+                         "[B, Co, nlat_out, nlon_out]")
+    B, Ci = x.shape[:2]
+    Co = w.shape[0]
+    _need(x, "x", (B, Ci, psi.nlat_in, psi.nlon_in))
+    if groups < 1 or Ci % groups or Co % groups:
+        raise ValueError(f"groups ({groups}) must divide in_channels ({Ci}) and out_channels ({Co})")
+    _need(w, "w", (Co, Ci // groups, psi.K))
+    _need(gy, "gy", (B, Co, psi.nlat_out, psi.nlon_out))
+    gx = gw = gb = None
+    if need_gx:
+        gx = torch.empty((B, Ci, psi.nlat_in, psi.nlon_in),
+                         dtype=torch.float32 if gx_dtype is None else gx_dtype, device=x.device)
+    if need_gw:
+        gw = torch.empty((Co, Ci // groups, psi.K), dtype=torch.float32, device=x.device)
+    if need_gbias:
+        gb = torch.empty((Co,), dtype=torch.float32, device=x.device)
+    _check(_lib.disco_fused_bwd(psi.handle, x.data_ptr(), _dtype_code(x), w.data_ptr(),
+                                _dtype_code(w), gy.data_ptr(), _dtype_code(gy),
+                                gx.data_ptr() if gx is not None else None,
+                                _dtype_code(gx) if gx is not None else F32,
+                                gw.data_ptr() if gw is not None else None,
+                                gb.data_ptr() if gb is not None else None,
+                                B, Ci, Co, groups, _stream(stream)), "fused_bwd")
+    return gx, gw, gb

@@ -25,6 +25,7 @@ SOURCES = [
     "kernels_einsum_mfma.hip",
     "kernels_fused_mfma.hip",
     "kernels_spectral.hip",
+    "kernels_backward.hip",
     "spectral_host.cpp",
     "kernel_timing.cpp",
 ]

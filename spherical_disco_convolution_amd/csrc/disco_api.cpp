@@ -199,6 +199,25 @@ int disco_psi_to_device(disco_psi* psi) {
         wins[n].val_off = (int32_t)h.windows[n].val_off;
         d.max_width = std::max(d.max_width, h.windows[n].width);
     }
+    // the transposed list: windows grouped by input row, then by output row
+    const int nlat_in = h.desc.nlat_in;
+    std::vector<int32_t> wtptr(nlat_in + 1, 0);
+    std::vector<DevWindow> wins_t(wins.size());
+    {
+        std::vector<int32_t> out_row(wins.size());
+        for (int j = 0; j < nlat_out; ++j)
+            for (int n = wptr[j]; n < wptr[j + 1]; ++n) out_row[n] = j;
+        for (const DevWindow& w : wins) ++wtptr[w.lat + 1];
+        for (int i = 0; i < nlat_in; ++i) wtptr[i + 1] += wtptr[i];
+        std::vector<int32_t> fill(wtptr.begin(), wtptr.end() - 1);
+        // forward windows are in output-row order, so each input row's list
+        // comes out sorted by output row
+        for (size_t n = 0; n < wins.size(); ++n) {
+            DevWindow t = wins[n];
+            t.lat = out_row[n];
+            wins_t[fill[wins[n].lat]++] = t;
+        }
+    }
     for (int j = 0; j < nlat_out; ++j) {
         d.max_windows = std::max(d.max_windows, wptr[j + 1] - wptr[j]);
         d.max_row_points = std::max(
@@ -219,6 +238,12 @@ int disco_psi_to_device(disco_psi* psi) {
     if ((rc = dev_alloc(d, &p, wins.size() * sizeof(DevWindow))) != DISCO_OK) goto fail;
     d.windows = static_cast<DevWindow*>(p);
     if ((rc = dev_copy(p, wins.data(), wins.size() * sizeof(DevWindow))) != DISCO_OK) goto fail;
+    if ((rc = dev_alloc(d, &p, wtptr.size() * sizeof(int32_t))) != DISCO_OK) goto fail;
+    d.wint_ptr = static_cast<int32_t*>(p);
+    if ((rc = dev_copy(p, wtptr.data(), wtptr.size() * sizeof(int32_t))) != DISCO_OK) goto fail;
+    if ((rc = dev_alloc(d, &p, wins_t.size() * sizeof(DevWindow))) != DISCO_OK) goto fail;
+    d.wins_t = static_cast<DevWindow*>(p);
+    if ((rc = dev_copy(p, wins_t.data(), wins_t.size() * sizeof(DevWindow))) != DISCO_OK) goto fail;
     if ((rc = dev_alloc(d, &p, vals.size() * sizeof(float))) != DISCO_OK) goto fail;
     d.vals = static_cast<float*>(p);
     if ((rc = dev_copy(p, vals.data(), vals.size() * sizeof(float))) != DISCO_OK) goto fail;
@@ -325,10 +350,15 @@ int disco_fused_is_spectral(const disco_psi* psi, int x_dtype, int32_t Ci, int32
     return fused_spectral_eligible(psi, x_dtype, Ci, Co, groups);
 }
 
-int disco_fused_fwd(const disco_psi* psi, const void* x, int x_dtype, const void* w, int w_dtype,
-                    const float* bias, void* y, int y_dtype, int32_t B, int32_t Ci, int32_t Co,
-                    int32_t groups, void* stream) {
-    clear_error();
+}  // extern "C"
+
+namespace {
+// Argument checks shared by the two fused entry points; *skip = true for an
+// empty batch (nothing to do).
+int check_fused_args(const disco_psi* psi, const void* x, int x_dtype, const void* w, int w_dtype,
+                     const float* bias, void* y, int y_dtype, int32_t B, int32_t Ci, int32_t Co,
+                     int32_t groups, bool* skip) {
+    *skip = false;
     if (psi == nullptr) return set_error(DISCO_EINVAL, "psi handle is NULL");
     if (!valid_dtype(x_dtype) || !valid_dtype(w_dtype) || !valid_dtype(y_dtype))
         return set_error(DISCO_EINVAL, "unknown dtype code (x %d, w %d, y %d)", x_dtype, w_dtype,
@@ -341,7 +371,10 @@ int disco_fused_fwd(const disco_psi* psi, const void* x, int x_dtype, const void
         return set_error(DISCO_EINVAL,
                          "groups (%d) must divide in_channels (%d) and out_channels (%d)", groups,
                          Ci, Co);
-    if (B == 0) return DISCO_OK;
+    if (B == 0) {
+        *skip = true;
+        return DISCO_OK;
+    }
     int dev = -1;
     int rc = current_device(&dev);
     if (rc != DISCO_OK) return rc;
@@ -356,7 +389,158 @@ int disco_fused_fwd(const disco_psi* psi, const void* x, int x_dtype, const void
     const size_t ny = (size_t)B * Co * d.nlat_out * d.nlon_out * dtype_size(y_dtype);
     if (overlap(y, ny, x, nx) || overlap(y, ny, w, nw) || (bias && overlap(y, ny, bias, Co * 4)))
         return set_error(DISCO_EINVAL, "y overlaps an input");
+    return DISCO_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int disco_fused_fwd(const disco_psi* psi, const void* x, int x_dtype, const void* w, int w_dtype,
+                    const float* bias, void* y, int y_dtype, int32_t B, int32_t Ci, int32_t Co,
+                    int32_t groups, void* stream) {
+    clear_error();
+    bool skip = false;
+    int rc = check_fused_args(psi, x, x_dtype, w, w_dtype, bias, y, y_dtype, B, Ci, Co, groups,
+                              &skip);
+    if (rc != DISCO_OK || skip) return rc;
     return launch_fused(psi, x, x_dtype, w, bias, y, y_dtype, B, Ci, Co, groups, stream);
+}
+
+int disco_contract_transpose(const disco_psi* psi, const void* gxk, int gxk_dtype, void* gx,
+                             int gx_dtype, int32_t B, int32_t C, void* stream) {
+    clear_error();
+    if (psi == nullptr) return set_error(DISCO_EINVAL, "psi handle is NULL");
+    if (!valid_dtype(gxk_dtype) || !valid_dtype(gx_dtype))
+        return set_error(DISCO_EINVAL, "unknown dtype code (gxk %d, gx %d)", gxk_dtype, gx_dtype);
+    if (B < 0 || C < 0) return set_error(DISCO_EINVAL, "B and C must be >= 0 (got %d, %d)", B, C);
+    if (B == 0 || C == 0) return DISCO_OK;
+    int dev = -1;
+    int rc = current_device(&dev);
+    if (rc != DISCO_OK) return rc;
+    if ((rc = check_psi_on_device(psi, dev)) != DISCO_OK) return rc;
+    if ((rc = check_device_ptr(gxk, "gxk", dev)) != DISCO_OK) return rc;
+    if ((rc = check_device_ptr(gx, "gx", dev)) != DISCO_OK) return rc;
+    const disco_psi_desc& d = psi->host.desc;
+    const size_t ngx = (size_t)B * C * d.nlat_in * d.nlon_in * dtype_size(gx_dtype);
+    const size_t ngxk =
+        (size_t)B * C * psi->host.K * d.nlat_out * d.nlon_out * dtype_size(gxk_dtype);
+    if (overlap(gx, ngx, gxk, ngxk)) return set_error(DISCO_EINVAL, "gx and gxk overlap");
+    return launch_contract_transpose(psi, gxk, gxk_dtype, gx, gx_dtype, B, C, stream);
+}
+
+namespace {
+int check_einsum_sizes(int32_t B, int32_t Ci, int32_t Co, int32_t groups, int32_t K,
+                       int32_t nlat_out, int32_t nlon_out) {
+    if (B < 0 || Ci < 1 || Co < 1 || K < 1 || nlat_out < 1 || nlon_out < 1)
+        return set_error(DISCO_EINVAL, "sizes must be positive (B %d Ci %d Co %d K %d nlat_out %d "
+                         "nlon_out %d)", B, Ci, Co, K, nlat_out, nlon_out);
+    if (groups < 1 || Ci % groups != 0 || Co % groups != 0)
+        return set_error(DISCO_EINVAL,
+                         "groups (%d) must divide in_channels (%d) and out_channels (%d)", groups,
+                         Ci, Co);
+    return DISCO_OK;
+}
+}  // namespace
+
+int disco_einsum_grad_xk(const void* gy, int gy_dtype, const void* w, int w_dtype, void* gxk,
+                         int gxk_dtype, int32_t B, int32_t Ci, int32_t Co, int32_t groups,
+                         int32_t K, int32_t nlat_out, int32_t nlon_out, void* stream) {
+    clear_error();
+    if (!valid_dtype(gy_dtype) || !valid_dtype(w_dtype) || !valid_dtype(gxk_dtype))
+        return set_error(DISCO_EINVAL, "unknown dtype code (gy %d, w %d, gxk %d)", gy_dtype,
+                         w_dtype, gxk_dtype);
+    int rc = check_einsum_sizes(B, Ci, Co, groups, K, nlat_out, nlon_out);
+    if (rc != DISCO_OK || B == 0) return rc;
+    int dev = -1;
+    if ((rc = current_device(&dev)) != DISCO_OK) return rc;
+    if ((rc = check_device_ptr(gy, "gy", dev)) != DISCO_OK) return rc;
+    if ((rc = check_device_ptr(w, "w", dev)) != DISCO_OK) return rc;
+    if ((rc = check_device_ptr(gxk, "gxk", dev)) != DISCO_OK) return rc;
+    const size_t hw = (size_t)nlat_out * nlon_out;
+    const size_t ngxk = (size_t)B * Ci * K * hw * dtype_size(gxk_dtype);
+    const size_t ngy = (size_t)B * Co * hw * dtype_size(gy_dtype);
+    const size_t nw = (size_t)Co * (Ci / groups) * K * dtype_size(w_dtype);
+    if (overlap(gxk, ngxk, gy, ngy) || overlap(gxk, ngxk, w, nw))
+        return set_error(DISCO_EINVAL, "gxk overlaps an input");
+    return launch_einsum_grad_xk(gy, gy_dtype, w, w_dtype, gxk, gxk_dtype, B, Ci, Co, groups, K,
+                                 nlat_out, nlon_out, stream);
+}
+
+int disco_einsum_grad_w(const void* xk, int xk_dtype, const void* gy, int gy_dtype, float* gw,
+                        int32_t B, int32_t Ci, int32_t Co, int32_t groups, int32_t K,
+                        int32_t nlat_out, int32_t nlon_out, void* stream) {
+    clear_error();
+    if (!valid_dtype(xk_dtype) || !valid_dtype(gy_dtype))
+        return set_error(DISCO_EINVAL, "unknown dtype code (xk %d, gy %d)", xk_dtype, gy_dtype);
+    int rc = check_einsum_sizes(B, Ci, Co, groups, K, nlat_out, nlon_out);
+    if (rc != DISCO_OK) return rc;
+    int dev = -1;
+    if ((rc = current_device(&dev)) != DISCO_OK) return rc;
+    if ((rc = check_device_ptr(gw, "gw", dev)) != DISCO_OK) return rc;
+    const size_t ngw = (size_t)Co * (Ci / groups) * K;
+    if (B == 0) return launch_fill_zero(gw, ngw, stream);   // an empty sum
+    if ((rc = check_device_ptr(xk, "xk", dev)) != DISCO_OK) return rc;
+    if ((rc = check_device_ptr(gy, "gy", dev)) != DISCO_OK) return rc;
+    const size_t hw = (size_t)nlat_out * nlon_out;
+    const size_t nxk = (size_t)B * Ci * K * hw * dtype_size(xk_dtype);
+    const size_t ngy = (size_t)B * Co * hw * dtype_size(gy_dtype);
+    if (overlap(gw, ngw * 4, xk, nxk) || overlap(gw, ngw * 4, gy, ngy))
+        return set_error(DISCO_EINVAL, "gw overlaps an input");
+    return launch_einsum_grad_w(xk, xk_dtype, gy, gy_dtype, gw, B, Ci, Co, groups, K, nlat_out,
+                                nlon_out, stream);
+}
+
+int disco_fused_bwd(const disco_psi* psi, const void* x, int x_dtype, const void* w, int w_dtype,
+                    const void* gy, int gy_dtype, void* gx, int gx_dtype, float* gw, float* gbias,
+                    int32_t B, int32_t Ci, int32_t Co, int32_t groups, void* stream) {
+    clear_error();
+    if (psi == nullptr) return set_error(DISCO_EINVAL, "psi handle is NULL");
+    if (!valid_dtype(x_dtype) || !valid_dtype(w_dtype) || !valid_dtype(gy_dtype) ||
+        (gx && !valid_dtype(gx_dtype)))
+        return set_error(DISCO_EINVAL, "unknown dtype code (x %d, w %d, gy %d, gx %d)", x_dtype,
+                         w_dtype, gy_dtype, gx_dtype);
+    if (gx == nullptr && gw == nullptr && gbias == nullptr)
+        return set_error(DISCO_EINVAL, "gx, gw and gbias are all NULL: nothing to compute");
+    const disco_psi_desc& d = psi->host.desc;
+    const int K = psi->host.K;
+    int rc = check_einsum_sizes(B, Ci, Co, groups, K, d.nlat_out, d.nlon_out);
+    if (rc != DISCO_OK) return rc;
+    int dev = -1;
+    if ((rc = current_device(&dev)) != DISCO_OK) return rc;
+    if ((rc = check_psi_on_device(psi, dev)) != DISCO_OK) return rc;
+    if (gw && (rc = check_device_ptr(gw, "gw", dev)) != DISCO_OK) return rc;
+    if (gbias && (rc = check_device_ptr(gbias, "gbias", dev)) != DISCO_OK) return rc;
+    const size_t ngw = (size_t)Co * (Ci / groups) * K;
+    if (B == 0) {   // empty sums; gx has no elements
+        if (gw && (rc = launch_fill_zero(gw, ngw, stream)) != DISCO_OK) return rc;
+        if (gbias && (rc = launch_fill_zero(gbias, (size_t)Co, stream)) != DISCO_OK) return rc;
+        return DISCO_OK;
+    }
+    if ((rc = check_device_ptr(gy, "gy", dev)) != DISCO_OK) return rc;
+    if ((gx || gw) && (rc = check_device_ptr(x, "x", dev)) != DISCO_OK) return rc;
+    if (gx && (rc = check_device_ptr(w, "w", dev)) != DISCO_OK) return rc;
+    if (gx && (rc = check_device_ptr(gx, "gx", dev)) != DISCO_OK) return rc;
+    const size_t nx = (size_t)B * Ci * d.nlat_in * d.nlon_in * dtype_size(x_dtype);
+    const size_t nw = (size_t)Co * (Ci / groups) * K * dtype_size(w_dtype);
+    const size_t ngy = (size_t)B * Co * d.nlat_out * d.nlon_out * dtype_size(gy_dtype);
+    const size_t ngx = gx ? (size_t)B * Ci * d.nlat_in * d.nlon_in * dtype_size(gx_dtype) : 0;
+    struct Span {
+        const void* p;
+        size_t n;
+    };
+    const Span outs[3] = {{gx, ngx}, {gw, gw ? ngw * 4 : 0}, {gbias, gbias ? (size_t)Co * 4 : 0}};
+    const Span ins[3] = {{x, (gx || gw) ? nx : 0}, {w, gx ? nw : 0}, {gy, ngy}};
+    for (int a = 0; a < 3; ++a) {
+        if (!outs[a].p) continue;
+        for (int b2 = 0; b2 < 3; ++b2)
+            if (ins[b2].p && overlap(outs[a].p, outs[a].n, ins[b2].p, ins[b2].n))
+                return set_error(DISCO_EINVAL, "a gradient output overlaps an input");
+        for (int b2 = a + 1; b2 < 3; ++b2)
+            if (outs[b2].p && overlap(outs[a].p, outs[a].n, outs[b2].p, outs[b2].n))
+                return set_error(DISCO_EINVAL, "gradient outputs overlap");
+    }
+    return launch_fused_bwd(psi, x, x_dtype, w, w_dtype, gy, gy_dtype, gx, gx_dtype, gw, gbias, B,
+                            Ci, Co, groups, stream);
 }
 
 }  // extern "C"

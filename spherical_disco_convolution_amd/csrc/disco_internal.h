@@ -86,6 +86,10 @@ struct DevPsi {
     int32_t* win_ptr = nullptr;   // [nlat_out + 1]
     DevWindow* windows = nullptr; // [nwin]
     float* vals = nullptr;        // [nnz, KP] float32, window order, zero padded
+    // the same windows listed per input row (sorted by output row), for the
+    // adjoint of the contraction; their `lat` field holds the output row
+    int32_t* wint_ptr = nullptr;  // [nlat_in + 1]
+    DevWindow* wins_t = nullptr;  // [nwin]
     // bf16 tap tables for the matrix-core fused kernel (see kernels_fused_mfma.hip)
     void* mfma_taps = nullptr;
     int64_t mfma_taps_bytes = 0;
@@ -120,6 +124,20 @@ int launch_fused(const disco_psi* psi, const void* x, int dtype, const void* w,
                  void* stream);
 // 1 if disco_fused_fwd takes the longitude-spectral path for these arguments
 int fused_spectral_eligible(const disco_psi* psi, int x_dtype, int Ci, int Co, int groups);
+
+// Backward (kernels_backward.hip)
+int launch_fill_zero(float* p, size_t n, void* stream);
+int launch_contract_transpose(const disco_psi* psi, const void* gxk, int gxk_dtype, void* gx,
+                              int gx_dtype, int B, int C, void* stream);
+int launch_einsum_grad_xk(const void* gy, int gy_dtype, const void* w, int w_dtype, void* gxk,
+                          int gxk_dtype, int B, int Ci, int Co, int groups, int K, int nlat_out,
+                          int nlon_out, void* stream);
+int launch_einsum_grad_w(const void* xk, int xk_dtype, const void* gy, int gy_dtype, float* gw,
+                         int B, int Ci, int Co, int groups, int K, int nlat_out, int nlon_out,
+                         void* stream);
+int launch_fused_bwd(const disco_psi* psi, const void* x, int x_dtype, const void* w, int w_dtype,
+                     const void* gy, int gy_dtype, void* gx, int gx_dtype, float* gw, float* gbias,
+                     int B, int Ci, int Co, int groups, void* stream);
 
 // Scope around one kernel launch: while disco_kernel_timing(1) is in effect,
 // records a HIP event on the launch stream at construction and at

@@ -1,0 +1,579 @@
+// Gradients of the forward DISCO convolution (gfx950, wave64, vector ALUs,
+// float32 accumulation).
+//
+// The forward equation of the DiscreteContinuousConvS2 page is linear in x
+// and in w, so its gradients are the adjoints of its two linear maps:
+//  * grad_xk[b, G*Ci/G + ci', k, j, q] = sum_{co in G} w[co, ci', k] gy[b, co, j, q]
+//    (adjoint of the channel/basis sum in X_K)          -> einsum_grad_xk
+//  * grad_w[co, ci', k] = sum_{b, j, q} gy[b, co, j, q] X_K[b, G(co)*Ci/G + ci', k, j, q]
+//    (adjoint of the channel/basis sum in w)            -> grad_w_partial + reduce
+//  * grad_x[b, c, i, (q s + p) mod nlon_in] += sum_k Psi[k, j, (i, p)] grad_xk[b, c, k, j, q]
+//    (adjoint of the sparse contraction)                -> contract_t_kernel
+// The page's fused mode recomputes X_K in the backward pass instead of
+// storing it; disco_fused_bwd does that in slabs of output rows, so the whole
+// K-expanded tensor never exists at once.
+//
+// Every kernel takes a window of output rows [row0, row0 + nrows): the
+// K-expanded tensors it reads or writes hold only those rows ([B, C, K,
+// nrows, nlon_out]); gy is always the whole [B, Co, nlat_out, nlon_out].
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+
+#include "disco_internal.h"
+#include "kernels_common.h"
+
+namespace disco {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+// ---------------------------------------------------------------------------
+// Adjoint of the contraction, gathered per input row (no atomics): one
+// workgroup per (input row i, channel c, batch b) sums over the windows
+// (j, i) of its transposed window list with j in the slab.  With
+// d = (n - p_lo - t) mod nlon_in, output q = d / s receives tap t from input
+// longitude n exactly when s divides d; walking t in steps of s from the
+// first such tap moves q down by one each step.  The window's K rows of
+// grad_xk (K x nlon_out floats) and a chunk of TC taps are staged in LDS.
+// ---------------------------------------------------------------------------
+template <typename TG, typename TO, int KP, int QR>
+__global__ __launch_bounds__(kThreads) void contract_t_kernel(
+    const TG* __restrict__ gxk, TO* __restrict__ gx, const int32_t* __restrict__ wt_ptr,
+    const DevWindow* __restrict__ wt, const float* __restrict__ vals, int C, int K, int nlat_in,
+    int nlon_in, int nlon_out, int s, int row0, int nrows, int accumulate, int TC) {
+    extern __shared__ float smem[];
+    float* G = smem;                              // [K][nlon_out]
+    float* tp = smem + (size_t)K * nlon_out;      // [TC][KP]
+    const int i = blockIdx.x, c = blockIdx.y, b = blockIdx.z;
+    const int w0 = wt_ptr[i], w1 = wt_ptr[i + 1];
+    TO* out = gx + (((size_t)b * C + c) * nlat_in + i) * nlon_in;
+    // windows of this input row whose output row lies in the slab (uniform)
+    bool any = false;
+    for (int wi = w0; wi < w1; ++wi) {
+        const int jr = wt[wi].lat - row0;
+        any = any || (jr >= 0 && jr < nrows);
+    }
+    if (accumulate && !any) return;
+    for (int n0 = 0; n0 < nlon_in; n0 += kThreads * QR) {
+        float acc[QR];
+#pragma unroll
+        for (int r = 0; r < QR; ++r) acc[r] = 0.0f;
+        for (int wi = w0; wi < w1; ++wi) {
+            const DevWindow wd = wt[wi];    // wd.lat is the output row j
+            const int jr = wd.lat - row0;
+            if (jr < 0 || jr >= nrows) continue;
+            const TG* gsrc = gxk + (((size_t)b * C + c) * K * nrows + jr) * nlon_out;
+            __syncthreads();   // the previous window's rows and taps are used
+            for (int u = threadIdx.x; u < K * nlon_out; u += kThreads) {
+                const int k = u / nlon_out, q = u - k * nlon_out;
+                G[u] = load_f(gsrc, (size_t)k * nrows * nlon_out + q);
+            }
+            for (int t0 = 0; t0 < wd.width; t0 += TC) {
+                const int tw = min(TC, wd.width - t0);
+                if (t0 > 0) __syncthreads();   // the previous chunk's taps are used
+                const float* v = vals + ((size_t)wd.val_off + t0) * KP;
+                for (int u = threadIdx.x; u < tw * KP; u += kThreads) tp[u] = v[u];
+                __syncthreads();
+#pragma unroll
+                for (int r = 0; r < QR; ++r) {
+                    const int n = n0 + threadIdx.x + kThreads * r;
+                    if (n >= nlon_in) continue;
+                    int d0 = (n - wd.p_lo - t0) % nlon_in;
+                    if (d0 < 0) d0 += nlon_in;
+                    const int ts = d0 % s;
+                    int q = (d0 - ts) / s;
+                    float a = 0.0f;
+                    for (int t = ts; t < tw; t += s) {
+                        const float* tv = tp + t * KP;
+#pragma unroll
+                        for (int k = 0; k < KP; ++k)
+                            if (k < K) a = fmaf(tv[k], G[k * nlon_out + q], a);
+                        if (--q < 0) q += nlon_out;
+                    }
+                    acc[r] += a;
+                }
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < QR; ++r) {
+            const int n = n0 + threadIdx.x + kThreads * r;
+            if (n >= nlon_in) continue;
+            const float prev = accumulate ? load_f(out, n) : 0.0f;
+            store_f(out, n, prev + acc[r]);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// grad_w partial sums: a 64 x 64 tile of [co in group][kappa = (ci', k)]
+// summed over one chunk of L output points (r, q) of one batch entry,
+// staged 16 points at a time through LDS; thread = 4 x 4 outputs.
+// partial[(b * nchunk + chunk)][co][kappa], co over all groups.
+// ---------------------------------------------------------------------------
+constexpr int kGwT = 64;   // tile edge
+constexpr int kGwS = 16;   // points per step
+template <typename TX, typename TG>
+__global__ __launch_bounds__(kThreads) void grad_w_partial(
+    const TX* __restrict__ xk, const TG* __restrict__ gy, float* __restrict__ partial, int Ci,
+    int Co, int groups, int K, int nlat_out, int nlon_out, int row0, int nrows, int L,
+    int nchunk) {
+    __shared__ float As[kGwS][kGwT + 4];   // gy[co][n]
+    __shared__ float Bs[kGwS][kGwT + 4];   // xk[kappa][n]
+    const int cig = Ci / groups, cog = Co / groups;
+    const int kd = cig * K;
+    const int kt = blockIdx.x, ct = blockIdx.y;
+    const int z = blockIdx.z;
+    const int chunk = z % nchunk;
+    const int bg = z / nchunk;
+    const int g = bg % groups, b = bg / groups;
+    const size_t P = (size_t)nrows * nlon_out;   // points of the slab
+    const size_t n0 = (size_t)chunk * L;
+    const size_t n1 = min(P, n0 + (size_t)L);
+    const int tx = threadIdx.x % 16, ty = threadIdx.x / 16;
+    // load roles: element e = threadIdx.x + 256 u (u < 4) of the 64 x 16 tile:
+    // row e / 16, point e % 16
+    const TG* gyb = gy + ((size_t)b * Co + (size_t)g * cog) * nlat_out * nlon_out +
+                    (size_t)row0 * nlon_out;
+    const TX* xkb = xk + ((size_t)b * Ci + (size_t)g * cig) * K * P;
+    float acc[4][4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[a][e] = 0.0f;
+    for (size_t nb = n0; nb < n1; nb += kGwS) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int e = threadIdx.x + kThreads * u;
+            const int row = e / kGwS, p = e % kGwS;
+            const size_t n = nb + p;
+            const int co = ct * kGwT + row;
+            const int kap = kt * kGwT + row;
+            As[p][row] = (co < cog && n < n1)
+                             ? load_f(gyb, (size_t)co * nlat_out * nlon_out + n)
+                             : 0.0f;
+            Bs[p][row] = (kap < kd && n < n1) ? load_f(xkb, (size_t)kap * P + n) : 0.0f;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int p = 0; p < kGwS; ++p) {
+            float av[4], bv[4];
+#pragma unroll
+            for (int a = 0; a < 4; ++a) av[a] = As[p][ty + 16 * a];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) bv[e] = Bs[p][tx + 16 * e];
+#pragma unroll
+            for (int a = 0; a < 4; ++a)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[a][e] = fmaf(av[a], bv[e], acc[a][e]);
+        }
+        __syncthreads();
+    }
+    float* out = partial + (size_t)(b * nchunk + chunk) * Co * kd;
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+        const int co = ct * kGwT + ty + 16 * a;
+        if (co >= cog) continue;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int kap = kt * kGwT + tx + 16 * e;
+            if (kap < kd) out[((size_t)g * cog + co) * kd + kap] = acc[a][e];
+        }
+    }
+}
+
+// gw[e] (+)= sum over the nparts partial arrays of e, in a fixed order
+__global__ __launch_bounds__(kThreads) void reduce_partials(const float* __restrict__ partial,
+                                                            float* __restrict__ gw, size_t n,
+                                                            int nparts, int accumulate) {
+    const size_t e = (size_t)blockIdx.x * kThreads + threadIdx.x;
+    if (e >= n) return;
+    float a = accumulate ? gw[e] : 0.0f;
+    for (int p = 0; p < nparts; ++p) a += partial[(size_t)p * n + e];
+    gw[e] = a;
+}
+
+// ---------------------------------------------------------------------------
+// grad_xk for a slab: thread = output point n of the slab plane, COT pairs
+// (ci', k) of one group per workgroup row; weights are wave-uniform.
+//   gxk[b, g cig + ci', k, r, q] = sum_{co' < cog} w[g cog + co', ci', k] gy[b, g cog + co', row0 + r, q]
+// ---------------------------------------------------------------------------
+template <typename TG, typename TW, typename TO, int COT>
+__global__ __launch_bounds__(kThreads) void einsum_grad_xk_kernel(
+    const TG* __restrict__ gy, const TW* __restrict__ w, TO* __restrict__ gxk, int Ci, int Co,
+    int groups, int K, int nlat_out, int nlon_out, int row0, int nrows) {
+    const int cig = Ci / groups, cog = Co / groups;
+    const int kd = cig * K;
+    const size_t P = (size_t)nrows * nlon_out;
+    const size_t n = (size_t)blockIdx.x * kThreads + threadIdx.x;
+    const int oc0 = blockIdx.y * COT;      // first (ci, k) pair over all groups: ci * K + k
+    const int b = blockIdx.z;
+    const int g = oc0 / kd;
+    if (n >= P) return;
+    float acc[COT];
+#pragma unroll
+    for (int c = 0; c < COT; ++c) acc[c] = 0.0f;
+    const TG* gyb = gy + ((size_t)b * Co + (size_t)g * cog) * nlat_out * nlon_out +
+                    (size_t)row0 * nlon_out + n;
+    const int kap0 = oc0 - g * kd;          // (ci', k) within the group
+    for (int co = 0; co < cog; ++co) {
+        const float gv = load_f(gyb, (size_t)co * nlat_out * nlon_out);
+        const TW* wr = w + ((size_t)g * cog + co) * kd + kap0;
+#pragma unroll
+        for (int c = 0; c < COT; ++c) acc[c] = fmaf(load_f(wr, c), gv, acc[c]);
+    }
+    // gxk layout [B, Ci, K, nrows, nlon_out]: pair oc = ci * K + k is plane oc
+    TO* out = gxk + ((size_t)b * Ci * K + oc0) * P + n;
+#pragma unroll
+    for (int c = 0; c < COT; ++c) store_f(out, (size_t)c * P, acc[c]);
+}
+
+// grad_bias[co] = sum_{b, j, q} gy[b, co, j, q]: one workgroup per co, fixed
+// order (per-thread strided sums, then a tree over the workgroup)
+template <typename TG>
+__global__ __launch_bounds__(kThreads) void grad_bias_kernel(const TG* __restrict__ gy,
+                                                             float* __restrict__ gb, int B, int Co,
+                                                             size_t HW) {
+    __shared__ float red[kThreads];
+    const int co = blockIdx.x;
+    float a = 0.0f;
+    for (int b = 0; b < B; ++b) {
+        const TG* p = gy + ((size_t)b * Co + co) * HW;
+        for (size_t n = threadIdx.x; n < HW; n += kThreads) a += load_f(p, n);
+    }
+    red[threadIdx.x] = a;
+    __syncthreads();
+    for (int h = kThreads / 2; h > 0; h >>= 1) {
+        if ((int)threadIdx.x < h) red[threadIdx.x] += red[threadIdx.x + h];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) gb[co] = red[0];
+}
+
+// float32 zeros (graph-capturable: no memset node)
+__global__ __launch_bounds__(kThreads) void fill_zero(float* __restrict__ p, size_t n) {
+    const size_t e = (size_t)blockIdx.x * kThreads + threadIdx.x;
+    if (e < n) p[e] = 0.0f;
+}
+
+int check(const char* what) {
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return set_error(DISCO_EHIP, "%s launch failed: %s", what, hipGetErrorString(e));
+    return DISCO_OK;
+}
+
+int pick_qr_t(int nlon_in) {
+    const int qr = (nlon_in + kThreads - 1) / kThreads;
+    return qr <= 1 ? 1 : qr <= 2 ? 2 : qr <= 3 ? 3 : qr <= 4 ? 4 : qr <= 6 ? 6 : 8;
+}
+
+// LDS of the transposed contraction: K rows of grad_xk plus TC taps; the
+// largest TC (256 down to 16) that keeps it within 64 KiB, or 0.
+int pick_tc(int K, int KP, int nlon_out, size_t* lds) {
+    for (int tc = 256; tc >= 16; tc /= 2) {
+        const size_t bytes = ((size_t)K * nlon_out + (size_t)tc * KP) * sizeof(float);
+        if (bytes <= 64 * 1024) {
+            *lds = bytes;
+            return tc;
+        }
+    }
+    return 0;
+}
+
+template <typename TG, typename TO, int KP>
+int contract_t_kp(const disco_psi* psi, const void* gxk, void* gx, int B, int C, int row0,
+                  int nrows, int accumulate, hipStream_t st) {
+    const HostPsi& h = psi->host;
+    const DevPsi& d = psi->dev;
+    const disco_psi_desc& D = h.desc;
+    size_t lds = 0;
+    const int TC = pick_tc(h.K, KP, D.nlon_out, &lds);
+    if (TC == 0)
+        return set_error(DISCO_EUNSUPPORTED, "K * nlon_out = %d too large for the transposed "
+                         "contraction (K rows of one output row must fit in 64 KiB)",
+                         h.K * D.nlon_out);
+    const int QR = pick_qr_t(D.nlon_in);
+    dim3 grid(D.nlat_in, C, B);
+#define DISCO_CT(Q)                                                                              \
+    hipLaunchKernelGGL((contract_t_kernel<TG, TO, KP, Q>), grid, dim3(kThreads), lds, st,        \
+                       (const TG*)gxk, (TO*)gx, d.wint_ptr, d.wins_t, d.vals, C, h.K, D.nlat_in,  \
+                       D.nlon_in, D.nlon_out, h.stride, row0, nrows, accumulate, TC)
+    KernelTimer timer("contract_transpose", st);
+    switch (QR) {
+        case 1: DISCO_CT(1); break;
+        case 2: DISCO_CT(2); break;
+        case 3: DISCO_CT(3); break;
+        case 4: DISCO_CT(4); break;
+        case 6: DISCO_CT(6); break;
+        default: DISCO_CT(8); break;
+    }
+#undef DISCO_CT
+    return check("contract_transpose");
+}
+
+template <typename TG, typename TO>
+int contract_t_dispatch(const disco_psi* psi, const void* gxk, void* gx, int B, int C, int row0,
+                        int nrows, int accumulate, hipStream_t st) {
+    switch (psi->dev.KP) {
+#define DISCO_CTK(N) \
+    case N: return contract_t_kp<TG, TO, N>(psi, gxk, gx, B, C, row0, nrows, accumulate, st);
+        DISCO_CTK(1) DISCO_CTK(2) DISCO_CTK(4) DISCO_CTK(8) DISCO_CTK(12) DISCO_CTK(16)
+        DISCO_CTK(20) DISCO_CTK(24) DISCO_CTK(28) DISCO_CTK(32)
+#undef DISCO_CTK
+        default:
+            return set_error(DISCO_EUNSUPPORTED, "K = %d is not supported by the transposed "
+                             "contraction (K <= 32)", psi->host.K);
+    }
+}
+
+int contract_t_any(const disco_psi* psi, const void* gxk, int gxk_dtype, void* gx, int gx_dtype,
+                   int B, int C, int row0, int nrows, int accumulate, hipStream_t st) {
+    if (gxk_dtype == DISCO_F32 && gx_dtype == DISCO_F32)
+        return contract_t_dispatch<float, float>(psi, gxk, gx, B, C, row0, nrows, accumulate, st);
+    if (gxk_dtype == DISCO_F32)
+        return contract_t_dispatch<float, bf16_t>(psi, gxk, gx, B, C, row0, nrows, accumulate, st);
+    if (gx_dtype == DISCO_F32)
+        return contract_t_dispatch<bf16_t, float>(psi, gxk, gx, B, C, row0, nrows, accumulate, st);
+    return contract_t_dispatch<bf16_t, bf16_t>(psi, gxk, gx, B, C, row0, nrows, accumulate, st);
+}
+
+// points per grad_w chunk: enough workgroups to fill the chip at least twice
+int grad_w_chunk(size_t P, int tiles, int B, int groups, int ncu) {
+    const size_t want = (size_t)2 * ncu;
+    size_t per = (size_t)tiles * B * groups;
+    size_t nchunk = std::max<size_t>(1, (want + per - 1) / per);
+    size_t L = (P + nchunk - 1) / nchunk;
+    L = std::max<size_t>(L, 1024);
+    L = (L + kGwS - 1) / kGwS * kGwS;
+    return (int)std::min<size_t>(L, (size_t)1 << 30);
+}
+
+int num_cus() {
+    int dev = 0, ncu = 256;
+    if (hipGetDevice(&dev) == hipSuccess)
+        (void)hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+    (void)hipGetLastError();
+    return ncu;
+}
+
+// grad_w partial sums of one slab into `partial` ([B nchunk][Co][cig K]);
+// returns the number of partial arrays written, or a negative error code
+int grad_w_slab(const void* xk, int xk_dtype, const void* gy, int gy_dtype, float* partial,
+                int B, int Ci, int Co, int groups, int K, int nlat_out, int nlon_out, int row0,
+                int nrows, int L, hipStream_t st) {
+    const int cig = Ci / groups, cog = Co / groups;
+    const size_t P = (size_t)nrows * nlon_out;
+    const int nchunk = (int)((P + L - 1) / L);
+    dim3 grid((cig * K + kGwT - 1) / kGwT, (cog + kGwT - 1) / kGwT, (unsigned)(B * groups * nchunk));
+#define DISCO_GW(TX, TG)                                                                          \
+    hipLaunchKernelGGL((grad_w_partial<TX, TG>), grid, dim3(kThreads), 0, st, (const TX*)xk,      \
+                       (const TG*)gy, partial, Ci, Co, groups, K, nlat_out, nlon_out, row0, nrows, \
+                       L, nchunk)
+    {
+        KernelTimer timer("grad_w_partial", st);
+        if (xk_dtype == DISCO_F32 && gy_dtype == DISCO_F32) DISCO_GW(float, float);
+        else if (xk_dtype == DISCO_F32) DISCO_GW(float, bf16_t);
+        else if (gy_dtype == DISCO_F32) DISCO_GW(bf16_t, float);
+        else DISCO_GW(bf16_t, bf16_t);
+    }
+#undef DISCO_GW
+    int rc = check("grad_w_partial");
+    return rc != DISCO_OK ? rc : B * nchunk;
+}
+
+int reduce_into(const float* partial, float* gw, size_t n, int nparts, int accumulate,
+                hipStream_t st) {
+    {
+        KernelTimer timer("reduce_partials", st);
+        hipLaunchKernelGGL(reduce_partials, dim3((unsigned)((n + kThreads - 1) / kThreads)),
+                           dim3(kThreads), 0, st, partial, gw, n, nparts, accumulate);
+    }
+    return check("reduce_partials");
+}
+
+template <typename TG, typename TW, typename TO>
+int grad_xk_typed(const void* gy, const void* w, void* gxk, int B, int Ci, int Co, int groups,
+                  int K, int nlat_out, int nlon_out, int row0, int nrows, hipStream_t st) {
+    const int kd = (Ci / groups) * K;
+    int cot = 8;
+    while (kd % cot) cot /= 2;
+    const size_t P = (size_t)nrows * nlon_out;
+    dim3 grid((unsigned)((P + kThreads - 1) / kThreads), (unsigned)(Ci * K / cot), (unsigned)B);
+#define DISCO_GX(N)                                                                             \
+    hipLaunchKernelGGL((einsum_grad_xk_kernel<TG, TW, TO, N>), grid, dim3(kThreads), 0, st,     \
+                       (const TG*)gy, (const TW*)w, (TO*)gxk, Ci, Co, groups, K, nlat_out,      \
+                       nlon_out, row0, nrows)
+    KernelTimer timer("einsum_grad_xk", st);
+    switch (cot) {
+        case 8: DISCO_GX(8); break;
+        case 4: DISCO_GX(4); break;
+        case 2: DISCO_GX(2); break;
+        default: DISCO_GX(1); break;
+    }
+#undef DISCO_GX
+    return check("einsum_grad_xk");
+}
+
+int grad_xk_any(const void* gy, int gy_dtype, const void* w, int w_dtype, void* gxk, int gxk_dtype,
+                int B, int Ci, int Co, int groups, int K, int nlat_out, int nlon_out, int row0,
+                int nrows, hipStream_t st) {
+#define DISCO_GXT(TG, TW, TO) \
+    return grad_xk_typed<TG, TW, TO>(gy, w, gxk, B, Ci, Co, groups, K, nlat_out, nlon_out, row0, nrows, st)
+    const bool g32 = gy_dtype == DISCO_F32, w32 = w_dtype == DISCO_F32, o32 = gxk_dtype == DISCO_F32;
+    if (g32 && w32 && o32) DISCO_GXT(float, float, float);
+    if (g32 && w32) DISCO_GXT(float, float, bf16_t);
+    if (g32 && o32) DISCO_GXT(float, bf16_t, float);
+    if (g32) DISCO_GXT(float, bf16_t, bf16_t);
+    if (w32 && o32) DISCO_GXT(bf16_t, float, float);
+    if (w32) DISCO_GXT(bf16_t, float, bf16_t);
+    if (o32) DISCO_GXT(bf16_t, bf16_t, float);
+    DISCO_GXT(bf16_t, bf16_t, bf16_t);
+#undef DISCO_GXT
+}
+
+}  // namespace
+
+int launch_fill_zero(float* p, size_t n, void* stream) {
+    if (n == 0) return DISCO_OK;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    {
+        KernelTimer timer("fill_zero", st);
+        hipLaunchKernelGGL(fill_zero, dim3((unsigned)((n + kThreads - 1) / kThreads)), dim3(kThreads),
+                           0, st, p, n);
+    }
+    return check("fill_zero");
+}
+
+// the contraction into an fp32 slab of output rows (kernels_generic.hip)
+
+int launch_contract_rows(const disco_psi* psi, const void* x, int x_dtype, float* xk, int B, int C,
+                         int row0, int nrows, hipStream_t st);
+
+int launch_contract_transpose(const disco_psi* psi, const void* gxk, int gxk_dtype, void* gx,
+                              int gx_dtype, int B, int C, void* stream) {
+    return contract_t_any(psi, gxk, gxk_dtype, gx, gx_dtype, B, C, 0, psi->host.desc.nlat_out, 0,
+                          static_cast<hipStream_t>(stream));
+}
+
+int launch_einsum_grad_xk(const void* gy, int gy_dtype, const void* w, int w_dtype, void* gxk,
+                          int gxk_dtype, int B, int Ci, int Co, int groups, int K, int nlat_out,
+                          int nlon_out, void* stream) {
+    return grad_xk_any(gy, gy_dtype, w, w_dtype, gxk, gxk_dtype, B, Ci, Co, groups, K, nlat_out,
+                       nlon_out, 0, nlat_out, static_cast<hipStream_t>(stream));
+}
+
+int launch_einsum_grad_w(const void* xk, int xk_dtype, const void* gy, int gy_dtype, float* gw,
+                         int B, int Ci, int Co, int groups, int K, int nlat_out, int nlon_out,
+                         void* stream) {
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int cig = Ci / groups, cog = Co / groups;
+    const int tiles = ((cig * K + kGwT - 1) / kGwT) * ((cog + kGwT - 1) / kGwT);
+    const size_t P = (size_t)nlat_out * nlon_out;
+    const int L = grad_w_chunk(P, tiles, B, groups, num_cus());
+    const int nparts = B * (int)((P + L - 1) / L);
+    const size_t n = (size_t)Co * cig * K;
+    void* ws = nullptr;
+    hipError_t e = hipMallocAsync(&ws, (size_t)nparts * n * sizeof(float), st);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return set_error(e == hipErrorOutOfMemory ? DISCO_ENOMEM : DISCO_EHIP,
+                         "hipMallocAsync for the grad_w partial sums failed: %s",
+                         hipGetErrorString(e));
+    }
+    float* partial = static_cast<float*>(ws);
+    int rc = grad_w_slab(xk, xk_dtype, gy, gy_dtype, partial, B, Ci, Co, groups, K, nlat_out,
+                         nlon_out, 0, nlat_out, L, st);
+    if (rc >= 0) rc = reduce_into(partial, gw, n, nparts, 0, st);
+    hipError_t fe = hipFreeAsync(ws, st);
+    if (rc != DISCO_OK) return rc;
+    if (fe != hipSuccess) {
+        (void)hipGetLastError();
+        return set_error(DISCO_EHIP, "hipFreeAsync failed: %s", hipGetErrorString(fe));
+    }
+    return DISCO_OK;
+}
+
+// Fused-mode backward: per slab of output rows, X_K (float32) is recomputed
+// from x, grad_w partial sums of the slab are reduced into gw, grad_xk of the
+// slab is formed from gy and w, and its transposed contraction is added into
+// gx.  Slabs of at most ceil(nlat_out / 8) rows (one slab when the two slab
+// tensors of the whole layer take at most 64 MiB), so the workspace is about
+// an eighth of the two whole K-expanded tensors.
+int launch_fused_bwd(const disco_psi* psi, const void* x, int x_dtype, const void* w, int w_dtype,
+                     const void* gy, int gy_dtype, void* gx, int gx_dtype, float* gw, float* gbias,
+                     int B, int Ci, int Co, int groups, void* stream) {
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const HostPsi& h = psi->host;
+    const disco_psi_desc& D = h.desc;
+    const int K = h.K, cig = Ci / groups, cog = Co / groups;
+    const size_t row_bytes = (size_t)B * Ci * K * D.nlon_out * sizeof(float);
+    int rows = D.nlat_out;
+    if ((size_t)2 * row_bytes * D.nlat_out > ((size_t)64 << 20)) rows = (D.nlat_out + 7) / 8;
+    const int nslab = (D.nlat_out + rows - 1) / rows;
+    const int tiles = ((cig * K + kGwT - 1) / kGwT) * ((cog + kGwT - 1) / kGwT);
+    const int L = grad_w_chunk((size_t)rows * D.nlon_out, tiles, B, groups, num_cus());
+    const int nparts_max = B * (int)(((size_t)rows * D.nlon_out + L - 1) / L);
+    const size_t ngw = (size_t)Co * cig * K;
+    auto up = [](size_t v) { return (v + 255) / 256 * 256; };
+    const size_t slab_bytes = up((size_t)rows * row_bytes);
+    const size_t xk_bytes = gw ? slab_bytes : 0;
+    const size_t gxk_bytes = gx ? slab_bytes : 0;
+    const size_t part_bytes = gw ? up((size_t)nparts_max * ngw * sizeof(float)) : 0;
+    void* ws = nullptr;
+    int rc = DISCO_OK;
+    if (gbias) {
+        {
+            KernelTimer timer("grad_bias", st);
+            if (gy_dtype == DISCO_F32)
+                hipLaunchKernelGGL(grad_bias_kernel<float>, dim3(Co), dim3(kThreads), 0, st,
+                                   (const float*)gy, gbias, B, Co, (size_t)D.nlat_out * D.nlon_out);
+            else
+                hipLaunchKernelGGL(grad_bias_kernel<bf16_t>, dim3(Co), dim3(kThreads), 0, st,
+                                   (const bf16_t*)gy, gbias, B, Co, (size_t)D.nlat_out * D.nlon_out);
+        }
+        if ((rc = check("grad_bias")) != DISCO_OK) return rc;
+    }
+    if (!gw && !gx) return DISCO_OK;
+    hipError_t e = hipMallocAsync(&ws, xk_bytes + gxk_bytes + part_bytes, st);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return set_error(e == hipErrorOutOfMemory ? DISCO_ENOMEM : DISCO_EHIP,
+                         "hipMallocAsync for the backward workspace failed: %s",
+                         hipGetErrorString(e));
+    }
+    float* xk = static_cast<float*>(ws);
+    float* gxk = reinterpret_cast<float*>(static_cast<char*>(ws) + xk_bytes);
+    float* partial = reinterpret_cast<float*>(static_cast<char*>(ws) + xk_bytes + gxk_bytes);
+    for (int sidx = 0; sidx < nslab && rc == DISCO_OK; ++sidx) {
+        const int row0 = sidx * rows;
+        const int nr = std::min(rows, D.nlat_out - row0);
+        if (gw) {
+            rc = launch_contract_rows(psi, x, x_dtype, xk, B, Ci, row0, nr, st);
+            int np = rc == DISCO_OK ? grad_w_slab(xk, DISCO_F32, gy, gy_dtype, partial, B, Ci, Co,
+                                                  groups, K, D.nlat_out, D.nlon_out, row0, nr, L, st)
+                                    : rc;
+            if (np < 0) {
+                rc = np;
+                break;
+            }
+            rc = reduce_into(partial, gw, ngw, np, sidx > 0, st);
+            if (rc != DISCO_OK) break;
+        }
+        if (gx) {
+            rc = grad_xk_any(gy, gy_dtype, w, w_dtype, gxk, DISCO_F32, B, Ci, Co, groups, K,
+                             D.nlat_out, D.nlon_out, row0, nr, st);
+            if (rc == DISCO_OK)
+                rc = contract_t_any(psi, gxk, DISCO_F32, gx, gx_dtype, B, Ci, row0, nr, sidx > 0, st);
+        }
+    }
+    hipError_t fe = hipFreeAsync(ws, st);
+    if (rc != DISCO_OK) return rc;
+    if (fe != hipSuccess) {
+        (void)hipGetLastError();
+        return set_error(DISCO_EHIP, "hipFreeAsync failed: %s", hipGetErrorString(fe));
+    }
+    return DISCO_OK;
+}
+
+}  // namespace disco

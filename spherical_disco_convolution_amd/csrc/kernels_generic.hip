@@ -34,15 +34,16 @@ template <typename TX, typename TO, int KP, int QR>
 __global__ __launch_bounds__(kThreads) void contract_kernel(
     const TX* __restrict__ x, TO* __restrict__ xk, const int32_t* __restrict__ win_ptr,
     const DevWindow* __restrict__ wins, const float* __restrict__ vals, int C, int K, int nlat_in,
-    int nlon_in, int nlat_out, int nlon_out, int s) {
+    int nlon_in, int nlon_out, int s, int row0, int nrows) {
+    // output rows row0 .. row0 + nrows - 1 into xk [B, C, K, nrows, nlon_out]
     extern __shared__ float ext[];
-    const int j = blockIdx.x;
+    const int j = row0 + blockIdx.x;
     const int c = blockIdx.y;
     const int b = blockIdx.z;
     const TX* xc = x + (size_t)(b * C + c) * nlat_in * nlon_in;
     const int w0 = win_ptr[j], w1 = win_ptr[j + 1];
-    const size_t plane = (size_t)nlat_out * nlon_out;
-    TO* out = xk + (size_t)(b * C + c) * K * plane + (size_t)j * nlon_out;
+    const size_t plane = (size_t)nrows * nlon_out;
+    TO* out = xk + (size_t)(b * C + c) * K * plane + (size_t)blockIdx.x * nlon_out;
 
     for (int q0 = 0; q0 < nlon_out; q0 += kThreads * QR) {
         float acc[QR][KP];
@@ -365,18 +366,19 @@ int pick_qr(int nlon_out) {
 }
 
 template <typename TX, typename TO, int KP>
-int contract_kp(const disco_psi* psi, const void* x, void* xk, int B, int C, hipStream_t st) {
+int contract_kp(const disco_psi* psi, const void* x, void* xk, int B, int C, int row0, int nrows,
+                hipStream_t st) {
     const HostPsi& h = psi->host;
     const DevPsi& d = psi->dev;
     const disco_psi_desc& D = h.desc;
     const int QR = pick_qr(D.nlon_out);
     const size_t lds = (size_t)(h.stride * (kThreads * QR - 1) + d.max_width) * sizeof(float);
     if (lds > 64 * 1024) return set_error(DISCO_EUNSUPPORTED, "row too long for the contraction kernel");
-    dim3 grid(D.nlat_out, C, B);
+    dim3 grid(nrows, C, B);
 #define DISCO_CONTRACT_LAUNCH(Q)                                                                  \
     hipLaunchKernelGGL((contract_kernel<TX, TO, KP, Q>), grid, dim3(kThreads), lds, st,           \
                        (const TX*)x, (TO*)xk, d.win_ptr, d.windows, d.vals, C, h.K, D.nlat_in,    \
-                       D.nlon_in, D.nlat_out, D.nlon_out, h.stride)
+                       D.nlon_in, D.nlon_out, h.stride, row0, nrows)
     KernelTimer timer("contract_kernel", st);
     switch (QR) {
         case 1: DISCO_CONTRACT_LAUNCH(1); break;
@@ -391,18 +393,15 @@ int contract_kp(const disco_psi* psi, const void* x, void* xk, int B, int C, hip
 }
 
 template <typename TX, typename TO>
-int contract_dispatch(const disco_psi* psi, const void* x, void* xk, int B, int C, hipStream_t st) {
+int contract_dispatch(const disco_psi* psi, const void* x, void* xk, int B, int C, hipStream_t st,
+                      int row0 = 0, int nrows = -1) {
+    if (nrows < 0) nrows = psi->host.desc.nlat_out;
     switch (psi->dev.KP) {
-        case 1: return contract_kp<TX, TO, 1>(psi, x, xk, B, C, st);
-        case 2: return contract_kp<TX, TO, 2>(psi, x, xk, B, C, st);
-        case 4: return contract_kp<TX, TO, 4>(psi, x, xk, B, C, st);
-        case 8: return contract_kp<TX, TO, 8>(psi, x, xk, B, C, st);
-        case 12: return contract_kp<TX, TO, 12>(psi, x, xk, B, C, st);
-        case 16: return contract_kp<TX, TO, 16>(psi, x, xk, B, C, st);
-        case 20: return contract_kp<TX, TO, 20>(psi, x, xk, B, C, st);
-        case 24: return contract_kp<TX, TO, 24>(psi, x, xk, B, C, st);
-        case 28: return contract_kp<TX, TO, 28>(psi, x, xk, B, C, st);
-        case 32: return contract_kp<TX, TO, 32>(psi, x, xk, B, C, st);
+#define DISCO_CK(N) \
+    case N: return contract_kp<TX, TO, N>(psi, x, xk, B, C, row0, nrows, st);
+        DISCO_CK(1) DISCO_CK(2) DISCO_CK(4) DISCO_CK(8) DISCO_CK(12) DISCO_CK(16) DISCO_CK(20)
+        DISCO_CK(24) DISCO_CK(28) DISCO_CK(32)
+#undef DISCO_CK
         default: return set_error(DISCO_EUNSUPPORTED, "K = %d is not supported by the contraction "
                                   "kernel (K <= 32)", psi->host.K);
     }
@@ -429,6 +428,15 @@ int launch_contract(const disco_psi* psi, const void* x, int x_dtype, void* xk, 
     if (x_dtype == DISCO_BF16 && xk_dtype == DISCO_F32)
         return contract_dispatch<bf16_t, float>(psi, x, xk, B, C, st);
     return contract_dispatch<bf16_t, bf16_t>(psi, x, xk, B, C, st);
+}
+
+// The contraction of output rows row0 .. row0 + nrows - 1 into a float32
+// [B, C, K, nrows, nlon_out] tensor (the fused backward's recomputed X_K).
+int launch_contract_rows(const disco_psi* psi, const void* x, int x_dtype, float* xk, int B, int C,
+                         int row0, int nrows, hipStream_t st) {
+    if (x_dtype == DISCO_F32)
+        return contract_dispatch<float, float>(psi, x, xk, B, C, st, row0, nrows);
+    return contract_dispatch<bf16_t, float>(psi, x, xk, B, C, st, row0, nrows);
 }
 
 // defined in kernels_einsum_mfma.hip

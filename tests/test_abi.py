@@ -168,3 +168,44 @@ def test_kernel_timing_host_logic():
     assert sdc._lib.disco_kernel_timing_read(None, 0, tot, cnt, -1) == sdc.DISCO_EINVAL
     assert sdc._lib.disco_kernel_timing_read(None, 16, tot, cnt, 1) == sdc.DISCO_EINVAL
     assert sdc._lib.disco_kernel_timing_read(None, 0, None, None, 0) == 0
+
+
+def test_backward_argument_errors_before_any_device_work():
+    lib = sdc._lib
+    P = ctypes.c_void_p
+    # NULL handle
+    assert lib.disco_contract_transpose(None, None, 0, None, 0, 1, 1, None) == sdc.DISCO_EINVAL
+    assert "NULL" in lib.disco_last_error().decode()
+    assert lib.disco_fused_bwd(None, None, 0, None, 0, None, 0, None, 0, None, None, 1, 1, 1, 1,
+                               None) == sdc.DISCO_EINVAL
+    # unknown dtype codes
+    assert lib.disco_einsum_grad_w(None, 7, None, 0, None, 1, 4, 4, 1, 3, 2, 2,
+                                   None) == sdc.DISCO_EINVAL
+    assert lib.disco_einsum_grad_xk(None, 0, None, 9, None, 0, 1, 4, 4, 1, 3, 2, 2,
+                                    None) == sdc.DISCO_EINVAL
+    # groups must divide both channel counts (the DistributedSpectralConvS2
+    # source on the pages raises ValueError for this)
+    assert lib.disco_einsum_grad_w(None, 0, None, 0, None, 1, 6, 4, 4, 3, 2, 2,
+                                   None) == sdc.DISCO_EINVAL
+    assert "groups" in lib.disco_last_error().decode()
+    assert lib.disco_einsum_grad_xk(None, 0, None, 0, None, 0, 1, 5, 4, 2, 3, 2, 2,
+                                    None) == sdc.DISCO_EINVAL
+    # non-positive sizes
+    assert lib.disco_einsum_grad_w(None, 0, None, 0, None, -1, 4, 4, 1, 3, 2, 2,
+                                   None) == sdc.DISCO_EINVAL
+    # a fused backward that asks for nothing
+    d = sdc._Desc()
+    d.nlat_in, d.nlon_in, d.nlat_out, d.nlon_out = 9, 16, 9, 16
+    d.kernel_shape[0], d.kernel_shape[1] = 3, 0
+    d.theta_cutoff = 0.7
+    h = P()
+    assert lib.disco_psi_build(ctypes.byref(d), ctypes.byref(h)) == 0
+    try:
+        assert lib.disco_fused_bwd(h, None, 0, None, 0, None, 0, None, 0, None, None, 1, 2, 2, 1,
+                                   None) == sdc.DISCO_EINVAL
+        assert "NULL" in lib.disco_last_error().decode()
+        # a handle with no device copy
+        assert lib.disco_contract_transpose(h, None, 0, None, 0, 1, 2, None) in (
+            sdc.DISCO_EINVAL, sdc.DISCO_EHIP)
+    finally:
+        lib.disco_psi_free(h)

@@ -52,7 +52,8 @@ def worst_band_rel_l2(got, ref, band=32):
     fr = np.fft.rfft(np.asarray(ref, np.float64), axis=-1)
     worst = 0.0
     for m0 in range(0, fr.shape[-1], band):
-        worst = max(worst, rel_l2(fg[..., m0:m0 + band], fr[..., m0:m0 + band]))
+        d = np.linalg.norm(fg[..., m0:m0 + band] - fr[..., m0:m0 + band])   # complex norms
+        worst = max(worst, float(d / max(np.linalg.norm(fr[..., m0:m0 + band]), 1e-300)))
     return worst
 
 

@@ -152,6 +152,23 @@ int disco_fused_fwd(const disco_psi* psi, const void* x, int x_dtype,
                     void* y, int y_dtype, int32_t B, int32_t Ci, int32_t Co,
                     int32_t groups, void* stream);
 
+/* The same result as disco_fused_fwd for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): this call allocates nothing.  It always takes the
+ * direct algorithms (the matrix-core kernel for the bf16 layers it accepts,
+ * the vector kernels otherwise; never the longitude-spectral one, whose
+ * workspace grows with the grid), and puts the matrix-core kernel's weight
+ * fragments (Ci * Co * 16 bytes) in a fixed 4 MiB device array of the
+ * library, held on each device it runs on until the process ends.  EINVAL,
+ * before any launch, when a layer needs more than those 4 MiB.  Every call
+ * on one device shares that array, so calls that overlap on one device
+ * (different streams, or other threads) race and must be ordered by the
+ * caller. */
+int disco_fused_fwd_noalloc(const disco_psi* psi, const void* x, int x_dtype,
+                            const void* w, int w_dtype, const float* bias,
+                            void* y, int y_dtype, int32_t B, int32_t Ci, int32_t Co,
+                            int32_t groups, void* stream);
+
 /* 1 if disco_fused_fwd with these arguments takes the longitude-spectral
  * path described above, 0 if it takes a direct kernel, negative on error
  * (NULL handle or handle not uploaded).  Reads DISCO_FUSED_PATH like the call

@@ -79,6 +79,8 @@ def _load():
                                         I32, I32, I32, I32, I32, I32, I32, P]),
         "disco_fused_fwd": (ctypes.c_int, [P, P, ctypes.c_int, P, ctypes.c_int, P, P,
                                            ctypes.c_int, I32, I32, I32, I32, P]),
+        "disco_fused_fwd_noalloc": (ctypes.c_int, [P, P, ctypes.c_int, P, ctypes.c_int, P, P,
+                                                   ctypes.c_int, I32, I32, I32, I32, P]),
         "disco_fused_is_spectral": (ctypes.c_int, [P, ctypes.c_int, I32, I32, I32]),
         "disco_contract_transpose": (ctypes.c_int, [P, P, ctypes.c_int, P, ctypes.c_int, I32, I32,
                                                     P]),
@@ -104,6 +106,7 @@ def _load():
 _lib = _load()
 EXPORTED = ("disco_psi_build", "disco_psi_query", "disco_psi_export", "disco_psi_to_device",
             "disco_psi_free", "disco_contract", "disco_einsum", "disco_fused_fwd",
+            "disco_fused_fwd_noalloc",
             "disco_fused_is_spectral", "disco_contract_transpose", "disco_einsum_grad_xk",
             "disco_einsum_grad_w", "disco_fused_bwd", "disco_kernel_timing", "disco_kernel_timing_read",
             "disco_last_error", "disco_version")
@@ -353,6 +356,28 @@ def fused_fwd(psi: Psi, x, w, groups: int = 1, bias=None, y=None, out_dtype=None
                                 groups, _stream(stream)), "fused_fwd")
     return y
 
+
+
+def fused_fwd_noalloc(psi: Psi, x, w, y, groups: int = 1, bias=None, stream=None):
+    """fused_fwd for callers that cannot allocate device memory: the direct
+    algorithms with the library's fixed scratch; y must be given."""
+    if x.dim() != 4 or w.dim() != 3:
+        raise ValueError("x must be [B, Ci, nlat_in, nlon_in] and w [Co, Ci/groups, K]")
+    B, Ci = x.shape[:2]
+    Co = w.shape[0]
+    _need(x, "x", (B, Ci, psi.nlat_in, psi.nlon_in))
+    if groups < 1 or Ci % groups or Co % groups:
+        raise ValueError(f"groups ({groups}) must divide in_channels ({Ci}) and out_channels ({Co})")
+    _need(w, "w", (Co, Ci // groups, psi.K))
+    _need(y, "y", (B, Co, psi.nlat_out, psi.nlon_out))
+    bptr = None
+    if bias is not None:
+        _need(bias, "bias", (Co,))
+        bptr = bias.data_ptr()
+    _check(_lib.disco_fused_fwd_noalloc(psi.handle, x.data_ptr(), _dtype_code(x), w.data_ptr(),
+                                        _dtype_code(w), bptr, y.data_ptr(), _dtype_code(y), B, Ci,
+                                        Co, groups, _stream(stream)), "fused_fwd_noalloc")
+    return y
 
 
 # ----------------------------------------------------------------------------

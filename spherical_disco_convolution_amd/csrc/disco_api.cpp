@@ -406,6 +406,17 @@ int disco_fused_fwd(const disco_psi* psi, const void* x, int x_dtype, const void
     return launch_fused(psi, x, x_dtype, w, bias, y, y_dtype, B, Ci, Co, groups, stream);
 }
 
+int disco_fused_fwd_noalloc(const disco_psi* psi, const void* x, int x_dtype, const void* w,
+                            int w_dtype, const float* bias, void* y, int y_dtype, int32_t B,
+                            int32_t Ci, int32_t Co, int32_t groups, void* stream) {
+    clear_error();
+    bool skip = false;
+    int rc = check_fused_args(psi, x, x_dtype, w, w_dtype, bias, y, y_dtype, B, Ci, Co, groups,
+                              &skip);
+    if (rc != DISCO_OK || skip) return rc;
+    return launch_fused_noalloc(psi, x, x_dtype, w, bias, y, y_dtype, B, Ci, Co, groups, stream);
+}
+
 int disco_contract_transpose(const disco_psi* psi, const void* gxk, int gxk_dtype, void* gx,
                              int gx_dtype, int32_t B, int32_t C, void* stream) {
     clear_error();

@@ -122,6 +122,11 @@ int launch_einsum(const void* xk, int xk_dtype, const void* w, int w_dtype, cons
 int launch_fused(const disco_psi* psi, const void* x, int dtype, const void* w,
                  const float* bias, void* y, int y_dtype, int B, int Ci, int Co, int groups,
                  void* stream);
+// The fused forward on the direct algorithms only, with the weight fragments
+// in the library's fixed device scratch (no allocation).
+int launch_fused_noalloc(const disco_psi* psi, const void* x, int dtype, const void* w,
+                         const float* bias, void* y, int y_dtype, int B, int Ci, int Co,
+                         int groups, void* stream);
 // 1 if disco_fused_fwd takes the longitude-spectral path for these arguments
 int fused_spectral_eligible(const disco_psi* psi, int x_dtype, int Ci, int Co, int groups);
 

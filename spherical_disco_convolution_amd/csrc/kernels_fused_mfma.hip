@@ -38,6 +38,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 
 #include "disco_internal.h"
 #include "kernels_common.h"
@@ -719,9 +720,49 @@ __global__ __launch_bounds__(768, 1) void fused_mfma(
 
 }  // namespace
 
+// Scratch of the no-allocation fused entry point: the direct kernel's weight
+// fragments live here instead of in stream-ordered workspace.  Host code
+// never uses the array's name as an address: each device's copy is looked up
+// once with hipGetSymbolAddress (noalloc_scratch) and that address is passed
+// to the kernels.  Every call on a device shares its copy; calls that overlap
+// on one device race.
+constexpr size_t kNoAllocScratchBytes = (size_t)4 << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+int noalloc_scratch(void** ptr, size_t* bytes) {
+    static std::mutex mu;
+    static void* addr[64] = {nullptr};
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return set_error(DISCO_EHIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+    }
+    if (dev < 0 || dev >= 64) return set_error(DISCO_EUNSUPPORTED, "device %d out of range", dev);
+    std::lock_guard<std::mutex> lock(mu);
+    if (addr[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || p == nullptr) {
+            (void)hipGetLastError();
+            return set_error(DISCO_EHIP, "hipGetSymbolAddress(scratch) failed on device %d: %s",
+                             dev, hipGetErrorString(e));
+        }
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    *bytes = kNoAllocScratchBytes;
+    return DISCO_OK;
+}
+
+// Bytes of weight fragments the direct matrix-core kernel needs.
+size_t fused_mfma_frag_bytes(int Ci, int Co) {
+    return (size_t)(Ci / 32) * 16 * (Co / 32) * 64 * sizeof(u32x4);
+}
+
 int try_launch_fused_mfma(const disco_psi* psi, const void* x, const void* w, const float* bias,
                           void* y, int y_dtype, int B, int Ci, int Co, int groups, hipStream_t st,
-                          int* rc) {
+                          int* rc, void* frag_ws, size_t frag_ws_bytes) {
     const DevPsi& d = psi->dev;
     const HostPsi& h = psi->host;
     const disco_psi_desc& D = h.desc;
@@ -739,15 +780,25 @@ int try_launch_fused_mfma(const disco_psi* psi, const void* x, const void* w, co
     const int32_t* dinfo = d.mfma_row_info;
     const u32x4* taps = static_cast<const u32x4*>(d.mfma_taps);
 
-    // weight fragments (stream-ordered workspace)
+    // weight fragments: the caller's fixed scratch, or stream-ordered workspace
     const size_t nfrag = (size_t)(Ci / 32) * 16 * (Co / 32) * 64;
     void* wsp = nullptr;
-    hipError_t e = hipMallocAsync(&wsp, nfrag * sizeof(u32x4), st);
-    if (e != hipSuccess) {
-        (void)hipGetLastError();
-        *rc = set_error(e == hipErrorOutOfMemory ? DISCO_ENOMEM : DISCO_EHIP,
-                        "hipMallocAsync for the weight fragments failed: %s", hipGetErrorString(e));
-        return 1;
+    if (frag_ws != nullptr) {
+        if (nfrag * sizeof(u32x4) > frag_ws_bytes) {
+            *rc = set_error(DISCO_EINVAL, "the weight fragments need %zu bytes of scratch; only "
+                            "%zu are available", nfrag * sizeof(u32x4), frag_ws_bytes);
+            return 1;
+        }
+        wsp = frag_ws;
+    } else {
+        hipError_t e = hipMallocAsync(&wsp, nfrag * sizeof(u32x4), st);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            *rc = set_error(e == hipErrorOutOfMemory ? DISCO_ENOMEM : DISCO_EHIP,
+                            "hipMallocAsync for the weight fragments failed: %s",
+                            hipGetErrorString(e));
+            return 1;
+        }
     }
     u32x4* wf = static_cast<u32x4*>(wsp);
     {
@@ -779,7 +830,7 @@ int try_launch_fused_mfma(const disco_psi* psi, const void* x, const void* w, co
     }
 #undef DISCO_FM
     hipError_t le = hipGetLastError();
-    hipError_t fe = hipFreeAsync(wsp, st);
+    hipError_t fe = frag_ws != nullptr ? hipSuccess : hipFreeAsync(wsp, st);
     if (le != hipSuccess) {
         *rc = set_error(DISCO_EHIP, "fused_mfma launch failed: %s", hipGetErrorString(le));
         return 1;

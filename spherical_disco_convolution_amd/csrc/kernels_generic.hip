@@ -612,25 +612,28 @@ int fused_vector(const disco_psi* psi, const void* x, const void* w, const float
 
 }  // namespace
 
-// defined in kernels_fused_mfma.hip; returns 1 if it handled the call
+// defined in kernels_fused_mfma.hip; returns 1 if it handled the call.  With
+// frag_ws non-NULL the weight fragments go there (frag_ws_bytes available)
+// instead of stream-ordered workspace.
 int try_launch_fused_mfma(const disco_psi* psi, const void* x, const void* w, const float* bias,
                           void* y, int y_dtype, int B, int Ci, int Co, int groups, hipStream_t st,
-                          int* rc);
+                          int* rc, void* frag_ws, size_t frag_ws_bytes);
+int noalloc_scratch(void** ptr, size_t* bytes);
 
 // defined in kernels_spectral.hip; returns 1 if it handled the call
 int try_launch_fused_spectral(const disco_psi* psi, const void* x, const void* w,
                               const float* bias, void* y, int y_dtype, int B, int Ci, int Co,
                               int groups, hipStream_t st, int* rc);
 
-int launch_fused(const disco_psi* psi, const void* x, int dtype, const void* w, const float* bias,
-                 void* y, int y_dtype, int B, int Ci, int Co, int groups, void* stream) {
-    hipStream_t st = static_cast<hipStream_t>(stream);
+namespace {
+// The direct algorithms: the matrix-core kernel for the bf16 layers it takes,
+// the vector kernels otherwise.
+int launch_fused_direct(const disco_psi* psi, const void* x, int dtype, const void* w,
+                        const float* bias, void* y, int y_dtype, int B, int Ci, int Co, int groups,
+                        hipStream_t st, void* frag_ws, size_t frag_ws_bytes) {
     int rc = DISCO_OK;
-    if (dtype == DISCO_BF16 &&
-        try_launch_fused_spectral(psi, x, w, bias, y, y_dtype, B, Ci, Co, groups, st, &rc))
-        return rc;
-    if (dtype == DISCO_BF16 &&
-        try_launch_fused_mfma(psi, x, w, bias, y, y_dtype, B, Ci, Co, groups, st, &rc))
+    if (dtype == DISCO_BF16 && try_launch_fused_mfma(psi, x, w, bias, y, y_dtype, B, Ci, Co,
+                                                     groups, st, &rc, frag_ws, frag_ws_bytes))
         return rc;
     if (dtype == DISCO_F32)
         return y_dtype == DISCO_F32
@@ -639,6 +642,29 @@ int launch_fused(const disco_psi* psi, const void* x, int dtype, const void* w, 
     return y_dtype == DISCO_F32
                ? fused_vector<bf16_t, float>(psi, x, w, bias, y, B, Ci, Co, groups, st)
                : fused_vector<bf16_t, bf16_t>(psi, x, w, bias, y, B, Ci, Co, groups, st);
+}
+}  // namespace
+
+int launch_fused(const disco_psi* psi, const void* x, int dtype, const void* w, const float* bias,
+                 void* y, int y_dtype, int B, int Ci, int Co, int groups, void* stream) {
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    int rc = DISCO_OK;
+    if (dtype == DISCO_BF16 &&
+        try_launch_fused_spectral(psi, x, w, bias, y, y_dtype, B, Ci, Co, groups, st, &rc))
+        return rc;
+    return launch_fused_direct(psi, x, dtype, w, bias, y, y_dtype, B, Ci, Co, groups, st, nullptr,
+                               0);
+}
+
+int launch_fused_noalloc(const disco_psi* psi, const void* x, int dtype, const void* w,
+                         const float* bias, void* y, int y_dtype, int B, int Ci, int Co,
+                         int groups, void* stream) {
+    void* ws = nullptr;
+    size_t bytes = 0;
+    int rc = noalloc_scratch(&ws, &bytes);
+    if (rc != DISCO_OK) return rc;
+    return launch_fused_direct(psi, x, dtype, w, bias, y, y_dtype, B, Ci, Co, groups,
+                               static_cast<hipStream_t>(stream), ws, bytes);
 }
 
 }  // namespace disco

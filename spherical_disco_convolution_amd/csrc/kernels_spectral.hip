@@ -539,13 +539,19 @@ __global__ __launch_bounds__(kRegThreads) void spec_rfft_reg(const uint32_t* __r
 // The merge fills Z in LDS (k and H - k together), step A reads it there,
 // step B stores y (lanes c consecutive).  Workgroup g transforms rows
 // g RW .. g RW + RW - 1.
-template <int H1, int H2, int RW, typename TY>
+//
+// FOLD = 2 (longitude stride 2): the rows of yh are the spectra Y of the
+// stride-1 correlation at 2N points (frequencies 0 .. N, row stride mp_in),
+// and the output keeps every second longitude.  Decimating by two sums the
+// two aliases of each frequency: X[m] = (Y[m] + conj(Y[N - m])) / 2.
+template <int H1, int H2, int RW, typename TY, int FOLD>
 __global__ __launch_bounds__(kRegThreads) void spec_irfft_reg(const uint32_t* __restrict__ yh,
                                                               TY* __restrict__ y,
                                                               const float* __restrict__ bias,
                                                               int Co, int nlat_out,
-                                                              int64_t nrows) {
-    constexpr int H = H1 * H2, N = 2 * H, MP = spec_mp_of(H);
+                                                              int64_t nrows, int mp_in) {
+    constexpr int H = H1 * H2, N = 2 * H;
+    static_assert(FOLD == 1 || FOLD == 2, "longitude strides 1 and 2");
     constexpr int P2 = H2 | 1, LP = H1 * P2;
     constexpr int TA = RW * H2, ITA = (TA + 63) / 64;
     constexpr int TB = RW * H1, ITB = (TB + 63) / 64;
@@ -563,14 +569,20 @@ __global__ __launch_bounds__(kRegThreads) void spec_irfft_reg(const uint32_t* __
         // every load first (addresses clamped to valid frequencies), so that
         // all are in flight together
         uint32_t la[RW][NPI], lb[RW][NPI];
+        uint32_t fa[FOLD == 2 ? RW : 1][FOLD == 2 ? NPI : 1];   // aliases (stride 2)
+        uint32_t fb[FOLD == 2 ? RW : 1][FOLD == 2 ? NPI : 1];
 #pragma unroll
         for (int r = 0; r < RW; ++r) {
-            const uint32_t* src = yh + min(g * RW + r, nrows - 1) * MP;
+            const uint32_t* src = yh + min(g * RW + r, nrows - 1) * (int64_t)mp_in;
 #pragma unroll
             for (int I = 0; I < NPI; ++I) {
                 const int m = min(lane + 64 * I, H / 2);
                 la[r][I] = src[m];
                 lb[r][I] = src[H - m];
+                if constexpr (FOLD == 2) {
+                    fa[r][I] = src[N - m];
+                    fb[r][I] = src[H + m];
+                }
             }
         }
         const float2 wl = root(lane, 1.0f / (float)N, 1.0f);   // W^-lane
@@ -583,6 +595,12 @@ __global__ __launch_bounds__(kRegThreads) void spec_irfft_reg(const uint32_t* __
                 if (m <= H / 2) {
                     float2 A = unpack_bf16x2(la[r][I]);
                     float2 Bc = cconj(unpack_bf16x2(lb[r][I]));
+                    if constexpr (FOLD == 2) {
+                        // X[m] = (Y[m] + conj(Y[N - m]))/2, and X[H - m] with
+                        // conj(Y[N - (H - m)]) = conj(Y[H + m])
+                        A = cscale(cadd(A, cconj(unpack_bf16x2(fa[r][I]))), 0.5f);
+                        Bc = cscale(cadd(Bc, unpack_bf16x2(fb[r][I])), 0.5f);
+                    }
                     if (m == 0) {
                         A.y = 0.0f;
                         Bc.y = 0.0f;
@@ -692,7 +710,7 @@ constexpr int kMt = 32;              // frequencies per work item (64 GEMM colum
 constexpr int kBts = 312;
 constexpr int kBkb = 40;             // bf16 per k block of a tile row
 constexpr int kSpecThreads = 256;
-constexpr int kSpecMaxWin = 8;       // windows per output row (one 16-deep MFMA step)
+constexpr int kSpecMaxWin = 16;      // windows per output row: one or two 16-deep MFMA steps
 constexpr int kXcds = 8;             // accelerator dies of the chip (L2 domains)
 
 // Both sums of the forward equation for work items (batch b, output row j,
@@ -725,15 +743,22 @@ constexpr int kXcds = 8;             // accelerator dies of the chip (L2 domains
 // fragment is reloaded for the next chunk right after its use (the weights
 // do not depend on the item), and the next
 // item's Psi_hat slice is loaded during the current item.
-template <int CO, int KT>
-__global__ __launch_bounds__(kSpecThreads) __attribute__((amdgpu_waves_per_eu(2))) void spec_mfma(
+// NW (8 or 16) is the window capacity: the window sum is one 16-deep MFMA
+// step per 8 windows (rows with at most 8 windows skip the second step).
+// With NW = 8 two workgroups fit a compute unit; NW = 16 doubles the spectra
+// and Psi_hat blocks and takes the whole LDS.
+template <int CO, int KT, int NW>
+__global__ __launch_bounds__(kSpecThreads) __attribute__((amdgpu_waves_per_eu(NW == 8 ? 2 : 1))) void spec_mfma(
     const uint32_t* __restrict__ xh, const bf16_t* __restrict__ wp,
     const uint32_t* __restrict__ psih, const int32_t* __restrict__ win_ptr,
     const DevWindow* __restrict__ wins, bf16_t* __restrict__ yh, int B, int Ci, int nlat_in,
     int nlat_out, int MP, int NX, int64_t psih_zero, int nwmax) {
+    static_assert(NW == 8 || NW == 16, "window capacity");
+    constexpr int NS = NW / 8;            // window-sum MFMA steps
+    constexpr int WPW = NW / 4;           // windows whose spectra each wave copies
     __shared__ __attribute__((aligned(16))) bf16_t bt[64 * kBts];
-    __shared__ __attribute__((aligned(16))) u32x4 xs[kSpecMaxWin * 32 * 8];   // [r][ci][piece]
-    __shared__ __attribute__((aligned(16))) uint32_t ps[kSpecMaxWin * KT * kMt];
+    __shared__ __attribute__((aligned(16))) u32x4 xs[NW * 32 * 8];   // [r][ci][piece]
+    __shared__ __attribute__((aligned(16))) uint32_t ps[NW * KT * kMt];
     __shared__ __attribute__((aligned(16))) bf16_t dump[32];   // 4 writes of 8 bytes, 8 apart
     constexpr int WGM = CO / 32;          // waves along the output channels
     constexpr int WGN = 4 / WGM;          // waves along the columns
@@ -792,11 +817,11 @@ __global__ __launch_bounds__(kSpecThreads) __attribute__((amdgpu_waves_per_eu(2)
     // ---- spectra stream: position p = (item p / nchunks, chunk p % nchunks).
     // The request cursor walks the positions in order (staying at the last).
     // A position's spectra block goes straight to LDS by DMA: wave w fills
-    // windows 2w and 2w + 1.  LDS slot ((r * 32 + ci) * 8 + pos) holds the
-    // 16-byte piece pos ^ (ci & 7) (4 frequencies) of channel ci's row in
-    // window r.  Window slots past the row's windows repeat window 0 (valid,
-    // finite; their B rows are zero).
-    int lat_lo = 0, lat_hi = 0;     // input rows of windows 2w, 2w + 1 of the requested item
+    // windows WPW w .. WPW w + WPW - 1.  LDS slot ((r * 32 + ci) * 8 + pos)
+    // holds the 16-byte piece pos ^ (ci & 7) (4 frequencies) of channel ci's
+    // row in window r.  Window slots past the row's windows repeat window 0
+    // (valid, finite; their B rows are zero).
+    int lat_w[WPW];                 // input rows of this wave's windows of the requested item
     int req_pos = 0, req_chunk = 0, req_b = 0;
     const int npos = nmine * nchunks;
     Cur rq = cur_first();
@@ -804,8 +829,11 @@ __global__ __launch_bounds__(kSpecThreads) __attribute__((amdgpu_waves_per_eu(2)
         int j;
         cur_bj(rq, req_b, j);
         const int w0 = win_ptr[j], nw = win_ptr[j + 1] - w0;
-        lat_lo = wins[w0 + (2 * wave < nw ? 2 * wave : 0)].lat;
-        lat_hi = wins[w0 + (2 * wave + 1 < nw ? 2 * wave + 1 : 0)].lat;
+#pragma unroll
+        for (int u = 0; u < WPW; ++u) {
+            const int r = WPW * wave + u;
+            lat_w[u] = wins[w0 + (r < nw ? r : 0)].lat;
+        }
     };
     auto request_next = [&]() {   // the next position
         if (req_pos + 1 < npos) {
@@ -819,8 +847,8 @@ __global__ __launch_bounds__(kSpecThreads) __attribute__((amdgpu_waves_per_eu(2)
     };
     const uint32_t xs_lds =
         __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_void*)&xs[0]);
-    // DMA of the requested position: 8 instructions per wave, instruction i
-    // covering channels 8 (i % 4) .. + 7 of window 2w + i / 4 (64 slots)
+    // DMA of the requested position: 4 WPW instructions per wave, instruction
+    // i covering channels 8 (i % 4) .. + 7 of window WPW w + i / 4 (64 slots)
     // this lane's source offsets (channel within the chunk and piece) of
     // instructions i and i + 4: constant over the stream
     size_t dma_off[4];
@@ -831,19 +859,20 @@ __global__ __launch_bounds__(kSpecThreads) __attribute__((amdgpu_waves_per_eu(2)
     }
     auto dma_x = [&]() {
         const size_t cb = (size_t)(req_b * Ci + req_chunk * 32) * plane + rq.mt * kMt;
-        const uint32_t* blo = xh + cb + (size_t)uniform(lat_lo) * MP;
-        const uint32_t* bhi = xh + cb + (size_t)uniform(lat_hi) * MP;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int r = 2 * wave + (i >> 2);
-            // window slots no output row has (r >= nwmax) are never read
-            if (r < nwmax)
-                dma_lds16((i < 4 ? blo : bhi) + dma_off[i & 3],
-                          xs_lds + (uint32_t)((r * 32 + 8 * (i & 3)) * 8 * 16));
+        for (int u = 0; u < WPW; ++u) {
+            const int r = WPW * wave + u;
+            const uint32_t* src = xh + cb + (size_t)uniform(lat_w[u]) * MP;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                // window slots no output row has (r >= nwmax) are never read
+                if (r < nwmax)
+                    dma_lds16(src + dma_off[q], xs_lds + (uint32_t)((r * 32 + 8 * q) * 8 * 16));
+            }
         }
     };
 
-    // ---- Psi_hat slice of an item, ps[(r KT + k) kMt + ml], by DMA: KT
+    // ---- Psi_hat slice of an item, ps[(r KT + k) kMt + ml], by DMA: NS KT
     // instructions of 64 16-byte slots (4 frequencies each), spread over the
     // waves; slots past the row's windows copy the table's zero block
     const uint32_t ps_lds =
@@ -852,7 +881,7 @@ __global__ __launch_bounds__(kSpecThreads) __attribute__((amdgpu_waves_per_eu(2)
         int b, j;
         cur_bj(c, b, j);
         const int w0 = win_ptr[j], nw = win_ptr[j + 1] - w0;
-        for (int i = wave; i < KT; i += 4) {
+        for (int i = wave; i < NS * KT; i += 4) {
             const int slot = 64 * i + lane;
             const int rk = slot >> 3, ml0 = (slot & 7) * 4;
             const uint32_t* src = rk < nw * KT
@@ -889,20 +918,25 @@ __global__ __launch_bounds__(kSpecThreads) __attribute__((amdgpu_waves_per_eu(2)
         // imaginary part of X_hat), rows (r, re/im) for r = 4 lg .. 4 lg + 3
         // (windows past the row's are zero in ps; basis columns k >= KT are
         // never read by the GEMM, so their lanes take column KT - 1's values)
-        u32x4 bq[8];
+        // step st covers windows 8 st .. 8 st + 7; rows with at most 8
+        // windows skip the second step (uniform)
+        const bool two = NS == 2 && nw > 8;
+        u32x4 bq[NS][8];
         {
             const int k = min(l32 >> 1, KT - 1), c = l32 & 1;
 #pragma unroll
+            for (int st = 0; st < NS; ++st)
+#pragma unroll
             for (int u = 0; u < 4; ++u) {
-                // the wave's 8 frequencies of (window 4 lg + u, basis k): 32 bytes
-                const u32x4* src =
-                    reinterpret_cast<const u32x4*>(ps + ((4 * lg + u) * KT + k) * kMt + f0);
+                // the wave's 8 frequencies of (window 8 st + 4 lg + u, basis k): 32 bytes
+                const u32x4* src = reinterpret_cast<const u32x4*>(
+                    ps + ((8 * st + 4 * lg + u) * KT + k) * kMt + f0);
                 const u32x4 lo = src[0], hi = src[1];
 #pragma unroll
                 for (int f = 0; f < 8; ++f) {
                     const uint32_t P = f < 4 ? lo[f] : hi[f - 4];   // bf16 (Pr, Pi), real low
                     // real column: (Pr, Pi); imaginary column: (-Pi, Pr)
-                    bq[f][u] = c ? (__builtin_rotateleft32(P, 16) ^ 0x8000u) : P;
+                    bq[st][f][u] = c ? (__builtin_rotateleft32(P, 16) ^ 0x8000u) : P;
                 }
             }
         }
@@ -919,13 +953,15 @@ __global__ __launch_bounds__(kSpecThreads) __attribute__((amdgpu_waves_per_eu(2)
 
         for (int cc = 0; cc < nchunks; ++cc) {
             // ---- window sum, one MFMA per frequency ----
-            u32x4 xa[4][2];
+            u32x4 xa[NS][4][2];
+#pragma unroll
+            for (int st = 0; st < NS; ++st)
 #pragma unroll
             for (int u = 0; u < 4; ++u)
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
-                    const int r = 4 * lg + u < nw ? 4 * lg + u : 0;
-                    xa[u][h] = xs[(r * 32 + l32) * 8 + (xsw ^ h)];
+                    const int r = 8 * st + 4 * lg + u < nw ? 8 * st + 4 * lg + u : 0;
+                    xa[st][u][h] = xs[(r * 32 + l32) * 8 + (xsw ^ h)];
                 }
             wave_lds_sync();   // this wave's spectra reads are done
             __syncthreads();   // every wave's: the block may be overwritten
@@ -938,14 +974,24 @@ __global__ __launch_bounds__(kSpecThreads) __attribute__((amdgpu_waves_per_eu(2)
             // frequency f + 1 is issued before frequency f's is converted and
             // written, so the matrix-core latency is hidden behind the writes
             auto window_mfma = [&](int f) {
-                const u32x4 a = {xa[0][f >> 2][f & 3], xa[1][f >> 2][f & 3], xa[2][f >> 2][f & 3],
-                                 xa[3][f >> 2][f & 3]};
                 floatx16 d;
 #pragma unroll
                 for (int e = 0; e < 16; ++e) d[e] = 0.0f;
-                return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                               __builtin_bit_cast(bf16x8_t, bq[f]), d,
-                                                               0, 0, 0);
+                const u32x4 a = {xa[0][0][f >> 2][f & 3], xa[0][1][f >> 2][f & 3],
+                                 xa[0][2][f >> 2][f & 3], xa[0][3][f >> 2][f & 3]};
+                d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                            __builtin_bit_cast(bf16x8_t, bq[0][f]),
+                                                            d, 0, 0, 0);
+                if constexpr (NS == 2) {
+                    if (two) {
+                        const u32x4 a1 = {xa[NS - 1][0][f >> 2][f & 3], xa[NS - 1][1][f >> 2][f & 3],
+                                          xa[NS - 1][2][f >> 2][f & 3], xa[NS - 1][3][f >> 2][f & 3]};
+                        d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            __builtin_bit_cast(bf16x8_t, a1),
+                            __builtin_bit_cast(bf16x8_t, bq[NS - 1][f]), d, 0, 0, 0);
+                    }
+                }
+                return d;
             };
             auto window_write = [&](const floatx16& d, int f) {
                 // column (k, c) -> tile row 2 (f0 + f) + c, pairs (k, ci),
@@ -1048,6 +1094,8 @@ int fused_spectral_eligible(const disco_psi* psi, int x_dtype, int Ci, int Co, i
         (Co != 128 && Co != 64) || h.K > 8)
         return 0;
     if (d.max_windows > kSpecMaxWin) return 0;
+    // stride 2: register transforms on both sides (the tables exist only then)
+    if (h.stride == 2 && h.desc.nlon_in != 1440 && h.desc.nlon_in != 720) return 0;
     // DISCO_FUSED_PATH=toeplitz selects the direct matrix-core kernel instead
     const char* e = std::getenv("DISCO_FUSED_PATH");
     return e == nullptr || std::strcmp(e, "toeplitz") != 0;
@@ -1090,6 +1138,7 @@ int try_launch_fused_spectral(const disco_psi* psi, const void* x, const void* w
     // the register-resident transforms cover these half lengths (their MP is
     // the table's)
     const bool reg = (H == 720 || H == 360 || H == 180) && MP == spec_mp_of(H);
+    const int S = h.stride;   // 1, or 2 with register transforms on both sides (eligibility)
     // one-wave workgroups, one group of rw rows each
     auto reg_grid = [](int64_t rows, int rw) { return dim3((unsigned)((rows + rw - 1) / rw)); };
 
@@ -1126,29 +1175,41 @@ int try_launch_fused_spectral(const disco_psi* psi, const void* x, const void* w
     const int64_t nrows_all = (int64_t)B * D.nlat_out;
     const int NX = (int)std::min<int64_t>(kXcds, nrows_all);
     const int64_t min_items = nrows_all / NX * (MP / kMt);
-    const int GX = (int)std::max<int64_t>(1, std::min<int64_t>(min_items, 2 * (int64_t)ncu / NX));
+    // window capacity: 8 (two workgroups per compute unit) or 16 (one)
+    const int NWC = d.max_windows <= 8 ? 8 : 16;
+    const int per_cu = NWC == 8 ? 2 : 1;
+    const int GX =
+        (int)std::max<int64_t>(1, std::min<int64_t>(min_items, per_cu * (int64_t)ncu / NX));
     dim3 grid((unsigned)(NX * GX));
-#define DISCO_SM(CC, KK)                                                                     \
-    hipLaunchKernelGGL((spec_mfma<CC, KK>), grid, dim3(kSpecThreads), 0, st, xh, wpd,         \
+#define DISCO_SM(CC, KK, NWT)                                                                \
+    hipLaunchKernelGGL((spec_mfma<CC, KK, NWT>), grid, dim3(kSpecThreads), 0, st, xh, wpd,   \
                        psih, d.win_ptr, d.windows, yh, B, Ci, D.nlat_in, D.nlat_out, MP, NX, \
                        (int64_t)h.windows.size() * K * MP, (int)d.max_windows)
-#define DISCO_SM_K(CC)                                                                       \
+#define DISCO_SM_K(CC, NWT)                                                                  \
     switch (K) {                                                                             \
-        case 1: DISCO_SM(CC, 1); break;                                                      \
-        case 2: DISCO_SM(CC, 2); break;                                                      \
-        case 3: DISCO_SM(CC, 3); break;                                                      \
-        case 4: DISCO_SM(CC, 4); break;                                                      \
-        case 5: DISCO_SM(CC, 5); break;                                                      \
-        case 6: DISCO_SM(CC, 6); break;                                                      \
-        case 7: DISCO_SM(CC, 7); break;                                                      \
-        default: DISCO_SM(CC, 8); break;                                                     \
+        case 1: DISCO_SM(CC, 1, NWT); break;                                                 \
+        case 2: DISCO_SM(CC, 2, NWT); break;                                                 \
+        case 3: DISCO_SM(CC, 3, NWT); break;                                                 \
+        case 4: DISCO_SM(CC, 4, NWT); break;                                                 \
+        case 5: DISCO_SM(CC, 5, NWT); break;                                                 \
+        case 6: DISCO_SM(CC, 6, NWT); break;                                                 \
+        case 7: DISCO_SM(CC, 7, NWT); break;                                                 \
+        default: DISCO_SM(CC, 8, NWT); break;                                                \
     }
     {
         KernelTimer timer("spec_mfma", st);
         if (Co == 128) {
-            DISCO_SM_K(128)
+            if (NWC == 8) {
+                DISCO_SM_K(128, 8)
+            } else {
+                DISCO_SM_K(128, 16)
+            }
         } else {
-            DISCO_SM_K(64)
+            if (NWC == 8) {
+                DISCO_SM_K(64, 8)
+            } else {
+                DISCO_SM_K(64, 16)
+            }
         }
     }
 #undef DISCO_SM_K
@@ -1156,25 +1217,29 @@ int try_launch_fused_spectral(const disco_psi* psi, const void* x, const void* w
     const int64_t yrows = (int64_t)B * Co * D.nlat_out;
     const dim3 igrid((unsigned)((yrows + kFftRows - 1) / kFftRows));
     const uint32_t* yh32 = reinterpret_cast<const uint32_t*>(yh);
-#define DISCO_IR(H1, H2, RW, TY)                                                               \
-    hipLaunchKernelGGL((spec_irfft_reg<H1, H2, RW, TY>),                                       \
+#define DISCO_IR(H1, H2, RW, TY, FD)                                                           \
+    hipLaunchKernelGGL((spec_irfft_reg<H1, H2, RW, TY, FD>),                                   \
                        reg_grid(yrows, RW),                                                    \
                        dim3(kRegThreads), 0, st, yh32, static_cast<TY*>(y), bias, Co,          \
-                       D.nlat_out, yrows)
-#define DISCO_IR_T(H1, H2, RW)                 \
+                       D.nlat_out, yrows, MP)
+#define DISCO_IR_T(H1, H2, RW, FD)             \
     if (y_dtype == DISCO_F32) {                \
-        DISCO_IR(H1, H2, RW, float);           \
+        DISCO_IR(H1, H2, RW, float, FD);       \
     } else {                                   \
-        DISCO_IR(H1, H2, RW, bf16_t);          \
+        DISCO_IR(H1, H2, RW, bf16_t, FD);      \
     }
     {
     KernelTimer timer("spec_irfft", st);
-    if (reg && H == 720) {
-        DISCO_IR_T(16, 45, 4)
+    if (S == 2 && H == 720) {
+        DISCO_IR_T(8, 45, 8, 2)          // 360-point half transform of the 720 outputs
+    } else if (S == 2) {
+        DISCO_IR_T(4, 45, 16, 2)         // H == 360: 180-point half transform
+    } else if (reg && H == 720) {
+        DISCO_IR_T(16, 45, 4, 1)
     } else if (reg && H == 360) {
-        DISCO_IR_T(8, 45, 8)
+        DISCO_IR_T(8, 45, 8, 1)
     } else if (reg && H == 180) {
-        DISCO_IR_T(4, 45, 16)
+        DISCO_IR_T(4, 45, 16, 1)
     } else if (y_dtype == DISCO_F32)
         hipLaunchKernelGGL(spec_irfft<float>, igrid, dim3(kFftThreads), fft_lds, st,
                            reinterpret_cast<const uint32_t*>(yh), static_cast<float*>(y), bias, N,

@@ -87,6 +87,42 @@ __global__ __launch_bounds__(256) void lds_read(uint32_t* __restrict__ out, int 
     if (r == 0x9e3779b9u) out[blockIdx.x] = r;
 }
 
+// 16-byte LDS reads in a given lane pattern (each wave reads 1 KB per
+// instruction): mode 0 contiguous (lane l at 16 l); mode 1 and 2 rows of
+// 128 bytes, one per lane (row l & 31, lane halves 4 KB apart), at 16-byte
+// piece (l & 7) (mode 1) or ((l >> 1) & 7) (mode 2) of the row.  On a 64-bank
+// LDS with 16-lane phases mode 1 has two-way conflicts and mode 2 none; with
+// 32 banks and 8-lane phases it is the other way round.
+__global__ __launch_bounds__(256) void lds_pattern(uint32_t* __restrict__ out, int iters, int mode) {
+    __shared__ uint4 buf[kLdsWords];
+    for (int i = threadIdx.x; i < kLdsWords; i += blockDim.x)
+        buf[i] = make_uint4(i, i * 3u, i * 5u, i * 7u);
+    __syncthreads();
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int l32 = lane & 31, lg = lane >> 5;
+    int base;
+    if (mode == 0) base = lane;
+    else if (mode == 1) base = lg * 256 + l32 * 8 + (l32 & 7);
+    else base = lg * 256 + l32 * 8 + ((l32 >> 1) & 7);
+    base += wave * 512;
+    uint4 acc = make_uint4(0, 0, 0, 0);
+    int off = 0;
+    for (int i = 0; i < iters; ++i) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            // in bounds: base < 2048, off + 512 u < 2048 before the mask
+            const uint4 v = buf[(base + ((off + 512 * u) & 2047)) & (kLdsWords - 1)];
+            acc.x ^= v.x;
+            acc.y ^= v.y;
+            acc.z ^= v.z;
+            acc.w ^= v.w;
+        }
+        off += 64;
+    }
+    const uint32_t r = acc.x ^ acc.y ^ acc.z ^ acc.w;
+    if (r == 0x9e3779b9u) out[blockIdx.x] = r;
+}
+
 template <typename F>
 int timed(F launch, int reps, float* ms) {
     hipEvent_t e0, e1;
@@ -161,6 +197,19 @@ int probe_lds_read(void* scratch, int per_cu, int iters, int reps, float* ms, do
     return timed([&] {
         hipLaunchKernelGGL(lds_read, dim3(grid), dim3(256), 0, nullptr,
                            static_cast<uint32_t*>(scratch), iters);
+    }, reps, ms);
+}
+
+// LDS read time for one lane pattern of lds_pattern (modes 0, 1, 2); two
+// workgroups of four waves per compute unit, each wave reading 8 KB per
+// iteration.  scratch: 4 bytes per workgroup.
+int probe_lds_pattern(void* scratch, int mode, int iters, int reps, float* ms, double* bytes) {
+    if (!scratch || !ms || !bytes || mode < 0 || mode > 2 || iters < 1 || reps < 1) return -1;
+    const int grid = grid_for(2);
+    *bytes = (double)grid * 4 * iters * 8 * 64 * 16.0;
+    return timed([&] {
+        hipLaunchKernelGGL(lds_pattern, dim3(grid), dim3(256), 0, nullptr,
+                           static_cast<uint32_t*>(scratch), iters, mode);
     }, reps, ms);
 }
 

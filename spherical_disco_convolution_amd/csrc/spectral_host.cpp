@@ -94,8 +94,13 @@ int build_spectral_tables(const HostPsi& h, std::vector<uint32_t>& psih, int32_t
     *mp = 0;
     *nrad = 0;
     const int N = h.desc.nlon_in;
-    if (h.stride != 1 || h.desc.nlon_out != N || N % 2 != 0 || N < 4 || N > kSpecMaxN ||
-        h.K > 8 || !spectral_plan(N / 2, radix, nrad))
+    // stride 1; or stride 2 where both transforms have register forms (input
+    // halves of 720 and 360 points): the stride-2 output is the stride-1
+    // correlation at every second longitude, folded in the frequency domain
+    const bool s1 = h.stride == 1 && h.desc.nlon_out == N;
+    const bool s2 = h.stride == 2 && (N == 1440 || N == 720);
+    if ((!s1 && !s2) || N % 2 != 0 || N < 4 || N > kSpecMaxN || h.K > 8 ||
+        !spectral_plan(N / 2, radix, nrad))
         return DISCO_OK;   // not eligible: no tables
     const int M = N / 2 + 1;
     const int MP = (M + 31) / 32 * 32;

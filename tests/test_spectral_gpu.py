@@ -107,9 +107,12 @@ def test_path_selection(sdc, monkeypatch):
     assert not sdc.fused_is_spectral(psi, torch.bfloat16, 128, 96, 1)    # Co tile
     assert not sdc.fused_is_spectral(psi, torch.bfloat16, 40, 64, 1)     # 32-channel chunks
     assert not sdc.fused_is_spectral(psi, torch.bfloat16, 128, 128, 2)   # groups
-    # stride 2 has no spectral tables
+    # stride 2 takes the spectral path only where both transforms have
+    # register forms (720 and 1440 input longitudes)
     p2 = sdc.psi_build(33, 64, 17, 32, (3, 3), 4 * math.pi / 16).to_device()
     assert not sdc.fused_is_spectral(p2, torch.bfloat16, 128, 128, 1)
+    p3 = sdc.psi_build(31, 720, 16, 360, (3, 3), 4 * math.pi / 30).to_device()
+    assert sdc.fused_is_spectral(p3, torch.bfloat16, 64, 64, 1)
     # N / 2 = 7 is not a product of 2, 3 and 5
     p7 = sdc.psi_build(9, 14, 9, 14, (3,), 0.7).to_device()
     assert not sdc.fused_is_spectral(p7, torch.bfloat16, 128, 128, 1)
@@ -242,6 +245,44 @@ def test_register_transforms(sdc, wl, monkeypatch):
     for out_dtype in (torch.float32, torch.bfloat16):
         yb = sdc.fused_fwd(psi, xd, wd, bias=bd, out_dtype=out_dtype)[..., cols].float().cpu().numpy()
         assert rel_l2(yb, refb) <= TOL_BF16
+
+
+# longitude stride 2: the stride-1 correlation's spectrum folded onto the
+# output grid's frequencies before the inverse transform; 15 input rows per
+# output row (two window-sum MFMA steps), like the 361x720 -> 181x360 layer
+STRIDE2 = [
+    Workload("s2_720_co64", 23, 1, 64, 64, 1, 61, 720, 31, 360, (3, 3), oracle.num_basis((3, 3)),
+             4 * math.pi / 30, "bf16"),
+    Workload("s2_1440_co128_b2", 24, 2, 32, 128, 1, 25, 1440, 13, 720, (3,), 3, 4 * math.pi / 12,
+             "bf16"),
+]
+
+
+@pytest.mark.parametrize("path", ["spectral", "toeplitz"])
+@pytest.mark.parametrize("wl", STRIDE2, ids=[w.name for w in STRIDE2])
+def test_stride2_spectral(sdc, wl, path, monkeypatch):
+    if path == "toeplitz":
+        monkeypatch.setenv("DISCO_FUSED_PATH", "toeplitz")
+    else:
+        monkeypatch.delenv("DISCO_FUSED_PATH", raising=False)
+    _say("stride 2", path, wl.name)
+    x, w = _prepare(wl)
+    psi = _psi(sdc, wl)
+    assert sdc.fused_is_spectral(psi, torch.bfloat16, wl.Ci, wl.Co, 1) == (path == "spectral")
+    xd, wd = _dev(x), _dev(w)
+    bias = np.linspace(-1, 1, wl.Co).astype(np.float32)
+    y = sdc.fused_fwd(psi, xd, wd, bias=torch.from_numpy(bias).cuda()).cpu().numpy()
+    cols = _sample_cols(wl.nlon_out, seed=5)
+    ref = oracle.forward(_desc(wl), x, w, 1, cols_out=cols, bias=bias)
+    err = rel_l2(y[..., cols], ref)
+    _say(f"  rel-L2 {err:.3e}")
+    assert err <= TOL_BF16
+    if path == "spectral":
+        frows = [0, wl.nlat_out // 3, wl.nlat_out // 2]
+        fref = oracle.forward(_desc(wl), x, w, 1, rows=frows)
+        band = worst_band_rel_l2(y[:, :, frows] - bias[None, :, None, None], fref)
+        _say(f"  worst 32-frequency band rel-L2 {band:.3e}")
+        assert band <= TOL_BF16
 
 
 def test_kernel_timing_names_the_spectral_kernels(sdc, monkeypatch):

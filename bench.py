@@ -150,11 +150,13 @@ def algorithmic_flops(wl, nnz_nonzero):
 
 
 def spec_mfma_flops(wl, windows):
-    """Algorithmic flops of one spec_mfma launch: the channel/basis product over
-    the real and imaginary parts of frequencies 0..N/2 (2 Co Ci K per output
-    row entry), plus one complex multiply-add (8 flops) per channel, window,
+    """Algorithmic flops of one launch of the spectral product kernel
+    (spec_mfma, or spec32_conv for float32): the channel/basis product over the
+    real and imaginary parts of the input grid's frequencies 0..N_in/2 (2 Co Ci
+    K per output row entry; a stride-2 layer folds them onto the output grid
+    afterwards), plus one complex multiply-add (8 flops) per channel, window,
     basis function and frequency of the window sum."""
-    M = wl.nlon_out // 2 + 1
+    M = wl.nlon_in // 2 + 1
     gemm = 2.0 * wl.B * wl.Co * wl.Ci * wl.K * wl.nlat_out * 2 * M
     window = 8.0 * wl.B * wl.Ci * windows * wl.K * M
     return gemm + window
@@ -455,7 +457,7 @@ def main():
     kernels_ms = {k: round(tot / n, 4) for k, (tot, n) in kt.items()}
     dom = max(kt, key=lambda k: kt[k][0])
     dom_s = kt[dom][0] / kt[dom][1] / 1000.0
-    if dom == "spec_mfma":
+    if dom in ("spec_mfma", "spec32_conv"):
         f_dom = spec_mfma_flops(wl, count_windows(psi))
     else:
         f_dom = f_alg

@@ -228,7 +228,8 @@ int disco_psi_to_device(disco_psi* psi) {
     rc = build_mfma_tables(psi, taps, info);
     if (rc != DISCO_OK) return rc;
     std::vector<uint32_t> spec_psih;
-    rc = build_spectral_tables(h, spec_psih, d.spec_radix, &d.spec_nrad, &d.spec_mp);
+    std::vector<float> spec_psih32;
+    rc = build_spectral_tables(h, spec_psih, spec_psih32, d.spec_radix, &d.spec_nrad, &d.spec_mp);
     if (rc != DISCO_OK) return rc;
 
     void* p = nullptr;
@@ -263,6 +264,13 @@ int disco_psi_to_device(disco_psi* psi) {
         d.spec_psih = p;
         if ((rc = dev_copy(p, spec_psih.data(), spec_psih.size() * sizeof(uint32_t))) != DISCO_OK)
             goto fail;
+        if (!spec_psih32.empty()) {
+            if ((rc = dev_alloc(d, &p, spec_psih32.size() * sizeof(float))) != DISCO_OK) goto fail;
+            d.spec_psih32 = static_cast<float*>(p);
+            if ((rc = dev_copy(p, spec_psih32.data(), spec_psih32.size() * sizeof(float))) !=
+                DISCO_OK)
+                goto fail;
+        }
     }
     d.device = dev;
     psi->dev = d;

@@ -64,8 +64,8 @@ bool parallel_ranges(size_t n, const std::function<void(size_t, size_t)>& fn);
 constexpr int kSpecMaxN = 1800;   // N/2 <= 900 bounds the transform butterflies per lane
 constexpr int kSpecMaxRadix = 12;
 int spectral_plan(int n, int32_t* radix, int32_t* nrad);
-int build_spectral_tables(const HostPsi& h, std::vector<uint32_t>& psih, int32_t* radix,
-                          int32_t* nrad, int32_t* mp);
+int build_spectral_tables(const HostPsi& h, std::vector<uint32_t>& psih, std::vector<float>& psih32,
+                          int32_t* radix, int32_t* nrad, int32_t* mp);
 
 // ---------------------------------------------------------------------------
 // Device form of Psi
@@ -98,6 +98,7 @@ struct DevPsi {
     int32_t mfma_ok = 0;
     // longitude-spectral tables for the spectral fused path (stride 1)
     void* spec_psih = nullptr;    // bf16 (re, im) words [nwin][K][spec_mp]
+    float* spec_psih32 = nullptr; // float32 (re, im) pairs [nwin][K][spec_mp], or none
     int32_t spec_mp = 0;          // padded frequency count; 0 = no tables
     int32_t spec_radix[kSpecMaxRadix] = {0};
     int32_t spec_nrad = 0;

@@ -620,10 +620,13 @@ int try_launch_fused_mfma(const disco_psi* psi, const void* x, const void* w, co
                           int* rc, void* frag_ws, size_t frag_ws_bytes);
 int noalloc_scratch(void** ptr, size_t* bytes);
 
-// defined in kernels_spectral.hip; returns 1 if it handled the call
+// defined in kernels_spectral.hip; each returns 1 if it handled the call
 int try_launch_fused_spectral(const disco_psi* psi, const void* x, const void* w,
                               const float* bias, void* y, int y_dtype, int B, int Ci, int Co,
                               int groups, hipStream_t st, int* rc);
+int try_launch_fused_spectral32(const disco_psi* psi, const void* x, const void* w,
+                                const float* bias, void* y, int y_dtype, int B, int Ci, int Co,
+                                int groups, hipStream_t st, int* rc);
 
 namespace {
 // The direct algorithms: the matrix-core kernel for the bf16 layers it takes,
@@ -651,6 +654,9 @@ int launch_fused(const disco_psi* psi, const void* x, int dtype, const void* w, 
     int rc = DISCO_OK;
     if (dtype == DISCO_BF16 &&
         try_launch_fused_spectral(psi, x, w, bias, y, y_dtype, B, Ci, Co, groups, st, &rc))
+        return rc;
+    if (dtype == DISCO_F32 &&
+        try_launch_fused_spectral32(psi, x, w, bias, y, y_dtype, B, Ci, Co, groups, st, &rc))
         return rc;
     return launch_fused_direct(psi, x, dtype, w, bias, y, y_dtype, B, Ci, Co, groups, st, nullptr,
                                0);

@@ -185,6 +185,10 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((float2v){lo, hi}, bf16x2v));
 }
 
+__device__ __forceinline__ void spec_store(uint32_t* p, int64_t i, float2 v) {
+    p[i] = pack_bf16x2(v.x, v.y);
+}
+
 constexpr int kFftThreads = 256;
 constexpr int kFftRows = kFftThreads / 64;   // one wave per row
 
@@ -194,12 +198,30 @@ __device__ __forceinline__ void fill_twiddles(float2* twl, int H) {
     for (int e = threadIdx.x; e < H; e += blockDim.x) twl[e] = root(e, inv_h, -1.0f);
 }
 
-// x rows (N real, bf16) -> x_hat rows (MP bf16 pairs; frequencies past N/2
-// are zero).  One wave per row, four rows per workgroup; LDS: one H-point
-// buffer per row and the H-point twiddle table.  Waves past the last row
-// leave after the table is built.
-__global__ __launch_bounds__(kFftThreads) void spec_rfft(const bf16_t* __restrict__ x,
-                                                         uint32_t* __restrict__ xh, int N, int MP,
+// Spectrum storage: bf16 (re, im) pairs in one 32-bit word (real part low),
+// or float32 pairs.
+__device__ __forceinline__ float2 spec_load(const uint32_t* p, int64_t i) {
+    const uint32_t v = p[i];
+    return make_float2(__uint_as_float(v << 16), __uint_as_float(v & 0xffff0000u));
+}
+__device__ __forceinline__ float2 spec_load(const float2* p, int64_t i) { return p[i]; }
+__device__ __forceinline__ void spec_store(float2* p, int64_t i, float2 v) { p[i] = v; }
+// two consecutive samples of a real row
+__device__ __forceinline__ float2 sample_pair(const bf16_t* row, int n) {
+    const uint32_t v = reinterpret_cast<const uint32_t*>(row)[n];
+    return make_float2(__uint_as_float(v << 16), __uint_as_float(v & 0xffff0000u));
+}
+__device__ __forceinline__ float2 sample_pair(const float* row, int n) {
+    return reinterpret_cast<const float2*>(row)[n];
+}
+
+// x rows (N real, bf16 or float32) -> x_hat rows (MP spectrum words;
+// frequencies past N/2 are zero).  One wave per row, four rows per workgroup;
+// LDS: one H-point buffer per row and the H-point twiddle table.  Waves past
+// the last row leave after the table is built.
+template <typename TX, typename TS>
+__global__ __launch_bounds__(kFftThreads) void spec_rfft(const TX* __restrict__ x,
+                                                         TS* __restrict__ xh, int N, int MP,
                                                          int64_t nrows, SpecPlan pl) {
     extern __shared__ float2 sm[];
     const int H = N / 2;
@@ -209,18 +231,15 @@ __global__ __launch_bounds__(kFftThreads) void spec_rfft(const bf16_t* __restric
     float2* b0 = sm + (size_t)wave * H;
     float2* twl = sm + (size_t)kFftRows * H;
     fill_twiddles(twl, H);
-    const uint32_t* xr = reinterpret_cast<const uint32_t*>(x + (live ? row : 0) * (size_t)N);
-    for (int n = lane; n < H; n += 64) {
-        const uint32_t v = xr[n];   // samples 2n (low half) and 2n + 1
-        b0[n] = make_float2(__uint_as_float(v << 16), __uint_as_float(v & 0xffff0000u));
-    }
+    const TX* xr = x + (live ? row : 0) * (size_t)N;
+    for (int n = lane; n < H; n += 64) b0[n] = sample_pair(xr, n);   // samples 2n, 2n + 1
     __syncthreads();   // the twiddle table
     if (!live) return;
     fft_wave(b0, H, pl, twl, -1.0f, lane);
     const float2* z = b0;
     // X[m] = (a + b)/2 - i W^m (a - b)/2, a = Z[m mod H], b = conj(Z[(H - m) mod H]),
     // W = exp(-2 pi i / N)
-    uint32_t* out = xh + row * (size_t)MP;
+    TS* out = xh + row * (size_t)MP;
     const float inv_n = 0.5f / (float)H;
     for (int m = lane; m < MP; m += 64) {
         float2 X = make_float2(0.0f, 0.0f);
@@ -230,15 +249,15 @@ __global__ __launch_bounds__(kFftThreads) void spec_rfft(const bf16_t* __restric
             const float2 e = cmul(root(m, inv_n, -1.0f), csub(a, b));
             X = cadd(cscale(cadd(a, b), 0.5f), cscale(make_float2(e.y, -e.x), 0.5f));
         }
-        out[m] = pack_bf16x2(X.x, X.y);
+        spec_store(out, m, X);
     }
 }
 
 // y_hat rows (MP bf16 pairs, frequencies 0..N/2 used) -> y rows (N) + bias,
 // one wave per row (LDS as for spec_rfft).  The imaginary parts of the zero and N/2 frequencies are
 // dropped (a real row's spectrum has none).
-template <typename TY>
-__global__ __launch_bounds__(kFftThreads) void spec_irfft(const uint32_t* __restrict__ yh,
+template <typename TS, typename TY>
+__global__ __launch_bounds__(kFftThreads) void spec_irfft(const TS* __restrict__ yh,
                                                           TY* __restrict__ y,
                                                           const float* __restrict__ bias, int N,
                                                           int MP, int Co, int nlat_out,
@@ -251,11 +270,8 @@ __global__ __launch_bounds__(kFftThreads) void spec_irfft(const uint32_t* __rest
     float2* b0 = sm + (size_t)wave * H;
     float2* twl = sm + (size_t)kFftRows * H;
     fill_twiddles(twl, H);
-    const uint32_t* src = yh + (live ? row : 0) * (size_t)MP;
-    auto spec = [&](int m) {
-        const uint32_t v = src[m];
-        return make_float2(__uint_as_float(v << 16), __uint_as_float(v & 0xffff0000u));
-    };
+    const TS* src = yh + (live ? row : 0) * (size_t)MP;
+    auto spec = [&](int m) { return spec_load(src, m); };
     // Z[m] = (a + b)/2 + i conj(W^m) (a - b)/2, a = X[m], b = conj(X[H - m]), m < H
     const float inv_n = 0.5f / (float)H;
     for (int m = lane; m < H; m += 64) {
@@ -1084,12 +1100,144 @@ __global__ __launch_bounds__(kSpecThreads) __attribute__((amdgpu_waves_per_eu(NW
     }
 }
 
+// ---------------------------------------------------------------------------
+// Float32 layers (stride 1): both sums per frequency on the vector ALUs, in
+// float32, on float32 spectra (Psi_hat tabulated in float64 and rounded once
+// to float32).  One workgroup per item (batch b, output row j, 32
+// frequencies m0 ..); input channels in chunks of 8:
+//   X_hat[ci, k, m] = sum_windows x_hat[b, ci, i, m] conj(Psi_hat[k, window, m])
+//     into an LDS tile, thread (ci, m);
+//   y_hat[co, m] += sum_{ci, k} w[co, ci, k] X_hat[ci, k, m]
+//     thread (co = cl + 32 r, m = 4 q .. 4 q + 3), the chunk's weights staged
+//     in LDS (one word per (co, ci, k), read by the 8 lanes of one co).
+// ---------------------------------------------------------------------------
+constexpr int kS32M = 32;    // frequencies per item
+constexpr int kS32C = 8;     // input channels per chunk
+template <int KT, int COR>
+__global__ __launch_bounds__(kSpecThreads) void spec32_conv(
+    const float2* __restrict__ xh, const float* __restrict__ w, const float2* __restrict__ psih,
+    const int32_t* __restrict__ win_ptr, const DevWindow* __restrict__ wins,
+    float2* __restrict__ yh, int Ci, int Co, int nlat_in, int nlat_out, int MP, int nwmax) {
+    extern __shared__ float2 s32[];
+    float2* ps = s32;                                  // [nwmax][KT][32]
+    float2* xt = ps + (size_t)nwmax * KT * kS32M;      // [kS32C][KT][32]
+    float* wt = reinterpret_cast<float*>(xt + kS32C * KT * kS32M);   // [Co][kS32C][KT]
+    int* lat = reinterpret_cast<int*>(wt + (size_t)Co * kS32C * KT); // [nwmax]
+    const int tid = threadIdx.x;
+    const int ntile = MP / kS32M;
+    int item = blockIdx.x;
+    const int mt = item % ntile;
+    item /= ntile;
+    const int j = item % nlat_out, b = item / nlat_out;
+    const int m0 = mt * kS32M;
+    const int w0 = win_ptr[j], nw = win_ptr[j + 1] - w0;   // <= nwmax
+    for (int e = tid; e < nw * KT * kS32M; e += kSpecThreads) {
+        const int m = e % kS32M, rk = e / kS32M;
+        ps[e] = psih[(size_t)(w0 * KT + rk) * MP + m0 + m];
+    }
+    for (int e = tid; e < nw; e += kSpecThreads) lat[e] = wins[w0 + e].lat;
+    // window-sum role: channel cs of the chunk, frequency ms
+    const int cs = tid / kS32M, ms = tid % kS32M;
+    // product role: channels cl + 32 r, frequencies 4 q .. 4 q + 3
+    const int cl = tid / 8, q = tid % 8;
+    float2 acc[COR][4];
+#pragma unroll
+    for (int r = 0; r < COR; ++r)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) acc[r][u] = make_float2(0.0f, 0.0f);
+#pragma unroll 1
+    for (int c0 = 0; c0 < Ci; c0 += kS32C) {
+        __syncthreads();   // the previous chunk's tile and weights are used (and ps, lat are in)
+        for (int e = tid; e < Co * kS32C * KT; e += kSpecThreads) {
+            const int co = e / (kS32C * KT), r = e - co * (kS32C * KT);
+            const int ci = c0 + r / KT, k = r % KT;
+            wt[e] = ci < Ci ? w[((size_t)co * Ci + ci) * KT + k] : 0.0f;
+        }
+        {
+            const int ci = c0 + cs;
+            float2 xa[KT];
+#pragma unroll
+            for (int k = 0; k < KT; ++k) xa[k] = make_float2(0.0f, 0.0f);
+            if (ci < Ci) {
+                const float2* xrow = xh + ((size_t)b * Ci + ci) * nlat_in * MP + m0 + ms;
+                // four windows' samples loaded together, then used
+#pragma unroll 1
+                for (int w4 = 0; w4 < nw; w4 += 4) {
+                    float2 xv[4];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+                        xv[u] = xrow[(size_t)lat[min(w4 + u, nw - 1)] * MP];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        if (w4 + u >= nw) break;
+                        const int wi = w4 + u;
+#pragma unroll
+                        for (int k = 0; k < KT; ++k) {
+                            const float2 P = ps[(wi * KT + k) * kS32M + ms];
+                            // x_hat * conj(Psi_hat)
+                            xa[k].x = fmaf(xv[u].x, P.x, fmaf(xv[u].y, P.y, xa[k].x));
+                            xa[k].y = fmaf(xv[u].y, P.x, fmaf(-xv[u].x, P.y, xa[k].y));
+                        }
+                    }
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < KT; ++k) xt[(cs * KT + k) * kS32M + ms] = xa[k];
+        }
+        __syncthreads();
+#pragma unroll 2
+        for (int c = 0; c < kS32C; ++c) {
+#pragma unroll
+            for (int k = 0; k < KT; ++k) {
+                const float4* xp = reinterpret_cast<const float4*>(xt + (c * KT + k) * kS32M + 4 * q);
+                const float4 x01 = xp[0], x23 = xp[1];
+                const float2 X[4] = {make_float2(x01.x, x01.y), make_float2(x01.z, x01.w),
+                                     make_float2(x23.x, x23.y), make_float2(x23.z, x23.w)};
+#pragma unroll
+                for (int r = 0; r < COR; ++r) {
+                    const int co = cl + 32 * r;
+                    const float wv = co < Co ? wt[(co * kS32C + c) * KT + k] : 0.0f;
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        acc[r][u].x = fmaf(wv, X[u].x, acc[r][u].x);
+                        acc[r][u].y = fmaf(wv, X[u].y, acc[r][u].y);
+                    }
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < COR; ++r) {
+        const int co = cl + 32 * r;
+        if (co < Co) {
+            float4* dst = reinterpret_cast<float4*>(
+                yh + (((size_t)b * Co + co) * nlat_out + j) * MP + m0 + 4 * q);
+            dst[0] = make_float4(acc[r][0].x, acc[r][0].y, acc[r][1].x, acc[r][1].y);
+            dst[1] = make_float4(acc[r][2].x, acc[r][2].y, acc[r][3].x, acc[r][3].y);
+        }
+    }
+}
+
+// LDS bytes of spec32_conv
+size_t spec32_lds(int K, int Co, int nwmax) {
+    return ((size_t)nwmax * K * kS32M + (size_t)kS32C * K * kS32M) * sizeof(float2) +
+           (size_t)Co * kS32C * K * sizeof(float) + (size_t)nwmax * sizeof(int);
+}
+
 }  // namespace
 
 // Which fused algorithm disco_fused_fwd takes for these arguments.
 int fused_spectral_eligible(const disco_psi* psi, int x_dtype, int Ci, int Co, int groups) {
     const DevPsi& d = psi->dev;
     const HostPsi& h = psi->host;
+    if (x_dtype == DISCO_F32) {
+        // float32, stride 1, up to 128 output channels, LDS of the vector kernel
+        if (d.spec_mp <= 0 || d.spec_psih32 == nullptr || h.stride != 1 || groups != 1 ||
+            h.K > 8 || Co > 128 || Ci < 1 || spec32_lds(h.K, Co, d.max_windows) > 64 * 1024)
+            return 0;
+        const char* e32 = std::getenv("DISCO_FUSED_PATH");
+        return e32 == nullptr || std::strcmp(e32, "toeplitz") != 0;
+    }
     if (d.spec_mp <= 0 || x_dtype != DISCO_BF16 || groups != 1 || Ci % 32 != 0 ||
         (Co != 128 && Co != 64) || h.K > 8)
         return 0;
@@ -1164,9 +1312,9 @@ int try_launch_fused_spectral(const disco_psi* psi, const void* x, const void* w
     } else if (reg && H == 180) {
         DISCO_RF(4, 45, 16);
     } else {
-        hipLaunchKernelGGL(spec_rfft, dim3((unsigned)((xrows + kFftRows - 1) / kFftRows)),
-                           dim3(kFftThreads), fft_lds, st, static_cast<const bf16_t*>(x), xh, N,
-                           MP, xrows, pl);
+        hipLaunchKernelGGL((spec_rfft<bf16_t, uint32_t>),
+                           dim3((unsigned)((xrows + kFftRows - 1) / kFftRows)), dim3(kFftThreads),
+                           fft_lds, st, static_cast<const bf16_t*>(x), xh, N, MP, xrows, pl);
     }
     }
 #undef DISCO_RF
@@ -1241,11 +1389,11 @@ int try_launch_fused_spectral(const disco_psi* psi, const void* x, const void* w
     } else if (reg && H == 180) {
         DISCO_IR_T(4, 45, 16, 1)
     } else if (y_dtype == DISCO_F32)
-        hipLaunchKernelGGL(spec_irfft<float>, igrid, dim3(kFftThreads), fft_lds, st,
+        hipLaunchKernelGGL((spec_irfft<uint32_t, float>), igrid, dim3(kFftThreads), fft_lds, st,
                            reinterpret_cast<const uint32_t*>(yh), static_cast<float*>(y), bias, N,
                            MP, Co, D.nlat_out, yrows, pl);
     else
-        hipLaunchKernelGGL(spec_irfft<bf16_t>, igrid, dim3(kFftThreads), fft_lds, st,
+        hipLaunchKernelGGL((spec_irfft<uint32_t, bf16_t>), igrid, dim3(kFftThreads), fft_lds, st,
                            reinterpret_cast<const uint32_t*>(yh), static_cast<bf16_t*>(y), bias, N,
                            MP, Co, D.nlat_out, yrows, pl);
     }
@@ -1255,6 +1403,106 @@ int try_launch_fused_spectral(const disco_psi* psi, const void* x, const void* w
     hipError_t fe = hipFreeAsync(ws, st);
     if (le != hipSuccess) {
         *rc = set_error(DISCO_EHIP, "spectral fused launch failed: %s", hipGetErrorString(le));
+        return 1;
+    }
+    if (fe != hipSuccess) {
+        (void)hipGetLastError();
+        *rc = set_error(DISCO_EHIP, "hipFreeAsync failed: %s", hipGetErrorString(fe));
+        return 1;
+    }
+    *rc = DISCO_OK;
+    return 1;
+}
+
+}  // namespace disco
+
+namespace disco {
+
+// The float32 spectral forward (stride 1): spec_rfft (float32 spectra),
+// spec32_conv, spec_irfft.  Returns 0 when the layer does not qualify.
+int try_launch_fused_spectral32(const disco_psi* psi, const void* x, const void* w,
+                                const float* bias, void* y, int y_dtype, int B, int Ci, int Co,
+                                int groups, hipStream_t st, int* rc) {
+    if (!fused_spectral_eligible(psi, DISCO_F32, Ci, Co, groups) || B <= 0) return 0;
+    // rows are read and written as float pairs
+    if ((reinterpret_cast<uintptr_t>(x) & 7) != 0 || (reinterpret_cast<uintptr_t>(y) & 7) != 0)
+        return 0;
+    const DevPsi& d = psi->dev;
+    const HostPsi& h = psi->host;
+    const disco_psi_desc& D = h.desc;
+    const int N = D.nlon_in, H = N / 2, MP = d.spec_mp, K = h.K;
+    SpecPlan pl;
+    pl.n = d.spec_nrad;
+    for (int i = 0; i < kSpecMaxRadix; ++i) pl.r[i] = d.spec_radix[i];
+    auto up = [](size_t v) { return (v + 255) / 256 * 256; };
+    const size_t xh_bytes = up((size_t)B * Ci * D.nlat_in * MP * sizeof(float2));
+    const size_t yh_bytes = up((size_t)B * Co * D.nlat_out * MP * sizeof(float2));
+    void* ws = nullptr;
+    hipError_t e = hipMallocAsync(&ws, xh_bytes + yh_bytes, st);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        *rc = set_error(e == hipErrorOutOfMemory ? DISCO_ENOMEM : DISCO_EHIP,
+                        "hipMallocAsync for the spectral workspace failed: %s",
+                        hipGetErrorString(e));
+        return 1;
+    }
+    float2* xh = static_cast<float2*>(ws);
+    float2* yh = reinterpret_cast<float2*>(static_cast<char*>(ws) + xh_bytes);
+    const size_t fft_lds = (size_t)(kFftRows + 1) * H * sizeof(float2);
+    const int64_t xrows = (int64_t)B * Ci * D.nlat_in;
+    {
+        KernelTimer timer("spec_rfft", st);
+        hipLaunchKernelGGL((spec_rfft<float, float2>),
+                           dim3((unsigned)((xrows + kFftRows - 1) / kFftRows)), dim3(kFftThreads),
+                           fft_lds, st, static_cast<const float*>(x), xh, N, MP, xrows, pl);
+    }
+    const int COR = (Co + 31) / 32;   // 1 .. 4 (Co <= 128)
+    const size_t lds = spec32_lds(K, Co, d.max_windows);
+    const dim3 grid((unsigned)((int64_t)B * D.nlat_out * (MP / kS32M)));
+#define DISCO_S32(KK, CR)                                                                        \
+    hipLaunchKernelGGL((spec32_conv<KK, CR>), grid, dim3(kSpecThreads), lds, st, xh,            \
+                       static_cast<const float*>(w), d.spec_psih32 == nullptr                   \
+                           ? nullptr                                                            \
+                           : reinterpret_cast<const float2*>(d.spec_psih32),                    \
+                       d.win_ptr, d.windows, yh, Ci, Co, D.nlat_in, D.nlat_out, MP,             \
+                       (int)d.max_windows)
+#define DISCO_S32_C(KK)                   \
+    switch (COR) {                        \
+        case 1: DISCO_S32(KK, 1); break;  \
+        case 2: DISCO_S32(KK, 2); break;  \
+        case 3: DISCO_S32(KK, 3); break;  \
+        default: DISCO_S32(KK, 4); break; \
+    }
+    {
+        KernelTimer timer("spec32_conv", st);
+        switch (K) {
+            case 1: DISCO_S32_C(1) break;
+            case 2: DISCO_S32_C(2) break;
+            case 3: DISCO_S32_C(3) break;
+            case 4: DISCO_S32_C(4) break;
+            case 5: DISCO_S32_C(5) break;
+            case 6: DISCO_S32_C(6) break;
+            case 7: DISCO_S32_C(7) break;
+            default: DISCO_S32_C(8) break;
+        }
+    }
+#undef DISCO_S32_C
+#undef DISCO_S32
+    const int64_t yrows = (int64_t)B * Co * D.nlat_out;
+    const dim3 igrid((unsigned)((yrows + kFftRows - 1) / kFftRows));
+    {
+        KernelTimer timer("spec_irfft", st);
+        if (y_dtype == DISCO_F32)
+            hipLaunchKernelGGL((spec_irfft<float2, float>), igrid, dim3(kFftThreads), fft_lds, st,
+                               yh, static_cast<float*>(y), bias, N, MP, Co, D.nlat_out, yrows, pl);
+        else
+            hipLaunchKernelGGL((spec_irfft<float2, bf16_t>), igrid, dim3(kFftThreads), fft_lds, st,
+                               yh, static_cast<bf16_t*>(y), bias, N, MP, Co, D.nlat_out, yrows, pl);
+    }
+    hipError_t le = hipGetLastError();
+    hipError_t fe = hipFreeAsync(ws, st);
+    if (le != hipSuccess) {
+        *rc = set_error(DISCO_EHIP, "float32 spectral launch failed: %s", hipGetErrorString(le));
         return 1;
     }
     if (fe != hipSuccess) {

@@ -14,6 +14,8 @@
 //   * Psi_hat per window for m < N/2 + 1, zero up to the padded count MP
 //     (a multiple of 32), stored as bf16 (re, im) pairs in one 32-bit word
 //     (real part in the low half): the matrix-core operand type it feeds;
+//     and, for stride 1 when it takes at most 256 MiB, as float32 pairs for
+//     float32 layers;
 //   * the radix plan (4, 2, 3, 5) of the N/2-point complex transform the
 //     real transforms are built on.
 #include <algorithm>
@@ -89,9 +91,10 @@ int spectral_plan(int n, int32_t* radix, int32_t* nrad) {
     return n == 1;
 }
 
-int build_spectral_tables(const HostPsi& h, std::vector<uint32_t>& psih, int32_t* radix,
-                          int32_t* nrad, int32_t* mp) {
+int build_spectral_tables(const HostPsi& h, std::vector<uint32_t>& psih, std::vector<float>& psih32,
+                          int32_t* radix, int32_t* nrad, int32_t* mp) {
     *mp = 0;
+    psih32.clear();
     *nrad = 0;
     const int N = h.desc.nlon_in;
     // stride 1; or stride 2 where both transforms have register forms (input
@@ -112,10 +115,13 @@ int build_spectral_tables(const HostPsi& h, std::vector<uint32_t>& psih, int32_t
         c[n] = std::cos(a);
         s[n] = std::sin(a);
     }
+    // the float32 table (float32 layers, stride 1) when it takes at most 256 MiB
+    const bool f32 = s1 && nwin * (size_t)K * MP * 8 <= ((size_t)256 << 20);
     try {
         // plus a zero block of 32 words at the end (a DMA source for the
         // slices of windows a row does not have)
         psih.assign(nwin * (size_t)K * MP + 32, 0u);
+        if (f32) psih32.assign(nwin * (size_t)K * MP * 2, 0.0f);
     } catch (const std::bad_alloc&) {
         return set_error(DISCO_ENOMEM, "host allocation for the spectral tables failed");
     }
@@ -136,8 +142,14 @@ int build_spectral_tables(const HostPsi& h, std::vector<uint32_t>& psih, int32_t
                         im[k] -= v[(size_t)t * K + k] * s[e];
                     }
                 }
-                for (int k = 0; k < K; ++k)
-                    psih[(w * K + k) * (size_t)MP + m] = bf16_of(re[k]) | (bf16_of(im[k]) << 16);
+                for (int k = 0; k < K; ++k) {
+                    const size_t e = (w * K + k) * (size_t)MP + m;
+                    psih[e] = bf16_of(re[k]) | (bf16_of(im[k]) << 16);
+                    if (f32) {
+                        psih32[2 * e] = (float)re[k];
+                        psih32[2 * e + 1] = (float)im[k];
+                    }
+                }
             }
         }
     };

@@ -348,7 +348,9 @@ WIDE = [
 
 
 @pytest.mark.parametrize("wl", WIDE, ids=[w.name for w in WIDE])
-def test_fused_generic_full_ring_windows(sdc, wl):
+def test_fused_generic_full_ring_windows(sdc, wl, monkeypatch):
+    # the direct kernels (float32 stride-1 layers otherwise go spectral)
+    monkeypatch.setenv("DISCO_FUSED_PATH", "toeplitz")
     _say("generic fused, full-ring windows", wl.name)
     x, w = _prepare(wl)
     psi = _psi(sdc, wl)

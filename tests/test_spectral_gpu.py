@@ -103,7 +103,8 @@ def test_path_selection(sdc, monkeypatch):
     monkeypatch.delenv("DISCO_FUSED_PATH")
     assert sdc.fused_is_spectral(psi, torch.bfloat16, 128, 128, 1)       # the default
     assert sdc.fused_is_spectral(psi, torch.bfloat16, 64, 64, 1)
-    assert not sdc.fused_is_spectral(psi, torch.float32, 128, 128, 1)    # bf16 only
+    assert sdc.fused_is_spectral(psi, torch.float32, 128, 128, 1)        # float32 kernels
+    assert not sdc.fused_is_spectral(psi, torch.float32, 128, 256, 1)    # float32: Co <= 128
     assert not sdc.fused_is_spectral(psi, torch.bfloat16, 128, 96, 1)    # Co tile
     assert not sdc.fused_is_spectral(psi, torch.bfloat16, 40, 64, 1)     # 32-channel chunks
     assert not sdc.fused_is_spectral(psi, torch.bfloat16, 128, 128, 2)   # groups
@@ -283,6 +284,51 @@ def test_stride2_spectral(sdc, wl, path, monkeypatch):
         band = worst_band_rel_l2(y[:, :, frows] - bias[None, :, None, None], fref)
         _say(f"  worst 32-frequency band rel-L2 {band:.3e}")
         assert band <= TOL_BF16
+
+
+# float32 layers at stride 1: float32 spectra and Psi_hat, both sums on the
+# vector ALUs in float32; held to the float32 bar
+SPEC32 = [
+    Workload("f32_c2_like", 25, 2, 32, 32, 1, 33, 64, 33, 64, (3, 3), 7, 4 * math.pi / 32, "f32"),
+    Workload("f32_ragged", 26, 1, 5, 7, 1, 17, 32, 17, 32, (3,), 3, 0.5, "f32"),
+    Workload("f32_co128_ci40_k8", 27, 1, 40, 128, 1, 25, 48, 25, 48, (2, 7), 8, 0.5, "f32"),
+    Workload("f32_wide_cap", 28, 1, 3, 2, 1, 17, 32, 17, 32, (3, 3), 7, 2.5, "f32"),
+    Workload("f32_k1", 29, 1, 2, 2, 1, 9, 16, 9, 16, (1,), 1, 0.7, "f32"),
+]
+
+
+@pytest.mark.parametrize("wl", SPEC32, ids=[w.name for w in SPEC32])
+def test_float32_spectral(sdc, wl, monkeypatch):
+    monkeypatch.delenv("DISCO_FUSED_PATH", raising=False)
+    _say("float32 spectral", wl.name)
+    x, w = draw_inputs(wl)
+    psi = _psi(sdc, wl)
+    assert sdc.fused_is_spectral(psi, torch.float32, wl.Ci, wl.Co, 1)
+    xd, wd = torch.from_numpy(x).cuda(), torch.from_numpy(w).cuda()
+    sdc.kernel_timing(True)
+    try:
+        y = sdc.fused_fwd(psi, xd, wd).cpu().numpy()
+        names = set(sdc.kernel_timing_read())
+    finally:
+        sdc.kernel_timing(False)
+    assert "spec32_conv" in names, names
+    ref = oracle.forward(_desc(wl), x, w, 1)
+    err, band = rel_l2(y, ref), worst_band_rel_l2(y, ref)
+    _say(f"  rel-L2 {err:.3e}, worst 32-frequency band {band:.3e}")
+    assert err <= 1e-5
+    assert band <= 1e-4
+    bias = np.linspace(-1, 1, wl.Co).astype(np.float32)
+    refb = oracle.forward(_desc(wl), x, w, 1, bias=bias)
+    yb = sdc.fused_fwd(psi, xd, wd, bias=torch.from_numpy(bias).cuda()).cpu().numpy()
+    assert rel_l2(yb, refb) <= 1e-5
+    yh = sdc.fused_fwd(psi, xd, wd, bias=torch.from_numpy(bias).cuda(),
+                       out_dtype=torch.bfloat16).float().cpu().numpy()
+    assert rel_l2(yh, refb) <= 8e-3
+    # the direct kernel on the same layer agrees to float32 rounding
+    monkeypatch.setenv("DISCO_FUSED_PATH", "toeplitz")
+    assert not sdc.fused_is_spectral(psi, torch.float32, wl.Ci, wl.Co, 1)
+    yd = sdc.fused_fwd(psi, xd, wd).cpu().numpy()
+    assert rel_l2(yd, y) <= 2e-6
 
 
 def test_kernel_timing_names_the_spectral_kernels(sdc, monkeypatch):

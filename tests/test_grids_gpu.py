@@ -5,8 +5,8 @@ grid_out (DistributedSpectralConvS2 page: "legendre-gauss", "lobatto",
 The grid only changes Psi (nodes and quadrature weights, built on the host);
 the device kernels are the ones the equiangular grid uses.  Each case runs
 the fused forward on the path the library picks (the longitude-spectral one
-for the bf16 stride-1 cases), the direct matrix-core path where bf16, and the
-unfused contraction + einsum.  Bars as elsewhere: relative L2 <= 1e-5 for
+for the stride-1 cases), the direct kernels where that is spectral or the
+layer is bf16, and the unfused contraction + einsum.  Bars as elsewhere: relative L2 <= 1e-5 for
 float32, <= 2e-2 for bf16 inputs.
 """
 import sys
@@ -48,7 +48,7 @@ CASES = [
     ("equiangular-trapezoidal", "equiangular-trapezoidal", 1, 32, 64, 33, 64, 33, 64, (2, 2), 0.25,
      "bf16", True),
     ("legendre-gauss", "equiangular", 1, 4, 6, 48, 96, 25, 48, (3, 3), 0.5, "f32", False),
-    ("lobatto", "legendre-gauss", 2, 3, 5, 17, 32, 16, 32, (3,), 0.6, "f32", False),
+    ("lobatto", "legendre-gauss", 2, 3, 5, 17, 32, 16, 32, (3,), 0.6, "f32", True),
 ]
 
 
@@ -85,7 +85,8 @@ def test_other_grids_forward(sdc, case, monkeypatch):
     err = rel_l2(y, ref)
     _say(f"  fused ({'spectral' if spectral else 'direct'}) rel-L2 {err:.3e}")
     assert err <= TOL[dt]
-    if dt == "bf16":
+    if spectral or dt == "bf16":
+        # the direct kernels on the same layer
         monkeypatch.setenv("DISCO_FUSED_PATH", "toeplitz")
         yt = sdc.fused_fwd(psi, xd, wd).float().cpu().numpy()
         assert rel_l2(yt, ref) <= TOL[dt]

@@ -91,7 +91,8 @@ def test_noalloc_matches_fused_fwd_twice(sdc, pair):
         if wl.dtype == "bf16":
             assert "fused_mfma" in names, names
         if spectral:
-            assert rel_l2(y.float().cpu().numpy(), y_ref.float().cpu().numpy()) <= 2e-2, wl.name
+            # two algorithms, each within tol of the oracle
+            assert rel_l2(y.float().cpu().numpy(), y_ref.float().cpu().numpy()) <= 2 * tol, wl.name
         else:
             assert torch.equal(y, y_ref), wl.name
 

@@ -274,28 +274,132 @@ __global__ __launch_bounds__(kThreads) void fused_depthwise(
     }
 }
 
-// The same sum with register tiling, for strides S = 1 and 2: thread tid
-// owns the QR consecutive outputs q0 + tid QR + r, whose input samples for
-// taps t0 .. t0 + DT - 1 form one run of (QR - 1) S + DT values.  That run is
-// read from LDS once per tap chunk and kept in registers; the folded taps are
-// LDS broadcasts.  The tap loop is padded to a multiple of DT with zero taps
-// (the samples they meet are real, finite inputs).
-constexpr int kDwTile = 16;   // taps per register chunk
+// The same sum with register tiling, for strides S = 1 and 2.  Thread tid
+// owns the QR (4, 6 or 8) consecutive outputs q0 + QR tid + r.  The samples of
+// a window's input row are staged in LDS from its first longitude on; for
+// stride 2 they are split by parity (even offsets in ext_e, odd in ext_o), so
+// that tap t = 2 u + p of output q reads ext_p[(q - q0) + u]: a run of
+// consecutive words per thread.  Per chunk of DT taps (32, then 8 for the
+// rest of the window) a thread reads its run with 16-byte LDS loads (8-byte
+// for QR = 6: lanes 16 or 24 bytes apart, free of bank conflicts) and the
+// chunk's folded taps as 16-byte broadcasts, then does QR DT multiply-adds
+// from registers.  Windows are padded to a multiple of 8 taps with zero taps
+// (the samples they meet are real, finite inputs).  Workgroups take (batch,
+// channel, output row) tasks in eight bands, band = workgroup index mod 8
+// (workgroups are dispatched to the accelerator dies round-robin): a band is
+// a range of (batch, channel) planes walked row by row, so the workgroups in
+// flight on a die share each row's Psi values and their planes' input rows in
+// its L2.
+constexpr int kDwT = 32;     // taps per main register chunk
+constexpr int kDwTail = 8;   // taps per chunk past the last full main chunk
+constexpr int kDwBands = 8;  // accelerator dies (L2 domains)
+
+// LDS words of one parity array (S = 2) or of the one sample array (S = 1)
+// for NT threads of QR outputs and windows padded to wpad taps: the last
+// chunk's runs end at QR NT + wpad / S - 1.  The odd array starts 16 banks
+// past a 32-word boundary after the even one.
+__host__ __device__ constexpr int dw_ext_words(int nt, int qr, int wpad, int s) {
+    return qr * nt + wpad / s;
+}
+__host__ __device__ constexpr int dw_odd_offset(int nt, int qr, int wpad) {
+    return (dw_ext_words(nt, qr, wpad, 2) + 31) / 32 * 32 + 16;
+}
+
+// One chunk of DT taps starting at t0 for the thread's QR outputs (own is
+// the first output's offset within the pass): acc[r] += sum_t tap[t0 + t] *
+// sample(own + r, t0 + t).  R = DT / S + QR words per array are read, in
+// loads of V words.
+template <int DT, int QR, int S>
+__device__ __forceinline__ void dw_chunk(const float* __restrict__ folded,
+                                         const float* __restrict__ ext_e,
+                                         const float* __restrict__ ext_o, int own, int t0,
+                                         float (&acc)[QR]) {
+    constexpr int V = QR == 6 ? 2 : 4;
+    constexpr int R = DT / S + QR;
+    static_assert(R % V == 0, "whole loads");
+    float tap[DT];
+#pragma unroll
+    for (int i = 0; i < DT / 4; ++i) {
+        const float4 f4 = *reinterpret_cast<const float4*>(folded + t0 + 4 * i);
+        tap[4 * i] = f4.x;
+        tap[4 * i + 1] = f4.y;
+        tap[4 * i + 2] = f4.z;
+        tap[4 * i + 3] = f4.w;
+    }
+    auto load_run = [&](const float* src, float (&e)[R]) {
+#pragma unroll
+        for (int i = 0; i < R / V; ++i) {
+            if constexpr (V == 4) {
+                const float4 a = *reinterpret_cast<const float4*>(src + 4 * i);
+                e[4 * i] = a.x;
+                e[4 * i + 1] = a.y;
+                e[4 * i + 2] = a.z;
+                e[4 * i + 3] = a.w;
+            } else {
+                const float2 a = *reinterpret_cast<const float2*>(src + 2 * i);
+                e[2 * i] = a.x;
+                e[2 * i + 1] = a.y;
+            }
+        }
+    };
+    if constexpr (S == 2) {
+        // output own + r, tap t0 + 2 u + p: ext_p[own + t0 / 2 + r + u]
+        float ee[R], eo[R];
+        load_run(ext_e + own + t0 / 2, ee);
+        load_run(ext_o + own + t0 / 2, eo);
+#pragma unroll
+        for (int u = 0; u < DT / 2; ++u)
+#pragma unroll
+            for (int r = 0; r < QR; ++r) {
+                acc[r] = fmaf(tap[2 * u], ee[r + u], acc[r]);
+                acc[r] = fmaf(tap[2 * u + 1], eo[r + u], acc[r]);
+            }
+    } else {
+        // output own + r, tap t0 + t: ext[own + t0 + r + t]
+        float e[R];
+        load_run(ext_e + own + t0, e);
+#pragma unroll
+        for (int t = 0; t < DT; ++t)
+#pragma unroll
+            for (int r = 0; r < QR; ++r) acc[r] = fmaf(tap[t], e[r + t], acc[r]);
+    }
+}
 
 template <typename T, typename TY, int KP, int QR, int S>
 __global__ __launch_bounds__(kThreads) void fused_depthwise_tiled(
     const T* __restrict__ x, const T* __restrict__ w, const float* __restrict__ bias,
     TY* __restrict__ y, const int32_t* __restrict__ win_ptr, const DevWindow* __restrict__ wins,
     const float* __restrict__ vals, int Ci, int Co, int groups, int K, int nlat_in, int nlon_in,
-    int nlat_out, int nlon_out, int max_width_padded) {
-    constexpr int DT = kDwTile;
-    constexpr int NE = (QR - 1) * S + DT;   // samples per chunk
-    extern __shared__ float smem[];
-    float* folded = smem;                           // [max_width_padded]
-    float* ext = smem + max_width_padded;           // [S (kThreads QR - 1) + max_width_padded]
-    const int j = blockIdx.x;
-    const int co = blockIdx.y;
-    const int b = blockIdx.z;
+    int nlat_out, int nlon_out, int wpad, int ntasks) {
+    extern __shared__ __attribute__((aligned(16))) float smem[];
+    const int NT = blockDim.x;
+    // task -> (plane = b Co + co, output row j); the whole workgroup returns
+    // together past the end (uniform)
+    const int band = (int)(blockIdx.x % kDwBands), slot = (int)(blockIdx.x / kDwBands);
+    int plane, j;
+    const int nplanes = ntasks / nlat_out;
+    if (nplanes >= kDwBands) {
+        // band = a contiguous range of planes, walked row-major: consecutive
+        // workgroups share the row's Psi values, and the band's planes' input
+        // rows stay in the die's L2 from one row to the next
+        const int p0 = (int)((int64_t)band * nplanes / kDwBands);
+        const int np = (int)((int64_t)(band + 1) * nplanes / kDwBands) - p0;
+        if (slot >= np * nlat_out) return;
+        j = slot / np;
+        plane = p0 + slot - j * np;
+    } else {
+        // few planes: contiguous ranges of the flattened (plane, row) tasks
+        const int per = (ntasks + kDwBands - 1) / kDwBands;
+        const int task = band * per + slot;
+        if (slot >= per || task >= ntasks) return;
+        j = task % nlat_out;
+        plane = task / nlat_out;
+    }
+    const int co = plane % Co;
+    const int b = plane / Co;
+    float* folded = smem;                                  // [wpad]
+    float* ext_e = smem + wpad;                            // S = 1: the samples in order
+    float* ext_o = ext_e + dw_odd_offset(NT, QR, wpad);    // S = 2 only
     const int cog = Co / groups;
     const int grp = co / cog;
     const T* xc = x + ((size_t)b * Ci + grp) * nlat_in * nlon_in;
@@ -305,21 +409,21 @@ __global__ __launch_bounds__(kThreads) void fused_depthwise_tiled(
     const int w0 = win_ptr[j], w1 = win_ptr[j + 1];
     TY* out = y + (((size_t)b * Co + co) * nlat_out + j) * nlon_out;
     const float bv = bias ? bias[co] : 0.0f;
-    const int tbase = threadIdx.x * QR * S;
+    const int tid = threadIdx.x;
+    const int own = QR * tid;   // first of this thread's outputs within a pass
 
-    for (int q0 = 0; q0 < nlon_out; q0 += kThreads * QR) {
+    for (int q0 = 0; q0 < nlon_out; q0 += QR * NT) {
         float acc[QR];
 #pragma unroll
         for (int r = 0; r < QR; ++r) acc[r] = 0.0f;
         for (int wi = w0; wi < w1; ++wi) {
             const DevWindow wd = wins[wi];
-            const int wpad = (wd.width + DT - 1) / DT * DT;
-            const int len = S * (kThreads * QR - 1) + wpad;
+            const int wp = (wd.width + kDwTail - 1) / kDwTail * kDwTail;
             const T* row = xc + (size_t)wd.lat * nlon_in;
             const int start = (int)(((int64_t)q0 * S + wd.p_lo) % nlon_in);
-            __syncthreads();
+            __syncthreads();   // the previous window's reads are done
             const float* v = vals + (size_t)wd.val_off * KP;
-            for (int t = threadIdx.x; t < wpad; t += kThreads) {
+            for (int t = tid; t < wp; t += NT) {
                 float f = 0.0f;
                 if (t < wd.width) {
 #pragma unroll
@@ -327,27 +431,45 @@ __global__ __launch_bounds__(kThreads) void fused_depthwise_tiled(
                 }
                 folded[t] = f;
             }
-            for (int u = threadIdx.x; u < len; u += kThreads) {
-                int p = start + u;
-                p -= (p / nlon_in) * nlon_in;
-                ext[u] = load_f(row, p);
-            }
-            __syncthreads();
-            for (int t0 = 0; t0 < wpad; t0 += DT) {
-                float e[NE];
+            // samples start + u (mod nlon_in) for the u this window's chunks
+            // read (S (QR NT + wp / S) of them, a multiple of 4), four per
+            // lane and step: for stride 2 samples u, u + 2 go to ext_e and
+            // u + 1, u + 3 to ext_o as 8-byte stores, for stride 1 all four
+            // as one 16-byte store
+            const int nunits = S * dw_ext_words(NT, QR, wp, S) / 4;
+            for (int g = tid; g < nunits; g += NT) {
+                int p0 = start + 4 * g;
+                while (p0 >= nlon_in) p0 -= nlon_in;
+                float v[4];
+                if (p0 + 3 < nlon_in) {
+                    const T* src = row + p0;
 #pragma unroll
-                for (int m = 0; m < NE; ++m) e[m] = ext[tbase + t0 + m];
+                    for (int e = 0; e < 4; ++e) v[e] = load_f(src, e);
+                } else {
 #pragma unroll
-                for (int t = 0; t < DT; ++t) {
-                    const float f = folded[t0 + t];
-#pragma unroll
-                    for (int r = 0; r < QR; ++r) acc[r] = fmaf(f, e[r * S + t], acc[r]);
+                    for (int e = 0; e < 4; ++e) {
+                        int p = p0 + e;
+                        while (p >= nlon_in) p -= nlon_in;   // rows shorter than 4 wrap more than once
+                        v[e] = load_f(row, p);
+                    }
+                }
+                if constexpr (S == 2) {
+                    *reinterpret_cast<float2*>(ext_e + 2 * g) = make_float2(v[0], v[2]);
+                    *reinterpret_cast<float2*>(ext_o + 2 * g) = make_float2(v[1], v[3]);
+                } else {
+                    *reinterpret_cast<float4*>(ext_e + 4 * g) = make_float4(v[0], v[1], v[2], v[3]);
                 }
             }
+            __syncthreads();
+            int t0 = 0;
+            for (; t0 + kDwT <= wp; t0 += kDwT)
+                dw_chunk<kDwT, QR, S>(folded, ext_e, ext_o, own, t0, acc);
+            for (; t0 < wp; t0 += kDwTail)
+                dw_chunk<kDwTail, QR, S>(folded, ext_e, ext_o, own, t0, acc);
         }
 #pragma unroll
         for (int r = 0; r < QR; ++r) {
-            const int q = q0 + threadIdx.x * QR + r;
+            const int q = q0 + own + r;
             if (q < nlon_out) store_f(out, q, acc[r] + bv);
         }
     }
@@ -536,28 +658,57 @@ int fused_depthwise_launch(const disco_psi* psi, const void* x, const void* w, c
     const int QR = pick_qr(D.nlon_out);
     dim3 grid(D.nlat_out, Co, B);
     if (h.stride <= 2) {
-        // register-tiled form; LDS holds the padded folded taps and the samples
-        const int wpad = (d.max_width + kDwTile - 1) / kDwTile * kDwTile;
-        const size_t tl = (size_t)(wpad + h.stride * (kThreads * QR - 1) + wpad) * sizeof(float);
-        if (tl <= 64 * 1024) {
-#define DISCO_DWT(Q, SS)                                                                          \
-    hipLaunchKernelGGL((fused_depthwise_tiled<T, TY, KP, Q, SS>), grid, dim3(kThreads), tl, st,   \
-                       (const T*)x, (const T*)w, bias, (TY*)y, d.win_ptr, d.windows, d.vals, Ci,  \
-                       Co, groups, h.K, D.nlat_in, D.nlon_in, D.nlat_out, D.nlon_out, wpad)
-#define DISCO_DWT_S(Q)             \
-    if (h.stride == 1) {           \
-        DISCO_DWT(Q, 1);           \
-    } else {                       \
-        DISCO_DWT(Q, 2);           \
-    }
+        // register-tiled form; LDS holds the padded folded taps and the
+        // staged samples (by parity for stride 2).  Outputs per thread: the
+        // QR of 4, 6, 8 whose passes leave the fewest idle outputs (the
+        // smaller on ties: at 720 outputs, 4 per thread with three waves
+        // timed 4.37 ms against 4.51 ms for 6 per thread with two, whose runs
+        // need 8-byte loads).
+        int qr = 4, nt = 64;
+        double best = -1.0;
+        for (int q : {4, 6, 8}) {
+            const int need = (D.nlon_out + q - 1) / q;
+            const int t = std::min(kThreads, (need + 63) / 64 * 64);
+            const int passes = (D.nlon_out + q * t - 1) / (q * t);
+            const double use = (double)D.nlon_out / ((double)passes * q * t);
+            if (use > best) {
+                best = use;
+                qr = q;
+                nt = t;
+            }
+        }
+        const int wpad = (d.max_width + kDwTail - 1) / kDwTail * kDwTail;
+        const int S = h.stride;
+        const size_t words = (size_t)wpad + (S == 2 ? (size_t)dw_odd_offset(nt, qr, wpad) +
+                                                          dw_ext_words(nt, qr, wpad, 2)
+                                                    : (size_t)dw_ext_words(nt, qr, wpad, 1));
+        const size_t tl = words * sizeof(float);
+        const int64_t ntasks = (int64_t)B * Co * D.nlat_out;
+        if (tl <= 64 * 1024 && ntasks < (int64_t)1 << 31) {
+            // workgroups per band: the largest band's tasks (see the kernel)
+            const int64_t nplanes = (int64_t)B * Co;
+            const int64_t per = nplanes >= kDwBands
+                                    ? (nplanes + kDwBands - 1) / kDwBands * D.nlat_out
+                                    : (ntasks + kDwBands - 1) / kDwBands;
+            const dim3 tgrid((unsigned)(per * kDwBands));
             KernelTimer timer("fused_depthwise", st);
-            switch (QR) {
-                case 1: DISCO_DWT_S(1) break;
-                case 2: DISCO_DWT_S(2) break;
-                case 3: DISCO_DWT_S(3) break;
-                case 4: DISCO_DWT_S(4) break;
-                case 6: DISCO_DWT_S(6) break;
-                default: DISCO_DWT_S(8) break;
+#define DISCO_DWT(Q, SS)                                                                          \
+    hipLaunchKernelGGL((fused_depthwise_tiled<T, TY, KP, Q, SS>), tgrid, dim3(nt), tl, st,        \
+                       (const T*)x, (const T*)w, bias, (TY*)y, d.win_ptr, d.windows, d.vals, Ci,  \
+                       Co, groups, h.K, D.nlat_in, D.nlon_in, D.nlat_out, D.nlon_out, wpad,       \
+                       (int)ntasks)
+#define DISCO_DWT_S(Q)   \
+    if (S == 1) {        \
+        DISCO_DWT(Q, 1); \
+    } else {             \
+        DISCO_DWT(Q, 2); \
+    }
+            if (qr == 4) {
+                DISCO_DWT_S(4)
+            } else if (qr == 6) {
+                DISCO_DWT_S(6)
+            } else {
+                DISCO_DWT_S(8)
             }
 #undef DISCO_DWT_S
 #undef DISCO_DWT

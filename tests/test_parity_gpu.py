@@ -98,10 +98,15 @@ SMALL = [
     W("k1_f32", 1, 2, 2, 1, 9, 16, 9, 16, (1,), 0.7, "f32"),
     W("nlat2_f32", 1, 2, 3, 1, 2, 8, 2, 4, (2,), 1.0, "f32"),
     W("wide_cap_f32", 1, 2, 2, 1, 17, 32, 17, 32, (3, 3), 2.5, "f32"),
-    # depthwise rows longer than one 256-thread pass: three outputs per thread
-    # at stride 1, two at stride 2 (the register-tiled depthwise kernel)
+    # the register-tiled depthwise kernel (four outputs per thread, 64 to 256
+    # threads): one pass of 192 threads at stride 1, one of 128 at stride 2,
+    # two passes of 256 at strides 1 and 2 (rows longer than 1024 outputs,
+    # with polar windows spanning the whole ring), a multiplier of 2 and bf16
     W("depthwise_long_s1_f32", 1, 4, 4, 4, 13, 600, 13, 600, (3, 3), 0.5, "f32"),
     W("depthwise_long_s2_f32", 2, 3, 3, 3, 17, 1024, 9, 512, (4,), 0.6, "f32"),
+    W("depthwise_2pass_s1_f32", 1, 2, 2, 2, 9, 1440, 9, 1440, (3,), 0.6, "f32"),
+    W("depthwise_2pass_s2_f32", 1, 2, 4, 2, 9, 2400, 5, 1200, (2, 2), 0.9, "f32"),
+    W("depthwise_s2_bf16", 1, 5, 5, 5, 25, 96, 13, 48, (5, 4), 0.5, "bf16"),
     # grouped bf16 layers on the matrix-core einsum: 64 output channels per
     # group (the streamed kernel) and 48 per group (the general tiled kernel)
     W("grouped_stream_bf16", 1, 64, 128, 2, 33, 64, 33, 64, (3, 3), 4 * math.pi / 32, "bf16"),

@@ -543,11 +543,13 @@ __global__ void spec_prep_w(const bf16_t* __restrict__ w, bf16_t* __restrict__ w
 }
 
 constexpr int kMt = 32;              // frequencies per work item (64 GEMM columns)
-// B tile row of spec_mfma: pair (k, ci) at 40 k + ci (each 32-pair block padded by
-// 8), 312 bf16 = 624 bytes per row (an odd multiple of 16 bytes).  The window
-// sum's 8-byte writes (lanes differing in k) then fall into distinct banks, as
-// do the GEMM's 16-byte reads (lanes differing in the row).
-constexpr int kBts = 312;
+// B tile row r of spec_mfma: pair (k, ci) at 40 (k ^ ((r >> 1) & 7)) + ci (32-pair
+// blocks padded by 8, their order permuted by the row pair), 320 bf16 = 640
+// bytes per row (160 words: 4 times an odd number).  On the 64-bank LDS the
+// GEMM's 16-byte reads (16 lanes of consecutive rows per phase) then cover
+// all banks, and so do the window sum's 8-byte writes (32 lanes per phase:
+// 8 basis blocks of two rows, in 2 x 4 lanes).
+constexpr int kBts = 320;
 constexpr int kBkb = 40;             // bf16 per k block of a tile row
 constexpr int kSpecThreads = 256;
 constexpr int kSpecMaxWin = 16;      // windows per output row: one or two 16-deep MFMA steps
@@ -562,10 +564,11 @@ constexpr int kXcds = 8;             // accelerator dies of the chip (L2 domains
 //    of x_hat as stored (lane = channel, four windows per lane half), read
 //    from the chunk's spectra block in LDS, which is filled with coalesced
 //    loads (eight lanes per 128-byte row); its 16-byte pieces are
-//    XOR-swizzled by channel so that the lanes' reads hit distinct banks.
+//    XOR-swizzled by channel pair, so that the 16 lanes of a read phase (two
+//    channels per 256 bytes of banks) hit distinct banks.
 //    Each wave owns 8 of the 32 frequencies and builds their B operands at
 //    the start of an item from the Psi_hat slice in LDS.  Results go to the
-//    bf16 LDS tile bt[(m, re/im)][40 k + ci].
+//    bf16 LDS tile bt[(m, re/im)][40 (k ^ (m & 7)) + ci].
 //  * Channel/basis GEMM: y_hat[co, (m, re/im)] += wp[co, (k, ci)] bt[(k, ci),
 //    (m, re/im)], 4 waves, wave tile 32 x 64 (CO = 128) or 32 x 32 (CO = 64),
 //    2 KT k-steps per chunk (the pairs of basis columns past KT are zero and
@@ -599,7 +602,6 @@ __global__ __launch_bounds__(kSpecThreads) __attribute__((amdgpu_waves_per_eu(NW
     __shared__ __attribute__((aligned(16))) bf16_t bt[64 * kBts];
     __shared__ __attribute__((aligned(16))) u32x4 xs[NW * 32 * 8];   // [r][ci][piece]
     __shared__ __attribute__((aligned(16))) uint32_t ps[NW * KT * kMt];
-    __shared__ __attribute__((aligned(16))) bf16_t dump[32];   // 4 writes of 8 bytes, 8 apart
     constexpr int WGM = CO / 32;          // waves along the output channels
     constexpr int WGN = 4 / WGM;          // waves along the columns
     constexpr int NTW = 2 / WGN;          // 32-column MFMA tiles per wave
@@ -658,7 +660,7 @@ __global__ __launch_bounds__(kSpecThreads) __attribute__((amdgpu_waves_per_eu(NW
     // The request cursor walks the positions in order (staying at the last).
     // A position's spectra block goes straight to LDS by DMA: wave w fills
     // windows WPW w .. WPW w + WPW - 1.  LDS slot ((r * 32 + ci) * 8 + pos)
-    // holds the 16-byte piece pos ^ (ci & 7) (4 frequencies) of channel ci's
+    // holds the 16-byte piece pos ^ ((ci >> 1) & 7) (4 frequencies) of channel ci's
     // row in window r.  Window slots past the row's windows repeat window 0
     // (valid, finite; their B rows are zero).
     int lat_w[WPW];                 // input rows of this wave's windows of the requested item
@@ -695,7 +697,7 @@ __global__ __launch_bounds__(kSpecThreads) __attribute__((amdgpu_waves_per_eu(NW
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const int ci = 8 * q + (lane >> 3);
-        dma_off[q] = (size_t)ci * plane + 4 * ((lane & 7) ^ (ci & 7));
+        dma_off[q] = (size_t)ci * plane + 4 * ((lane & 7) ^ ((ci >> 1) & 7));
     }
     auto dma_x = [&]() {
         const size_t cb = (size_t)(req_b * Ci + req_chunk * 32) * plane + rq.mt * kMt;
@@ -783,7 +785,7 @@ __global__ __launch_bounds__(kSpecThreads) __attribute__((amdgpu_waves_per_eu(NW
         // A-operand reads: lane (channel l32, windows 4 lg + u, clamped to
         // window 0 past the row's windows), pieces 2 wave + h (swizzled by
         // the channel; 2 wave is even, so the h = 1 piece is the other's ^ 1)
-        const int xsw = (2 * wave) ^ (l32 & 7);
+        const int xsw = (2 * wave) ^ ((l32 >> 1) & 7);
 
         floatx16 acc[NTW];
 #pragma unroll
@@ -835,17 +837,19 @@ __global__ __launch_bounds__(kSpecThreads) __attribute__((amdgpu_waves_per_eu(NW
             };
             auto window_write = [&](const floatx16& d, int f) {
                 // column (k, c) -> tile row 2 (f0 + f) + c, pairs (k, ci),
-                // ci = 8 q + 4 lg + (0..3).  Columns KT <= k < 8 are written
-                // but never read; lanes of columns k >= 8 (no tile block)
-                // write the shared dump instead of branching around it.
-                bf16_t* dst =
-                    l32 < 16 ? bt + (2 * (f0 + f) + (l32 & 1)) * kBts + (l32 >> 1) * kBkb + 4 * lg
-                             : dump;
+                // ci = 8 q + 4 lg + (0..3), in block k ^ f of the row ((row >>
+                // 1) & 7 = f: f0 is a multiple of 8).  Columns KT <= k < 8
+                // are written but never read; lanes of columns k >= 8 have no
+                // tile block and write nothing.
+                if (l32 < 16) {
+                    bf16_t* dst = bt + (2 * (f0 + f) + (l32 & 1)) * kBts +
+                                  ((l32 >> 1) ^ f) * kBkb + 4 * lg;
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const uint2 pk = make_uint2(pack_bf16x2(d[4 * q], d[4 * q + 1]),
-                                                pack_bf16x2(d[4 * q + 2], d[4 * q + 3]));
-                    *reinterpret_cast<uint2*>(dst + 8 * q) = pk;
+                    for (int q = 0; q < 4; ++q) {
+                        const uint2 pk = make_uint2(pack_bf16x2(d[4 * q], d[4 * q + 1]),
+                                                    pack_bf16x2(d[4 * q + 2], d[4 * q + 3]));
+                        *reinterpret_cast<uint2*>(dst + 8 * q) = pk;
+                    }
                 }
             };
             floatx16 dcur = window_mfma(0);
@@ -863,6 +867,9 @@ __global__ __launch_bounds__(kSpecThreads) __attribute__((amdgpu_waves_per_eu(NW
             __builtin_amdgcn_s_setprio(2);
             const int cn = cc + 1 < nchunks ? cc + 1 : 0;   // weights of the next chunk
             const bf16_t* bb = bt + (wn * (64 / WGN) + l32) * kBts + 8 * lg;
+            // block permutation of this lane's rows (wn * (64 / WGN) + 32 t +
+            // l32: the same for every t)
+            const int bsw = (l32 >> 1) & 7;
             const u32x4* wnext = wf + (size_t)cn * 16 * WGM * 64;
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) {
@@ -871,7 +878,8 @@ __global__ __launch_bounds__(kSpecThreads) __attribute__((amdgpu_waves_per_eu(NW
                 for (int t = 0; t < NTW; ++t) {
                     const bf16x8_t bf =
                         *reinterpret_cast<const bf16x8_t*>(bb + t * 32 * kBts +
-                                                           (ks >> 1) * kBkb + 16 * (ks & 1));
+                                                           ((ks >> 1) ^ bsw) * kBkb +
+                                                           16 * (ks & 1));
                     // transposed product: lane column = output channel, rows =
                     // the tile's columns (frequency, re/im)
                     acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf, af, acc[t], 0, 0, 0);

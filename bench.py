@@ -58,27 +58,45 @@ HBM_PEAK_GBS = 8000.0
 
 METRIC = "DISCO fwd output-points\u00b7Cout/s at 721x1440 C=128 K=7; % HBM/MFMA roofline"
 
-# rocprofv3 HBM counters at the headline workload, per launch of a kernel or
-# per call (summed over the call's launches): FETCH_SIZE x 2.000 + WRITE_SIZE
-# x 1.000 (factors from a 512 MiB device copy, see profiles/).  Keyed by the SHA-1 of the kernel source
+# rocprofv3 HBM counters per launch of a kernel or per call (summed over the
+# call's launches): FETCH_SIZE x 2.000 + WRITE_SIZE x 1.000 (factors from a
+# 512 MiB device copy, see profiles/).  Keyed by the SHA-1 of the kernel source
 # the counters were taken with: when the source has changed the figure is
 # stale and `traffic` is reported as null.
 MEASURED_TRAFFIC_BYTES = {
-    ("c4", "fused_spectral"): {"bytes": 2041565112, "source": "kernels_spectral.hip",
-                               "sha1": "0b83d543098c288513e3306217d414739f9e5c56",
-                               "profile": "profiles/fused_spectral_c4_hbm_counters.md"},
-    ("c4", "spec_mfma"): {"bytes": 699515569, "source": "kernels_spectral.hip",
-                          "sha1": "0b83d543098c288513e3306217d414739f9e5c56",
-                          "profile": "profiles/fused_spectral_c4_hbm_counters.md"},
-    ("c4", "fused"): {"bytes": 1377027391, "source": "kernels_fused_mfma.hip",
-                      "sha1": "d3a7660ad665af7d9a8ccdb85b7aff879512fa4e",
-                      "profile": "profiles/fused_mfma_c4_hbm_counters.md"},
-    ("c4", "contract"): {"bytes": 2870807783, "source": "kernels_fused_mfma.hip",
-                         "sha1": "d3a7660ad665af7d9a8ccdb85b7aff879512fa4e",
-                         "profile": "profiles/contract_mfma_c4_hbm_counters.md"},
-    ("c4", "einsum"): {"bytes": 2437461650, "source": "kernels_einsum_mfma.hip",
-                       "sha1": "4683e91365bc9e8ddd3298a6ec541ce2c779c88c",
-                       "profile": "profiles/einsum_ring_c4_hbm_counters.md"},
+    ("c4", "fused_spectral"): {"bytes": 2028649898, "source": "kernels_spectral.hip",
+                  "sha1": "edf977f4cb490582353d16647645b4af8c5d49d8",
+                  "profile": "profiles/c4_counters.md"},
+    ("c4", "spec_mfma"): {"bytes": 686585818, "source": "kernels_spectral.hip",
+                  "sha1": "edf977f4cb490582353d16647645b4af8c5d49d8",
+                  "profile": "profiles/c4_counters.md"},
+    ("c4", "fused"): {"bytes": 1379033638, "source": "kernels_fused_mfma.hip",
+                  "sha1": "9d4ba7f7e50c3907e1c4d661f1e41df3000f8bde",
+                  "profile": "profiles/c4_counters.md"},
+    ("c4", "contract"): {"bytes": 2874297037, "source": "kernels_fused_mfma.hip",
+                  "sha1": "9d4ba7f7e50c3907e1c4d661f1e41df3000f8bde",
+                  "profile": "profiles/c4_counters.md"},
+    ("c4", "einsum"): {"bytes": 2436400128, "source": "kernels_einsum_mfma.hip",
+                  "sha1": "4683e91365bc9e8ddd3298a6ec541ce2c779c88c",
+                  "profile": "profiles/c4_counters.md"},
+    ("c3", "fused_spectral"): {"bytes": 380877709, "source": "kernels_spectral.hip",
+                  "sha1": "edf977f4cb490582353d16647645b4af8c5d49d8",
+                  "profile": "profiles/c3_counters.md"},
+    ("c3", "spec_mfma"): {"bytes": 172848571, "source": "kernels_spectral.hip",
+                  "sha1": "edf977f4cb490582353d16647645b4af8c5d49d8",
+                  "profile": "profiles/c3_counters.md"},
+    ("c5", "fused"): {"bytes": 1781389596, "source": "kernels_generic.hip",
+                  "sha1": "af55f7727176d3d320835ae69aec87e579ec0390",
+                  "profile": "profiles/c5_counters.md"},
+    ("c5", "fused_depthwise"): {"bytes": 1781389596, "source": "kernels_generic.hip",
+                  "sha1": "af55f7727176d3d320835ae69aec87e579ec0390",
+                  "profile": "profiles/c5_counters.md"},
+    ("c2", "fused_spectral"): {"bytes": 274448059, "source": "kernels_spectral.hip",
+                  "sha1": "edf977f4cb490582353d16647645b4af8c5d49d8",
+                  "profile": "profiles/c2_counters.md"},
+    ("c2", "spec32_conv"): {"bytes": 200190370, "source": "kernels_spectral.hip",
+                  "sha1": "edf977f4cb490582353d16647645b4af8c5d49d8",
+                  "profile": "profiles/c2_counters.md"},
 }
 CSRC = os.path.join(ROOT, "spherical_disco_convolution_amd", "csrc")
 

@@ -137,16 +137,23 @@ int disco_einsum(const void* xk, int xk_dtype, const void* w, int w_dtype,
  * result as disco_contract followed by disco_einsum, without storing xk in
  * device memory.  x_dtype and w_dtype must be equal.
  *
- * Stride-1 layers (nlon_in == nlon_out, even, N/2 a product of 2, 3 and 5,
- * N <= 1800) with bf16 x and w, groups == 1, Ci a multiple of 32, Co 64 or
- * 128, K <= 8 and at most 8 input rows per output row run in the
- * longitude-spectral form: the forward equation's longitude shift makes each
- * window a circular correlation, so it is evaluated with real DFTs along
- * longitude (three kernels, a stream-ordered workspace of
- * B*Ci*nlat_in*MP*4 + B*Co*nlat_out*MP*4 bytes with MP = N/2 + 1 rounded up
- * to 32).  The environment variable DISCO_FUSED_PATH=toeplitz selects the
- * direct matrix-core kernel for them instead.  Other layers run the direct
- * kernels. */
+ * Some layers run in the longitude-spectral form: the forward equation's
+ * longitude shift makes each window a circular correlation, so it is
+ * evaluated with real DFTs along longitude (a forward transform, the window
+ * and channel/basis sums per frequency, an inverse transform), in a
+ * stream-ordered workspace of B*Ci*nlat_in*MP*E + B*Co*nlat_out*MP*E bytes
+ * with MP = N_in/2 + 1 rounded up to 32 and E = 4 (bf16 spectra) or 8
+ * (float32 spectra).  They are, with N = nlon_in even, N/2 a product of 2, 3
+ * and 5 and N <= 1800, groups == 1 and K <= 8:
+ *  - bf16 x and w, Ci a multiple of 32, Co 64 or 128, at most 16 input rows
+ *    per output row, and stride 1, or stride 2 with N = 720 or 1440 (the
+ *    stride-2 output is the stride-1 correlation at every second longitude,
+ *    its spectrum folded onto the output grid's frequencies);
+ *  - float32 x and w, stride 1, Co <= 128 (both sums on the vector ALUs).
+ * The environment variable DISCO_FUSED_PATH=toeplitz selects the direct
+ * kernels for them instead.  Other layers run the direct kernels: the
+ * matrix-core kernel for bf16 layers it accepts, the vector kernels
+ * otherwise. */
 int disco_fused_fwd(const disco_psi* psi, const void* x, int x_dtype,
                     const void* w, int w_dtype, const float* bias,
                     void* y, int y_dtype, int32_t B, int32_t Ci, int32_t Co,

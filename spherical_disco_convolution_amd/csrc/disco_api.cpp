@@ -218,8 +218,10 @@ int disco_psi_to_device(disco_psi* psi) {
             wins_t[fill[wins[n].lat]++] = t;
         }
     }
+    d.min_windows = nlat_out > 0 ? wptr[1] - wptr[0] : 0;
     for (int j = 0; j < nlat_out; ++j) {
         d.max_windows = std::max(d.max_windows, wptr[j + 1] - wptr[j]);
+        d.min_windows = std::min(d.min_windows, wptr[j + 1] - wptr[j]);
         d.max_row_points = std::max(
             d.max_row_points, (int32_t)(h.row_ptr[j + 1] - h.row_ptr[j]));
     }

@@ -83,6 +83,7 @@ struct DevPsi {
     int32_t max_row_points = 0;   // max support points of one output row
     int32_t max_width = 0;        // widest window
     int32_t max_windows = 0;      // most windows of one output row
+    int32_t min_windows = 0;      // fewest windows of one output row
     int32_t* win_ptr = nullptr;   // [nlat_out + 1]
     DevWindow* windows = nullptr; // [nwin]
     float* vals = nullptr;        // [nnz, KP] float32, window order, zero padded

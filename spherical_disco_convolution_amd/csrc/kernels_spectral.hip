@@ -1073,7 +1073,10 @@ int fused_spectral_eligible(const disco_psi* psi, int x_dtype, int Ci, int Co, i
     if (d.spec_mp <= 0 || x_dtype != DISCO_BF16 || groups != 1 || Ci % 32 != 0 ||
         (Co != 128 && Co != 64) || h.K > 8)
         return 0;
-    if (d.max_windows > kSpecMaxWin) return 0;
+    // the matrix-core kernel reads each row's first window, so every output
+    // row needs one (a cap narrower than the input row spacing can miss
+    // every input row)
+    if (d.max_windows > kSpecMaxWin || d.min_windows < 1) return 0;
     // stride 2: register transforms on both sides (the tables exist only then)
     if (h.stride == 2 && h.desc.nlon_in != 1440 && h.desc.nlon_in != 720) return 0;
     // DISCO_FUSED_PATH=toeplitz selects the direct matrix-core kernel instead

@@ -49,6 +49,11 @@ CASES = [
      "bf16", True),
     ("legendre-gauss", "equiangular", 1, 4, 6, 48, 96, 25, 48, (3, 3), 0.5, "f32", False),
     ("lobatto", "legendre-gauss", 2, 3, 5, 17, 32, 16, 32, (3,), 0.6, "f32", True),
+    # a cap narrower than the input spacing: output rows 0 and 16 (the poles)
+    # have no input row in reach, so no windows and an all-zero output row;
+    # bf16 takes the direct kernel, float32 the vector spectral one
+    ("legendre-gauss", "equiangular", 1, 32, 64, 16, 32, 17, 32, (3, 3), 0.12, "bf16", False),
+    ("legendre-gauss", "equiangular", 1, 4, 8, 16, 32, 17, 32, (3, 3), 0.12, "f32", True),
 ]
 
 
@@ -69,7 +74,7 @@ def _dev(a, dt):
     return t.to(torch.bfloat16) if dt == "bf16" else t
 
 
-@pytest.mark.parametrize("case", CASES, ids=[f"{c[0]}-{c[1]}-{c[11]}" for c in CASES])
+@pytest.mark.parametrize("case", CASES, ids=[f"{c[0]}-{c[1]}-{c[11]}-{c[10]}" for c in CASES])
 def test_other_grids_forward(sdc, case, monkeypatch):
     gin, gout, B, Ci, Co, nli, nfi, nlo, nfo, ks, cut, dt, spectral = case
     _say("grid", gin, gout, dt)
@@ -85,6 +90,9 @@ def test_other_grids_forward(sdc, case, monkeypatch):
     err = rel_l2(y, ref)
     _say(f"  fused ({'spectral' if spectral else 'direct'}) rel-L2 {err:.3e}")
     assert err <= TOL[dt]
+    # output rows with no support are exactly zero (no bias here)
+    empty = ~np.any(ref != 0.0, axis=(0, 1, 3))
+    assert np.all(y[:, :, empty, :] == 0.0)
     if spectral or dt == "bf16":
         # the direct kernels on the same layer
         monkeypatch.setenv("DISCO_FUSED_PATH", "toeplitz")

@@ -871,18 +871,35 @@ __global__ __launch_bounds__(kSpecThreads) __attribute__((amdgpu_waves_per_eu(NW
             // l32: the same for every t)
             const int bsw = (l32 >> 1) & 7;
             const u32x4* wnext = wf + (size_t)cn * 16 * WGM * 64;
+            auto bfrag = [&](int ks, int t) {
+                return *reinterpret_cast<const bf16x8_t*>(bb + t * 32 * kBts +
+                                                          ((ks >> 1) ^ bsw) * kBkb +
+                                                          16 * (ks & 1));
+            };
+            // B fragments read two k-steps ahead of their MFMAs, so that the
+            // LDS latency hides behind the two steps in between
+            bf16x8_t bq0[NTW], bq1[NTW];
+#pragma unroll
+            for (int t = 0; t < NTW; ++t) bq0[t] = bfrag(0, t);
+#pragma unroll
+            for (int t = 0; t < NTW; ++t) bq1[t] = bfrag(1, t);
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) {
                 const bf16x8_t af = __builtin_bit_cast(bf16x8_t, wq[ks]);
+                bf16x8_t bn[NTW];
+                if (ks + 2 < NKS) {
+#pragma unroll
+                    for (int t = 0; t < NTW; ++t) bn[t] = bfrag(ks + 2, t);
+                }
+                // transposed product: lane column = output channel, rows = the
+                // tile's columns (frequency, re/im)
+#pragma unroll
+                for (int t = 0; t < NTW; ++t)
+                    acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bq0[t], af, acc[t], 0, 0, 0);
 #pragma unroll
                 for (int t = 0; t < NTW; ++t) {
-                    const bf16x8_t bf =
-                        *reinterpret_cast<const bf16x8_t*>(bb + t * 32 * kBts +
-                                                           ((ks >> 1) ^ bsw) * kBkb +
-                                                           16 * (ks & 1));
-                    // transposed product: lane column = output channel, rows =
-                    // the tile's columns (frequency, re/im)
-                    acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf, af, acc[t], 0, 0, 0);
+                    bq0[t] = bq1[t];
+                    if (ks + 2 < NKS) bq1[t] = bn[t];
                 }
                 wq[ks] = wnext[(size_t)ks * WGM * 64];
                 // reloads stay in k-step order right after their use: then the

@@ -39,6 +39,11 @@ the support it evaluates).  It runs before the GPU is touched.
 matrix-core rate and LDS read rate from hand-written micro-benchmarks
 (libdisco_probe.so), beside the published peaks the roofline divides by.
 `cold_ms` is the fused call after a 1 GiB write has flushed the caches.
+
+Warm-up: after idling, the GPU runs the first 30-40 back-to-back calls at
+lower clocks (at 721x1440, 128 channels: 0.78-0.95 ms per call, settling to
+0.68-0.70 ms); the default 50 untimed calls put the timed region in the
+sustained state a serving or training loop runs in.
 """
 from __future__ import annotations
 
@@ -127,8 +132,10 @@ COPY_CALIBRATION_BYTES = 512 << 20
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    # the GPU reaches its sustained clocks after about 30 back-to-back calls
+    # (~25 ms of load); 50 untimed calls put the timed ones past that ramp
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default=None, help="c1..c5 (default: the headline case c4)")
     ap.add_argument("--grid", default="equiangular",
                     choices=["equiangular", "legendre-gauss", "lobatto", "equiangular-trapezoidal"],

@@ -107,8 +107,9 @@ int disco_psi_export(const disco_psi* psi, int64_t* row_ptr, int32_t* in_lat,
  * EINVAL if the handle already lives on another device. */
 int disco_psi_to_device(disco_psi* psi);
 
-/* Free host and device memory of the handle.  NULL is ignored.  The caller
- * must make sure no enqueued work still uses it. */
+/* Free host and device memory of the handle, including its workspace (it
+ * waits for the last call that used the workspace).  NULL is ignored.  The
+ * caller must make sure no enqueued work still uses the handle's tables. */
 void disco_psi_free(disco_psi* psi);
 
 /* Sparse contraction (the inner sum of the forward equation):
@@ -141,9 +142,18 @@ int disco_einsum(const void* xk, int xk_dtype, const void* w, int w_dtype,
  * longitude shift makes each window a circular correlation, so it is
  * evaluated with real DFTs along longitude (a forward transform, the window
  * and channel/basis sums per frequency, an inverse transform), in a
- * stream-ordered workspace of B*Ci*nlat_in*MP*E + B*Co*nlat_out*MP*E bytes
- * with MP = N_in/2 + 1 rounded up to 32 and E = 4 (bf16 spectra) or 8
- * (float32 spectra).  They are, with N = nlon_in even, N/2 a product of 2, 3
+ * workspace of B*Ci*nlat_in*MP*E + B*Co*nlat_out*MP*E bytes with MP =
+ * N_in/2 + 1 rounded up to 32 and E = 4 (bf16 spectra) or 8 (float32
+ * spectra).
+ *
+ * Workspace (this call and disco_fused_bwd): the handle keeps one device
+ * buffer, allocated with hipMalloc on first need, grown to the largest
+ * request and freed by disco_psi_free.  A call that uses it on a stream
+ * other than the previous user's first waits for that user's completion
+ * event, so calls through one handle are ordered across streams (use one
+ * handle per stream for concurrency).  While the stream is being captured
+ * into a HIP graph the call takes stream-ordered memory instead
+ * (hipMallocAsync / hipFreeAsync nodes that the graph owns).  They are, with N = nlon_in even, N/2 a product of 2, 3
  * and 5 and N <= 1800, groups == 1 and K <= 8:
  *  - bf16 x and w, Ci a multiple of 32, Co 64 or 128, at most 16 input rows
  *    per output row, and stride 1, or stride 2 with N = 720 or 1440 (the
@@ -192,8 +202,9 @@ int disco_fused_is_spectral(const disco_psi* psi, int x_dtype, int32_t Ci, int32
  * the gradients below are the adjoints of its two linear maps.  gy is the
  * gradient of the loss with respect to y, [B, Co, nlat_out, nlon_out].  All
  * sums are accumulated in float32; sums over points run in a fixed order, so
- * results are reproducible.  Work is enqueued on `stream`; the calls that
- * need scratch memory take it stream-ordered on that stream. */
+ * results are reproducible.  Work is enqueued on `stream`; disco_fused_bwd
+ * takes its scratch from the handle's workspace (described at
+ * disco_fused_fwd), disco_einsum_grad_w stream-ordered on that stream. */
 
 /* Adjoint of disco_contract:
  *   gx[b,c,i,n] = sum over (j, q, p) with (q*s + p) mod nlon_in = n of

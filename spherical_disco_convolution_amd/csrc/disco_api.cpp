@@ -87,6 +87,88 @@ void free_device(disco::DevPsi& d) {
     d = disco::DevPsi();
 }
 
+}  // namespace
+
+WorkspaceLease::WorkspaceLease(const disco_psi* psi, size_t bytes, hipStream_t st) : st_(st) {
+    if (psi == nullptr) return;   // no lease wanted
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(st, &cs) != hipSuccess) {
+        (void)hipGetLastError();
+        return;   // unknown: the caller allocates stream-ordered memory
+    }
+    if (cs != hipStreamCaptureStatusNone) return;
+    Workspace& ws = psi->ws;
+    ws.mu.lock();
+    ws_ = &ws;
+    if (bytes == 0) bytes = 256;
+    if (ws.done == nullptr && hipEventCreateWithFlags(&ws.done, hipEventDisableTiming) != hipSuccess) {
+        (void)hipGetLastError();
+        ws.done = nullptr;
+        rc_ = set_error(DISCO_EHIP, "hipEventCreateWithFlags for the workspace failed");
+        return;
+    }
+    if (ws.cap < bytes) {
+        if (ws.ptr != nullptr) {
+            // the previous user may still run: wait, then free
+            if (ws.used) (void)hipEventSynchronize(ws.done);
+            (void)hipFree(ws.ptr);
+            ws.ptr = nullptr;
+            ws.cap = 0;
+            ws.used = false;
+        }
+        hipError_t e = hipMalloc(&ws.ptr, bytes);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            ws.ptr = nullptr;
+            rc_ = set_error(e == hipErrorOutOfMemory ? DISCO_ENOMEM : DISCO_EHIP,
+                            "hipMalloc(%zu) for the workspace failed: %s", bytes,
+                            hipGetErrorString(e));
+            return;
+        }
+        ws.cap = bytes;
+    }
+    if (ws.used && ws.last != st) {
+        if (hipStreamWaitEvent(st, ws.done, 0) != hipSuccess) {
+            (void)hipGetLastError();
+            rc_ = set_error(DISCO_EHIP, "hipStreamWaitEvent on the workspace failed");
+            return;
+        }
+    }
+    ptr_ = ws.ptr;
+}
+
+WorkspaceLease::~WorkspaceLease() {
+    if (ws_ == nullptr) return;
+    if (ptr_ != nullptr) {
+        if (hipEventRecord(ws_->done, st_) == hipSuccess) {
+            ws_->last = st_;
+            ws_->used = true;
+        } else {
+            // no event to order the next user by: make sure this use is over
+            (void)hipGetLastError();
+            (void)hipStreamSynchronize(st_);
+            ws_->used = false;
+        }
+    }
+    ws_->mu.unlock();
+}
+
+void release_workspace(Workspace& ws) {
+    std::lock_guard<std::mutex> lock(ws.mu);
+    if (ws.ptr != nullptr) {
+        if (ws.used && ws.done != nullptr) (void)hipEventSynchronize(ws.done);
+        (void)hipFree(ws.ptr);
+    }
+    if (ws.done != nullptr) (void)hipEventDestroy(ws.done);
+    ws.ptr = nullptr;
+    ws.cap = 0;
+    ws.done = nullptr;
+    ws.last = nullptr;
+    ws.used = false;
+}
+
+namespace {
+
 int dev_alloc(disco::DevPsi& d, void** ptr, size_t bytes) {
     if (bytes == 0) bytes = 16;
     hipError_t e = hipMalloc(ptr, bytes);
@@ -288,9 +370,11 @@ void disco_psi_free(disco_psi* psi) {
         int cur = -1;
         if (hipGetDevice(&cur) == hipSuccess && cur != psi->dev.device) {
             (void)hipSetDevice(psi->dev.device);
+            release_workspace(psi->ws);
             free_device(psi->dev);
             (void)hipSetDevice(cur);
         } else {
+            release_workspace(psi->ws);
             free_device(psi->dev);
         }
     }

@@ -6,6 +6,7 @@
 
 #include <cstdint>
 #include <functional>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -106,11 +107,27 @@ struct DevPsi {
     std::vector<void*> allocations;
 };
 
+// Device workspace that a Psi handle keeps between calls (the spectral
+// algorithm's spectra, the matrix-core kernel's weight fragments).  It grows
+// to the largest request and lives until the handle is freed.  `done` is
+// recorded on the launch stream after every call that used it; a call on
+// another stream first waits for it, so calls through one handle on several
+// streams are ordered, not racing.
+struct Workspace {
+    std::mutex mu;
+    void* ptr = nullptr;
+    size_t cap = 0;
+    hipEvent_t done = nullptr;
+    hipStream_t last = nullptr;
+    bool used = false;
+};
+
 }  // namespace disco
 
 struct disco_psi {
     disco::HostPsi host;
     disco::DevPsi dev;
+    mutable disco::Workspace ws;
 };
 
 namespace disco {
@@ -150,6 +167,30 @@ int launch_fused_bwd(const disco_psi* psi, const void* x, int x_dtype, const voi
 // records a HIP event on the launch stream at construction and at
 // destruction, for disco_kernel_timing_read.  The name must be a string
 // literal.
+// Scope around the launches of one call that use the handle's workspace:
+// holds its lock, grows it to `bytes` (hipMalloc), orders the launch stream
+// after the previous user's stream, and at destruction records `done` on the
+// stream.  ptr() is null while the stream is being captured into a graph
+// (the caller then allocates stream-ordered memory that the graph owns) and
+// on failure (error() says which), and for a null handle.
+class WorkspaceLease {
+  public:
+    WorkspaceLease(const disco_psi* psi, size_t bytes, hipStream_t st);
+    ~WorkspaceLease();
+    WorkspaceLease(const WorkspaceLease&) = delete;
+    WorkspaceLease& operator=(const WorkspaceLease&) = delete;
+    void* ptr() const { return ptr_; }
+    int error() const { return rc_; }
+
+  private:
+    Workspace* ws_ = nullptr;
+    hipStream_t st_ = nullptr;
+    void* ptr_ = nullptr;
+    int rc_ = DISCO_OK;
+};
+// Frees a handle's workspace (waits for its last user first).
+void release_workspace(Workspace& ws);
+
 class KernelTimer {
   public:
     KernelTimer(const char* name, hipStream_t st);

@@ -535,12 +535,19 @@ int launch_fused_bwd(const disco_psi* psi, const void* x, int x_dtype, const voi
         if ((rc = check("grad_bias")) != DISCO_OK) return rc;
     }
     if (!gw && !gx) return DISCO_OK;
-    hipError_t e = hipMallocAsync(&ws, xk_bytes + gxk_bytes + part_bytes, st);
-    if (e != hipSuccess) {
-        (void)hipGetLastError();
-        return set_error(e == hipErrorOutOfMemory ? DISCO_ENOMEM : DISCO_EHIP,
-                         "hipMallocAsync for the backward workspace failed: %s",
-                         hipGetErrorString(e));
+    // the handle's workspace; stream-ordered memory while a graph is captured
+    WorkspaceLease lease(psi, xk_bytes + gxk_bytes + part_bytes, st);
+    if (lease.error() != DISCO_OK) return lease.error();
+    ws = lease.ptr();
+    const bool own_ws = ws == nullptr;
+    if (own_ws) {
+        hipError_t e = hipMallocAsync(&ws, xk_bytes + gxk_bytes + part_bytes, st);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            return set_error(e == hipErrorOutOfMemory ? DISCO_ENOMEM : DISCO_EHIP,
+                             "hipMallocAsync for the backward workspace failed: %s",
+                             hipGetErrorString(e));
+        }
     }
     float* xk = static_cast<float*>(ws);
     float* gxk = reinterpret_cast<float*>(static_cast<char*>(ws) + xk_bytes);
@@ -567,7 +574,7 @@ int launch_fused_bwd(const disco_psi* psi, const void* x, int x_dtype, const voi
                 rc = contract_t_any(psi, gxk, DISCO_F32, gx, gx_dtype, B, Ci, row0, nr, sidx > 0, st);
         }
     }
-    hipError_t fe = hipFreeAsync(ws, st);
+    hipError_t fe = own_ws ? hipFreeAsync(ws, st) : hipSuccess;
     if (rc != DISCO_OK) return rc;
     if (fe != hipSuccess) {
         (void)hipGetLastError();

@@ -783,6 +783,14 @@ int try_launch_fused_mfma(const disco_psi* psi, const void* x, const void* w, co
     // weight fragments: the caller's fixed scratch, or stream-ordered workspace
     const size_t nfrag = (size_t)(Ci / 32) * 16 * (Co / 32) * 64;
     void* wsp = nullptr;
+    // without the caller's scratch: the handle's workspace (stream-ordered
+    // memory while a graph is captured)
+    WorkspaceLease lease(frag_ws != nullptr ? nullptr : psi, nfrag * sizeof(u32x4), st);
+    if (lease.error() != DISCO_OK) {
+        *rc = lease.error();
+        return 1;
+    }
+    const bool own_ws = frag_ws == nullptr && lease.ptr() == nullptr;
     if (frag_ws != nullptr) {
         if (nfrag * sizeof(u32x4) > frag_ws_bytes) {
             *rc = set_error(DISCO_EINVAL, "the weight fragments need %zu bytes of scratch; only "
@@ -790,6 +798,8 @@ int try_launch_fused_mfma(const disco_psi* psi, const void* x, const void* w, co
             return 1;
         }
         wsp = frag_ws;
+    } else if (!own_ws) {
+        wsp = lease.ptr();
     } else {
         hipError_t e = hipMallocAsync(&wsp, nfrag * sizeof(u32x4), st);
         if (e != hipSuccess) {
@@ -830,7 +840,7 @@ int try_launch_fused_mfma(const disco_psi* psi, const void* x, const void* w, co
     }
 #undef DISCO_FM
     hipError_t le = hipGetLastError();
-    hipError_t fe = frag_ws != nullptr ? hipSuccess : hipFreeAsync(wsp, st);
+    hipError_t fe = own_ws ? hipFreeAsync(wsp, st) : hipSuccess;
     if (le != hipSuccess) {
         *rc = set_error(DISCO_EHIP, "fused_mfma launch failed: %s", hipGetErrorString(le));
         return 1;

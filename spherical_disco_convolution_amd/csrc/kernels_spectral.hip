@@ -1117,14 +1117,23 @@ int try_launch_fused_spectral(const disco_psi* psi, const void* x, const void* w
     const size_t xh_bytes = up((size_t)B * Ci * D.nlat_in * MP * 4);
     const size_t yh_bytes = up((size_t)B * Co * D.nlat_out * MP * 4);
     const size_t wp_bytes = up((size_t)Co * Ci * 8 * 2);
-    void* ws = nullptr;
-    hipError_t e = hipMallocAsync(&ws, xh_bytes + yh_bytes + wp_bytes, st);
-    if (e != hipSuccess) {
-        (void)hipGetLastError();
-        *rc = set_error(e == hipErrorOutOfMemory ? DISCO_ENOMEM : DISCO_EHIP,
-                        "hipMallocAsync for the spectral workspace failed: %s",
-                        hipGetErrorString(e));
+    // the handle's workspace; stream-ordered memory while a graph is captured
+    WorkspaceLease lease(psi, xh_bytes + yh_bytes + wp_bytes, st);
+    if (lease.error() != DISCO_OK) {
+        *rc = lease.error();
         return 1;
+    }
+    void* ws = lease.ptr();
+    const bool own_ws = ws == nullptr;
+    if (own_ws) {
+        hipError_t e = hipMallocAsync(&ws, xh_bytes + yh_bytes + wp_bytes, st);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            *rc = set_error(e == hipErrorOutOfMemory ? DISCO_ENOMEM : DISCO_EHIP,
+                            "hipMallocAsync for the spectral workspace failed: %s",
+                            hipGetErrorString(e));
+            return 1;
+        }
     }
     uint32_t* xh = static_cast<uint32_t*>(ws);
     bf16_t* yh = reinterpret_cast<bf16_t*>(static_cast<char*>(ws) + xh_bytes);
@@ -1252,7 +1261,7 @@ int try_launch_fused_spectral(const disco_psi* psi, const void* x, const void* w
 #undef DISCO_IR_T
 #undef DISCO_IR
     hipError_t le = hipGetLastError();
-    hipError_t fe = hipFreeAsync(ws, st);
+    hipError_t fe = own_ws ? hipFreeAsync(ws, st) : hipSuccess;
     if (le != hipSuccess) {
         *rc = set_error(DISCO_EHIP, "spectral fused launch failed: %s", hipGetErrorString(le));
         return 1;
@@ -1289,14 +1298,23 @@ int try_launch_fused_spectral32(const disco_psi* psi, const void* x, const void*
     auto up = [](size_t v) { return (v + 255) / 256 * 256; };
     const size_t xh_bytes = up((size_t)B * Ci * D.nlat_in * MP * sizeof(float2));
     const size_t yh_bytes = up((size_t)B * Co * D.nlat_out * MP * sizeof(float2));
-    void* ws = nullptr;
-    hipError_t e = hipMallocAsync(&ws, xh_bytes + yh_bytes, st);
-    if (e != hipSuccess) {
-        (void)hipGetLastError();
-        *rc = set_error(e == hipErrorOutOfMemory ? DISCO_ENOMEM : DISCO_EHIP,
-                        "hipMallocAsync for the spectral workspace failed: %s",
-                        hipGetErrorString(e));
+    // the handle's workspace; stream-ordered memory while a graph is captured
+    WorkspaceLease lease(psi, xh_bytes + yh_bytes, st);
+    if (lease.error() != DISCO_OK) {
+        *rc = lease.error();
         return 1;
+    }
+    void* ws = lease.ptr();
+    const bool own_ws = ws == nullptr;
+    if (own_ws) {
+        hipError_t e = hipMallocAsync(&ws, xh_bytes + yh_bytes, st);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            *rc = set_error(e == hipErrorOutOfMemory ? DISCO_ENOMEM : DISCO_EHIP,
+                            "hipMallocAsync for the spectral workspace failed: %s",
+                            hipGetErrorString(e));
+            return 1;
+        }
     }
     float2* xh = static_cast<float2*>(ws);
     float2* yh = reinterpret_cast<float2*>(static_cast<char*>(ws) + xh_bytes);
@@ -1352,7 +1370,7 @@ int try_launch_fused_spectral32(const disco_psi* psi, const void* x, const void*
                                yh, static_cast<bf16_t*>(y), bias, N, MP, Co, D.nlat_out, yrows, pl);
     }
     hipError_t le = hipGetLastError();
-    hipError_t fe = hipFreeAsync(ws, st);
+    hipError_t fe = own_ws ? hipFreeAsync(ws, st) : hipSuccess;
     if (le != hipSuccess) {
         *rc = set_error(DISCO_EHIP, "float32 spectral launch failed: %s", hipGetErrorString(le));
         return 1;

@@ -175,6 +175,44 @@ def test_spectral_determinism(sdc, monkeypatch):
     assert np.array_equal(a, b)
 
 
+def test_workspace_reuse_across_streams_and_sizes(sdc, monkeypatch):
+    """The handle keeps its workspace between calls.  Calls of two batch sizes
+    (the workspace grows between them) alternate on two streams without host
+    synchronisation; each result must equal, bit for bit, the same call made
+    alone on the current stream (the spectral sums run in a fixed order)."""
+    monkeypatch.delenv("DISCO_FUSED_PATH", raising=False)
+    wl = SPECTRAL[1]   # B = 2
+    x, w = _prepare(wl)
+    psi = _psi(sdc, wl)
+    xd, wd = _dev(x), _dev(w)
+    x1 = xd[:1].contiguous()
+    assert sdc.fused_is_spectral(psi, torch.bfloat16, wl.Ci, wl.Co, 1)
+    want1 = sdc.fused_fwd(psi, x1, wd).cpu().numpy()
+    want2 = sdc.fused_fwd(psi, xd, wd).cpu().numpy()
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    s1.wait_stream(torch.cuda.current_stream())
+    s2.wait_stream(torch.cuda.current_stream())
+    outs = []
+    for rep in range(3):
+        y1 = torch.empty((1, wl.Co, wl.nlat_out, wl.nlon_out), device="cuda")
+        y2 = torch.empty((2, wl.Co, wl.nlat_out, wl.nlon_out), device="cuda")
+        for t in (y1, y2):
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        sdc.fused_fwd(psi, x1, wd, y=y1, stream=s1)
+        sdc.fused_fwd(psi, xd, wd, y=y2, stream=s2)
+        outs.append((y1, y2))
+    torch.cuda.synchronize()
+    for rep, (y1, y2) in enumerate(outs):
+        _say(f"workspace reuse rep {rep}")
+        assert np.array_equal(y1.cpu().numpy(), want1)
+        assert np.array_equal(y2.cpu().numpy(), want2)
+    # and against the oracle, once
+    ref = oracle.forward(_desc(wl), x, w, 1)
+    assert rel_l2(outs[-1][1].cpu().numpy(), ref) <= TOL_BF16
+
+
 def _sample_rows(nlat):
     rows = {0, 1, 2, 5, nlat // 7, nlat // 3, nlat // 2, (2 * nlat) // 3, nlat - 6, nlat - 2, nlat - 1}
     return sorted(r for r in rows if 0 <= r < nlat)

@@ -255,6 +255,25 @@ constexpr int kRegThreads = 64;   // one wave per workgroup
 
 constexpr int spec_mp_of(int H) { return (H + 32) / 32 * 32; }   // (H + 1) rounded up to 32
 
+// w [Co][Ci][K] bf16 -> the GEMM's A operands in fragment order:
+// wp[chunk][k-step][co / 32][lane][8], lane (l32, lg) holding row co = 32 * tile
+// + l32 and pairs kappa = 16 k-step + 8 lg .. + 7 of the chunk, where a chunk's
+// 256 pairs are ordered kappa = k * 32 + ci (basis index padded to 8 with
+// zeros).  One wave's fragment is 1 KB of contiguous memory.
+__device__ __forceinline__ void prep_w_elem(const bf16_t* __restrict__ w, bf16_t* __restrict__ wp,
+                                            int Co, int Ci, int K, size_t n) {
+    const int e = (int)(n & 7);
+    const int lane = (int)((n >> 3) & 63);
+    const size_t f = n >> 9;                  // (chunk * 16 + k-step) * (Co / 32) + tile
+    const int tile = (int)(f % (Co / 32));
+    const size_t cs = f / (Co / 32);
+    const int ks = (int)(cs % 16), cc = (int)(cs / 16);
+    const int co = tile * 32 + (lane & 31);
+    const int kap = 16 * ks + 8 * (lane >> 5) + e;   // k * 32 + ci
+    const int k = kap >> 5, ci = kap & 31;
+    wp[n] = k < K ? w[((size_t)co * Ci + cc * 32 + ci) * K + k] : (bf16_t)0;
+}
+
 // x rows (N = 2 H real bf16 samples, H = H1 H2) -> x_hat rows (MP bf16 pairs),
 // RW rows per wave and step.  The H-point transform of z[n] = x[2n] + i x[2n+1]
 // is split with n = H2 a + b and k = c + H1 d:
@@ -266,11 +285,17 @@ constexpr int spec_mp_of(int H) { return (H + 32) / 32 * 32; }   // (H + 1) roun
 // the even/odd split, which writes four frequencies per 16-byte store.
 // Workgroup g transforms rows g RW .. g RW + RW - 1.  (A persistent form that
 // loads the next group during the current one needs more than 256 registers
-// and is slower.)
+// and is slower.)  The first nprep workgroups instead write the weight
+// fragments (kPrepPerWg elements each, the work of spec_prep_w), so that the
+// call needs no launch of its own for them.
+constexpr int kPrepPerWg = 64 * 16;
 template <int H1, int H2, int RW>
 __global__ __launch_bounds__(kRegThreads) void spec_rfft_reg(const uint32_t* __restrict__ x,
                                                              uint32_t* __restrict__ xh,
-                                                             int64_t nrows) {
+                                                             int64_t nrows,
+                                                             const bf16_t* __restrict__ w,
+                                                             bf16_t* __restrict__ wp, int Co,
+                                                             int Ci, int K, int nprep) {
     constexpr int H = H1 * H2, MP = spec_mp_of(H);
     constexpr int P2 = H2 | 1, LP = H1 * P2;
     constexpr int TA = RW * H2, ITA = (TA + 63) / 64;
@@ -279,7 +304,17 @@ __global__ __launch_bounds__(kRegThreads) void spec_rfft_reg(const uint32_t* __r
     static_assert(MP - H - 1 <= 64, "one lane per padding word");
     __shared__ float2 buf[RW * LP];
     const int lane = threadIdx.x;
-    const int64_t g = blockIdx.x;   // the grid is the row-group count
+    if ((int)blockIdx.x < nprep) {
+        const size_t total = (size_t)Co * Ci * 8;
+        const size_t n0 = (size_t)blockIdx.x * kPrepPerWg + lane;
+#pragma unroll 4
+        for (int t = 0; t < kPrepPerWg / 64; ++t) {
+            const size_t n = n0 + 64 * t;
+            if (n < total) prep_w_elem(w, wp, Co, Ci, K, n);
+        }
+        return;
+    }
+    const int64_t g = (int64_t)blockIdx.x - nprep;   // the grid is nprep + the row-group count
 
     uint32_t raw[ITA][H1];
 #pragma unroll
@@ -520,26 +555,11 @@ __global__ __launch_bounds__(kRegThreads) void spec_irfft_reg(const uint32_t* __
     }
 }
 
-// w [Co][Ci][K] bf16 -> the GEMM's A operands in fragment order:
-// wp[chunk][k-step][co / 32][lane][8], lane (l32, lg) holding row co = 32 * tile
-// + l32 and pairs kappa = 16 k-step + 8 lg .. + 7 of the chunk, where a chunk's
-// 256 pairs are ordered kappa = k * 32 + ci (basis index padded to 8 with
-// zeros).  One wave's fragment is 1 KB of contiguous memory.
+// the weight fragments alone (for the Stockham transforms' launches)
 __global__ void spec_prep_w(const bf16_t* __restrict__ w, bf16_t* __restrict__ wp, int Co, int Ci,
                             int K) {
     const size_t n = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const size_t total = (size_t)Co * Ci * 8;
-    if (n >= total) return;
-    const int e = (int)(n & 7);
-    const int lane = (int)((n >> 3) & 63);
-    const size_t f = n >> 9;                  // (chunk * 16 + k-step) * (Co / 32) + tile
-    const int tile = (int)(f % (Co / 32));
-    const size_t cs = f / (Co / 32);
-    const int ks = (int)(cs % 16), cc = (int)(cs / 16);
-    const int co = tile * 32 + (lane & 31);
-    const int kap = 16 * ks + 8 * (lane >> 5) + e;   // k * 32 + ci
-    const int k = kap >> 5, ci = kap & 31;
-    wp[n] = k < K ? w[((size_t)co * Ci + cc * 32 + ci) * K + k] : (bf16_t)0;
+    if (n < (size_t)Co * Ci * 8) prep_w_elem(w, wp, Co, Ci, K, n);
 }
 
 constexpr int kMt = 32;              // frequencies per work item (64 GEMM columns)
@@ -1152,7 +1172,7 @@ int try_launch_fused_spectral(const disco_psi* psi, const void* x, const void* w
     auto reg_grid = [](int64_t rows, int rw) { return dim3((unsigned)((rows + rw - 1) / rw)); };
 
     const size_t nwp = (size_t)Co * Ci * 8;
-    {
+    if (!reg) {
         KernelTimer timer("spec_prep_w", st);
         hipLaunchKernelGGL(spec_prep_w, dim3((unsigned)((nwp + 255) / 256)), dim3(256), 0, st,
                            static_cast<const bf16_t*>(w), wpd, Co, Ci, K);
@@ -1160,10 +1180,13 @@ int try_launch_fused_spectral(const disco_psi* psi, const void* x, const void* w
     const size_t fft_lds = (size_t)(kFftRows + 1) * H * sizeof(float2);
     const int64_t xrows = (int64_t)B * Ci * D.nlat_in;
     const uint32_t* x32 = static_cast<const uint32_t*>(x);
+    // the register transforms' launch also writes the weight fragments
+    const int nprep = (int)((nwp + kPrepPerWg - 1) / kPrepPerWg);
 #define DISCO_RF(H1, H2, RW)                                                                   \
     hipLaunchKernelGGL((spec_rfft_reg<H1, H2, RW>),                                            \
-                       reg_grid(xrows, RW),                                                    \
-                       dim3(kRegThreads), 0, st, x32, xh, xrows)
+                       dim3((unsigned)(nprep + (xrows + RW - 1) / RW)),                        \
+                       dim3(kRegThreads), 0, st, x32, xh, xrows,                               \
+                       static_cast<const bf16_t*>(w), wpd, Co, Ci, K, nprep)
     {
     KernelTimer timer("spec_rfft", st);
     if (reg && H == 720) {

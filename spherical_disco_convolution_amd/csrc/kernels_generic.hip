@@ -411,6 +411,7 @@ __global__ __launch_bounds__(kThreads) void fused_depthwise_tiled(
     const float bv = bias ? bias[co] : 0.0f;
     const int tid = threadIdx.x;
     const int own = QR * tid;   // first of this thread's outputs within a pass
+    const int adv = (4 * NT) % nlon_in;   // staging stride of one thread, reduced
 
     for (int q0 = 0; q0 < nlon_out; q0 += QR * NT) {
         float acc[QR];
@@ -437,9 +438,12 @@ __global__ __launch_bounds__(kThreads) void fused_depthwise_tiled(
             // u + 1, u + 3 to ext_o as 8-byte stores, for stride 1 all four
             // as one 16-byte store
             const int nunits = S * dw_ext_words(NT, QR, wp, S) / 4;
+            // this thread's first sample, reduced mod nlon_in once; each later
+            // unit advances it by adv < nlon_in, so one conditional
+            // subtraction keeps it reduced
+            int p0 = start + 4 * tid;
+            while (p0 >= nlon_in) p0 -= nlon_in;
             for (int g = tid; g < nunits; g += NT) {
-                int p0 = start + 4 * g;
-                while (p0 >= nlon_in) p0 -= nlon_in;
                 float v[4];
                 if (p0 + 3 < nlon_in) {
                     const T* src = row + p0;
@@ -459,6 +463,8 @@ __global__ __launch_bounds__(kThreads) void fused_depthwise_tiled(
                 } else {
                     *reinterpret_cast<float4*>(ext_e + 4 * g) = make_float4(v[0], v[1], v[2], v[3]);
                 }
+                p0 += adv;
+                if (p0 >= nlon_in) p0 -= nlon_in;
             }
             __syncthreads();
             int t0 = 0;

@@ -90,11 +90,11 @@ MEASURED_TRAFFIC_BYTES = {
     ("c3", "spec_mfma"): {"bytes": 172868811, "source": "kernels_spectral.hip",
                   "sha1": "25e47443029f5a5ef9274bd43327c7a4da020602",
                   "profile": "profiles/c3_counters.md"},
-    ("c5", "fused"): {"bytes": 1781389596, "source": "kernels_generic.hip",
-                  "sha1": "af55f7727176d3d320835ae69aec87e579ec0390",
+    ("c5", "fused"): {"bytes": 1809295723, "source": "kernels_generic.hip",
+                  "sha1": "0b0f754a0f19c0c2bf7543f130f0d68a9336835a",
                   "profile": "profiles/c5_counters.md"},
-    ("c5", "fused_depthwise"): {"bytes": 1781389596, "source": "kernels_generic.hip",
-                  "sha1": "af55f7727176d3d320835ae69aec87e579ec0390",
+    ("c5", "fused_depthwise"): {"bytes": 1809295723, "source": "kernels_generic.hip",
+                  "sha1": "0b0f754a0f19c0c2bf7543f130f0d68a9336835a",
                   "profile": "profiles/c5_counters.md"},
     ("c2", "fused_spectral"): {"bytes": 274487424, "source": "kernels_spectral.hip",
                   "sha1": "25e47443029f5a5ef9274bd43327c7a4da020602",

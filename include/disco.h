@@ -161,7 +161,11 @@ int disco_einsum(const void* xk, int xk_dtype, const void* w, int w_dtype,
  *    its spectrum folded onto the output grid's frequencies);
  *  - float32 x and w, stride 1, Co <= 128 (both sums on the vector ALUs).
  * The environment variable DISCO_FUSED_PATH=toeplitz selects the direct
- * kernels for them instead.  Other layers run the direct kernels: the
+ * kernels for them instead.  Rows with 9 to 16 windows (input rows per
+ * output row) are summed in two halves of their windows on the 8-window
+ * matrix-core kernel when every row has at least two windows;
+ * DISCO_SPEC_HALVES=0 selects the 16-window kernel for them instead (same
+ * sums, one workgroup per compute unit).  Other layers run the direct kernels: the
  * matrix-core kernel for bf16 layers it accepts, the vector kernels
  * otherwise. */
 int disco_fused_fwd(const disco_psi* psi, const void* x, int x_dtype,

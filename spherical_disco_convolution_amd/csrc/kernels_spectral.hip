@@ -615,7 +615,7 @@ __global__ __launch_bounds__(kSpecThreads) __attribute__((amdgpu_waves_per_eu(NW
     const uint32_t* __restrict__ xh, const bf16_t* __restrict__ wp,
     const uint32_t* __restrict__ psih, const int32_t* __restrict__ win_ptr,
     const DevWindow* __restrict__ wins, bf16_t* __restrict__ yh, int B, int Ci, int nlat_in,
-    int nlat_out, int MP, int NX, int64_t psih_zero, int nwmax) {
+    int nlat_out, int MP, int NX, int64_t psih_zero, int nwmax, int NP) {
     static_assert(NW == 8 || NW == 16, "window capacity");
     constexpr int NS = NW / 8;            // window-sum MFMA steps
     constexpr int WPW = NW / 4;           // windows whose spectra each wave copies
@@ -644,21 +644,29 @@ __global__ __launch_bounds__(kSpecThreads) __attribute__((amdgpu_waves_per_eu(NW
     const size_t plane = (size_t)nlat_in * MP;
 
     // Item cursor: item n of this workgroup is l = slot + n GX of its band,
-    // frequency tile mt = l / brows and band row ro = l % brows.  Cursors step
-    // through the items in order (stopping at the last), so no item is decoded
-    // by division more than once.
+    // frequency tile mt = l / brows and band row ro = l % brows.  With NP = 2
+    // an item is visited twice, once per half of its row's windows (part 0:
+    // the first ceil(nw / 2), part 1: the rest; the host passes NP = 2 only
+    // when every row has at least two windows), and the channel/basis GEMM
+    // accumulates both halves before y_hat is stored.  Cursors step through
+    // the (item, part) pairs in order (stopping at the last), so no item is
+    // decoded by division more than once.
     struct Cur {
-        int n, mt, ro;
+        int n, mt, ro, part;
     };
     auto cur_first = [&]() {
         Cur c;
         c.n = 0;
         c.mt = slot / brows;
         c.ro = slot - c.mt * brows;
+        c.part = 0;
         return c;
     };
     auto cur_next = [&](Cur& c) {
-        if (c.n + 1 < nmine) {
+        if (c.part + 1 < NP) {
+            ++c.part;
+        } else if (c.n + 1 < nmine) {
+            c.part = 0;
             ++c.n;
             c.ro += GX;
             while (c.ro >= brows) {
@@ -675,6 +683,20 @@ __global__ __launch_bounds__(kSpecThreads) __attribute__((amdgpu_waves_per_eu(NW
             j -= b * nlat_out;
         }
     };
+    // the windows of the cursor's (item, part): [w0, w0 + nw)
+    auto cur_windows = [&](const Cur& c, int j, int& w0, int& nw) {
+        w0 = win_ptr[j];
+        nw = win_ptr[j + 1] - w0;
+        if (NP == 2) {
+            const int h = (nw + 1) >> 1;
+            if (c.part == 0) {
+                nw = h;
+            } else {
+                w0 += h;
+                nw -= h;
+            }
+        }
+    };
 
     // ---- spectra stream: position p = (item p / nchunks, chunk p % nchunks).
     // The request cursor walks the positions in order (staying at the last).
@@ -685,12 +707,12 @@ __global__ __launch_bounds__(kSpecThreads) __attribute__((amdgpu_waves_per_eu(NW
     // (valid, finite; their B rows are zero).
     int lat_w[WPW];                 // input rows of this wave's windows of the requested item
     int req_pos = 0, req_chunk = 0, req_b = 0;
-    const int npos = nmine * nchunks;
+    const int npos = nmine * NP * nchunks;
     Cur rq = cur_first();
     auto request_item = [&]() {   // the window rows of the request cursor's item
-        int j;
+        int j, w0, nw;
         cur_bj(rq, req_b, j);
-        const int w0 = win_ptr[j], nw = win_ptr[j + 1] - w0;
+        cur_windows(rq, j, w0, nw);
 #pragma unroll
         for (int u = 0; u < WPW; ++u) {
             const int r = WPW * wave + u;
@@ -740,9 +762,9 @@ __global__ __launch_bounds__(kSpecThreads) __attribute__((amdgpu_waves_per_eu(NW
     const uint32_t ps_lds =
         __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_void*)&ps[0]);
     auto dma_ps = [&](const Cur& c) {
-        int b, j;
+        int b, j, w0, nw;
         cur_bj(c, b, j);
-        const int w0 = win_ptr[j], nw = win_ptr[j + 1] - w0;
+        cur_windows(c, j, w0, nw);
         for (int i = wave; i < NS * KT; i += 4) {
             const int slot = 64 * i + lane;
             const int rk = slot >> 3, ml0 = (slot & 7) * 4;
@@ -769,12 +791,13 @@ __global__ __launch_bounds__(kSpecThreads) __attribute__((amdgpu_waves_per_eu(NW
     wait_vmcnt<0>();
     __syncthreads();   // ps, zero columns, first spectra block
 
-    for (int n = 0; n < nmine; ++n) {
-        int b, j;
+    floatx16 acc[NTW];   // y_hat of the current item, over its NP parts
+    for (int v = 0; v < nmine * NP; ++v) {
+        int b, j, w0, nw;
         cur_bj(cur, b, j);
         const int m0 = cur.mt * kMt;
-        const int w0 = uniform(win_ptr[j]);
-        const int nw = uniform(win_ptr[j + 1]) - w0;   // <= kSpecMaxWin (checked on the host)
+        cur_windows(cur, j, w0, nw);
+        nw = uniform(nw);   // <= kSpecMaxWin (checked on the host)
 
         // B operands of the window sum: lane column n = 2 k + c (c: real,
         // imaginary part of X_hat), rows (r, re/im) for r = 4 lg .. 4 lg + 3
@@ -807,11 +830,12 @@ __global__ __launch_bounds__(kSpecThreads) __attribute__((amdgpu_waves_per_eu(NW
         // the channel; 2 wave is even, so the h = 1 piece is the other's ^ 1)
         const int xsw = (2 * wave) ^ ((l32 >> 1) & 7);
 
-        floatx16 acc[NTW];
+        if (cur.part == 0) {
 #pragma unroll
-        for (int t = 0; t < NTW; ++t)
+            for (int t = 0; t < NTW; ++t)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) acc[t][e] = 0.0f;
+                for (int e = 0; e < 16; ++e) acc[t][e] = 0.0f;
+        }
 
         for (int cc = 0; cc < nchunks; ++cc) {
             // ---- window sum, one MFMA per frequency ----
@@ -931,6 +955,11 @@ __global__ __launch_bounds__(kSpecThreads) __attribute__((amdgpu_waves_per_eu(NW
             __builtin_amdgcn_s_setprio(0);
             wait_vmcnt<NKS>();
             __syncthreads();   // spectra of p + 1 in LDS; B tile free
+        }
+        if (cur.part + 1 < NP) {   // the item's other half of its windows next
+            cur = nxt;
+            cur_next(nxt);
+            continue;
         }
         // ---- y_hat (bf16 (re, im) pairs), staged through the free B tile so
         // that each store instruction writes whole 128-byte row segments.  The
@@ -1207,8 +1236,15 @@ int try_launch_fused_spectral(const disco_psi* psi, const void* x, const void* w
     const int64_t nrows_all = (int64_t)B * D.nlat_out;
     const int NX = (int)std::min<int64_t>(kXcds, nrows_all);
     const int64_t min_items = nrows_all / NX * (MP / kMt);
-    // window capacity: 8 (two workgroups per compute unit) or 16 (one)
-    const int NWC = d.max_windows <= 8 ? 8 : 16;
+    // window capacity: 8 (two workgroups per compute unit) or 16 (one).
+    // Rows with 9 to 16 windows run on the 8-window kernel in two halves
+    // (each item visited once per half of its windows, both accumulated
+    // before y_hat is stored) when every row has at least two windows.
+    const char* eh = std::getenv("DISCO_SPEC_HALVES");
+    const bool halves = d.max_windows > 8 && d.min_windows >= 2 && !(eh && eh[0] == '0');
+    const int NWC = d.max_windows <= 8 || halves ? 8 : 16;
+    const int NPART = halves ? 2 : 1;
+    const int nwmax = halves ? (d.max_windows + 1) / 2 : d.max_windows;
     const int per_cu = NWC == 8 ? 2 : 1;
     const int GX =
         (int)std::max<int64_t>(1, std::min<int64_t>(min_items, per_cu * (int64_t)ncu / NX));
@@ -1216,7 +1252,7 @@ int try_launch_fused_spectral(const disco_psi* psi, const void* x, const void* w
 #define DISCO_SM(CC, KK, NWT)                                                                \
     hipLaunchKernelGGL((spec_mfma<CC, KK, NWT>), grid, dim3(kSpecThreads), 0, st, xh, wpd,   \
                        psih, d.win_ptr, d.windows, yh, B, Ci, D.nlat_in, D.nlat_out, MP, NX, \
-                       (int64_t)h.windows.size() * K * MP, (int)d.max_windows)
+                       (int64_t)h.windows.size() * K * MP, nwmax, NPART)
 #define DISCO_SM_K(CC, NWT)                                                                  \
     switch (K) {                                                                             \
         case 1: DISCO_SM(CC, 1, NWT); break;                                                 \

@@ -297,26 +297,39 @@ STRIDE2 = [
 ]
 
 
-@pytest.mark.parametrize("path", ["spectral", "toeplitz"])
+@pytest.mark.parametrize("path", ["spectral", "spectral16", "toeplitz"])
 @pytest.mark.parametrize("wl", STRIDE2, ids=[w.name for w in STRIDE2])
 def test_stride2_spectral(sdc, wl, path, monkeypatch):
+    """spectral: rows of up to 15 windows in two halves on the 8-window
+    kernel; spectral16: the same rows on the 16-window kernel
+    (DISCO_SPEC_HALVES=0); toeplitz: the direct matrix-core kernel."""
+    monkeypatch.delenv("DISCO_SPEC_HALVES", raising=False)
     if path == "toeplitz":
         monkeypatch.setenv("DISCO_FUSED_PATH", "toeplitz")
     else:
         monkeypatch.delenv("DISCO_FUSED_PATH", raising=False)
+        if path == "spectral16":
+            monkeypatch.setenv("DISCO_SPEC_HALVES", "0")
+        sdc.kernel_timing(True)
     _say("stride 2", path, wl.name)
     x, w = _prepare(wl)
     psi = _psi(sdc, wl)
-    assert sdc.fused_is_spectral(psi, torch.bfloat16, wl.Ci, wl.Co, 1) == (path == "spectral")
+    assert sdc.fused_is_spectral(psi, torch.bfloat16, wl.Ci, wl.Co, 1) == (path != "toeplitz")
     xd, wd = _dev(x), _dev(w)
     bias = np.linspace(-1, 1, wl.Co).astype(np.float32)
-    y = sdc.fused_fwd(psi, xd, wd, bias=torch.from_numpy(bias).cuda()).cpu().numpy()
+    try:
+        y = sdc.fused_fwd(psi, xd, wd, bias=torch.from_numpy(bias).cuda()).cpu().numpy()
+    finally:
+        ran = set(sdc.kernel_timing_read())
+        sdc.kernel_timing(False)
+    if path != "toeplitz":
+        assert "spec_mfma" in ran, ran
     cols = _sample_cols(wl.nlon_out, seed=5)
     ref = oracle.forward(_desc(wl), x, w, 1, cols_out=cols, bias=bias)
     err = rel_l2(y[..., cols], ref)
     _say(f"  rel-L2 {err:.3e}")
     assert err <= TOL_BF16
-    if path == "spectral":
+    if path != "toeplitz":
         frows = [0, wl.nlat_out // 3, wl.nlat_out // 2]
         fref = oracle.forward(_desc(wl), x, w, 1, rows=frows)
         band = worst_band_rel_l2(y[:, :, frows] - bias[None, :, None, None], fref)

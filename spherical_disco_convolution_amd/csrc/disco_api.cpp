@@ -285,6 +285,7 @@ int disco_psi_to_device(disco_psi* psi) {
     const int nlat_in = h.desc.nlat_in;
     std::vector<int32_t> wtptr(nlat_in + 1, 0);
     std::vector<DevWindow> wins_t(wins.size());
+    std::vector<int32_t> orig_t(wins.size());   // forward index of each transposed window
     {
         std::vector<int32_t> out_row(wins.size());
         for (int j = 0; j < nlat_out; ++j)
@@ -297,10 +298,16 @@ int disco_psi_to_device(disco_psi* psi) {
         for (size_t n = 0; n < wins.size(); ++n) {
             DevWindow t = wins[n];
             t.lat = out_row[n];
+            orig_t[fill[wins[n].lat]] = (int32_t)n;
             wins_t[fill[wins[n].lat]++] = t;
         }
     }
     d.min_windows = nlat_out > 0 ? wptr[1] - wptr[0] : 0;
+    d.t_min_windows = nlat_in > 0 ? wtptr[1] - wtptr[0] : 0;
+    for (int i = 0; i < nlat_in; ++i) {
+        d.t_max_windows = std::max(d.t_max_windows, wtptr[i + 1] - wtptr[i]);
+        d.t_min_windows = std::min(d.t_min_windows, wtptr[i + 1] - wtptr[i]);
+    }
     for (int j = 0; j < nlat_out; ++j) {
         d.max_windows = std::max(d.max_windows, wptr[j + 1] - wptr[j]);
         d.min_windows = std::min(d.min_windows, wptr[j + 1] - wptr[j]);
@@ -348,6 +355,28 @@ int disco_psi_to_device(disco_psi* psi) {
         d.spec_psih = p;
         if ((rc = dev_copy(p, spec_psih.data(), spec_psih.size() * sizeof(uint32_t))) != DISCO_OK)
             goto fail;
+        if (h.stride == 1) {
+            // the adjoint's table: windows in the transposed order, each
+            // Psi_hat conjugated (the matrix-core kernel multiplies by the
+            // conjugate of its table, and the adjoint of the correlation is
+            // the convolution, Psi_hat itself); the same trailing zero block
+            const size_t blk = (size_t)h.K * d.spec_mp;
+            std::vector<uint32_t> pt;
+            try {
+                pt.assign(spec_psih.size(), 0u);
+            } catch (const std::bad_alloc&) {
+                rc = set_error(DISCO_ENOMEM, "host allocation for the adjoint table failed");
+                goto fail;
+            }
+            for (size_t n = 0; n < wins_t.size(); ++n) {
+                const uint32_t* src = spec_psih.data() + (size_t)orig_t[n] * blk;
+                uint32_t* dst = pt.data() + n * blk;
+                for (size_t e = 0; e < blk; ++e) dst[e] = src[e] ^ 0x80000000u;   // imag sign
+            }
+            if ((rc = dev_alloc(d, &p, pt.size() * sizeof(uint32_t))) != DISCO_OK) goto fail;
+            d.spec_psih_t = p;
+            if ((rc = dev_copy(p, pt.data(), pt.size() * sizeof(uint32_t))) != DISCO_OK) goto fail;
+        }
         if (!spec_psih32.empty()) {
             if ((rc = dev_alloc(d, &p, spec_psih32.size() * sizeof(float))) != DISCO_OK) goto fail;
             d.spec_psih32 = static_cast<float*>(p);

@@ -85,6 +85,8 @@ struct DevPsi {
     int32_t max_width = 0;        // widest window
     int32_t max_windows = 0;      // most windows of one output row
     int32_t min_windows = 0;      // fewest windows of one output row
+    int32_t t_max_windows = 0;    // most windows of one input row (transposed list)
+    int32_t t_min_windows = 0;    // fewest windows of one input row
     int32_t* win_ptr = nullptr;   // [nlat_out + 1]
     DevWindow* windows = nullptr; // [nwin]
     float* vals = nullptr;        // [nnz, KP] float32, window order, zero padded
@@ -101,6 +103,7 @@ struct DevPsi {
     // longitude-spectral tables for the spectral fused path (stride 1)
     void* spec_psih = nullptr;    // bf16 (re, im) words [nwin][K][spec_mp]
     float* spec_psih32 = nullptr; // float32 (re, im) pairs [nwin][K][spec_mp], or none
+    void* spec_psih_t = nullptr;  // stride 1: conj(Psi_hat) in the transposed window order
     int32_t spec_mp = 0;          // padded frequency count; 0 = no tables
     int32_t spec_radix[kSpecMaxRadix] = {0};
     int32_t spec_nrad = 0;
@@ -148,6 +151,13 @@ int launch_fused_noalloc(const disco_psi* psi, const void* x, int dtype, const v
                          int groups, void* stream);
 // 1 if disco_fused_fwd takes the longitude-spectral path for these arguments
 int fused_spectral_eligible(const disco_psi* psi, int x_dtype, int Ci, int Co, int groups);
+// The adjoint in x on the longitude-spectral kernels (stride-1 layers, bf16
+// x, w and gy): 1 if it applies; the launcher returns 0 when it does not (rc
+// untouched), else 1 with *rc the result.
+int spectral_grad_x_eligible(const disco_psi* psi, int x_dtype, int gy_dtype, int Ci, int Co,
+                             int groups);
+int try_launch_grad_x_spectral(const disco_psi* psi, const void* gy, const void* w, void* gx,
+                               int gx_dtype, int B, int Ci, int Co, hipStream_t st, int* rc);
 
 // Backward (kernels_backward.hip)
 int launch_fill_zero(float* p, size_t n, void* stream);

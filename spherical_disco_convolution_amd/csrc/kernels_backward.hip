@@ -506,6 +506,16 @@ int launch_fused_bwd(const disco_psi* psi, const void* x, int x_dtype, const voi
     hipStream_t st = static_cast<hipStream_t>(stream);
     const HostPsi& h = psi->host;
     const disco_psi_desc& D = h.desc;
+    // stride-1 bf16 layers with a bf16 gradient: grad_x on the spectral
+    // kernels (the convolution adjoint of each window's correlation), whole
+    if (gx && x_dtype == DISCO_BF16 && w_dtype == DISCO_BF16 &&
+        spectral_grad_x_eligible(psi, x_dtype, gy_dtype, Ci, Co, groups)) {
+        int src = DISCO_OK;
+        if (try_launch_grad_x_spectral(psi, gy, w, gx, gx_dtype, B, Ci, Co, st, &src)) {
+            if (src != DISCO_OK) return src;
+            gx = nullptr;
+        }
+    }
     const int K = h.K, cig = Ci / groups, cog = Co / groups;
     const size_t row_bytes = (size_t)B * Ci * K * D.nlon_out * sizeof(float);
     int rows = D.nlat_out;

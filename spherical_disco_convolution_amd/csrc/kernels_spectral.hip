@@ -261,7 +261,7 @@ constexpr int spec_mp_of(int H) { return (H + 32) / 32 * 32; }   // (H + 1) roun
 // 256 pairs are ordered kappa = k * 32 + ci (basis index padded to 8 with
 // zeros).  One wave's fragment is 1 KB of contiguous memory.
 __device__ __forceinline__ void prep_w_elem(const bf16_t* __restrict__ w, bf16_t* __restrict__ wp,
-                                            int Co, int Ci, int K, size_t n) {
+                                            int Co, int Ci, int K, size_t n, int wt) {
     const int e = (int)(n & 7);
     const int lane = (int)((n >> 3) & 63);
     const size_t f = n >> 9;                  // (chunk * 16 + k-step) * (Co / 32) + tile
@@ -271,7 +271,11 @@ __device__ __forceinline__ void prep_w_elem(const bf16_t* __restrict__ w, bf16_t
     const int co = tile * 32 + (lane & 31);
     const int kap = 16 * ks + 8 * (lane >> 5) + e;   // k * 32 + ci
     const int k = kap >> 5, ci = kap & 31;
-    wp[n] = k < K ? w[((size_t)co * Ci + cc * 32 + ci) * K + k] : (bf16_t)0;
+    // wt: w is stored [Ci][Co][K] (the forward layer's weights, read by the
+    // adjoint, whose GEMM maps the layer's output channels to its inputs)
+    const size_t src = wt ? ((size_t)(cc * 32 + ci) * Co + co) * K + k
+                          : ((size_t)co * Ci + cc * 32 + ci) * K + k;
+    wp[n] = k < K ? w[src] : (bf16_t)0;
 }
 
 // x rows (N = 2 H real bf16 samples, H = H1 H2) -> x_hat rows (MP bf16 pairs),
@@ -295,7 +299,7 @@ __global__ __launch_bounds__(kRegThreads) void spec_rfft_reg(const uint32_t* __r
                                                              int64_t nrows,
                                                              const bf16_t* __restrict__ w,
                                                              bf16_t* __restrict__ wp, int Co,
-                                                             int Ci, int K, int nprep) {
+                                                             int Ci, int K, int nprep, int wt) {
     constexpr int H = H1 * H2, MP = spec_mp_of(H);
     constexpr int P2 = H2 | 1, LP = H1 * P2;
     constexpr int TA = RW * H2, ITA = (TA + 63) / 64;
@@ -310,7 +314,7 @@ __global__ __launch_bounds__(kRegThreads) void spec_rfft_reg(const uint32_t* __r
 #pragma unroll 4
         for (int t = 0; t < kPrepPerWg / 64; ++t) {
             const size_t n = n0 + 64 * t;
-            if (n < total) prep_w_elem(w, wp, Co, Ci, K, n);
+            if (n < total) prep_w_elem(w, wp, Co, Ci, K, n, wt);
         }
         return;
     }
@@ -557,9 +561,9 @@ __global__ __launch_bounds__(kRegThreads) void spec_irfft_reg(const uint32_t* __
 
 // the weight fragments alone (for the Stockham transforms' launches)
 __global__ void spec_prep_w(const bf16_t* __restrict__ w, bf16_t* __restrict__ wp, int Co, int Ci,
-                            int K) {
+                            int K, int wt) {
     const size_t n = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (n < (size_t)Co * Ci * 8) prep_w_elem(w, wp, Co, Ci, K, n);
+    if (n < (size_t)Co * Ci * 8) prep_w_elem(w, wp, Co, Ci, K, n, wt);
 }
 
 constexpr int kMt = 32;              // frequencies per work item (64 GEMM columns)
@@ -1150,21 +1154,125 @@ int fused_spectral_eligible(const disco_psi* psi, int x_dtype, int Ci, int Co, i
     return e == nullptr || std::strcmp(e, "toeplitz") != 0;
 }
 
+namespace {
+
+// One bf16 longitude-spectral pass: rows of x (B x Ci planes of nin rows of
+// N samples) -> x_hat; per output row (B x Co planes of nout rows) the window
+// sums over its window list (win_ptr / wins, Psi_hat table psih in the list's
+// order, multiplied conjugated) and the channel/basis GEMM; the inverse
+// transform into y (+ bias).  The forward layer is (x, w, its windows,
+// Psi_hat); its adjoint in x is (gy, w read transposed, the transposed
+// windows, conj(Psi_hat) in their order), at stride 1.
+struct SpecCall {
+    const void* x;
+    int nin;
+    const void* w;
+    int wt;                    // w stored [Ci][Co][K] (read transposed)
+    const int32_t* win_ptr;
+    const DevWindow* wins;
+    size_t nwin;
+    int max_windows, min_windows;
+    const uint32_t* psih;
+    int nout;
+    const float* bias;
+    void* y;
+    int y_dtype;
+    int B, Ci, Co;
+};
+
+int run_spectral_bf16(const disco_psi* psi, const SpecCall& c, hipStream_t st, int* rc);
+
+}  // namespace
+
 int try_launch_fused_spectral(const disco_psi* psi, const void* x, const void* w,
                               const float* bias, void* y, int y_dtype, int B, int Ci, int Co,
                               int groups, hipStream_t st, int* rc) {
     if (!fused_spectral_eligible(psi, DISCO_BF16, Ci, Co, groups) || B <= 0) return 0;
     const DevPsi& d = psi->dev;
     const HostPsi& h = psi->host;
+    SpecCall c;
+    c.x = x;
+    c.nin = h.desc.nlat_in;
+    c.w = w;
+    c.wt = 0;
+    c.win_ptr = d.win_ptr;
+    c.wins = d.windows;
+    c.nwin = h.windows.size();
+    c.max_windows = d.max_windows;
+    c.min_windows = d.min_windows;
+    c.psih = static_cast<const uint32_t*>(d.spec_psih);
+    c.nout = h.desc.nlat_out;
+    c.bias = bias;
+    c.y = y;
+    c.y_dtype = y_dtype;
+    c.B = B;
+    c.Ci = Ci;
+    c.Co = Co;
+    return run_spectral_bf16(psi, c, st, rc);
+}
+
+// The adjoint in x of the fused forward, for stride-1 bf16 layers with bf16
+// gradients: gx = irfft(sum over output rows j and k of Psi_hat[k, j, i, m]
+// sum_co w[co, ci, k] gy_hat[co, j, m]), on the forward's kernels.
+int spectral_grad_x_eligible(const disco_psi* psi, int x_dtype, int gy_dtype, int Ci, int Co,
+                             int groups) {
+    const DevPsi& d = psi->dev;
+    const HostPsi& h = psi->host;
+    if (d.spec_psih_t == nullptr || h.stride != 1 || x_dtype != DISCO_BF16 ||
+        gy_dtype != DISCO_BF16 || groups != 1 || h.K > 8 || Co % 32 != 0 ||
+        (Ci != 64 && Ci != 128) || d.t_max_windows > kSpecMaxWin || d.t_min_windows < 1)
+        return 0;
+    const char* e = std::getenv("DISCO_FUSED_PATH");
+    return e == nullptr || std::strcmp(e, "toeplitz") != 0;
+}
+
+int try_launch_grad_x_spectral(const disco_psi* psi, const void* gy, const void* w, void* gx,
+                               int gx_dtype, int B, int Ci, int Co, hipStream_t st, int* rc) {
+    if (!spectral_grad_x_eligible(psi, DISCO_BF16, DISCO_BF16, Ci, Co, 1) || B <= 0) return 0;
+    const DevPsi& d = psi->dev;
+    const HostPsi& h = psi->host;
+    SpecCall c;
+    c.x = gy;
+    c.nin = h.desc.nlat_out;
+    c.w = w;
+    c.wt = 1;
+    c.win_ptr = d.wint_ptr;
+    c.wins = d.wins_t;
+    c.nwin = h.windows.size();
+    c.max_windows = d.t_max_windows;
+    c.min_windows = d.t_min_windows;
+    c.psih = static_cast<const uint32_t*>(d.spec_psih_t);
+    c.nout = h.desc.nlat_in;
+    c.bias = nullptr;
+    c.y = gx;
+    c.y_dtype = gx_dtype;
+    c.B = B;
+    c.Ci = Co;   // the adjoint's GEMM maps the layer's output channels
+    c.Co = Ci;   // to its input channels
+    return run_spectral_bf16(psi, c, st, rc);
+}
+
+namespace {
+
+int run_spectral_bf16(const disco_psi* psi, const SpecCall& c, hipStream_t st, int* rc) {
+    const DevPsi& d = psi->dev;
+    const HostPsi& h = psi->host;
     const disco_psi_desc& D = h.desc;
+    const void* x = c.x;
+    const void* w = c.w;
+    const int wt = c.wt;
+    const float* bias = c.bias;
+    void* y = c.y;
+    const int y_dtype = c.y_dtype, B = c.B, Ci = c.Ci, Co = c.Co;
+    const int nlat_in = c.nin, nlat_out = c.nout;
     const int N = D.nlon_in, H = N / 2, MP = d.spec_mp, K = h.K;
     SpecPlan pl;
     pl.n = d.spec_nrad;
     for (int i = 0; i < kSpecMaxRadix; ++i) pl.r[i] = d.spec_radix[i];
 
     auto up = [](size_t v) { return (v + 255) / 256 * 256; };
-    const size_t xh_bytes = up((size_t)B * Ci * D.nlat_in * MP * 4);
-    const size_t yh_bytes = up((size_t)B * Co * D.nlat_out * MP * 4);
+    const size_t xh_bytes = up((size_t)B * Ci * nlat_in * MP * 4);
+    const size_t yh_bytes = up((size_t)B * Co * nlat_out * MP * 4);
     const size_t wp_bytes = up((size_t)Co * Ci * 8 * 2);
     // the handle's workspace; stream-ordered memory while a graph is captured
     WorkspaceLease lease(psi, xh_bytes + yh_bytes + wp_bytes, st);
@@ -1187,7 +1295,7 @@ int try_launch_fused_spectral(const disco_psi* psi, const void* x, const void* w
     uint32_t* xh = static_cast<uint32_t*>(ws);
     bf16_t* yh = reinterpret_cast<bf16_t*>(static_cast<char*>(ws) + xh_bytes);
     bf16_t* wpd = reinterpret_cast<bf16_t*>(static_cast<char*>(ws) + xh_bytes + yh_bytes);
-    const uint32_t* psih = static_cast<const uint32_t*>(d.spec_psih);
+    const uint32_t* psih = c.psih;
 
     int dev = 0, ncu = 256;
     if (hipGetDevice(&dev) == hipSuccess)
@@ -1204,10 +1312,10 @@ int try_launch_fused_spectral(const disco_psi* psi, const void* x, const void* w
     if (!reg) {
         KernelTimer timer("spec_prep_w", st);
         hipLaunchKernelGGL(spec_prep_w, dim3((unsigned)((nwp + 255) / 256)), dim3(256), 0, st,
-                           static_cast<const bf16_t*>(w), wpd, Co, Ci, K);
+                           static_cast<const bf16_t*>(w), wpd, Co, Ci, K, wt);
     }
     const size_t fft_lds = (size_t)(kFftRows + 1) * H * sizeof(float2);
-    const int64_t xrows = (int64_t)B * Ci * D.nlat_in;
+    const int64_t xrows = (int64_t)B * Ci * nlat_in;
     const uint32_t* x32 = static_cast<const uint32_t*>(x);
     // the register transforms' launch also writes the weight fragments
     const int nprep = (int)((nwp + kPrepPerWg - 1) / kPrepPerWg);
@@ -1215,7 +1323,7 @@ int try_launch_fused_spectral(const disco_psi* psi, const void* x, const void* w
     hipLaunchKernelGGL((spec_rfft_reg<H1, H2, RW>),                                            \
                        dim3((unsigned)(nprep + (xrows + RW - 1) / RW)),                        \
                        dim3(kRegThreads), 0, st, x32, xh, xrows,                               \
-                       static_cast<const bf16_t*>(w), wpd, Co, Ci, K, nprep)
+                       static_cast<const bf16_t*>(w), wpd, Co, Ci, K, nprep, wt)
     {
     KernelTimer timer("spec_rfft", st);
     if (reg && H == 720) {
@@ -1233,7 +1341,7 @@ int try_launch_fused_spectral(const disco_psi* psi, const void* x, const void* w
 #undef DISCO_RF
     // bands of output rows, one per XCD; GX workgroups per band, at most the
     // smallest band's item count
-    const int64_t nrows_all = (int64_t)B * D.nlat_out;
+    const int64_t nrows_all = (int64_t)B * nlat_out;
     const int NX = (int)std::min<int64_t>(kXcds, nrows_all);
     const int64_t min_items = nrows_all / NX * (MP / kMt);
     // window capacity: 8 (two workgroups per compute unit) or 16 (one).
@@ -1241,18 +1349,18 @@ int try_launch_fused_spectral(const disco_psi* psi, const void* x, const void* w
     // (each item visited once per half of its windows, both accumulated
     // before y_hat is stored) when every row has at least two windows.
     const char* eh = std::getenv("DISCO_SPEC_HALVES");
-    const bool halves = d.max_windows > 8 && d.min_windows >= 2 && !(eh && eh[0] == '0');
-    const int NWC = d.max_windows <= 8 || halves ? 8 : 16;
+    const bool halves = c.max_windows > 8 && c.min_windows >= 2 && !(eh && eh[0] == '0');
+    const int NWC = c.max_windows <= 8 || halves ? 8 : 16;
     const int NPART = halves ? 2 : 1;
-    const int nwmax = halves ? (d.max_windows + 1) / 2 : d.max_windows;
+    const int nwmax = halves ? (c.max_windows + 1) / 2 : c.max_windows;
     const int per_cu = NWC == 8 ? 2 : 1;
     const int GX =
         (int)std::max<int64_t>(1, std::min<int64_t>(min_items, per_cu * (int64_t)ncu / NX));
     dim3 grid((unsigned)(NX * GX));
 #define DISCO_SM(CC, KK, NWT)                                                                \
     hipLaunchKernelGGL((spec_mfma<CC, KK, NWT>), grid, dim3(kSpecThreads), 0, st, xh, wpd,   \
-                       psih, d.win_ptr, d.windows, yh, B, Ci, D.nlat_in, D.nlat_out, MP, NX, \
-                       (int64_t)h.windows.size() * K * MP, nwmax, NPART)
+                       psih, c.win_ptr, c.wins, yh, B, Ci, nlat_in, nlat_out, MP, NX,           \
+                       (int64_t)c.nwin * K * MP, nwmax, NPART)
 #define DISCO_SM_K(CC, NWT)                                                                  \
     switch (K) {                                                                             \
         case 1: DISCO_SM(CC, 1, NWT); break;                                                 \
@@ -1282,14 +1390,14 @@ int try_launch_fused_spectral(const disco_psi* psi, const void* x, const void* w
     }
 #undef DISCO_SM_K
 #undef DISCO_SM
-    const int64_t yrows = (int64_t)B * Co * D.nlat_out;
+    const int64_t yrows = (int64_t)B * Co * nlat_out;
     const dim3 igrid((unsigned)((yrows + kFftRows - 1) / kFftRows));
     const uint32_t* yh32 = reinterpret_cast<const uint32_t*>(yh);
 #define DISCO_IR(H1, H2, RW, TY, FD)                                                           \
     hipLaunchKernelGGL((spec_irfft_reg<H1, H2, RW, TY, FD>),                                   \
                        reg_grid(yrows, RW),                                                    \
                        dim3(kRegThreads), 0, st, yh32, static_cast<TY*>(y), bias, Co,          \
-                       D.nlat_out, yrows, MP)
+                       nlat_out, yrows, MP)
 #define DISCO_IR_T(H1, H2, RW, FD)             \
     if (y_dtype == DISCO_F32) {                \
         DISCO_IR(H1, H2, RW, float, FD);       \
@@ -1311,11 +1419,11 @@ int try_launch_fused_spectral(const disco_psi* psi, const void* x, const void* w
     } else if (y_dtype == DISCO_F32)
         hipLaunchKernelGGL((spec_irfft<uint32_t, float>), igrid, dim3(kFftThreads), fft_lds, st,
                            reinterpret_cast<const uint32_t*>(yh), static_cast<float*>(y), bias, N,
-                           MP, Co, D.nlat_out, yrows, pl);
+                           MP, Co, nlat_out, yrows, pl);
     else
         hipLaunchKernelGGL((spec_irfft<uint32_t, bf16_t>), igrid, dim3(kFftThreads), fft_lds, st,
                            reinterpret_cast<const uint32_t*>(yh), static_cast<bf16_t*>(y), bias, N,
-                           MP, Co, D.nlat_out, yrows, pl);
+                           MP, Co, nlat_out, yrows, pl);
     }
 #undef DISCO_IR_T
 #undef DISCO_IR
@@ -1333,6 +1441,8 @@ int try_launch_fused_spectral(const disco_psi* psi, const void* x, const void* w
     *rc = DISCO_OK;
     return 1;
 }
+
+}  // namespace
 
 }  // namespace disco
 

@@ -152,6 +152,49 @@ def test_fused_backward(sdc, wl):
     assert torch.equal(gw3, gw)
 
 
+# stride-1 bf16 layers with a bf16 gradient: grad_x takes the longitude-
+# spectral kernels (the adjoint of each window's circular correlation is a
+# circular convolution: Psi_hat instead of its conjugate, the transposed
+# window lists, the weights read transposed), held to the bf16 bar; grad_w
+# keeps the exact float32 path
+SPECTRAL_BWD = [
+    W("spec_c4_like", 1, 64, 64, 1, 61, 120, 61, 120, (3, 3), 4 * math.pi / 60, "bf16"),
+    W("spec_n720_co32_b2", 2, 128, 32, 1, 11, 720, 11, 720, (3,), 0.6, "bf16"),
+    W("spec_lat_up", 1, 64, 96, 1, 21, 96, 41, 96, (3, 3), 0.5, "bf16"),
+]
+
+
+@pytest.mark.parametrize("wl", SPECTRAL_BWD, ids=[c.name for c in SPECTRAL_BWD])
+def test_fused_backward_spectral_grad_x(sdc, wl):
+    _say("spectral grad_x", wl.name)
+    x, w, gy = _inputs(wl)
+    gy = round_bf16(gy)
+    d = _desc(wl)
+    gx_ref, gw_ref = oracle.backward(d, x, w, gy, wl.groups)
+    psi = _psi(sdc, wl)
+    gyd = _dev(gy, "bf16")
+    sdc.kernel_timing(True)
+    try:
+        gx, gw, _ = sdc.fused_bwd(psi, _dev(x, "bf16"), _dev(w, "bf16"), gyd)
+        ran = set(sdc.kernel_timing_read())
+    finally:
+        sdc.kernel_timing(False)
+    assert "spec_mfma" in ran and "contract_transpose" not in ran, ran
+    gx = gx.cpu().numpy()
+    e_x = rel_l2(gx, gx_ref)
+    e_w = rel_l2(gw.cpu().numpy(), gw_ref)
+    # per input row, so that an error confined to a few rows shows
+    rows = [float(np.linalg.norm(gx[:, :, i] - gx_ref[:, :, i]) /
+                  max(np.linalg.norm(gx_ref[:, :, i]), 1e-300)) for i in range(wl.nlat_in)]
+    _say(f"  gx {e_x:.3e} (worst row {max(rows):.3e}) gw {e_w:.3e}")
+    assert e_x <= 2e-2 and max(rows) <= 3e-2
+    assert e_w <= TOL
+    # a float32 gradient keeps the float32 path (exact to the float32 bar)
+    gx32, _, _ = sdc.fused_bwd(psi, _dev(x, "bf16"), _dev(w, "bf16"), torch.from_numpy(gy).cuda(),
+                               need_gw=False)
+    assert rel_l2(gx32.cpu().numpy(), gx_ref) <= TOL
+
+
 def test_fused_backward_slabs_and_full_ring_windows(sdc):
     # 181 x 360 at 64 channels, K = 7: the two slab tensors of the whole layer
     # take more than 64 MiB, so X_K is recomputed in 8 slabs of 23 rows; the

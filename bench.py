@@ -39,6 +39,8 @@ the support it evaluates).  It runs before the GPU is touched.
 matrix-core rate and LDS read rate from hand-written micro-benchmarks
 (libdisco_probe.so), beside the published peaks the roofline divides by.
 `cold_ms` is the fused call after a 1 GiB write has flushed the caches.
+`bwd_ms` / `bwd_grad_x_ms` time disco_fused_bwd (gradient in the layer's
+dtype) for gx and gw, and for gx alone.
 
 Warm-up: after idling, the GPU runs the first 30-40 back-to-back calls at
 lower clocks (at 721x1440, 128 channels: 0.78-0.95 ms per call, settling to
@@ -538,6 +540,21 @@ def main():
                                          "frac": round(gbps / HBM_PEAK_GBS, 4),
                                          "traffic": measured_traffic(key, name, args.grid)}
         del xk
+    if not args.no_unfused and not args.fused_only:
+        # the fused backward (gradient in the layer's dtype): gx and gw, and
+        # gx alone
+        gy = torch.randn((wl.B, wl.Co, wl.nlat_out, wl.nlon_out), device="cuda").to(tdt)
+        bwd = lambda: sdc.fused_bwd(psi, xd, wd, gy, groups=wl.groups)
+        bwd_x = lambda: sdc.fused_bwd(psi, xd, wd, gy, groups=wl.groups, need_gw=False)
+        for _ in range(2):
+            bwd()
+            bwd_x()
+        n = 5
+        _, t_b = time_region(bwd, n, torch)
+        _, t_bx = time_region(bwd_x, n, torch)
+        extra["bwd_ms"] = round(t_b / n * 1000, 3)
+        extra["bwd_grad_x_ms"] = round(t_bx / n * 1000, 3)
+        del gy
     if not args.fused_only and not args.no_peaks:
         extra["measured_peaks"] = measure_peaks()
     line = {

@@ -244,7 +244,15 @@ int disco_einsum_grad_w(const void* xk, int xk_dtype, const void* gy, int gy_dty
  * each overwritten; a NULL pointer skips that gradient (not all three).
  * X_K is recomputed in float32, in slabs of at most ceil(nlat_out / 8)
  * output rows (one slab when the layer's two slab tensors take at most
- * 64 MiB), so neither K-expanded tensor is ever held whole. */
+ * 64 MiB), so neither K-expanded tensor is ever held whole.
+ * Stride-1 layers with bf16 x, w and gy, groups == 1, Ci 64 or 128 and Co a
+ * multiple of 32 take gx on the longitude-spectral kernels instead: the
+ * adjoint of each window's circular correlation is a circular convolution,
+ * so gx = irfft(sum over output rows and k of Psi_hat * sum_co w * rfft(gy)),
+ * with bf16 spectra and float32 accumulation (the bf16 bar, not float32
+ * exactness); DISCO_FUSED_PATH=toeplitz selects the float32 path for them.
+ * Layers with one input channel per group take gx with the weights folded
+ * into the taps (gy contracted directly, no grad_xk), in float32. */
 int disco_fused_bwd(const disco_psi* psi, const void* x, int x_dtype, const void* w, int w_dtype,
                     const void* gy, int gy_dtype, void* gx, int gx_dtype, float* gw, float* gbias,
                     int32_t B, int32_t Ci, int32_t Co, int32_t groups, void* stream);

@@ -107,6 +107,77 @@ __global__ __launch_bounds__(kThreads) void contract_t_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Adjoint in x for one input channel per group (m = Co/groups output channels
+// per group): the weights fold into the taps, as in the forward's depthwise
+// kernel, so gy is contracted directly without grad_xk:
+//   gx[b, g, i, n] = sum_{co in g} sum_{windows (j, i)} sum_t
+//                    (sum_k w[co, 0, k] Psi[k, j, (i, p_lo + t)]) gy[b, co, j, q]
+// with the (n, t) -> q rule of contract_t_kernel.  One workgroup per (input
+// row i, group g, batch b); per window and output channel the gy row and the
+// folded taps are staged in LDS, so the inner loop is one LDS read and one
+// multiply-add per tap (K of each in the unfolded form).
+// ---------------------------------------------------------------------------
+template <typename TG, typename TW, typename TO, int QR>
+__global__ __launch_bounds__(kThreads) void contract_t_folded_kernel(
+    const TG* __restrict__ gy, const TW* __restrict__ w, TO* __restrict__ gx,
+    const int32_t* __restrict__ wt_ptr, const DevWindow* __restrict__ wt,
+    const float* __restrict__ vals, int Co, int groups, int K, int KP, int nlat_in, int nlon_in,
+    int nlat_out, int nlon_out, int s) {
+    extern __shared__ float smem[];
+    float* G = smem;                  // [nlon_out]: the gy row
+    float* wk = smem + nlon_out;      // [K]: the output channel's weights
+    float* f = wk + K;                // [width]: the folded taps
+    const int i = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x;
+    const int m = Co / groups;
+    const int w0 = wt_ptr[i], w1 = wt_ptr[i + 1];
+    TO* out = gx + (((size_t)b * groups + g) * nlat_in + i) * nlon_in;
+    for (int n0 = 0; n0 < nlon_in; n0 += kThreads * QR) {
+        float acc[QR];
+#pragma unroll
+        for (int r = 0; r < QR; ++r) acc[r] = 0.0f;
+        for (int cm = 0; cm < m; ++cm) {
+            const int co = g * m + cm;
+            for (int wi = w0; wi < w1; ++wi) {
+                const DevWindow wd = wt[wi];   // wd.lat is the output row j
+                const TG* grow = gy + (((size_t)b * Co + co) * nlat_out + wd.lat) * nlon_out;
+                __syncthreads();   // the previous window's row and taps are used
+                for (int u = tid; u < nlon_out; u += kThreads) G[u] = load_f(grow, u);
+                if (tid < K) wk[tid] = load_f(w, (size_t)co * K + tid);
+                __syncthreads();
+                const float* v = vals + (size_t)wd.val_off * KP;
+                for (int t = tid; t < wd.width; t += kThreads) {
+                    float a = 0.0f;
+                    for (int k = 0; k < K; ++k) a = fmaf(wk[k], v[(size_t)t * KP + k], a);
+                    f[t] = a;
+                }
+                __syncthreads();
+#pragma unroll
+                for (int r = 0; r < QR; ++r) {
+                    const int n = n0 + tid + kThreads * r;
+                    if (n >= nlon_in) continue;
+                    int d0 = (n - wd.p_lo) % nlon_in;
+                    if (d0 < 0) d0 += nlon_in;
+                    const int ts = d0 % s;
+                    int q = (d0 - ts) / s;
+                    float a = 0.0f;
+                    for (int t = ts; t < wd.width; t += s) {
+                        a = fmaf(f[t], G[q], a);
+                        if (--q < 0) q += nlon_out;
+                    }
+                    acc[r] += a;
+                }
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < QR; ++r) {
+            const int n = n0 + tid + kThreads * r;
+            if (n < nlon_in) store_f(out, n, acc[r]);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // grad_w partial sums: a 64 x 64 tile of [co in group][kappa = (ci', k)]
 // summed over one chunk of L output points (r, q) of one batch entry,
 // staged 16 points at a time through LDS; thread = 4 x 4 outputs.
@@ -450,6 +521,54 @@ int launch_fill_zero(float* p, size_t n, void* stream) {
 int launch_contract_rows(const disco_psi* psi, const void* x, int x_dtype, float* xk, int B, int C,
                          int row0, int nrows, hipStream_t st);
 
+// The folded adjoint in x over the whole layer (one input channel per group).
+template <typename TG, typename TW, typename TO>
+int contract_t_folded_t(const disco_psi* psi, const void* gy, const void* w, void* gx, int B,
+                        int Co, int groups, hipStream_t st) {
+    const HostPsi& h = psi->host;
+    const DevPsi& d = psi->dev;
+    const disco_psi_desc& D = h.desc;
+    const size_t lds = ((size_t)D.nlon_out + h.K + d.max_width) * sizeof(float);
+    if (lds > 64 * 1024)
+        return set_error(DISCO_EUNSUPPORTED, "rows too long for the folded transposed contraction");
+    const int q0 = pick_qr_t(D.nlon_in);
+    const int QR = q0 <= 1 ? 1 : q0 <= 2 ? 2 : q0 <= 4 ? 4 : 8;
+    dim3 grid(D.nlat_in, groups, B);
+#define DISCO_CTF(Q)                                                                          \
+    hipLaunchKernelGGL((contract_t_folded_kernel<TG, TW, TO, Q>), grid, dim3(kThreads), lds, st, \
+                       (const TG*)gy, (const TW*)w, (TO*)gx, d.wint_ptr, d.wins_t, d.vals, Co,  \
+                       groups, h.K, d.KP, D.nlat_in, D.nlon_in, D.nlat_out, D.nlon_out, h.stride)
+    KernelTimer timer("contract_transpose_folded", st);
+    switch (QR) {
+        case 1: DISCO_CTF(1); break;
+        case 2: DISCO_CTF(2); break;
+        case 4: DISCO_CTF(4); break;
+        default: DISCO_CTF(8); break;
+    }
+#undef DISCO_CTF
+    return check("contract_transpose_folded");
+}
+
+template <typename TG, typename TW>
+int contract_t_folded_o(const disco_psi* psi, const void* gy, const void* w, void* gx,
+                        int gx_dtype, int B, int Co, int groups, hipStream_t st) {
+    return gx_dtype == DISCO_F32
+               ? contract_t_folded_t<TG, TW, float>(psi, gy, w, gx, B, Co, groups, st)
+               : contract_t_folded_t<TG, TW, bf16_t>(psi, gy, w, gx, B, Co, groups, st);
+}
+
+int contract_t_folded(const disco_psi* psi, const void* gy, int gy_dtype, const void* w,
+                      int w_dtype, void* gx, int gx_dtype, int B, int Co, int groups,
+                      hipStream_t st) {
+    if (gy_dtype == DISCO_F32)
+        return w_dtype == DISCO_F32
+                   ? contract_t_folded_o<float, float>(psi, gy, w, gx, gx_dtype, B, Co, groups, st)
+                   : contract_t_folded_o<float, bf16_t>(psi, gy, w, gx, gx_dtype, B, Co, groups, st);
+    return w_dtype == DISCO_F32
+               ? contract_t_folded_o<bf16_t, float>(psi, gy, w, gx, gx_dtype, B, Co, groups, st)
+               : contract_t_folded_o<bf16_t, bf16_t>(psi, gy, w, gx, gx_dtype, B, Co, groups, st);
+}
+
 int launch_contract_transpose(const disco_psi* psi, const void* gxk, int gxk_dtype, void* gx,
                               int gx_dtype, int B, int C, void* stream) {
     return contract_t_any(psi, gxk, gxk_dtype, gx, gx_dtype, B, C, 0, psi->host.desc.nlat_out, 0,
@@ -517,6 +636,14 @@ int launch_fused_bwd(const disco_psi* psi, const void* x, int x_dtype, const voi
         }
     }
     const int K = h.K, cig = Ci / groups, cog = Co / groups;
+    // one input channel per group: grad_x with the weights folded into the
+    // taps, over the whole layer (no grad_xk)
+    if (gx && cig == 1 && B > 0) {
+        const int frc = contract_t_folded(psi, gy, gy_dtype, w, w_dtype, gx, gx_dtype, B, Co,
+                                          groups, st);
+        if (frc != DISCO_OK) return frc;
+        gx = nullptr;
+    }
     const size_t row_bytes = (size_t)B * Ci * K * D.nlon_out * sizeof(float);
     int rows = D.nlat_out;
     if ((size_t)2 * row_bytes * D.nlat_out > ((size_t)64 << 20)) rows = (D.nlat_out + 7) / 8;

@@ -245,10 +245,12 @@ int disco_einsum_grad_w(const void* xk, int xk_dtype, const void* gy, int gy_dty
  * X_K is recomputed in float32, in slabs of at most ceil(nlat_out / 8)
  * output rows (one slab when the layer's two slab tensors take at most
  * 64 MiB), so neither K-expanded tensor is ever held whole.
- * Stride-1 layers with bf16 x, w and gy, groups == 1, Ci 64 or 128 and Co a
- * multiple of 32 take gx on the longitude-spectral kernels instead: the
- * adjoint of each window's circular correlation is a circular convolution,
- * so gx = irfft(sum over output rows and k of Psi_hat * sum_co w * rfft(gy)),
+ * Layers on the longitude-spectral path's tables (stride 1, or stride 2 at
+ * 720 or 1440 input longitudes) with bf16 x, w and gy, groups == 1, Ci 64 or
+ * 128 and Co a multiple of 32 take gx on the longitude-spectral kernels
+ * instead: the adjoint of each window's circular correlation is a circular
+ * convolution, so gx = irfft(sum over output rows and k of Psi_hat * sum_co
+ * w * rfft(gy)) (at stride 2 gy with a zero inserted after each sample),
  * with bf16 spectra and float32 accumulation (the bf16 bar, not float32
  * exactness); DISCO_FUSED_PATH=toeplitz selects the float32 path for them.
  * Layers with one input channel per group take gx with the weights folded

@@ -355,7 +355,7 @@ int disco_psi_to_device(disco_psi* psi) {
         d.spec_psih = p;
         if ((rc = dev_copy(p, spec_psih.data(), spec_psih.size() * sizeof(uint32_t))) != DISCO_OK)
             goto fail;
-        if (h.stride == 1) {
+        if (h.stride == 1 || h.stride == 2) {
             // the adjoint's table: windows in the transposed order, each
             // Psi_hat conjugated (the matrix-core kernel multiplies by the
             // conjugate of its table, and the adjoint of the correlation is

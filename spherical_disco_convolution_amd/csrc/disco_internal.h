@@ -103,7 +103,7 @@ struct DevPsi {
     // longitude-spectral tables for the spectral fused path (stride 1)
     void* spec_psih = nullptr;    // bf16 (re, im) words [nwin][K][spec_mp]
     float* spec_psih32 = nullptr; // float32 (re, im) pairs [nwin][K][spec_mp], or none
-    void* spec_psih_t = nullptr;  // stride 1: conj(Psi_hat) in the transposed window order
+    void* spec_psih_t = nullptr;  // conj(Psi_hat) in the transposed window order (the adjoint)
     int32_t spec_mp = 0;          // padded frequency count; 0 = no tables
     int32_t spec_radix[kSpecMaxRadix] = {0};
     int32_t spec_nrad = 0;
@@ -151,9 +151,10 @@ int launch_fused_noalloc(const disco_psi* psi, const void* x, int dtype, const v
                          int groups, void* stream);
 // 1 if disco_fused_fwd takes the longitude-spectral path for these arguments
 int fused_spectral_eligible(const disco_psi* psi, int x_dtype, int Ci, int Co, int groups);
-// The adjoint in x on the longitude-spectral kernels (stride-1 layers, bf16
-// x, w and gy): 1 if it applies; the launcher returns 0 when it does not (rc
-// untouched), else 1 with *rc the result.
+// The adjoint in x on the longitude-spectral kernels (stride-1 and stride-2
+// layers with spectral tables, bf16 x, w and gy): 1 if it applies; the
+// launcher returns 0 when it does not (rc untouched), else 1 with *rc the
+// result.
 int spectral_grad_x_eligible(const disco_psi* psi, int x_dtype, int gy_dtype, int Ci, int Co,
                              int groups);
 int try_launch_grad_x_spectral(const disco_psi* psi, const void* gy, const void* w, void* gx,

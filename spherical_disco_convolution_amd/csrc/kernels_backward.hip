@@ -625,8 +625,9 @@ int launch_fused_bwd(const disco_psi* psi, const void* x, int x_dtype, const voi
     hipStream_t st = static_cast<hipStream_t>(stream);
     const HostPsi& h = psi->host;
     const disco_psi_desc& D = h.desc;
-    // stride-1 bf16 layers with a bf16 gradient: grad_x on the spectral
-    // kernels (the convolution adjoint of each window's correlation), whole
+    // bf16 layers with spectral tables and a bf16 gradient: grad_x on the
+    // spectral kernels (the convolution adjoint of each window's
+    // correlation), whole
     if (gx && x_dtype == DISCO_BF16 && w_dtype == DISCO_BF16 &&
         spectral_grad_x_eligible(psi, x_dtype, gy_dtype, Ci, Co, groups)) {
         int src = DISCO_OK;

@@ -559,6 +559,15 @@ __global__ __launch_bounds__(kRegThreads) void spec_irfft_reg(const uint32_t* __
     }
 }
 
+// bf16 samples -> 32-bit words (sample, 0): rows of n samples become rows of
+// 2 n samples with a zero after each (the adjoint of keeping every second
+// longitude)
+__global__ void spec_zero_insert(const bf16_t* __restrict__ in, uint32_t* __restrict__ out,
+                                 size_t n) {
+    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) out[i] = (uint32_t)__builtin_bit_cast(uint16_t, in[i]);
+}
+
 // the weight fragments alone (for the Stockham transforms' launches)
 __global__ void spec_prep_w(const bf16_t* __restrict__ w, bf16_t* __restrict__ wp, int Co, int Ci,
                             int K, int wt) {
@@ -1178,6 +1187,8 @@ struct SpecCall {
     void* y;
     int y_dtype;
     int B, Ci, Co;
+    int fold;       // longitude stride of the output (1, or 2: folded inverse)
+    int upsample;   // x rows hold nlon_in / 2 samples: zero-inserted to nlon_in first
 };
 
 int run_spectral_bf16(const disco_psi* psi, const SpecCall& c, hipStream_t st, int* rc);
@@ -1208,17 +1219,21 @@ int try_launch_fused_spectral(const disco_psi* psi, const void* x, const void* w
     c.B = B;
     c.Ci = Ci;
     c.Co = Co;
+    c.fold = h.stride;
+    c.upsample = 0;
     return run_spectral_bf16(psi, c, st, rc);
 }
 
-// The adjoint in x of the fused forward, for stride-1 bf16 layers with bf16
-// gradients: gx = irfft(sum over output rows j and k of Psi_hat[k, j, i, m]
-// sum_co w[co, ci, k] gy_hat[co, j, m]), on the forward's kernels.
+// The adjoint in x of the fused forward, for bf16 layers with bf16 gradients
+// at stride 1 or 2 (the layers with spectral tables): gx = irfft(sum over
+// output rows j and k of Psi_hat[k, j, i, m] sum_co w[co, ci, k]
+// gy_hat[co, j, m]), on the forward's kernels; at stride 2 gy_hat is the
+// spectrum of gy with zeros inserted between its samples.
 int spectral_grad_x_eligible(const disco_psi* psi, int x_dtype, int gy_dtype, int Ci, int Co,
                              int groups) {
     const DevPsi& d = psi->dev;
     const HostPsi& h = psi->host;
-    if (d.spec_psih_t == nullptr || h.stride != 1 || x_dtype != DISCO_BF16 ||
+    if (d.spec_psih_t == nullptr || (h.stride != 1 && h.stride != 2) || x_dtype != DISCO_BF16 ||
         gy_dtype != DISCO_BF16 || groups != 1 || h.K > 8 || Co % 32 != 0 ||
         (Ci != 64 && Ci != 128) || d.t_max_windows > kSpecMaxWin || d.t_min_windows < 1)
         return 0;
@@ -1249,6 +1264,10 @@ int try_launch_grad_x_spectral(const disco_psi* psi, const void* gy, const void*
     c.B = B;
     c.Ci = Co;   // the adjoint's GEMM maps the layer's output channels
     c.Co = Ci;   // to its input channels
+    // stride 2: the adjoint of keeping every second longitude inserts zeros
+    // between gy's samples, after which it is the stride-1 adjoint
+    c.fold = 1;
+    c.upsample = h.stride == 2;
     return run_spectral_bf16(psi, c, st, rc);
 }
 
@@ -1258,7 +1277,7 @@ int run_spectral_bf16(const disco_psi* psi, const SpecCall& c, hipStream_t st, i
     const DevPsi& d = psi->dev;
     const HostPsi& h = psi->host;
     const disco_psi_desc& D = h.desc;
-    const void* x = c.x;
+    const void* x = c.x;   // replaced by the zero-inserted rows (upsample)
     const void* w = c.w;
     const int wt = c.wt;
     const float* bias = c.bias;
@@ -1274,8 +1293,11 @@ int run_spectral_bf16(const disco_psi* psi, const SpecCall& c, hipStream_t st, i
     const size_t xh_bytes = up((size_t)B * Ci * nlat_in * MP * 4);
     const size_t yh_bytes = up((size_t)B * Co * nlat_out * MP * 4);
     const size_t wp_bytes = up((size_t)Co * Ci * 8 * 2);
+    // zero-inserted rows (upsample): B Ci nlat_in rows of N bf16
+    const size_t xu_bytes = c.upsample ? up((size_t)B * Ci * nlat_in * N * 2) : 0;
+    const size_t ws_bytes = xh_bytes + yh_bytes + wp_bytes + xu_bytes;
     // the handle's workspace; stream-ordered memory while a graph is captured
-    WorkspaceLease lease(psi, xh_bytes + yh_bytes + wp_bytes, st);
+    WorkspaceLease lease(psi, ws_bytes, st);
     if (lease.error() != DISCO_OK) {
         *rc = lease.error();
         return 1;
@@ -1283,7 +1305,7 @@ int run_spectral_bf16(const disco_psi* psi, const SpecCall& c, hipStream_t st, i
     void* ws = lease.ptr();
     const bool own_ws = ws == nullptr;
     if (own_ws) {
-        hipError_t e = hipMallocAsync(&ws, xh_bytes + yh_bytes + wp_bytes, st);
+        hipError_t e = hipMallocAsync(&ws, ws_bytes, st);
         if (e != hipSuccess) {
             (void)hipGetLastError();
             *rc = set_error(e == hipErrorOutOfMemory ? DISCO_ENOMEM : DISCO_EHIP,
@@ -1296,6 +1318,16 @@ int run_spectral_bf16(const disco_psi* psi, const SpecCall& c, hipStream_t st, i
     bf16_t* yh = reinterpret_cast<bf16_t*>(static_cast<char*>(ws) + xh_bytes);
     bf16_t* wpd = reinterpret_cast<bf16_t*>(static_cast<char*>(ws) + xh_bytes + yh_bytes);
     const uint32_t* psih = c.psih;
+    if (c.upsample) {
+        // word n of an upsampled row is the bf16 pair (gy[n], 0)
+        uint32_t* xu = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + xh_bytes + yh_bytes +
+                                                   wp_bytes);
+        const size_t nw = (size_t)B * Ci * nlat_in * (N / 2);
+        KernelTimer timer("spec_zero_insert", st);
+        hipLaunchKernelGGL(spec_zero_insert, dim3((unsigned)((nw + 255) / 256)), dim3(256), 0, st,
+                           static_cast<const bf16_t*>(x), xu, nw);
+        x = xu;
+    }
 
     int dev = 0, ncu = 256;
     if (hipGetDevice(&dev) == hipSuccess)
@@ -1304,7 +1336,7 @@ int run_spectral_bf16(const disco_psi* psi, const SpecCall& c, hipStream_t st, i
     // the register-resident transforms cover these half lengths (their MP is
     // the table's)
     const bool reg = (H == 720 || H == 360 || H == 180) && MP == spec_mp_of(H);
-    const int S = h.stride;   // 1, or 2 with register transforms on both sides (eligibility)
+    const int S = c.fold;   // 1, or 2 with register transforms on both sides (eligibility)
     // one-wave workgroups, one group of rw rows each
     auto reg_grid = [](int64_t rows, int rw) { return dim3((unsigned)((rows + rw - 1) / rw)); };
 

@@ -152,15 +152,19 @@ def test_fused_backward(sdc, wl):
     assert torch.equal(gw3, gw)
 
 
-# stride-1 bf16 layers with a bf16 gradient: grad_x takes the longitude-
-# spectral kernels (the adjoint of each window's circular correlation is a
-# circular convolution: Psi_hat instead of its conjugate, the transposed
-# window lists, the weights read transposed), held to the bf16 bar; grad_w
-# keeps the exact float32 path
+# bf16 layers with spectral tables (stride 1, or 2 at 720 / 1440 longitudes)
+# and a bf16 gradient: grad_x takes the longitude-spectral kernels (the
+# adjoint of each window's circular correlation is a circular convolution:
+# Psi_hat instead of its conjugate, the transposed window lists, the weights
+# read transposed), held to the bf16 bar; grad_w keeps the exact float32 path
 SPECTRAL_BWD = [
     W("spec_c4_like", 1, 64, 64, 1, 61, 120, 61, 120, (3, 3), 4 * math.pi / 60, "bf16"),
     W("spec_n720_co32_b2", 2, 128, 32, 1, 11, 720, 11, 720, (3,), 0.6, "bf16"),
     W("spec_lat_up", 1, 64, 96, 1, 21, 96, 41, 96, (3, 3), 0.5, "bf16"),
+    # stride 2 (zeros inserted between gy's samples, then the stride-1
+    # adjoint): 720 -> 360 and 1440 -> 720 longitudes
+    W("spec_s2_720", 1, 64, 32, 1, 61, 720, 31, 360, (3, 3), 4 * math.pi / 30, "bf16"),
+    W("spec_s2_1440", 1, 64, 32, 1, 25, 1440, 13, 720, (3,), 0.3, "bf16"),
 ]
 
 

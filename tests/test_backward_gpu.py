@@ -286,3 +286,34 @@ def test_full_size_c4_backward_channel_subsets(sdc):
     e_b = rel_l2(gb.cpu().numpy(), gy.astype(np.float64).sum(axis=(0, 2, 3)))
     _say(f"  c4 gx {e_x:.3e} gw {e_w:.3e} gbias {e_b:.3e}")
     assert e_x <= TOL and e_w <= TOL and e_b <= TOL
+
+
+def test_full_size_c4_spectral_grad_x_channel_subsets(sdc):
+    """721x1440, 128 -> 128 channels, K = 7, bf16 inputs and a bf16 gradient:
+    grad_x on the longitude-spectral kernels for the whole layer; the oracle
+    evaluates the adjoint on 3 input channels (bf16 bar, whole and per input
+    row)."""
+    wl = WORKLOADS["c4"]
+    _say("full-size c4 spectral grad_x")
+    x, w, gy = _inputs(wl)
+    gy = round_bf16(gy)
+    d = _desc(wl)
+    csr = oracle.psi(d)
+    psi = _psi(sdc, wl)
+    sdc.kernel_timing(True)
+    try:
+        gx, _, _ = sdc.fused_bwd(psi, _dev(x, "bf16"), _dev(w, "bf16"), _dev(gy, "bf16"),
+                                 need_gw=False)
+        ran = set(sdc.kernel_timing_read())
+    finally:
+        sdc.kernel_timing(False)
+    assert "spec_mfma" in ran and "contract_transpose" not in ran, ran
+    ci_sub = [0, 61, 127]
+    gxk = oracle.einsum_grad_xk(gy, w[:, ci_sub, :], 1)
+    gx_ref = oracle.contract_transpose(d, gxk, csr=csr)
+    got = gx[:, ci_sub].cpu().numpy()
+    e_x = rel_l2(got, gx_ref)
+    rows = [float(np.linalg.norm(got[:, :, i] - gx_ref[:, :, i]) /
+                  max(np.linalg.norm(gx_ref[:, :, i]), 1e-300)) for i in range(wl.nlat_in)]
+    _say(f"  c4 spectral gx {e_x:.3e} (worst row {max(rows):.3e})")
+    assert e_x <= 2e-2 and max(rows) <= 3e-2

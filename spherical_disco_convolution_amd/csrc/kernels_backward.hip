@@ -178,6 +178,97 @@ __global__ __launch_bounds__(kThreads) void contract_t_folded_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// grad_w partial sums on the matrix cores, for a bf16 gy and one group: a
+// 128 x 128 tile of [co][kappa] over one chunk of points; four waves of
+// 64 x 64, each 2 x 2 v_mfma_f32_32x32x16_bf16 per 16 points.  The operands
+// load straight from memory along the point axis (lane l: row l % 32 of its
+// tile, points 8 (l / 32) .. + 7 of the step: 16 bytes of gy, 32 bytes of a
+// float32 X_K rounded to bf16 as it is loaded).  partial[(b nchunk +
+// chunk)][co][kappa], the layout of grad_w_partial.
+// ---------------------------------------------------------------------------
+typedef __bf16 gw_bf16x8 __attribute__((ext_vector_type(8)));
+typedef float gw_floatx16 __attribute__((ext_vector_type(16)));
+constexpr int kGwM = 128;   // tile edge of the matrix-core kernel
+
+__device__ __forceinline__ gw_bf16x8 gw_load8(const bf16_t* p) {
+    return *reinterpret_cast<const gw_bf16x8*>(p);
+}
+__device__ __forceinline__ gw_bf16x8 gw_load8(const float* p) {
+    const float4 a = *reinterpret_cast<const float4*>(p);
+    const float4 b = *reinterpret_cast<const float4*>(p + 4);
+    typedef float f8 __attribute__((ext_vector_type(8)));
+    const f8 v = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    return __builtin_convertvector(v, gw_bf16x8);   // round to nearest even
+}
+
+template <typename TX>
+__global__ __launch_bounds__(kThreads) void grad_w_mfma(
+    const TX* __restrict__ xk, const bf16_t* __restrict__ gy, float* __restrict__ partial, int Co,
+    int kd, int nlat_out, int nlon_out, int row0, int nrows, int L, int nchunk) {
+    const int kt = blockIdx.x, ct = blockIdx.y;
+    const int z = blockIdx.z;
+    const int chunk = z % nchunk, b = z / nchunk;
+    const size_t P = (size_t)nrows * nlon_out;   // points of the slab
+    const size_t n0 = (size_t)chunk * L;
+    const size_t n1 = min(P, n0 + (size_t)L);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int l32 = lane & 31, lg = lane >> 5;
+    const int co0 = ct * kGwM + (wave & 1) * 64, ka0 = kt * kGwM + (wave >> 1) * 64;
+    const bf16_t* gyb = gy + (size_t)b * Co * nlat_out * nlon_out + (size_t)row0 * nlon_out;
+    const TX* xkb = xk + (size_t)b * kd * P;
+    const bf16_t* arow[2];
+    const TX* brow[2];
+    bool aok[2], bok[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int co = co0 + 32 * u + l32, ka = ka0 + 32 * u + l32;
+        aok[u] = co < Co;
+        bok[u] = ka < kd;
+        arow[u] = gyb + (size_t)min(co, Co - 1) * nlat_out * nlon_out;
+        brow[u] = xkb + (size_t)min(ka, kd - 1) * P;
+    }
+    gw_floatx16 acc[2][2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int v = 0; v < 2; ++v)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[u][v][e] = 0.0f;
+    const gw_bf16x8 zero = {};
+    for (size_t nb = n0; nb < n1; nb += 16) {
+        // P, L and the chunk starts are multiples of 8: a lane's 8 points
+        // are all inside the chunk or all past it
+        const size_t p = nb + 8 * lg;
+        const bool pin = p + 8 <= n1;
+        gw_bf16x8 af[2], bf[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            af[u] = aok[u] && pin ? gw_load8(arow[u] + p) : zero;
+            bf[u] = bok[u] && pin ? gw_load8(brow[u] + p) : zero;
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int v = 0; v < 2; ++v)
+                acc[u][v] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[u], bf[v], acc[u][v], 0, 0, 0);
+    }
+    // lane: column kappa = ka0 + 32 v + l32, rows co = co0 + 32 u + 8 (e / 4) + 4 lg + e % 4
+    float* out = partial + (size_t)(b * nchunk + chunk) * Co * kd;
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int v = 0; v < 2; ++v) {
+            const int ka = ka0 + 32 * v + l32;
+            if (ka >= kd) continue;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int co = co0 + 32 * u + 8 * (e >> 2) + 4 * lg + (e & 3);
+                if (co < Co) out[(size_t)co * kd + ka] = acc[u][v][e];
+            }
+        }
+}
+
+// ---------------------------------------------------------------------------
 // grad_w partial sums: a 64 x 64 tile of [co in group][kappa = (ci', k)]
 // summed over one chunk of L output points (r, q) of one batch entry,
 // staged 16 points at a time through LDS; thread = 4 x 4 outputs.
@@ -410,6 +501,23 @@ int contract_t_any(const disco_psi* psi, const void* gxk, int gxk_dtype, void* g
 }
 
 // points per grad_w chunk: enough workgroups to fill the chip at least twice
+// The matrix-core grad_w kernel takes bf16 gy (a bf16 gradient asks for the
+// bf16 bar: X_K is rounded to bf16 as it is loaded), one group, and rows and
+// chunks of whole 16-byte pieces.
+bool grad_w_mfma_ok(int xk_dtype, int gy_dtype, int groups, int nlon_out, int L, const void* gy) {
+    return gy_dtype == DISCO_BF16 && (xk_dtype == DISCO_F32 || xk_dtype == DISCO_BF16) &&
+           groups == 1 && nlon_out % 8 == 0 && L % 16 == 0 &&
+           (reinterpret_cast<uintptr_t>(gy) & 15) == 0;
+}
+
+// output tiles of one group's grad_w for the chunk split: 128 x 128 on the
+// matrix cores, 64 x 64 otherwise
+int grad_w_tiles(int gy_dtype, int groups, int cig, int cog, int K, int nlon_out) {
+    if (gy_dtype == DISCO_BF16 && groups == 1 && nlon_out % 8 == 0)
+        return ((cig * K + kGwM - 1) / kGwM) * ((cog + kGwM - 1) / kGwM);
+    return ((cig * K + kGwT - 1) / kGwT) * ((cog + kGwT - 1) / kGwT);
+}
+
 int grad_w_chunk(size_t P, int tiles, int B, int groups, int ncu) {
     const size_t want = (size_t)2 * ncu;
     size_t per = (size_t)tiles * B * groups;
@@ -436,6 +544,23 @@ int grad_w_slab(const void* xk, int xk_dtype, const void* gy, int gy_dtype, floa
     const int cig = Ci / groups, cog = Co / groups;
     const size_t P = (size_t)nrows * nlon_out;
     const int nchunk = (int)((P + L - 1) / L);
+    if (grad_w_mfma_ok(xk_dtype, gy_dtype, groups, nlon_out, L, gy)) {
+        const int kd = Ci * K;
+        dim3 mgrid((kd + kGwM - 1) / kGwM, (Co + kGwM - 1) / kGwM, (unsigned)(B * nchunk));
+        {
+            KernelTimer timer("grad_w_mfma", st);
+            if (xk_dtype == DISCO_F32)
+                hipLaunchKernelGGL((grad_w_mfma<float>), mgrid, dim3(kThreads), 0, st,
+                                   (const float*)xk, (const bf16_t*)gy, partial, Co, kd, nlat_out,
+                                   nlon_out, row0, nrows, L, nchunk);
+            else
+                hipLaunchKernelGGL((grad_w_mfma<bf16_t>), mgrid, dim3(kThreads), 0, st,
+                                   (const bf16_t*)xk, (const bf16_t*)gy, partial, Co, kd, nlat_out,
+                                   nlon_out, row0, nrows, L, nchunk);
+        }
+        const int rc = check("grad_w_mfma");
+        return rc != DISCO_OK ? rc : B * nchunk;
+    }
     dim3 grid((cig * K + kGwT - 1) / kGwT, (cog + kGwT - 1) / kGwT, (unsigned)(B * groups * nchunk));
 #define DISCO_GW(TX, TG)                                                                          \
     hipLaunchKernelGGL((grad_w_partial<TX, TG>), grid, dim3(kThreads), 0, st, (const TX*)xk,      \
@@ -587,7 +712,7 @@ int launch_einsum_grad_w(const void* xk, int xk_dtype, const void* gy, int gy_dt
                          void* stream) {
     hipStream_t st = static_cast<hipStream_t>(stream);
     const int cig = Ci / groups, cog = Co / groups;
-    const int tiles = ((cig * K + kGwT - 1) / kGwT) * ((cog + kGwT - 1) / kGwT);
+    const int tiles = grad_w_tiles(gy_dtype, groups, cig, cog, K, nlon_out);
     const size_t P = (size_t)nlat_out * nlon_out;
     const int L = grad_w_chunk(P, tiles, B, groups, num_cus());
     const int nparts = B * (int)((P + L - 1) / L);
@@ -649,7 +774,7 @@ int launch_fused_bwd(const disco_psi* psi, const void* x, int x_dtype, const voi
     int rows = D.nlat_out;
     if ((size_t)2 * row_bytes * D.nlat_out > ((size_t)64 << 20)) rows = (D.nlat_out + 7) / 8;
     const int nslab = (D.nlat_out + rows - 1) / rows;
-    const int tiles = ((cig * K + kGwT - 1) / kGwT) * ((cog + kGwT - 1) / kGwT);
+    const int tiles = grad_w_tiles(gy_dtype, groups, cig, cog, K, D.nlon_out);
     const int L = grad_w_chunk((size_t)rows * D.nlon_out, tiles, B, groups, num_cus());
     const int nparts_max = B * (int)(((size_t)rows * D.nlon_out + L - 1) / L);
     const size_t ngw = (size_t)Co * cig * K;

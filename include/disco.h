@@ -232,7 +232,11 @@ int disco_einsum_grad_xk(const void* gy, int gy_dtype, const void* w, int w_dtyp
  *   gw[co,ci',k] = sum_{b,j,q} gy[b,co,j,q] * xk[b, G(co)*Ci/G + ci', k, j, q]
  * xk [B, Ci, K, nlat_out, nlon_out] (the saved intermediate), gy [B, Co,
  * nlat_out, nlon_out]; gw [Co, Ci/groups, K] float32, overwritten (zeros for
- * B = 0).  Partial sums over chunks of points, then one reduction. */
+ * B = 0).  Partial sums over chunks of points, then one reduction.  A bf16
+ * gy with groups == 1 and nlon_out a multiple of 8 takes the partial sums
+ * on the matrix cores, a float32 xk rounded to bf16 as it is read (the
+ * bf16 bar); otherwise they run in float32 on the vector ALUs.  The same
+ * holds for disco_fused_bwd's gw. */
 int disco_einsum_grad_w(const void* xk, int xk_dtype, const void* gy, int gy_dtype, float* gw,
                         int32_t B, int32_t Ci, int32_t Co, int32_t groups, int32_t K,
                         int32_t nlat_out, int32_t nlon_out, void* stream);

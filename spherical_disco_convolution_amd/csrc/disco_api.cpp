@@ -377,6 +377,28 @@ int disco_psi_to_device(disco_psi* psi) {
             d.spec_psih_t = p;
             if ((rc = dev_copy(p, pt.data(), pt.size() * sizeof(uint32_t))) != DISCO_OK) goto fail;
         }
+        if (!spec_psih32.empty() && h.stride == 1) {
+            // the float32 adjoint's table: transposed order, imaginary parts negated
+            const size_t blk = (size_t)h.K * d.spec_mp * 2;
+            std::vector<float> pt;
+            try {
+                pt.assign(spec_psih32.size(), 0.0f);
+            } catch (const std::bad_alloc&) {
+                rc = set_error(DISCO_ENOMEM, "host allocation for the adjoint table failed");
+                goto fail;
+            }
+            for (size_t n = 0; n < wins_t.size(); ++n) {
+                const float* src = spec_psih32.data() + (size_t)orig_t[n] * blk;
+                float* dst = pt.data() + n * blk;
+                for (size_t e = 0; e < blk; e += 2) {
+                    dst[e] = src[e];
+                    dst[e + 1] = -src[e + 1];
+                }
+            }
+            if ((rc = dev_alloc(d, &p, pt.size() * sizeof(float))) != DISCO_OK) goto fail;
+            d.spec_psih32_t = static_cast<float*>(p);
+            if ((rc = dev_copy(p, pt.data(), pt.size() * sizeof(float))) != DISCO_OK) goto fail;
+        }
         if (!spec_psih32.empty()) {
             if ((rc = dev_alloc(d, &p, spec_psih32.size() * sizeof(float))) != DISCO_OK) goto fail;
             d.spec_psih32 = static_cast<float*>(p);

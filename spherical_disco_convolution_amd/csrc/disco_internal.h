@@ -104,6 +104,7 @@ struct DevPsi {
     void* spec_psih = nullptr;    // bf16 (re, im) words [nwin][K][spec_mp]
     float* spec_psih32 = nullptr; // float32 (re, im) pairs [nwin][K][spec_mp], or none
     void* spec_psih_t = nullptr;  // conj(Psi_hat) in the transposed window order (the adjoint)
+    float* spec_psih32_t = nullptr;   // the same for the float32 table
     int32_t spec_mp = 0;          // padded frequency count; 0 = no tables
     int32_t spec_radix[kSpecMaxRadix] = {0};
     int32_t spec_nrad = 0;
@@ -159,6 +160,10 @@ int spectral_grad_x_eligible(const disco_psi* psi, int x_dtype, int gy_dtype, in
                              int groups);
 int try_launch_grad_x_spectral(const disco_psi* psi, const void* gy, const void* w, void* gx,
                                int gx_dtype, int B, int Ci, int Co, hipStream_t st, int* rc);
+// The same for float32 layers (stride 1, float32 x, w and gy), in float32.
+int spectral_grad_x32_eligible(const disco_psi* psi, int Ci, int Co, int groups);
+int try_launch_grad_x_spectral32(const disco_psi* psi, const void* gy, const void* w, void* gx,
+                                 int gx_dtype, int B, int Ci, int Co, hipStream_t st, int* rc);
 
 // Backward (kernels_backward.hip)
 int launch_fill_zero(float* p, size_t n, void* stream);

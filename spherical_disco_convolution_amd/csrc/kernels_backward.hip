@@ -761,6 +761,16 @@ int launch_fused_bwd(const disco_psi* psi, const void* x, int x_dtype, const voi
             gx = nullptr;
         }
     }
+    // float32 stride-1 layers with a float32 gradient: the same on the float32
+    // spectral kernels (float32 spectra: the float32 bar)
+    if (gx && x_dtype == DISCO_F32 && w_dtype == DISCO_F32 && gy_dtype == DISCO_F32 &&
+        spectral_grad_x32_eligible(psi, Ci, Co, groups)) {
+        int src = DISCO_OK;
+        if (try_launch_grad_x_spectral32(psi, gy, w, gx, gx_dtype, B, Ci, Co, st, &src)) {
+            if (src != DISCO_OK) return src;
+            gx = nullptr;
+        }
+    }
     const int K = h.K, cig = Ci / groups, cog = Co / groups;
     // one input channel per group: grad_x with the weights folded into the
     // taps, over the whole layer (no grad_xk)

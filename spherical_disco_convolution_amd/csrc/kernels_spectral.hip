@@ -1028,7 +1028,8 @@ template <int KT, int COR>
 __global__ __launch_bounds__(kSpecThreads) void spec32_conv(
     const float2* __restrict__ xh, const float* __restrict__ w, const float2* __restrict__ psih,
     const int32_t* __restrict__ win_ptr, const DevWindow* __restrict__ wins,
-    float2* __restrict__ yh, int Ci, int Co, int nlat_in, int nlat_out, int MP, int nwmax) {
+    float2* __restrict__ yh, int Ci, int Co, int nlat_in, int nlat_out, int MP, int nwmax,
+    int wtr) {
     extern __shared__ float2 s32[];
     float2* ps = s32;                                  // [nwmax][KT][32]
     float2* xt = ps + (size_t)nwmax * KT * kS32M;      // [kS32C][KT][32]
@@ -1062,7 +1063,9 @@ __global__ __launch_bounds__(kSpecThreads) void spec32_conv(
         for (int e = tid; e < Co * kS32C * KT; e += kSpecThreads) {
             const int co = e / (kS32C * KT), r = e - co * (kS32C * KT);
             const int ci = c0 + r / KT, k = r % KT;
-            wt[e] = ci < Ci ? w[((size_t)co * Ci + ci) * KT + k] : 0.0f;
+            // wtr: w stored [Ci][Co][K] (the layer's weights, read by its adjoint)
+            wt[e] = ci < Ci ? w[(wtr ? (size_t)ci * Co + co : (size_t)co * Ci + ci) * KT + k]
+                            : 0.0f;
         }
         {
             const int ci = c0 + cs;
@@ -1182,6 +1185,7 @@ struct SpecCall {
     size_t nwin;
     int max_windows, min_windows;
     const uint32_t* psih;
+    const float* psih32;       // float32 layers: Psi_hat pairs in the list's order
     int nout;
     const float* bias;
     void* y;
@@ -1201,7 +1205,7 @@ int try_launch_fused_spectral(const disco_psi* psi, const void* x, const void* w
     if (!fused_spectral_eligible(psi, DISCO_BF16, Ci, Co, groups) || B <= 0) return 0;
     const DevPsi& d = psi->dev;
     const HostPsi& h = psi->host;
-    SpecCall c;
+    SpecCall c{};
     c.x = x;
     c.nin = h.desc.nlat_in;
     c.w = w;
@@ -1246,7 +1250,7 @@ int try_launch_grad_x_spectral(const disco_psi* psi, const void* gy, const void*
     if (!spectral_grad_x_eligible(psi, DISCO_BF16, DISCO_BF16, Ci, Co, 1) || B <= 0) return 0;
     const DevPsi& d = psi->dev;
     const HostPsi& h = psi->host;
-    SpecCall c;
+    SpecCall c{};
     c.x = gy;
     c.nin = h.desc.nlat_out;
     c.w = w;
@@ -1482,6 +1486,10 @@ namespace disco {
 
 // The float32 spectral forward (stride 1): spec_rfft (float32 spectra),
 // spec32_conv, spec_irfft.  Returns 0 when the layer does not qualify.
+namespace {
+int run_spectral_f32(const disco_psi* psi, const SpecCall& c, hipStream_t st, int* rc);
+}  // namespace
+
 int try_launch_fused_spectral32(const disco_psi* psi, const void* x, const void* w,
                                 const float* bias, void* y, int y_dtype, int B, int Ci, int Co,
                                 int groups, hipStream_t st, int* rc) {
@@ -1491,14 +1499,89 @@ int try_launch_fused_spectral32(const disco_psi* psi, const void* x, const void*
         return 0;
     const DevPsi& d = psi->dev;
     const HostPsi& h = psi->host;
+    SpecCall c{};
+    c.x = x;
+    c.nin = h.desc.nlat_in;
+    c.w = w;
+    c.wt = 0;
+    c.win_ptr = d.win_ptr;
+    c.wins = d.windows;
+    c.nwin = h.windows.size();
+    c.max_windows = d.max_windows;
+    c.min_windows = d.min_windows;
+    c.psih32 = d.spec_psih32;
+    c.nout = h.desc.nlat_out;
+    c.bias = bias;
+    c.y = y;
+    c.y_dtype = y_dtype;
+    c.B = B;
+    c.Ci = Ci;
+    c.Co = Co;
+    c.fold = 1;
+    return run_spectral_f32(psi, c, st, rc);
+}
+
+// The adjoint in x of the float32 spectral forward (stride 1, float32 x, w
+// and gy): the transposed windows, conj(Psi_hat) in their order, the
+// weights read transposed; float32 throughout.
+int spectral_grad_x32_eligible(const disco_psi* psi, int Ci, int Co, int groups) {
+    const DevPsi& d = psi->dev;
+    const HostPsi& h = psi->host;
+    if (d.spec_psih32_t == nullptr || h.stride != 1 || groups != 1 || h.K > 8 || Ci > 128 ||
+        Co < 1 || d.t_min_windows < 1 || spec32_lds(h.K, Ci, d.t_max_windows) > 64 * 1024)
+        return 0;
+    const char* e = std::getenv("DISCO_FUSED_PATH");
+    return e == nullptr || std::strcmp(e, "toeplitz") != 0;
+}
+
+int try_launch_grad_x_spectral32(const disco_psi* psi, const void* gy, const void* w, void* gx,
+                                 int gx_dtype, int B, int Ci, int Co, hipStream_t st, int* rc) {
+    if (!spectral_grad_x32_eligible(psi, Ci, Co, 1) || B <= 0) return 0;
+    if ((reinterpret_cast<uintptr_t>(gy) & 7) != 0 || (reinterpret_cast<uintptr_t>(gx) & 7) != 0)
+        return 0;
+    const DevPsi& d = psi->dev;
+    const HostPsi& h = psi->host;
+    SpecCall c{};
+    c.x = gy;
+    c.nin = h.desc.nlat_out;
+    c.w = w;
+    c.wt = 1;
+    c.win_ptr = d.wint_ptr;
+    c.wins = d.wins_t;
+    c.nwin = h.windows.size();
+    c.max_windows = d.t_max_windows;
+    c.min_windows = d.t_min_windows;
+    c.psih32 = d.spec_psih32_t;
+    c.nout = h.desc.nlat_in;
+    c.bias = nullptr;
+    c.y = gx;
+    c.y_dtype = gx_dtype;
+    c.B = B;
+    c.Ci = Co;   // the adjoint maps the layer's output channels to its inputs
+    c.Co = Ci;
+    c.fold = 1;
+    return run_spectral_f32(psi, c, st, rc);
+}
+
+namespace {
+
+int run_spectral_f32(const disco_psi* psi, const SpecCall& c, hipStream_t st, int* rc) {
+    const DevPsi& d = psi->dev;
+    const HostPsi& h = psi->host;
     const disco_psi_desc& D = h.desc;
+    const void* x = c.x;
+    const void* w = c.w;
+    const float* bias = c.bias;
+    void* y = c.y;
+    const int y_dtype = c.y_dtype, B = c.B, Ci = c.Ci, Co = c.Co;
+    const int nlat_in = c.nin, nlat_out = c.nout;
     const int N = D.nlon_in, H = N / 2, MP = d.spec_mp, K = h.K;
     SpecPlan pl;
     pl.n = d.spec_nrad;
     for (int i = 0; i < kSpecMaxRadix; ++i) pl.r[i] = d.spec_radix[i];
     auto up = [](size_t v) { return (v + 255) / 256 * 256; };
-    const size_t xh_bytes = up((size_t)B * Ci * D.nlat_in * MP * sizeof(float2));
-    const size_t yh_bytes = up((size_t)B * Co * D.nlat_out * MP * sizeof(float2));
+    const size_t xh_bytes = up((size_t)B * Ci * nlat_in * MP * sizeof(float2));
+    const size_t yh_bytes = up((size_t)B * Co * nlat_out * MP * sizeof(float2));
     // the handle's workspace; stream-ordered memory while a graph is captured
     WorkspaceLease lease(psi, xh_bytes + yh_bytes, st);
     if (lease.error() != DISCO_OK) {
@@ -1520,7 +1603,7 @@ int try_launch_fused_spectral32(const disco_psi* psi, const void* x, const void*
     float2* xh = static_cast<float2*>(ws);
     float2* yh = reinterpret_cast<float2*>(static_cast<char*>(ws) + xh_bytes);
     const size_t fft_lds = (size_t)(kFftRows + 1) * H * sizeof(float2);
-    const int64_t xrows = (int64_t)B * Ci * D.nlat_in;
+    const int64_t xrows = (int64_t)B * Ci * nlat_in;
     {
         KernelTimer timer("spec_rfft", st);
         hipLaunchKernelGGL((spec_rfft<float, float2>),
@@ -1528,15 +1611,13 @@ int try_launch_fused_spectral32(const disco_psi* psi, const void* x, const void*
                            fft_lds, st, static_cast<const float*>(x), xh, N, MP, xrows, pl);
     }
     const int COR = (Co + 31) / 32;   // 1 .. 4 (Co <= 128)
-    const size_t lds = spec32_lds(K, Co, d.max_windows);
-    const dim3 grid((unsigned)((int64_t)B * D.nlat_out * (MP / kS32M)));
+    const size_t lds = spec32_lds(K, Co, c.max_windows);
+    const dim3 grid((unsigned)((int64_t)B * nlat_out * (MP / kS32M)));
 #define DISCO_S32(KK, CR)                                                                        \
     hipLaunchKernelGGL((spec32_conv<KK, CR>), grid, dim3(kSpecThreads), lds, st, xh,            \
-                       static_cast<const float*>(w), d.spec_psih32 == nullptr                   \
-                           ? nullptr                                                            \
-                           : reinterpret_cast<const float2*>(d.spec_psih32),                    \
-                       d.win_ptr, d.windows, yh, Ci, Co, D.nlat_in, D.nlat_out, MP,             \
-                       (int)d.max_windows)
+                       static_cast<const float*>(w), reinterpret_cast<const float2*>(c.psih32), \
+                       c.win_ptr, c.wins, yh, Ci, Co, nlat_in, nlat_out, MP, c.max_windows,     \
+                       c.wt)
 #define DISCO_S32_C(KK)                   \
     switch (COR) {                        \
         case 1: DISCO_S32(KK, 1); break;  \
@@ -1559,16 +1640,16 @@ int try_launch_fused_spectral32(const disco_psi* psi, const void* x, const void*
     }
 #undef DISCO_S32_C
 #undef DISCO_S32
-    const int64_t yrows = (int64_t)B * Co * D.nlat_out;
+    const int64_t yrows = (int64_t)B * Co * nlat_out;
     const dim3 igrid((unsigned)((yrows + kFftRows - 1) / kFftRows));
     {
         KernelTimer timer("spec_irfft", st);
         if (y_dtype == DISCO_F32)
             hipLaunchKernelGGL((spec_irfft<float2, float>), igrid, dim3(kFftThreads), fft_lds, st,
-                               yh, static_cast<float*>(y), bias, N, MP, Co, D.nlat_out, yrows, pl);
+                               yh, static_cast<float*>(y), bias, N, MP, Co, nlat_out, yrows, pl);
         else
             hipLaunchKernelGGL((spec_irfft<float2, bf16_t>), igrid, dim3(kFftThreads), fft_lds, st,
-                               yh, static_cast<bf16_t*>(y), bias, N, MP, Co, D.nlat_out, yrows, pl);
+                               yh, static_cast<bf16_t*>(y), bias, N, MP, Co, nlat_out, yrows, pl);
     }
     hipError_t le = hipGetLastError();
     hipError_t fe = own_ws ? hipFreeAsync(ws, st) : hipSuccess;
@@ -1584,5 +1665,7 @@ int try_launch_fused_spectral32(const disco_psi* psi, const void* x, const void*
     *rc = DISCO_OK;
     return 1;
 }
+
+}  // namespace
 
 }  // namespace disco

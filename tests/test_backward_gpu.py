@@ -225,6 +225,11 @@ def test_fused_backward_spectral_grad_x(sdc, wl):
     assert e_x <= 2e-2 and max(rows) <= 3e-2
     # grad_w on the matrix cores: X_K rounded to bf16 (the bf16 bar)
     assert e_w <= 2e-2 and e_wc <= 3e-2
+    # bf16 gx: the same sums, rounded once on store
+    gx16, _, _ = sdc.fused_bwd(psi, _dev(x, "bf16"), _dev(w, "bf16"), gyd, need_gw=False,
+                               gx_dtype=torch.bfloat16)
+    assert gx16.dtype == torch.bfloat16
+    assert rel_l2(gx16.float().cpu().numpy(), gx) <= 4e-3
     # a float32 gradient keeps the float32 path (exact to the float32 bar)
     gx32, _, _ = sdc.fused_bwd(psi, _dev(x, "bf16"), _dev(w, "bf16"), torch.from_numpy(gy).cuda(),
                                need_gw=False)
@@ -349,3 +354,25 @@ def test_full_size_c4_spectral_grad_x_channel_subsets(sdc):
                   max(np.linalg.norm(gx_ref[:, :, i]), 1e-300)) for i in range(wl.nlat_in)]
     _say(f"  c4 spectral gx {e_x:.3e} (worst row {max(rows):.3e})")
     assert e_x <= 2e-2 and max(rows) <= 3e-2
+
+
+@pytest.mark.parametrize("wl", [CASES[0], CASES[1], CASES[6]],
+                         ids=[CASES[0].name, CASES[1].name, CASES[6].name])
+def test_fused_backward_spectral_grad_x_f32(sdc, wl):
+    """float32 stride-1 layers with a float32 gradient: grad_x on the float32
+    spectral kernels (float32 spectra), held to the float32 bar."""
+    x, w, gy = _inputs(wl)
+    d = _desc(wl)
+    gx_ref, _ = oracle.backward(d, x, w, gy, wl.groups)
+    psi = _psi(sdc, wl)
+    sdc.kernel_timing(True)
+    try:
+        gx, _, _ = sdc.fused_bwd(psi, _dev(x, "f32"), _dev(w, "f32"), torch.from_numpy(gy).cuda(),
+                                 need_gw=False)
+        ran = set(sdc.kernel_timing_read())
+    finally:
+        sdc.kernel_timing(False)
+    assert "spec32_conv" in ran and "contract_transpose" not in ran, ran
+    e = rel_l2(gx.cpu().numpy(), gx_ref)
+    _say(f"spectral float32 grad_x {wl.name}: {e:.3e}")
+    assert e <= TOL

@@ -257,6 +257,8 @@ int disco_einsum_grad_w(const void* xk, int xk_dtype, const void* gy, int gy_dty
  * w * rfft(gy)) (at stride 2 gy with a zero inserted after each sample),
  * with bf16 spectra and float32 accumulation (the bf16 bar, not float32
  * exactness); DISCO_FUSED_PATH=toeplitz selects the float32 path for them.
+ * Float32 stride-1 layers with a float32 gy (groups == 1, Ci <= 128) take
+ * gx on the float32 spectral kernels (float32 spectra, the float32 bar).
  * Layers with one input channel per group take gx with the weights folded
  * into the taps (gy contracted directly, no grad_xk), in float32. */
 int disco_fused_bwd(const disco_psi* psi, const void* x, int x_dtype, const void* w, int w_dtype,

@@ -248,8 +248,13 @@ int disco_einsum_grad_w(const void* xk, int xk_dtype, const void* gy, int gy_dty
  * each overwritten; a NULL pointer skips that gradient (not all three).
  * X_K is recomputed in float32, in slabs of at most ceil(nlat_out / 8)
  * output rows (one slab when the layer's two slab tensors take at most
- * 64 MiB), so neither K-expanded tensor is ever held whole.
- * Layers on the longitude-spectral path's tables (stride 1, or stride 2 at
+ * 64 MiB), so neither K-expanded tensor is ever held whole.  The exception
+ * is gw of a bf16 layer with a bf16 gy and groups == 1 that the matrix-core
+ * contraction takes (Ci a multiple of 32, K <= 8, stride 1 or 2, nlon_in and
+ * nlon_out multiples of 8, x and gy 16-byte aligned): its X_K is recomputed
+ * whole in bf16 on the matrix cores (at most 4 GiB, in the handle's
+ * workspace, which keeps it between calls) and grad_w sums it there (the
+ * bf16 bar).  Layers on the longitude-spectral path's tables (stride 1, or stride 2 at
  * 720 or 1440 input longitudes) with bf16 x, w and gy, groups == 1, Ci 64 or
  * 128 and Co a multiple of 32 take gx on the longitude-spectral kernels
  * instead: the adjoint of each window's circular correlation is a circular

@@ -150,6 +150,13 @@ int launch_fused(const disco_psi* psi, const void* x, int dtype, const void* w,
 int launch_fused_noalloc(const disco_psi* psi, const void* x, int dtype, const void* w,
                          const float* bias, void* y, int y_dtype, int B, int Ci, int Co,
                          int groups, void* stream);
+// The matrix-core contraction (kernels_fused_mfma.hip): bf16 x into a bf16
+// [B, C, K, nlat_out, nlon_out] X_K, whole layer.  contract_mfma_ok says
+// whether it takes these arguments; the launcher returns 0 when it does not
+// (rc untouched), else 1 with *rc the result.
+bool contract_mfma_ok(const disco_psi* psi, const void* x, const void* xk, int B, int C);
+int try_launch_contract_mfma(const disco_psi* psi, const void* x, void* xk, int B, int C,
+                             hipStream_t st, int* rc);
 // 1 if disco_fused_fwd takes the longitude-spectral path for these arguments
 int fused_spectral_eligible(const disco_psi* psi, int x_dtype, int Ci, int Co, int groups);
 // The adjoint in x on the longitude-spectral kernels (stride-1 and stride-2

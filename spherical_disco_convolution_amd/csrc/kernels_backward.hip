@@ -744,6 +744,70 @@ int launch_einsum_grad_w(const void* xk, int xk_dtype, const void* gy, int gy_dt
 // gx.  Slabs of at most ceil(nlat_out / 8) rows (one slab when the two slab
 // tensors of the whole layer take at most 64 MiB), so the workspace is about
 // an eighth of the two whole K-expanded tensors.
+// Largest bf16 X_K the fused backward recomputes whole on the matrix cores
+// (1.86 GB for 128 channels, K = 7 at 721 x 1440); larger layers take the
+// float32 slabs.
+constexpr size_t kWholeXk16Max = (size_t)4 << 30;
+
+// grad_w of a bf16 layer with a bf16 gradient and one group: the matrix-core
+// contraction writes the whole bf16 X_K into the handle's workspace, the
+// matrix-core partial sums run over every point, and one reduction writes gw.
+// Returns 0 when the layer is not one this takes (rc untouched), else 1 with
+// *rc the result.
+static int grad_w_whole_bf16(const disco_psi* psi, const void* x, const void* gy, float* gw, int B,
+                      int Ci, int Co, hipStream_t st, int* rc) {
+    const HostPsi& h = psi->host;
+    const disco_psi_desc& D = h.desc;
+    const int K = h.K;
+    const size_t P = (size_t)D.nlat_out * D.nlon_out;
+    auto up = [](size_t v) { return (v + 255) / 256 * 256; };
+    const size_t xk_bytes = up((size_t)B * Ci * K * P * sizeof(bf16_t));
+    if (xk_bytes > kWholeXk16Max) return 0;
+    const int tiles = grad_w_tiles(DISCO_BF16, 1, Ci, Co, K, D.nlon_out);
+    const int L = grad_w_chunk(P, tiles, B, 1, num_cus());
+    // the workspace is 256-byte aligned: only x's alignment is in question
+    if (!contract_mfma_ok(psi, x, x, B, Ci) || !grad_w_mfma_ok(DISCO_BF16, DISCO_BF16, 1,
+                                                               D.nlon_out, L, gy))
+        return 0;
+    const int nparts = B * (int)((P + L - 1) / L);
+    const size_t ngw = (size_t)Co * Ci * K;
+    const size_t part_bytes = up((size_t)nparts * ngw * sizeof(float));
+    WorkspaceLease lease(psi, xk_bytes + part_bytes, st);
+    if (lease.error() != DISCO_OK) {
+        *rc = lease.error();
+        return 1;
+    }
+    void* ws = lease.ptr();
+    const bool own_ws = ws == nullptr;
+    if (own_ws) {
+        hipError_t e = hipMallocAsync(&ws, xk_bytes + part_bytes, st);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            *rc = set_error(e == hipErrorOutOfMemory ? DISCO_ENOMEM : DISCO_EHIP,
+                            "hipMallocAsync for the backward workspace failed: %s",
+                            hipGetErrorString(e));
+            return 1;
+        }
+    }
+    bf16_t* xk = static_cast<bf16_t*>(ws);
+    float* partial = reinterpret_cast<float*>(static_cast<char*>(ws) + xk_bytes);
+    int r = DISCO_OK;
+    if (!try_launch_contract_mfma(psi, x, xk, B, Ci, st, &r))
+        r = set_error(DISCO_EHIP, "matrix-core contraction declined a layer it was checked for");
+    if (r == DISCO_OK) {
+        const int np = grad_w_slab(xk, DISCO_BF16, gy, DISCO_BF16, partial, B, Ci, Co, 1, K,
+                                   D.nlat_out, D.nlon_out, 0, D.nlat_out, L, st);
+        r = np < 0 ? np : reduce_into(partial, gw, ngw, np, 0, st);
+    }
+    hipError_t fe = own_ws ? hipFreeAsync(ws, st) : hipSuccess;
+    if (r == DISCO_OK && fe != hipSuccess) {
+        (void)hipGetLastError();
+        r = set_error(DISCO_EHIP, "hipFreeAsync failed: %s", hipGetErrorString(fe));
+    }
+    *rc = r;
+    return 1;
+}
+
 int launch_fused_bwd(const disco_psi* psi, const void* x, int x_dtype, const void* w, int w_dtype,
                      const void* gy, int gy_dtype, void* gx, int gx_dtype, float* gw, float* gbias,
                      int B, int Ci, int Co, int groups, void* stream) {
@@ -779,6 +843,16 @@ int launch_fused_bwd(const disco_psi* psi, const void* x, int x_dtype, const voi
                                           groups, st);
         if (frc != DISCO_OK) return frc;
         gx = nullptr;
+    }
+    // bf16 x and gy, one group: X_K recomputed whole, in bf16, by the
+    // matrix-core contraction, then the matrix-core grad_w partial sums over
+    // every point (they hold X_K to bf16 as they load it in any case)
+    if (gw && B > 0 && x_dtype == DISCO_BF16 && gy_dtype == DISCO_BF16 && groups == 1) {
+        int grc = DISCO_OK;
+        if (grad_w_whole_bf16(psi, x, gy, gw, B, Ci, Co, st, &grc)) {
+            if (grc != DISCO_OK) return grc;
+            gw = nullptr;
+        }
     }
     const size_t row_bytes = (size_t)B * Ci * K * D.nlon_out * sizeof(float);
     int rows = D.nlat_out;

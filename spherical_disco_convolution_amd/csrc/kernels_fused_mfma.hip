@@ -854,20 +854,27 @@ int try_launch_fused_mfma(const disco_psi* psi, const void* x, const void* w, co
     return 1;
 }
 
+bool contract_mfma_ok(const disco_psi* psi, const void* x, const void* xk, int B, int C) {
+    const DevPsi& d = psi->dev;
+    const HostPsi& h = psi->host;
+    const disco_psi_desc& D = h.desc;
+    if (!d.mfma_ok || C % 32 != 0 || h.K > 8 || B <= 0) return false;
+    if (h.stride != 1 && h.stride != 2) return false;
+    // 16-byte loads of x rows and 16-byte stores of xk rows
+    if ((reinterpret_cast<uintptr_t>(x) & 15) != 0 || (reinterpret_cast<uintptr_t>(xk) & 15) != 0 ||
+        D.nlon_out % 8 != 0)
+        return false;
+    // channel offsets of one 32-channel chunk are 32-bit
+    return (int64_t)D.nlat_in * D.nlon_in * 32 < ((int64_t)1 << 31);
+}
+
 int try_launch_contract_mfma(const disco_psi* psi, const void* x, void* xk, int B, int C,
                              hipStream_t st, int* rc) {
     const DevPsi& d = psi->dev;
     const HostPsi& h = psi->host;
     const disco_psi_desc& D = h.desc;
-    if (!d.mfma_ok || C % 32 != 0 || h.K > 8 || B <= 0) return 0;
+    if (!contract_mfma_ok(psi, x, xk, B, C)) return 0;
     const int S = h.stride;
-    if (S != 1 && S != 2) return 0;
-    // 16-byte loads of x rows and 16-byte stores of xk rows
-    if ((reinterpret_cast<uintptr_t>(x) & 15) != 0 || (reinterpret_cast<uintptr_t>(xk) & 15) != 0 ||
-        D.nlon_out % 8 != 0)
-        return 0;
-    // channel offsets of one 32-channel chunk are 32-bit
-    if ((int64_t)D.nlat_in * D.nlon_in * 32 >= ((int64_t)1 << 31)) return 0;
     int dev = 0, ncu = 256;
     if (hipGetDevice(&dev) == hipSuccess)
         (void)hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);

@@ -212,6 +212,8 @@ def test_fused_backward_spectral_grad_x(sdc, wl):
         sdc.kernel_timing(False)
     assert "spec_mfma" in ran and "contract_transpose" not in ran, ran
     assert "grad_w_mfma" in ran and "grad_w_partial" not in ran, ran
+    # X_K recomputed whole in bf16 on the matrix cores, not in float32 slabs
+    assert "contract_mfma" in ran and "contract_kernel" not in ran, ran
     gx = gx.cpu().numpy()
     e_x = rel_l2(gx, gx_ref)
     gw = gw.cpu().numpy()
@@ -323,6 +325,36 @@ def test_full_size_c4_backward_channel_subsets(sdc):
     e_b = rel_l2(gb.cpu().numpy(), gy.astype(np.float64).sum(axis=(0, 2, 3)))
     _say(f"  c4 gx {e_x:.3e} gw {e_w:.3e} gbias {e_b:.3e}")
     assert e_x <= TOL and e_w <= TOL and e_b <= TOL
+
+
+def test_full_size_c4_backward_bf16_gradient_grad_w(sdc):
+    """721x1440, 128 -> 128 channels, K = 7, bf16 inputs and a bf16 gradient:
+    the fused backward recomputes the whole X_K in bf16 on the matrix cores
+    and sums grad_w there; the oracle evaluates gw on 3 x 3 channel pairs
+    (the bf16 bar, whole and per output channel)."""
+    wl = WORKLOADS["c4"]
+    _say("full-size c4 backward, bf16 gradient: grad_w")
+    x, w, gy = _inputs(wl)
+    gy = round_bf16(gy)
+    d = _desc(wl)
+    psi = _psi(sdc, wl)
+    sdc.kernel_timing(True)
+    try:
+        _, gw, _ = sdc.fused_bwd(psi, _dev(x, "bf16"), _dev(w, "bf16"), _dev(gy, "bf16"),
+                                 need_gx=False)
+        ran = set(sdc.kernel_timing_read())
+    finally:
+        sdc.kernel_timing(False)
+    assert "contract_mfma" in ran and "grad_w_mfma" in ran, ran
+    assert "contract_kernel" not in ran, ran
+    ci_sub, co_sub = [0, 61, 127], [5, 64, 126]
+    xk = oracle.contract(d, x[:, ci_sub])
+    gw_ref = oracle.einsum_grad_w(gy[:, co_sub], xk, 1)
+    got = gw[co_sub][:, ci_sub].cpu().numpy()
+    e_w = rel_l2(got, gw_ref)
+    e_wc = max(rel_l2(got[c], gw_ref[c]) for c in range(len(co_sub)))
+    _say(f"  c4 gw {e_w:.3e} (worst channel {e_wc:.3e})")
+    assert e_w <= 2e-2 and e_wc <= 3e-2
 
 
 def test_full_size_c4_spectral_grad_x_channel_subsets(sdc):

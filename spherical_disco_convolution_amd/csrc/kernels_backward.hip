@@ -268,6 +268,110 @@ __global__ __launch_bounds__(kThreads) void grad_w_mfma(
         }
 }
 
+// The same partial sums from a bf16 X_K, staged through LDS: per step of 64
+// points the workgroup copies 128 bytes of each of its tile's 128 gy rows and
+// 128 X_K rows into LDS (8 lanes per row, 16 bytes per lane: whole row
+// segments, each row read once for the four waves), then every wave runs its
+// 2 x 2 MFMAs over the step's four 16-point slices from there.  The next
+// step's rows are loaded into registers while the MFMAs run.
+constexpr int kGwP = 64;            // points per staged step
+constexpr int kGwPitch = kGwP + 8;  // LDS row pitch in bf16 (144 bytes)
+
+__global__ __launch_bounds__(kThreads) void grad_w_mfma_lds(
+    const bf16_t* __restrict__ xk, const bf16_t* __restrict__ gy, float* __restrict__ partial,
+    int Co, int kd, int nlat_out, int nlon_out, int row0, int nrows, int L, int nchunk) {
+    __shared__ __attribute__((aligned(16))) bf16_t sa[kGwM * kGwPitch];   // gy rows of the tile
+    __shared__ __attribute__((aligned(16))) bf16_t sb[kGwM * kGwPitch];   // X_K rows of the tile
+    const int kt = blockIdx.x, ct = blockIdx.y;
+    const int z = blockIdx.z;
+    const int chunk = z % nchunk, b = z / nchunk;
+    const size_t P = (size_t)nrows * nlon_out;   // points of the slab
+    const size_t n0 = (size_t)chunk * L;
+    const size_t n1 = min(P, n0 + (size_t)L);
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int l32 = lane & 31, lg = lane >> 5;
+    // staging: thread tid copies 8-point piece tid % 8 of tile rows tid / 8 + 32 r
+    const int piece = tid & 7, srow = tid >> 3;
+    const bf16_t* gyb = gy + (size_t)b * Co * nlat_out * nlon_out + (size_t)row0 * nlon_out;
+    const bf16_t* xkb = xk + (size_t)b * kd * P;
+    const bf16_t* asrc[4];
+    const bf16_t* bsrc[4];
+    bool aok[4], bok[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int co = ct * kGwM + srow + 32 * r, ka = kt * kGwM + srow + 32 * r;
+        aok[r] = co < Co;
+        bok[r] = ka < kd;
+        asrc[r] = gyb + (size_t)min(co, Co - 1) * nlat_out * nlon_out;
+        bsrc[r] = xkb + (size_t)min(ka, kd - 1) * P;
+    }
+    const gw_bf16x8 zero = {};
+    gw_bf16x8 ra[4], rb[4];
+    // P, L and the chunk starts are multiples of 8: a piece's 8 points are
+    // all inside the chunk or all past it (then zeros, which add nothing)
+    auto fetch = [&](size_t nb) {
+        const size_t p = nb + 8 * piece;
+        const bool pin = p + 8 <= n1;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            ra[r] = aok[r] && pin ? gw_load8(asrc[r] + p) : zero;
+            rb[r] = bok[r] && pin ? gw_load8(bsrc[r] + p) : zero;
+        }
+    };
+    const int am = (wave & 1) * 64, bm = (wave >> 1) * 64;   // the wave's 64 x 64 sub-tile
+    gw_floatx16 acc[2][2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int v = 0; v < 2; ++v)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[u][v][e] = 0.0f;
+    if (n0 < n1) fetch(n0);
+    for (size_t nb = n0; nb < n1; nb += kGwP) {
+        __syncthreads();   // every wave is done reading the previous step
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            *reinterpret_cast<gw_bf16x8*>(sa + (srow + 32 * r) * kGwPitch + 8 * piece) = ra[r];
+            *reinterpret_cast<gw_bf16x8*>(sb + (srow + 32 * r) * kGwPitch + 8 * piece) = rb[r];
+        }
+        __syncthreads();
+        if (nb + kGwP < n1) fetch(nb + kGwP);   // in flight during this step's MFMAs
+#pragma unroll
+        for (int s = 0; s < kGwP / 16; ++s) {
+            gw_bf16x8 af[2], bf[2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                af[u] = *reinterpret_cast<const gw_bf16x8*>(sa + (am + 32 * u + l32) * kGwPitch +
+                                                            16 * s + 8 * lg);
+                bf[u] = *reinterpret_cast<const gw_bf16x8*>(sb + (bm + 32 * u + l32) * kGwPitch +
+                                                            16 * s + 8 * lg);
+            }
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+                for (int v = 0; v < 2; ++v)
+                    acc[u][v] =
+                        __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[u], bf[v], acc[u][v], 0, 0, 0);
+        }
+    }
+    // lane: column kappa = ka0 + 32 v + l32, rows co = co0 + 32 u + 8 (e / 4) + 4 lg + e % 4
+    const int co0 = ct * kGwM + am, ka0 = kt * kGwM + bm;
+    float* out = partial + (size_t)(b * nchunk + chunk) * Co * kd;
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int v = 0; v < 2; ++v) {
+            const int ka = ka0 + 32 * v + l32;
+            if (ka >= kd) continue;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int co = co0 + 32 * u + 8 * (e >> 2) + 4 * lg + (e & 3);
+                if (co < Co) out[(size_t)co * kd + ka] = acc[u][v][e];
+            }
+        }
+}
+
 // ---------------------------------------------------------------------------
 // grad_w partial sums: a 64 x 64 tile of [co in group][kappa = (ci', k)]
 // summed over one chunk of L output points (r, q) of one batch entry,
@@ -554,7 +658,7 @@ int grad_w_slab(const void* xk, int xk_dtype, const void* gy, int gy_dtype, floa
                                    (const float*)xk, (const bf16_t*)gy, partial, Co, kd, nlat_out,
                                    nlon_out, row0, nrows, L, nchunk);
             else
-                hipLaunchKernelGGL((grad_w_mfma<bf16_t>), mgrid, dim3(kThreads), 0, st,
+                hipLaunchKernelGGL(grad_w_mfma_lds, mgrid, dim3(kThreads), 0, st,
                                    (const bf16_t*)xk, (const bf16_t*)gy, partial, Co, kd, nlat_out,
                                    nlon_out, row0, nrows, L, nchunk);
         }

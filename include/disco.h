@@ -265,7 +265,10 @@ int disco_einsum_grad_w(const void* xk, int xk_dtype, const void* gy, int gy_dty
  * Float32 stride-1 layers with a float32 gy (groups == 1, Ci <= 128) take
  * gx on the float32 spectral kernels (float32 spectra, the float32 bar).
  * Layers with one input channel per group take gx with the weights folded
- * into the taps (gy contracted directly, no grad_xk), in float32. */
+ * into the taps (gy contracted directly, no grad_xk), in float32, and, at
+ * stride 1 or 2 with K <= 32, gw with no X_K at all: per window the
+ * correlation of gy's output row with x's input row, folded with the
+ * window's Psi values, in float32. */
 int disco_fused_bwd(const disco_psi* psi, const void* x, int x_dtype, const void* w, int w_dtype,
                     const void* gy, int gy_dtype, void* gx, int gx_dtype, float* gw, float* gbias,
                     int32_t B, int32_t Ci, int32_t Co, int32_t groups, void* stream);

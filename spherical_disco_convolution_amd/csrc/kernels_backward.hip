@@ -373,6 +373,136 @@ __global__ __launch_bounds__(kThreads) void grad_w_mfma_lds(
 }
 
 // ---------------------------------------------------------------------------
+// grad_w of layers with one input channel per group, with no X_K.  For output
+// channel co (input channel c = co / (Co / groups)) and basis function k,
+//   gw[co, 0, k] = sum_{b, j} sum_{windows (i, p_lo) of row j} sum_t
+//                  Psi_k[window, t] * S[t],
+//   S[t] = sum_q gy[b, co, j, q] * x[b, c, i, (s q + p_lo + t) mod nlon_in].
+// One workgroup per (output row, output channel, batch).  Per window the
+// input row's samples from p_lo on are staged in LDS by residue mod s
+// (ext_p[m] = sample p_lo + s m + p), so output t = s a + p at tap q reads
+// ext_p[a + q].  Thread items are (8 consecutive a, a slice of q) with an
+// 8 x 8 register tile per residue; each item's S values go to LDS per q
+// slice; then one thread per t sums the slices and folds S[t] with the
+// window's K values into its gw registers.  A workgroup reduction writes
+// partial[(b nlat_out + j)][co][k], which reduce_partials sums in order.
+// ---------------------------------------------------------------------------
+constexpr int kDwgR = 8;        // register tile edge
+constexpr int kDwgMaxK = 32;    // largest K
+
+template <typename TX, typename TG, int S>
+__global__ __launch_bounds__(kThreads) void grad_w_depthwise(
+    const TX* __restrict__ x, const TG* __restrict__ gy, float* __restrict__ partial,
+    const int32_t* __restrict__ win_ptr, const DevWindow* __restrict__ wins,
+    const float* __restrict__ vals, int Co, int groups, int K, int KP, int nlat_in, int nlon_in,
+    int nlat_out, int nlon_out, int QP, int GQ, int M4, int area) {
+    extern __shared__ __attribute__((aligned(16))) float dsm[];
+    float* gys = dsm;             // [GQ >= QP]: gy row j, zeros past nlon_out
+    float* ext = gys + GQ;        // [S][M4]
+    float* sl = ext + S * M4;     // [area]: S values per q slice
+    const int j = blockIdx.x, co = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x;
+    const int c = co / (Co / groups);
+    const TG* gyr = gy + (((size_t)b * Co + co) * nlat_out + j) * nlon_out;
+    const TX* xc = x + ((size_t)b * groups + c) * nlat_in * nlon_in;
+    for (int q = tid; q < QP; q += kThreads) gys[q] = q < nlon_out ? load_f(gyr, q) : 0.0f;
+    float gwk[kDwgMaxK];
+#pragma unroll
+    for (int k = 0; k < kDwgMaxK; ++k) gwk[k] = 0.0f;
+    const int nqb = QP / kDwgR;   // q blocks
+    const int w0 = win_ptr[j], w1 = win_ptr[j + 1];
+    for (int wi = w0; wi < w1; ++wi) {
+        const DevWindow wd = wins[wi];
+        if (wd.width <= 0) continue;     // uniform over the workgroup
+        const int A = (wd.width + S - 1) / S;
+        const int NA = (A + kDwgR - 1) / kDwgR;
+        const int M = NA * kDwgR + QP;   // ext_p entries the items read
+        const int TW = S * NA * kDwgR;   // t entries per slice
+        const int NQ = max(1, min(min(nqb, kThreads / NA), area / TW));
+        const int qbs = (nqb + NQ - 1) / NQ;   // q blocks per slice
+        const TX* row = xc + (size_t)wd.lat * nlon_in;
+        __syncthreads();   // the previous window's reads are done; gys is written
+        for (int u = tid; u < S * M; u += kThreads) {
+            const int m = u / S, p = u - m * S;
+            ext[p * M4 + m] = load_f(row, (size_t)(((int64_t)wd.p_lo + u) % nlon_in));
+        }
+        __syncthreads();
+        for (int it = tid; it < NA * NQ; it += kThreads) {
+            const int ab = it % NA, qs = it / NA;
+            const int a0 = ab * kDwgR;
+            const int qa = qs * qbs * kDwgR, qb = min(QP, qa + qbs * kDwgR);
+            float acc[S][kDwgR];
+#pragma unroll
+            for (int p = 0; p < S; ++p)
+#pragma unroll
+                for (int r = 0; r < kDwgR; ++r) acc[p][r] = 0.0f;
+            for (int q = qa; q < qb; q += kDwgR) {
+                float g[kDwgR];
+#pragma unroll
+                for (int i = 0; i < kDwgR / 4; ++i) {
+                    const float4 v = *reinterpret_cast<const float4*>(gys + q + 4 * i);
+                    g[4 * i] = v.x;
+                    g[4 * i + 1] = v.y;
+                    g[4 * i + 2] = v.z;
+                    g[4 * i + 3] = v.w;
+                }
+#pragma unroll
+                for (int p = 0; p < S; ++p) {
+                    // ext_p[a0 + q .. a0 + q + 15]: a0 + q is a multiple of 8
+                    float e[2 * kDwgR];
+#pragma unroll
+                    for (int i = 0; i < 2 * kDwgR / 4; ++i) {
+                        const float4 v =
+                            *reinterpret_cast<const float4*>(ext + p * M4 + a0 + q + 4 * i);
+                        e[4 * i] = v.x;
+                        e[4 * i + 1] = v.y;
+                        e[4 * i + 2] = v.z;
+                        e[4 * i + 3] = v.w;
+                    }
+#pragma unroll
+                    for (int u = 0; u < kDwgR; ++u)
+#pragma unroll
+                        for (int r = 0; r < kDwgR; ++r) acc[p][r] = fmaf(g[u], e[r + u], acc[p][r]);
+                }
+            }
+            float* dst = sl + qs * TW;
+#pragma unroll
+            for (int p = 0; p < S; ++p)
+#pragma unroll
+                for (int r = 0; r < kDwgR; ++r) dst[S * (a0 + r) + p] = acc[p][r];
+        }
+        __syncthreads();
+        const float* v = vals + (size_t)wd.val_off * KP;
+        for (int t = tid; t < wd.width; t += kThreads) {
+            float st = 0.0f;
+            for (int qs = 0; qs < NQ; ++qs) st += sl[qs * TW + t];
+#pragma unroll
+            for (int k = 0; k < kDwgMaxK; ++k)
+                if (k < K) gwk[k] = fmaf(v[(size_t)t * KP + k], st, gwk[k]);
+        }
+    }
+    // workgroup sum of gwk: lane shuffles within each wave, then LDS
+    __syncthreads();
+    float* red = dsm;   // [kThreads / 64][kDwgMaxK], inside gys (GQ >= 4 kDwgMaxK)
+    const int lane = tid & 63, wave = tid >> 6;
+#pragma unroll
+    for (int k = 0; k < kDwgMaxK; ++k) {
+        if (k < K) {
+            float a = gwk[k];
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) a += __shfl_xor(a, off);
+            if (lane == 0) red[wave * kDwgMaxK + k] = a;
+        }
+    }
+    __syncthreads();
+    if (tid < K) {
+        float a = 0.0f;
+        for (int w = 0; w < kThreads / 64; ++w) a += red[w * kDwgMaxK + tid];
+        partial[((size_t)(b * nlat_out + j) * Co + co) * K + tid] = a;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // grad_w partial sums: a 64 x 64 tile of [co in group][kappa = (ci', k)]
 // summed over one chunk of L output points (r, q) of one batch entry,
 // staged 16 points at a time through LDS; thread = 4 x 4 outputs.
@@ -858,6 +988,90 @@ constexpr size_t kWholeXk16Max = (size_t)4 << 30;
 // matrix-core partial sums run over every point, and one reduction writes gw.
 // Returns 0 when the layer is not one this takes (rc untouched), else 1 with
 // *rc the result.
+// grad_w of a layer with one input channel per group (stride 1 or 2) with no
+// X_K: grad_w_depthwise into per-(batch, output row) partials in the
+// handle's workspace, then one reduction into gw.  Returns 0 when the layer
+// is not one this takes (rc untouched), else 1 with *rc the result.
+template <typename TX, typename TG>
+void launch_grad_w_depthwise(const disco_psi* psi, const void* x, const void* gy, float* partial,
+                             int B, int Co, int groups, int QP, int GQ, int M4, int area,
+                             size_t lds, hipStream_t st) {
+    const HostPsi& h = psi->host;
+    const DevPsi& d = psi->dev;
+    const disco_psi_desc& D = h.desc;
+    dim3 grid(D.nlat_out, Co, B);
+#define DISCO_GWD(SS)                                                                             \
+    hipLaunchKernelGGL((grad_w_depthwise<TX, TG, SS>), grid, dim3(kThreads), lds, st,             \
+                       (const TX*)x, (const TG*)gy, partial, d.win_ptr, d.windows, d.vals, Co,    \
+                       groups, h.K, d.KP, D.nlat_in, D.nlon_in, D.nlat_out, D.nlon_out, QP, GQ,  \
+                       M4, area)
+    if (h.stride == 1) DISCO_GWD(1);
+    else DISCO_GWD(2);
+#undef DISCO_GWD
+}
+
+static int grad_w_depthwise_run(const disco_psi* psi, const void* x, int x_dtype, const void* gy,
+                                int gy_dtype, float* gw, int B, int Co, int groups,
+                                hipStream_t st, int* rc) {
+    const HostPsi& h = psi->host;
+    const DevPsi& d = psi->dev;
+    const disco_psi_desc& D = h.desc;
+    const int S = h.stride, K = h.K;
+    if ((S != 1 && S != 2) || K > kDwgMaxK || B <= 0 || d.max_width < 1) return 0;
+    const int QP = (D.nlon_out + kDwgR - 1) / kDwgR * kDwgR;
+    const int GQ = std::max(QP, 4 * kDwgMaxK);
+    const int NA = ((d.max_width + S - 1) / S + kDwgR - 1) / kDwgR;
+    const int M4 = (NA * kDwgR + QP + 3) / 4 * 4;
+    const int area = std::max(S * NA * kDwgR, 4096);
+    const size_t lds = ((size_t)GQ + (size_t)S * M4 + area) * sizeof(float);
+    if (lds > 64 * 1024) return 0;
+    const int nparts = B * D.nlat_out;
+    const size_t n = (size_t)Co * K;
+    const size_t part_bytes = (size_t)nparts * n * sizeof(float);
+    WorkspaceLease lease(psi, part_bytes, st);
+    if (lease.error() != DISCO_OK) {
+        *rc = lease.error();
+        return 1;
+    }
+    void* ws = lease.ptr();
+    const bool own_ws = ws == nullptr;
+    if (own_ws) {
+        hipError_t e = hipMallocAsync(&ws, part_bytes, st);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            *rc = set_error(e == hipErrorOutOfMemory ? DISCO_ENOMEM : DISCO_EHIP,
+                            "hipMallocAsync for the backward workspace failed: %s",
+                            hipGetErrorString(e));
+            return 1;
+        }
+    }
+    float* partial = static_cast<float*>(ws);
+    {
+        KernelTimer timer("grad_w_depthwise", st);
+        if (x_dtype == DISCO_F32 && gy_dtype == DISCO_F32)
+            launch_grad_w_depthwise<float, float>(psi, x, gy, partial, B, Co, groups, QP, GQ, M4,
+                                                  area, lds, st);
+        else if (x_dtype == DISCO_F32)
+            launch_grad_w_depthwise<float, bf16_t>(psi, x, gy, partial, B, Co, groups, QP, GQ, M4,
+                                                   area, lds, st);
+        else if (gy_dtype == DISCO_F32)
+            launch_grad_w_depthwise<bf16_t, float>(psi, x, gy, partial, B, Co, groups, QP, GQ, M4,
+                                                   area, lds, st);
+        else
+            launch_grad_w_depthwise<bf16_t, bf16_t>(psi, x, gy, partial, B, Co, groups, QP, GQ,
+                                                    M4, area, lds, st);
+    }
+    int r = check("grad_w_depthwise");
+    if (r == DISCO_OK) r = reduce_into(partial, gw, n, nparts, 0, st);
+    hipError_t fe = own_ws ? hipFreeAsync(ws, st) : hipSuccess;
+    if (r == DISCO_OK && fe != hipSuccess) {
+        (void)hipGetLastError();
+        r = set_error(DISCO_EHIP, "hipFreeAsync failed: %s", hipGetErrorString(fe));
+    }
+    *rc = r;
+    return 1;
+}
+
 static int grad_w_whole_bf16(const disco_psi* psi, const void* x, const void* gy, float* gw, int B,
                       int Ci, int Co, hipStream_t st, int* rc) {
     const HostPsi& h = psi->host;
@@ -954,6 +1168,14 @@ int launch_fused_bwd(const disco_psi* psi, const void* x, int x_dtype, const voi
     if (gw && B > 0 && x_dtype == DISCO_BF16 && gy_dtype == DISCO_BF16 && groups == 1) {
         int grc = DISCO_OK;
         if (grad_w_whole_bf16(psi, x, gy, gw, B, Ci, Co, st, &grc)) {
+            if (grc != DISCO_OK) return grc;
+            gw = nullptr;
+        }
+    }
+    // one input channel per group: grad_w straight from x and gy, no X_K
+    if (gw && B > 0 && cig == 1) {
+        int grc = DISCO_OK;
+        if (grad_w_depthwise_run(psi, x, x_dtype, gy, gy_dtype, gw, B, Co, groups, st, &grc)) {
             if (grc != DISCO_OK) return grc;
             gw = nullptr;
         }

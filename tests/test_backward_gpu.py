@@ -161,8 +161,16 @@ def test_fused_backward(sdc, wl):
     gx_ref, gw_ref = oracle.backward(d, x, w, gy, wl.groups)
     psi = _psi(sdc, wl)
     gyd = torch.from_numpy(gy).cuda()
-    gx, gw, gb = sdc.fused_bwd(psi, _dev(x, wl.dtype), _dev(w, wl.dtype), gyd, groups=wl.groups,
-                               need_gbias=True)
+    sdc.kernel_timing(True)
+    try:
+        gx, gw, gb = sdc.fused_bwd(psi, _dev(x, wl.dtype), _dev(w, wl.dtype), gyd,
+                                   groups=wl.groups, need_gbias=True)
+        ran = set(sdc.kernel_timing_read())
+    finally:
+        sdc.kernel_timing(False)
+    if wl.Ci // wl.groups == 1:
+        # one input channel per group: grad_w straight from x and gy, no X_K
+        assert "grad_w_depthwise" in ran and "contract_kernel" not in ran, ran
     e_x = rel_l2(gx.cpu().numpy(), gx_ref)
     e_w = rel_l2(gw.cpu().numpy(), gw_ref)
     e_b = rel_l2(gb.cpu().numpy(), gy.astype(np.float64).sum(axis=(0, 2, 3)))

@@ -389,6 +389,7 @@ __global__ __launch_bounds__(kThreads) void grad_w_mfma_lds(
 // ---------------------------------------------------------------------------
 constexpr int kDwgR = 8;        // register tile edge
 constexpr int kDwgMaxK = 32;    // largest K
+constexpr int kDwgSlices = 16;  // most q slices per window
 
 template <typename TX, typename TG, int S>
 __global__ __launch_bounds__(kThreads) void grad_w_depthwise(
@@ -418,13 +419,19 @@ __global__ __launch_bounds__(kThreads) void grad_w_depthwise(
         const int NA = (A + kDwgR - 1) / kDwgR;
         const int M = NA * kDwgR + QP;   // ext_p entries the items read
         const int TW = S * NA * kDwgR;   // t entries per slice
-        const int NQ = max(1, min(min(nqb, kThreads / NA), area / TW));
+        // at most kDwgSlices slices: the fold below sums them serially per t
+        const int NQ = max(1, min(min(min(nqb, kThreads / NA), area / TW), kDwgSlices));
         const int qbs = (nqb + NQ - 1) / NQ;   // q blocks per slice
         const TX* row = xc + (size_t)wd.lat * nlon_in;
         __syncthreads();   // the previous window's reads are done; gys is written
+        // sample p_lo + u (mod nlon_in): reduced once, then advanced by
+        // kThreads per step (a while loop: rows may be shorter than kThreads)
+        int pos = (int)(((unsigned)wd.p_lo + (unsigned)tid) % (unsigned)nlon_in);
         for (int u = tid; u < S * M; u += kThreads) {
             const int m = u / S, p = u - m * S;
-            ext[p * M4 + m] = load_f(row, (size_t)(((int64_t)wd.p_lo + u) % nlon_in));
+            ext[p * M4 + m] = load_f(row, pos);
+            pos += kThreads;
+            while (pos >= nlon_in) pos -= nlon_in;
         }
         __syncthreads();
         for (int it = tid; it < NA * NQ; it += kThreads) {

@@ -177,6 +177,109 @@ __global__ __launch_bounds__(kThreads) void contract_t_folded_kernel(
     }
 }
 
+// The same adjoint with register tiles, for strides S = 1 and 2 with
+// nlon_in = S nlon_out.  A thread item owns the 8 outputs
+// n = S (A0 + r) + P, r < 8.  For a window starting at p_lo these outputs
+// see the taps of one parity p as a one-dimensional convolution:
+// gx[n_r] += sum_u f[S u + p] gy[(a0 + r - u) mod nlon_out], with p and a0
+// the same for all 8.  The window's folded taps are staged in LDS split by
+// parity (zeros past the window), and the gy row with an offset of
+// nlon_out + 8 so that every index of the convolution is in range without
+// a modulo.  Per chunk of 8 taps an item reads 8 taps (16-byte loads) and
+// 15 gy values for 64 multiply-adds.
+constexpr int kCtR = 8;   // outputs per item and taps per chunk
+
+template <typename TG, typename TW, typename TO, int S, int IT>
+__global__ __launch_bounds__(kThreads) void contract_t_folded_tiled(
+    const TG* __restrict__ gy, const TW* __restrict__ w, TO* __restrict__ gx,
+    const int32_t* __restrict__ wt_ptr, const DevWindow* __restrict__ wt,
+    const float* __restrict__ vals, int Co, int groups, int K, int KP, int nlat_in, int nlon_in,
+    int nlat_out, int nlon_out, int GXN, int UWP) {
+    extern __shared__ __attribute__((aligned(16))) float tsm[];
+    float* gxs = tsm;               // [GXN]: gy row, gxs[m] = gy[(m - nlon_out - 8) mod nlon_out]
+    float* fs = gxs + GXN;          // [S][UWP]: folded taps by parity, zeros past the window
+    float* wk = fs + S * UWP;       // [K]
+    const int i = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x;
+    const int mch = Co / groups;
+    const int NB = (nlon_out + kCtR - 1) / kCtR;   // 8-output blocks per residue
+    const int off = nlon_out + kCtR;
+    const int w0 = wt_ptr[i], w1 = wt_ptr[i + 1];
+    float acc[IT][kCtR];
+#pragma unroll
+    for (int it = 0; it < IT; ++it)
+#pragma unroll
+        for (int r = 0; r < kCtR; ++r) acc[it][r] = 0.0f;
+    for (int cm = 0; cm < mch; ++cm) {
+        const int co = g * mch + cm;
+        for (int wi = w0; wi < w1; ++wi) {
+            const DevWindow wd = wt[wi];   // wd.lat is the output row j
+            const TG* grow = gy + (((size_t)b * Co + co) * nlat_out + wd.lat) * nlon_out;
+            __syncthreads();   // the previous window's row and taps are used
+            for (int m = tid; m < GXN; m += kThreads)
+                gxs[m] = load_f(grow, (size_t)((unsigned)(m + 2 * nlon_out - off) %
+                                               (unsigned)nlon_out));
+            if (tid < K) wk[tid] = load_f(w, (size_t)co * K + tid);
+            __syncthreads();
+            const float* v = vals + (size_t)wd.val_off * KP;
+            for (int e = tid; e < S * UWP; e += kThreads) {
+                const int p = e / UWP, u = e - p * UWP;
+                const int t = S * u + p;
+                float a = 0.0f;
+                if (t < wd.width)
+                    for (int k = 0; k < K; ++k) a = fmaf(wk[k], v[(size_t)t * KP + k], a);
+                fs[e] = a;
+            }
+            __syncthreads();
+            const int c = wd.p_lo / S, e0 = wd.p_lo - c * S;
+#pragma unroll
+            for (int it = 0; it < IT; ++it) {
+                const int item = tid + it * kThreads;
+                if (item >= S * NB) continue;
+                const int P = item / NB, A0 = (item - P * NB) * kCtR;
+                const int p = P >= e0 ? P - e0 : P - e0 + S;
+                int a0 = A0 - c - (P >= e0 ? 0 : 1);
+                a0 %= nlon_out;
+                if (a0 < 0) a0 += nlon_out;
+                // taps of parity p in the window: u < up
+                const int up = wd.width > p ? (wd.width - p + S - 1) / S : 0;
+                const float* fp = fs + p * UWP;
+                for (int u0 = 0; u0 < up; u0 += kCtR) {
+                    float fv[kCtR];
+#pragma unroll
+                    for (int q = 0; q < kCtR / 4; ++q) {
+                        const float4 x4 = *reinterpret_cast<const float4*>(fp + u0 + 4 * q);
+                        fv[4 * q] = x4.x;
+                        fv[4 * q + 1] = x4.y;
+                        fv[4 * q + 2] = x4.z;
+                        fv[4 * q + 3] = x4.w;
+                    }
+                    // gv[k] = gy[(a0 - u0 - 7 + k) mod nlon_out], k < 15
+                    const float* gb = gxs + (a0 + off - u0 - (kCtR - 1));
+                    float gv[2 * kCtR - 1];
+#pragma unroll
+                    for (int k = 0; k < 2 * kCtR - 1; ++k) gv[k] = gb[k];
+#pragma unroll
+                    for (int uu = 0; uu < kCtR; ++uu)
+#pragma unroll
+                        for (int r = 0; r < kCtR; ++r)
+                            acc[it][r] = fmaf(fv[uu], gv[r - uu + kCtR - 1], acc[it][r]);
+                }
+            }
+        }
+    }
+    TO* out = gx + (((size_t)b * groups + g) * nlat_in + i) * nlon_in;
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+        const int item = tid + it * kThreads;
+        if (item >= S * NB) continue;
+        const int P = item / NB, A0 = (item - P * NB) * kCtR;
+#pragma unroll
+        for (int r = 0; r < kCtR; ++r)
+            if (A0 + r < nlon_out) store_f(out, (size_t)S * (A0 + r) + P, acc[it][r]);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // grad_w partial sums on the matrix cores, for a bf16 gy and one group: a
 // 128 x 128 tile of [co][kappa] over one chunk of points; four waves of
@@ -923,9 +1026,72 @@ int contract_t_folded_o(const disco_psi* psi, const void* gy, const void* w, voi
                : contract_t_folded_t<TG, TW, bf16_t>(psi, gy, w, gx, B, Co, groups, st);
 }
 
+// The register-tiled form: returns 0 when the layer is not one it takes
+// (stride 1 or 2 with nlon_in = S nlon_out, at most two items per thread, the
+// LDS within 64 KiB), else 1 with *rc the result.
+template <typename TG, typename TW, typename TO>
+int contract_t_folded_tiled_t(const disco_psi* psi, const void* gy, const void* w, void* gx, int B,
+                              int Co, int groups, hipStream_t st, int* rc) {
+    const HostPsi& h = psi->host;
+    const DevPsi& d = psi->dev;
+    const disco_psi_desc& D = h.desc;
+    const int S = h.stride;
+    if ((S != 1 && S != 2) || D.nlon_in != S * D.nlon_out || d.max_width < 1 ||
+        D.nlon_out < kCtR)
+        return 0;
+    const int NB = (D.nlon_out + kCtR - 1) / kCtR;
+    const int IT = (S * NB + kThreads - 1) / kThreads;
+    if (IT > 2) return 0;
+    // gy indices a0 + off - u0 - 7 + k: a0 < nlon_out, u0 < UWP, k < 15
+    const int UWP = ((d.max_width + S - 1) / S + kCtR - 1) / kCtR * kCtR;
+    const int GXN = (2 * D.nlon_out + 2 * kCtR + 3) / 4 * 4;
+    if (UWP > D.nlon_out + kCtR) return 0;
+    const size_t lds = ((size_t)GXN + (size_t)S * UWP + h.K) * sizeof(float);
+    if (lds > 64 * 1024) return 0;
+    dim3 grid(D.nlat_in, groups, B);
+#define DISCO_CTT(SS, II)                                                                       \
+    hipLaunchKernelGGL((contract_t_folded_tiled<TG, TW, TO, SS, II>), grid, dim3(kThreads), lds, \
+                       st, (const TG*)gy, (const TW*)w, (TO*)gx, d.wint_ptr, d.wins_t, d.vals,   \
+                       Co, groups, h.K, d.KP, D.nlat_in, D.nlon_in, D.nlat_out, D.nlon_out, GXN, \
+                       UWP)
+    {
+        KernelTimer timer("contract_transpose_folded_tiled", st);
+        if (S == 1 && IT == 1) DISCO_CTT(1, 1);
+        else if (S == 1) DISCO_CTT(1, 2);
+        else if (IT == 1) DISCO_CTT(2, 1);
+        else DISCO_CTT(2, 2);
+    }
+#undef DISCO_CTT
+    *rc = check("contract_transpose_folded_tiled");
+    return 1;
+}
+
+template <typename TG, typename TW>
+int contract_t_folded_tiled_o(const disco_psi* psi, const void* gy, const void* w, void* gx,
+                              int gx_dtype, int B, int Co, int groups, hipStream_t st, int* rc) {
+    return gx_dtype == DISCO_F32
+               ? contract_t_folded_tiled_t<TG, TW, float>(psi, gy, w, gx, B, Co, groups, st, rc)
+               : contract_t_folded_tiled_t<TG, TW, bf16_t>(psi, gy, w, gx, B, Co, groups, st, rc);
+}
+
 int contract_t_folded(const disco_psi* psi, const void* gy, int gy_dtype, const void* w,
                       int w_dtype, void* gx, int gx_dtype, int B, int Co, int groups,
                       hipStream_t st) {
+    int trc = DISCO_OK;
+    int took;
+    if (gy_dtype == DISCO_F32)
+        took = w_dtype == DISCO_F32
+                   ? contract_t_folded_tiled_o<float, float>(psi, gy, w, gx, gx_dtype, B, Co,
+                                                             groups, st, &trc)
+                   : contract_t_folded_tiled_o<float, bf16_t>(psi, gy, w, gx, gx_dtype, B, Co,
+                                                              groups, st, &trc);
+    else
+        took = w_dtype == DISCO_F32
+                   ? contract_t_folded_tiled_o<bf16_t, float>(psi, gy, w, gx, gx_dtype, B, Co,
+                                                              groups, st, &trc)
+                   : contract_t_folded_tiled_o<bf16_t, bf16_t>(psi, gy, w, gx, gx_dtype, B, Co,
+                                                               groups, st, &trc);
+    if (took) return trc;
     if (gy_dtype == DISCO_F32)
         return w_dtype == DISCO_F32
                    ? contract_t_folded_o<float, float>(psi, gy, w, gx, gx_dtype, B, Co, groups, st)

@@ -171,6 +171,9 @@ def test_fused_backward(sdc, wl):
     if wl.Ci // wl.groups == 1:
         # one input channel per group: grad_w straight from x and gy, no X_K
         assert "grad_w_depthwise" in ran and "contract_kernel" not in ran, ran
+        # stride 1 or 2 with nlon_in = s nlon_out: grad_x on the register-tiled
+        # folded kernel
+        assert "contract_transpose_folded_tiled" in ran, ran
     e_x = rel_l2(gx.cpu().numpy(), gx_ref)
     e_w = rel_l2(gw.cpu().numpy(), gw_ref)
     e_b = rel_l2(gb.cpu().numpy(), gy.astype(np.float64).sum(axis=(0, 2, 3)))

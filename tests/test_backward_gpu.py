@@ -61,6 +61,12 @@ CASES = [
     W("k1_f32", 1, 2, 2, 1, 9, 16, 9, 16, (1,), 0.7, "f32"),
     W("c4_like_bf16", 1, 64, 64, 1, 61, 120, 61, 120, (3, 3), 4 * math.pi / 60, "bf16"),
     W("s2_bf16", 1, 32, 16, 1, 73, 144, 37, 72, (3, 3), 4 * math.pi / 36, "bf16"),
+    # one input channel per group in bf16 (the folded grad_x and the X_K-free
+    # grad_w on bf16 operands)
+    W("depthwise_bf16", 1, 8, 8, 8, 33, 64, 17, 32, (5, 4), 6 * math.pi / 16, "bf16"),
+    # 2304 longitudes at stride 1: the register-tiled grad_x takes two items
+    # per thread, and polar windows span the whole ring
+    W("depthwise_wide_s1_f32", 1, 2, 2, 2, 9, 2304, 9, 2304, (3,), 0.5, "f32"),
 ]
 
 
